@@ -1,0 +1,140 @@
+"""Seeded synthetic inputs for the chunked gated delta rule.
+
+This module is shared by the oracle-side tests and the GPU-side tests and
+benchmark.  It holds none of the method's arithmetic: it only draws random
+tensors and applies the gating law that produces the g and beta inputs
+(g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b), in float32, as the
+fused gating kernel on the page "[Qwen3.5][Feature] support fla triton kernel
+for qwen3.5" (FastDeploy PR #7024), section "Usage or Command", item 5,
+defines them).
+
+Draw order (one torch.Generator, seeded): [sequence lengths], q, k, v, a, b,
+A_log, dt_bias, initial_state.  q/k/v are drawn in float32 and rounded to
+bfloat16 (round to nearest even); the float32 check mode uses those same
+bf16-representable values stored as float32, so one oracle run serves both.
+"N(0, s)" below means standard deviation s.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int                 # per-sequence length (equal-length) or 0 for varlen
+    H: int
+    HV: int
+    K: int
+    V: int
+    use_l2norm: bool = True
+    scale: Optional[float] = None          # None -> 1/sqrt(K)
+    a_log_hi: float = math.log(16.0)      # A_log ~ U(0, a_log_hi)
+    b_std: float = 1.0                     # b ~ N(0, b_std)
+    qk_std: float = 1.0                    # q, k ~ N(0, qk_std)
+    init: str = "none"                     # "none" | "all" | "odd"
+    init_std: float = 0.05
+    n_seqs: int = 0                        # varlen: number of sequences
+    max_len: int = 0                       # varlen: lengths ~ U{min_len..max_len}
+    min_len: int = 1
+    lengths: Optional[tuple] = None        # varlen: explicit lengths (overrides the draw)
+
+    @property
+    def varlen(self) -> bool:
+        return self.n_seqs > 0
+
+    @property
+    def eff_scale(self) -> float:
+        return self.scale if self.scale is not None else self.K ** -0.5
+
+
+# The five workloads the throughput metric and the parity suite are quoted on.
+WORKLOADS = {
+    # Tiny check: B=1, T=256, H=HV=2, K=V=64, L2 norm on, no initial state.
+    "tiny": Workload("tiny", B=1, T=256, H=2, HV=2, K=64, V=64),
+    # Equal-length GVA prefill: B=4, T=4096, H=16, HV=32, K=V=128, initial state.
+    "gva": Workload("gva", B=4, T=4096, H=16, HV=32, K=128, V=128, init="all"),
+    # Varlen packed prefill: 64 sequences, lengths ~ U{1..2048}, initial state on odd ones.
+    "varlen": Workload("varlen", B=1, T=0, H=16, HV=32, K=128, V=128, init="odd",
+                       n_seqs=64, max_len=2048),
+    # Long-context single sequence: T=131072, slow decay A_log ~ U(0, ln 4).
+    "long": Workload("long", B=1, T=131072, H=16, HV=32, K=128, V=128,
+                     a_log_hi=math.log(4.0)),
+    # Wide large-batch prefill: B=16, T=16384, H=32, HV=64, no L2 norm,
+    # scale 1/sqrt(128), b ~ N(0, 2), initial state.
+    "wide": Workload("wide", B=16, T=16384, H=32, HV=64, K=128, V=128, use_l2norm=False,
+                     scale=128 ** -0.5, b_std=2.0, init="all"),
+}
+
+# The wide workload as literally specified diverges (no L2 norm with q,k ~ N(0,1)
+# at K=128 gives |k|^2 ~ 128, so the erase factor 1 - beta*|k|^2 is ~ -100).
+# Its parity counterpart keeps every shape, flag, scale and gate law but draws
+# q, k ~ N(0, 1/sqrt(K)), i.e. |k|^2 ~ 1.
+WORKLOADS["wide_stable"] = dataclasses.replace(WORKLOADS["wide"], name="wide_stable",
+                                               qk_std=128 ** -0.5)
+
+
+def scaled(w: Workload, name: str, **kw) -> Workload:
+    """A smaller variant of a workload with the same distributions."""
+    return dataclasses.replace(w, name=name, **kw)
+
+
+def make_inputs(w: Workload, seed: int = 0, device="cpu", io_dtype=torch.bfloat16):
+    """Draws one batch of inputs for workload ``w``.
+
+    Returns a dict with q, k [B,T,H,K] and v [B,T,HV,V] in ``io_dtype``
+    (bf16 values; float32 holds the same values), g, beta [B,T,HV] float32,
+    initial_state [N,HV,K,V] float32 or None, cu_seqlens [N+1] int32 or None,
+    scale, use_l2norm, and the sequence lengths as a Python list.
+    """
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    f32 = torch.float32
+    if w.varlen:
+        if w.lengths is not None:
+            lens = list(w.lengths)
+        else:
+            lens = torch.randint(w.min_len, w.max_len + 1, (w.n_seqs,), generator=gen,
+                                 device=dev).tolist()
+        N = len(lens)
+        B, T = 1, int(sum(lens))
+        cu = torch.zeros(N + 1, dtype=torch.int32)
+        if N:
+            cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+        cu = cu.to(dev)
+    else:
+        N, B, T = w.B, w.B, w.T
+        lens = [T] * B
+        cu = None
+    H, HV, K, V = w.H, w.HV, w.K, w.V
+
+    def randn(*shape, std=1.0):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=f32) * std
+
+    def io(x):
+        return x.to(torch.bfloat16).to(io_dtype)
+
+    q = io(randn(B, T, H, K, std=w.qk_std))
+    k = io(randn(B, T, H, K, std=w.qk_std))
+    v = io(randn(B, T, HV, V))
+    a = randn(B, T, HV)
+    b = randn(B, T, HV, std=w.b_std)
+    a_log = torch.rand(HV, generator=gen, device=dev, dtype=f32) * w.a_log_hi
+    dt_bias = torch.rand(HV, generator=gen, device=dev, dtype=f32)
+    g = -torch.exp(a_log) * torch.nn.functional.softplus(a + dt_bias)
+    beta = torch.sigmoid(b)
+    if w.init == "none":
+        s0 = None
+    else:
+        s0 = randn(N, HV, K, V, std=w.init_std)
+        if w.init == "odd":
+            s0[0::2] = 0.0
+    return dict(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), initial_state=s0,
+                cu_seqlens=cu, scale=w.eff_scale, use_l2norm=w.use_l2norm, lens=lens,
+                N=N, workload=w)
