@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked gated delta rule forward pass on one MI355X.
+
+One step = one full forward pass (every kernel of the path) over one batch of
+seeded synthetic inputs already resident in HBM.  Default workload: the
+equal-length GVA prefill, B=4, T=4096, H=16 key heads, HV=32 value heads,
+K=V=128, bf16, in-kernel L2 norm, fp32 initial and final state.
+
+Prints one JSON line: tokens/s, the roofline position of the dominant kernel
+(timed live with HIP events through the library's timing hook), the whole-path
+roofline, and the fp64 oracle timed on this host's cores on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gva")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--cpu-units", type=int, default=0, help="oracle units for the CPU baseline (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def chunk_count(lens):
+    return sum((L + 63) // 64 for L in lens)
+
+
+def kernel_bytes(w, x, eb):
+    """Algorithmic bytes of each kernel: what it must read and write, once."""
+    T_tot = sum(x["lens"])
+    N, H, HV, K, V = x["N"], w.H, w.HV, w.K, w.V
+    nrec = chunk_count(x["lens"]) * HV
+    rec_bytes = nrec * ((3 * 64 * K + 64 * V + 64 * 64) * eb + 4)
+    q_k = 2 * T_tot * H * K * eb
+    v = T_tot * HV * V * eb
+    gb = 2 * T_tot * HV * 4
+    o = T_tot * HV * V * eb
+    s_in = N * HV * K * V * 4 if x["initial_state"] is not None else 0
+    s_out = N * HV * K * V * 4
+    return {
+        "prep_kernel": q_k + v + gb + rec_bytes,
+        "scan_kernel": rec_bytes + s_in + o + s_out,
+        "chunk_index_kernel": 4 * (2 * (N + 1) + chunk_count(x["lens"])),
+        "path": q_k + v + gb + o + s_in + s_out,
+    }
+
+
+def path_flops(w, x):
+    """Algorithmic flops of the method per forward pass: per token and value
+    head 6KV (W.h, K^T.V_new, Q.h) + C(3K + 2V) (the causal intra-chunk
+    products K.K^T, Q.K^T, the W recompute, U and P.V_new), C = 64."""
+    T_tot = sum(x["lens"])
+    return T_tot * w.HV * (6 * w.K * w.V + 64 * (3 * w.K + 2 * w.V))
+
+
+def cpu_baseline(x, units_wanted):
+    import numpy as np
+    import oracle
+    w = x["workload"]
+    N, HV = x["N"], w.HV
+    ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    U = units_wanted or min(N * HV, max(4 * ncpu, 16))
+    units = np.unique(np.linspace(0, N * HV - 1, U).round().astype(np.int64))
+    threads = int(min(ncpu, len(units)))
+    cpu = lambda t: None if t is None else t.cpu()
+    args = [cpu(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    s0 = cpu(x["initial_state"])
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.recurrent(*args, scale=x["scale"], use_l2norm=x["use_l2norm"], initial_state=s0, cu_seqlens=cu,
+                     units=units, nthreads=threads)
+    dt = time.perf_counter() - t0
+    lens = x["lens"]
+    unit_tokens = sum(lens[int(u) // HV] for u in units)
+    return {"value": unit_tokens / HV / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(units)} of {N * HV} (sequence, value head) units of the same inputs "
+                      f"({unit_tokens} unit-tokens, fp64 token recurrence, {dt:.2f} s wall)",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_chunked_delta_amd as gdn
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dtype = torch.bfloat16 if args.dtype == "bf16" else torch.float32
+    eb = 2 if args.dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
+    x = make_inputs(w, seed=0, device=dev, io_dtype=dtype)
+    B, T = x["q"].shape[0], x["q"].shape[1]
+    N = x["N"]
+    shape = gdn.make_shape(B, T, w.H, w.HV, w.K, w.V, N, gdn.GDN_BF16 if eb == 2 else gdn.GDN_F32)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, w.HV, w.V), dtype=dtype, device=dev)
+    fin = torch.empty((N, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step():
+        st = gdn.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["use_l2norm"],
+                               x["initial_state"], x["cu_seqlens"], out, fin, shape, ws, stream=stream)
+        if st != 0:
+            raise gdn.GdnError(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gdn.gdn_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = gdn.gdn_profile_read()
+    gdn.gdn_profile_enable(False)
+
+    tokens = sum(x["lens"])
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = tokens / (ms / 1e3)
+    kb = kernel_bytes(w, x, eb)
+    kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in prof.items() if n}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    dom_us = kernels[dom]["avg_us"]
+    ach = kb[dom] / (dom_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(dom_us, 2)}
+    path_us = sum(v["avg_us"] for v in kernels.values())
+    flops = path_flops(w, x)
+    path = {"algorithmic_bytes": kb["path"], "algorithmic_flops": flops, "kernel_us": round(path_us, 2),
+            "hbm_frac": round(kb["path"] / (path_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(flops / (path_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[args.dtype], 4),
+            "roofline_tokens_per_s": round(tokens / max(kb["path"] / (HBM_PEAK_GBS * 1e9),
+                                                         flops / (MFMA_PEAK_TFLOPS[args.dtype] * 1e12)))}
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={B} T={T} N={N} H={w.H} HV={w.HV} K={w.K} V={w.V} "
+                               f"l2norm={w.use_l2norm} initial_state={w.init}",
+                   "tokens": tokens, "global_batch": N, "seq_len": T if N == B else None,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "path": path,
+        "kernels": {k: {kk: round(vv, 2) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(x, args.cpu_units)
+        cb.pop("seconds")
+        cb["value"] = round(cb["value"], 1)
+        res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,15 @@
+"""MI355X-native chunked gated delta rule forward pass (GDN prefill).
+
+The compute path is the C-ABI library ``libgdn.so`` (hand-written HIP kernels
+for gfx950, declared in ``include/gdn.h``); this package only marshals
+arguments to it.
+"""
+from ._binding import (EXPORTED, GDN_BF16, GDN_F32, GDN_OK, LIB_PATH, GdnError, chunk_gated_delta_rule,
+                       gdn_chunk_fwd, gdn_chunk_fwd_workspace_bytes, gdn_profile_enable,
+                       gdn_profile_read, gdn_shape, gdn_status_str, load_library,
+                       make_shape)
+
+__all__ = ["EXPORTED", "GDN_BF16", "GDN_F32", "GDN_OK", "LIB_PATH", "GdnError", "chunk_gated_delta_rule",
+           "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_profile_enable",
+           "gdn_profile_read", "gdn_shape", "gdn_status_str", "load_library",
+           "make_shape"]

@@ -1,0 +1,181 @@
+"""ctypes binding of the C ABI in include/gdn.h.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of libgdn.so.  There is no CPU path; if the library is missing or the
+tensors are not on a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK = 0
+GDN_BF16 = 0
+GDN_F32 = 1
+EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_profile_enable", "gdn_profile_read",
+            "gdn_status_str")
+
+_DTYPES = {torch.bfloat16: GDN_BF16, torch.float32: GDN_F32}
+
+
+class gdn_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class GdnError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(gdn_status_str(status))
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libgdn.so (once) and declares the exported signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
+                           "(or python gated_deltanet_chunked_delta_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.gdn_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(gdn_shape)]
+    lib.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P, P,
+                                  ctypes.POINTER(gdn_shape), P, ctypes.c_size_t, P]
+    lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_profile_enable.argtypes = [ctypes.c_int]
+    lib.gdn_profile_enable.restype = ctypes.c_int
+    lib.gdn_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.gdn_profile_read.restype = ctypes.c_int
+    lib.gdn_status_str.argtypes = [ctypes.c_int]
+    lib.gdn_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def gdn_status_str(status: int) -> str:
+    return load_library().gdn_status_str(int(status)).decode()
+
+
+def gdn_profile_enable(enable: bool) -> int:
+    """Starts (True) or stops (False) event timing of the library's kernels;
+    either way the accumulated totals are cleared."""
+    return int(load_library().gdn_profile_enable(int(bool(enable))))
+
+
+def gdn_profile_read():
+    """Returns {kernel name: (total ms, launches)} accumulated since enabling
+    (synchronises on the recorded events)."""
+    lib = load_library()
+    n = 8
+    names = (ctypes.c_char_p * n)()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    k = lib.gdn_profile_read(n, names, ms, cnt)
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(min(k, n))}
+
+
+def make_shape(B, T, H, HV, K, V, N, dtype) -> gdn_shape:
+    return gdn_shape(int(B), int(T), int(H), int(HV), int(K), int(V), int(N), int(dtype))
+
+
+def gdn_chunk_fwd_workspace_bytes(shape: gdn_shape) -> int:
+    return int(load_library().gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, scale, use_l2norm, initial_state, cu_seqlens, out, final_state,
+                  shape: gdn_shape, workspace, workspace_bytes=None, stream=None) -> int:
+    """Direct call of the C entry point with tensors as device buffers.
+
+    Returns the status code (0 = GDN_OK); does not raise on a bad status.
+    ``stream`` is a raw hipStream_t handle (int) or None for torch's current
+    stream on q's device.
+    """
+    lib = load_library()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return int(lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                                 int(bool(use_l2norm)), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
+                                 _ptr(final_state), ctypes.byref(shape), _ptr(workspace),
+                                 int(workspace_bytes), ctypes.c_void_p(int(stream))))
+
+
+def _check(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+                           cu_seqlens=None, use_qk_l2norm_in_kernel=False, workspace=None, out=None,
+                           final_state=None):
+    """Forward chunked gated delta rule on the GPU.
+
+    q, k [B,T,H,K] and v [B,T,HV,V] (bf16, or fp32 for the check mode);
+    g, beta [B,T,HV] fp32; initial_state [N,HV,K,V] fp32 or None;
+    cu_seqlens [N+1] int32 on the device or None.  Returns
+    ``(o [B,T,HV,V], final_state [N,HV,K,V] fp32 or None)``.  ``scale=None``
+    means 1/sqrt(K).  Optional preallocated ``workspace`` (uint8),
+    ``out`` and ``final_state`` are used as given.
+    """
+    _check(q.dim() == 4 and k.shape == q.shape, "q and k must be [B,T,H,K] of equal shape")
+    B, T, H, K = q.shape
+    _check(v.dim() == 4 and v.shape[:2] == (B, T), "v must be [B,T,HV,V]")
+    HV, V = v.shape[2], v.shape[3]
+    _check(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype,
+           "q, k, v must share one dtype (bfloat16 or float32)")
+    _check(tuple(g.shape) == (B, T, HV) and g.dtype == torch.float32, "g must be float32 [B,T,HV]")
+    _check(tuple(beta.shape) == (B, T, HV) and beta.dtype == torch.float32, "beta must be float32 [B,T,HV]")
+    _check(q.is_cuda, "tensors must be on a GPU device (there is no CPU path)")
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state),
+                    ("cu_seqlens", cu_seqlens)):
+        _check(t is None or t.device == q.device, f"{name} must be on {q.device}")
+    if cu_seqlens is not None:
+        _check(B == 1, "cu_seqlens requires B == 1")
+        _check(cu_seqlens.dim() == 1 and cu_seqlens.dtype == torch.int32, "cu_seqlens must be int32 [N+1]")
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _check(tuple(initial_state.shape) == (N, HV, K, V) and initial_state.dtype == torch.float32,
+               f"initial_state must be float32 [{N},{HV},{K},{V}]")
+    if scale is None:
+        scale = K ** -0.5
+    q, k, v, g, beta = (t.contiguous() for t in (q, k, v, g, beta))
+    if initial_state is not None:
+        initial_state = initial_state.contiguous()
+    shape = make_shape(B, T, H, HV, K, V, N, _DTYPES[q.dtype])
+    need = gdn_chunk_fwd_workspace_bytes(shape)
+    if need == 0:
+        raise GdnError(-4 if (HV % H or K not in (64, 128) or V not in (64, 128)) else -2)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, T, HV, V), dtype=q.dtype, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=q.device)
+    if not output_final_state:
+        final_state = None
+    st = gdn_chunk_fwd(q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, initial_state, cu_seqlens, out,
+                       final_state, shape, workspace)
+    if st != GDN_OK:
+        raise GdnError(st)
+    return out, final_state

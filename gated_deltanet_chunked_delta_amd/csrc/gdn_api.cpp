@@ -1,0 +1,228 @@
+// C-ABI entry points (include/gdn.h): host-side argument checks, workspace
+// carving and the launch sequence.  Nothing here touches the device before
+// every check has passed.
+#include <limits.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+int64_t chunk_records(int B, int T, int N, bool varlen) {
+    const int64_t per_seq = ((int64_t)T + kChunk - 1) / kChunk;
+    if (!varlen) return (int64_t)B * per_seq;
+    // sum over sequences of ceil(len/64) <= floor(T/64) + N
+    return (int64_t)T / kChunk + N;
+}
+
+int elem_bytes(int dtype) { return dtype == GDN_BF16 ? 2 : dtype == GDN_F32 ? 4 : 0; }
+
+}  // namespace gdn
+
+namespace {
+
+struct Layout {
+    size_t seq_chunk_off, chunk_seq, decay, wneg, qs, kt, ut, pm, total;
+    int64_t nc_max;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_shape(const gdn_shape *s) {
+    if (!s) return GDN_ERR_NULL;
+    if (s->B < 0 || s->T < 0 || s->N < 0 || s->H <= 0 || s->HV <= 0) return GDN_ERR_SHAPE;
+    if (gdn::elem_bytes(s->dtype) == 0) return GDN_ERR_DTYPE;
+    if ((s->K != 64 && s->K != 128) || (s->V != 64 && s->V != 128)) return GDN_ERR_UNSUPPORTED;
+    if (s->HV % s->H != 0) return GDN_ERR_UNSUPPORTED;
+    // every index the kernels form from these stays in range
+    if ((int64_t)s->B * s->T > INT_MAX) return GDN_ERR_SHAPE;
+    if ((int64_t)s->N * s->HV * (s->V / 16) > INT_MAX / 2) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+
+// One layout serves both batch modes: with B == 1 the record count is the
+// larger of the two bounds.
+Layout layout_of(const gdn_shape &s) {
+    Layout L{};
+    int64_t nc = gdn::chunk_records(s.B, s.T, s.N, false);
+    if (s.B == 1) {
+        const int64_t nv = gdn::chunk_records(s.B, s.T, s.N, true);
+        if (nv > nc) nc = nv;
+    }
+    L.nc_max = nc;
+    const size_t eb = (size_t)gdn::elem_bytes(s.dtype);
+    const size_t recs = (size_t)nc * (size_t)s.HV;
+    size_t off = 0;
+    L.seq_chunk_off = off; off = align256(off + sizeof(int32_t) * ((size_t)s.N + 1));
+    L.chunk_seq = off;     off = align256(off + sizeof(int32_t) * (size_t)nc);
+    L.decay = off;         off = align256(off + sizeof(float) * recs);
+    L.wneg = off;          off = align256(off + eb * recs * 64 * (size_t)s.K);
+    L.qs = off;            off = align256(off + eb * recs * 64 * (size_t)s.K);
+    L.kt = off;            off = align256(off + eb * recs * 64 * (size_t)s.K);
+    L.ut = off;            off = align256(off + eb * recs * 64 * (size_t)s.V);
+    L.pm = off;            off = align256(off + eb * recs * 64 * 64);
+    L.total = off;
+    return L;
+}
+
+// Kernel timing hook (gdn_profile_enable / gdn_profile_read): HIP events
+// recorded on the caller's stream around each kernel of every forward pass.
+struct EventProfiler : gdn::Profiler {
+    struct Rec {
+        int kind;
+        hipEvent_t a, b;
+    };
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    std::vector<Rec> pending;
+    hipEvent_t open[gdn::kNumKernelKinds] = {};
+    double total_ms[gdn::kNumKernelKinds] = {};
+    int64_t launches[gdn::kNumKernelKinds] = {};
+
+    hipEvent_t take() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    void begin(int kind, hipStream_t st) override {
+        hipEvent_t e = take();
+        if (e) (void)hipEventRecord(e, st);
+        open[kind] = e;
+    }
+    void end(int kind, hipStream_t st) override {
+        hipEvent_t e = take();
+        if (e) (void)hipEventRecord(e, st);
+        if (open[kind] && e) pending.push_back(Rec{kind, open[kind], e});
+        open[kind] = nullptr;
+    }
+    void drain() {
+        for (const Rec &r : pending) {
+            float ms = 0.f;
+            if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+                total_ms[r.kind] += ms;
+                launches[r.kind] += 1;
+            }
+            pool.push_back(r.a);
+            pool.push_back(r.b);
+        }
+        pending.clear();
+    }
+    void reset() {
+        drain();
+        for (int i = 0; i < gdn::kNumKernelKinds; ++i) {
+            total_ms[i] = 0.0;
+            launches[i] = 0;
+        }
+    }
+};
+
+EventProfiler g_prof;
+
+}  // namespace
+
+extern "C" {
+
+int gdn_profile_enable(int enable) {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    g_prof.reset();
+    g_prof.on = enable != 0;
+    return GDN_OK;
+}
+
+int gdn_profile_read(int max_kinds, const char **names, double *total_ms, int64_t *launches) {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    g_prof.drain();
+    const int n = max_kinds < gdn::kNumKernelKinds ? max_kinds : gdn::kNumKernelKinds;
+    for (int i = 0; i < n; ++i) {
+        if (names) names[i] = gdn::kernel_name(i);
+        if (total_ms) total_ms[i] = g_prof.total_ms[i];
+        if (launches) launches[i] = g_prof.launches[i];
+    }
+    return gdn::kNumKernelKinds;
+}
+
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape) {
+    if (check_shape(shape) != GDN_OK) return 0;
+    if ((int64_t)layout_of(*shape).nc_max * shape->HV > INT_MAX) return 0;
+    return layout_of(*shape).total;
+}
+
+int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  float scale, int use_l2norm, const float *initial_state, const int32_t *cu_seqlens,
+                  void *out, float *final_state, const gdn_shape *shape, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN_OK) return st;
+    const gdn_shape &s = *shape;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen ? s.B != 1 : s.N != s.B) return GDN_ERR_SHAPE;
+    const bool any_tokens = (int64_t)s.B * s.T > 0;
+    if (any_tokens && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
+    const Layout L = layout_of(s);
+    if (L.nc_max * s.HV > INT_MAX) return GDN_ERR_SHAPE;
+    if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255u) != 0)
+        return GDN_ERR_WORKSPACE;
+
+    gdn::Params p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.initial_state = initial_state;
+    p.cu_seqlens = cu_seqlens;
+    p.out = out;
+    p.final_state = final_state;
+    p.B = s.B;
+    p.T = s.T;
+    p.H = s.H;
+    p.HV = s.HV;
+    p.K = s.K;
+    p.V = s.V;
+    p.N = s.N;
+    p.nc_max = (int)L.nc_max;
+    p.scale = scale;
+    p.use_l2norm = use_l2norm ? 1 : 0;
+    char *ws = (char *)workspace;
+    p.seq_chunk_off = (int32_t *)(ws + L.seq_chunk_off);
+    p.chunk_seq = (int32_t *)(ws + L.chunk_seq);
+    p.decay = (float *)(ws + L.decay);
+    p.wneg = ws + L.wneg;
+    p.qs = ws + L.qs;
+    p.kt = ws + L.kt;
+    p.ut = ws + L.ut;
+    p.pm = ws + L.pm;
+    hipError_t err;
+    {
+        std::lock_guard<std::mutex> lock(g_prof.mu);
+        err = gdn::launch_forward(p, s.dtype, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
+    }
+    return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+const char *gdn_status_str(int status) {
+    switch (status) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: sizes negative or inconsistent";
+        case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown dtype code";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: K/V not in {64,128} or HV % H != 0";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: a kernel launch failed";
+        default: return "unknown gdn_status";
+    }
+}
+
+}  // extern "C"

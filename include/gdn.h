@@ -1,0 +1,137 @@
+/*
+ * gdn.h -- C ABI of the chunked gated delta rule forward pass (GDN prefill)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (per sequence n and value head j, key head jk = j / (HV/H)):
+ *
+ *   S <- S0[n, j]                                   (K x V, zero if absent)
+ *   for each token t of the sequence, in order:
+ *     qh, kh = q[t, jk], k[t, jk]                   (optionally L2-normalised:
+ *                                                    x / sqrt(sum x^2 + 1e-6))
+ *     S      = exp(g[t, j]) S
+ *     S      = S + kh (beta[t, j] (v[t, j] - S^T kh))^T
+ *     out[t, j] = scale S^T qh
+ *   final_state[n, j] = S
+ *
+ * This is the gated delta rule of the Gated Delta Networks paper
+ * (arXiv:2412.06464), which the page "NPU Training Operators - GDN" cites in its
+ * section on the operator's semantics, computed with the 64-token chunked WY
+ * algorithm that the same section lists step by step and that the page
+ * "[Qwen3.5][Feature] support fla triton kernel for qwen3.5" (FastDeploy PR
+ * #7024) names as the prefill path in its Motivation section.  The argument
+ * list mirrors the prefill call in that PR's "Usage or Command" section, item 1
+ * (q, k, v, g, beta, scale, initial_state, output_final_state,
+ * use_qk_l2norm_in_kernel) plus the FlashAttention-style cu_seqlens that the
+ * NPU page's tiling section and the LightLLM page "gdn.py"
+ * (_gdn_prefill_kernel) pass for packed variable-length batches.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major memory.
+ *   - The caller owns every buffer (including the workspace).  The library
+ *     never allocates device memory, frees or keeps pointers, and never
+ *     synchronises the host (the timing hook below aside):
+ *     work is enqueued on `stream` and runs asynchronously.
+ *   - All argument checks happen on the host before anything is enqueued; on
+ *     error a negative gdn_status is returned and nothing was launched.
+ *   - Device-side preconditions (documented, not checked): cu_seqlens is
+ *     non-decreasing with cu_seqlens[0] == 0 and cu_seqlens[N] == T;
+ *     g <= 0; beta in [0, 1]; no NaN/Inf in the inputs.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = -2,       /* sizes negative or inconsistent (e.g. N != B without cu_seqlens,
+                                 B != 1 with cu_seqlens) */
+    GDN_ERR_DTYPE = -3,       /* unknown dtype code */
+    GDN_ERR_UNSUPPORTED = -4, /* K or V not in {64, 128}, or HV not a multiple of H */
+    GDN_ERR_WORKSPACE = -5,   /* workspace NULL while needed, or smaller than required */
+    GDN_ERR_LAUNCH = -6       /* the HIP runtime reported an error at launch */
+} gdn_status;
+
+/* Element type of q, k, v and out.  g, beta and both states are always fp32.
+ * GDN_F32 is a check mode: the same algorithm with fp32 operands everywhere. */
+typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* Problem sizes.
+ *   B, T  : batch rows and tokens per row of q/k/v/out ([B, T, ...]).  With
+ *           cu_seqlens, B must be 1 and T is the total packed token count.
+ *   H, HV : key/query heads and value heads; HV % H == 0, value head j uses
+ *           key head j / (HV/H) (contiguous groups).
+ *   K, V  : key and value head dimensions, each 64 or 128.
+ *   N     : number of sequences: N == B without cu_seqlens, else the length
+ *           of cu_seqlens minus one.  States are [N, HV, K, V].
+ *   dtype : gdn_dtype of q, k, v and out. */
+typedef struct gdn_shape {
+    int32_t B, T, H, HV, K, V, N;
+    int32_t dtype;
+} gdn_shape;
+
+/* Bytes of device workspace gdn_chunk_fwd needs for `shape` (0 on invalid
+ * shapes).  Depends only on the sizes and the dtype. */
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape);
+
+/* Chunked gated delta rule forward pass (prefill).
+ *
+ *   q, k          [B, T, H, K]   dtype          read
+ *   v             [B, T, HV, V]  dtype          read
+ *   g             [B, T, HV]     fp32           read; log-space forget gate (<= 0)
+ *   beta          [B, T, HV]     fp32           read; delta-rule write strength
+ *   scale         output scale (the Python binding maps None to 1/sqrt(K))
+ *   use_l2norm    non-zero: normalise every q and k row in-kernel
+ *   initial_state [N, HV, K, V]  fp32 or NULL   read; NULL = zero state, not read
+ *   cu_seqlens    [N+1] int32 or NULL           read on the device only (never
+ *                 copied to the host); NULL = B equal-length sequences of T
+ *   out           [B, T, HV, V]  dtype          written (every element)
+ *   final_state   [N, HV, K, V]  fp32 or NULL   written; NULL = not produced.
+ *                 May alias initial_state exactly (in-place state update);
+ *                 must not overlap any other argument.
+ *   shape         sizes, see gdn_shape (host pointer)
+ *   workspace     device scratch of at least gdn_chunk_fwd_workspace_bytes
+ *                 bytes (256-byte aligned); contents on entry are ignored
+ *   stream        hipStream_t to enqueue on (NULL = the default stream)
+ *
+ * `out` must not overlap any input.  Sequences of length 0 produce no rows and
+ * their final state equals their initial state (or zero).
+ * Returns GDN_OK or a negative gdn_status (see above). */
+int gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                  const float *g, const float *beta,
+                  float scale, int use_l2norm,
+                  const float *initial_state, const int32_t *cu_seqlens,
+                  void *out, float *final_state,
+                  const gdn_shape *shape, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* Kernel timing hook, for measurement.  While enabled, every gdn_chunk_fwd
+ * call records HIP events on its stream just before and just after each
+ * kernel it enqueues (events are created on first use and reused).
+ * gdn_profile_enable(1) starts recording, gdn_profile_enable(0) stops; both
+ * discard what was accumulated so far.  Returns GDN_OK. */
+int gdn_profile_enable(int enable);
+
+/* Waits for the recorded events, adds the duration of each recorded launch to
+ * its kernel's total and reports, for up to max_kinds kernels of the forward
+ * pass (in launch order): a static name, the accumulated milliseconds and the
+ * number of launches.  Any output pointer may be NULL.  Returns the number of
+ * kernel kinds the forward pass has.  Host-blocking (it synchronises on the
+ * events), so call it outside a timed region. */
+int gdn_profile_read(int max_kinds, const char **names, double *total_ms, int64_t *launches);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *gdn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

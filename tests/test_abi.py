@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/gdn.h declares, and
+reject bad arguments on the host before anything is enqueued (the argument
+pointers here are never dereferenced: every call below fails a check first).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_chunked_delta_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20   # a non-null address that is never touched
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gdn.load_library()
+    names = declared_functions()
+    assert names == sorted(gdn.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_header_compiles_as_c():
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        open(src, "w").write('#include "gdn.h"\nint main(void){gdn_shape s={0};(void)s;return 0;}\n')
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-c", src,
+                        "-o", os.path.join(d, "t.o")], check=True)
+
+
+def _call(shape, ws=FAKE, ws_bytes=1 << 40, cu=None, ptrs=FAKE):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    return lib.gdn_chunk_fwd(P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), 1.0, 1, None,
+                             None if cu is None else P(cu), P(ptrs), None,
+                             None if shape is None else ctypes.byref(shape), P(ws) if ws else None,
+                             ws_bytes, None)
+
+
+def test_workspace_size_is_monotone_and_rejects_bad_shapes():
+    s1 = gdn.make_shape(4, 4096, 16, 32, 128, 128, 4, gdn.GDN_BF16)
+    s2 = gdn.make_shape(4, 4096, 16, 32, 128, 128, 4, gdn.GDN_F32)
+    b1, b2 = gdn.gdn_chunk_fwd_workspace_bytes(s1), gdn.gdn_chunk_fwd_workspace_bytes(s2)
+    assert 0 < b1 < b2
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 16, 32, 96, 128, 4, 0)) == 0
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 3, 32, 128, 128, 4, 0)) == 0
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 16, 32, 128, 128, 4, 7)) == 0
+
+
+@pytest.mark.parametrize("shape,cu,want", [
+    (None, None, -1),                                           # no shape
+    (gdn.make_shape(4, 64, 2, 4, 128, 128, 3, 0), None, -2),    # N != B without cu_seqlens
+    (gdn.make_shape(2, 64, 2, 4, 128, 128, 2, 0), FAKE, -2),    # B != 1 with cu_seqlens
+    (gdn.make_shape(1, -1, 2, 4, 128, 128, 1, 0), None, -2),    # negative T
+    (gdn.make_shape(1, 64, 2, 4, 128, 128, 1, 5), None, -3),    # unknown dtype
+    (gdn.make_shape(1, 64, 2, 4, 96, 128, 1, 0), None, -4),     # K not supported
+    (gdn.make_shape(1, 64, 2, 4, 128, 32, 1, 0), None, -4),     # V not supported
+    (gdn.make_shape(1, 64, 3, 4, 128, 128, 1, 0), None, -4),    # HV % H != 0
+])
+def test_argument_errors(shape, cu, want):
+    assert _call(shape, cu=cu) == want
+
+
+def test_null_tensor_and_workspace_errors():
+    s = gdn.make_shape(1, 64, 2, 4, 128, 128, 1, 0)
+    assert _call(s, ptrs=0) == -1
+    assert _call(s, ws=0) == -5
+    assert _call(s, ws_bytes=16) == -5
+    assert _call(s, ws=FAKE + 16) == -5     # misaligned
+
+
+def test_status_strings():
+    for st in range(-6, 1):
+        assert gdn.gdn_status_str(st).startswith("GDN_")
+    assert gdn.gdn_status_str(-99) == "unknown gdn_status"
+
+
+def test_python_wrapper_rejects_cpu_tensors_and_bad_shapes():
+    import torch
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    v = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    g = torch.zeros(1, 8, 4)
+    with pytest.raises(ValueError):   # CPU tensors: there is no CPU path
+        gdn.chunk_gated_delta_rule(q, q, v, g, g)
+    with pytest.raises(ValueError):   # beta with H heads instead of HV
+        gdn.chunk_gated_delta_rule(q, q, v, g, torch.zeros(1, 8, 2))

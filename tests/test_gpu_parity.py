@@ -1,0 +1,197 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (max-abs error against the oracle): bf16 inputs -> 2e-2 on o and 1e-2 on
+the final state; fp32 check mode -> 1e-4 on both.  Small cases run the whole
+oracle; the full-size workloads compare sampled (sequence, value head) units,
+in the same launch configuration the benchmark times.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: (2e-2, 1e-2), torch.float32: (1e-4, 1e-4)}
+
+
+def _gdn():
+    import gated_deltanet_chunked_delta_amd as gdn
+    gdn.load_library()
+    return gdn
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(x, dtype=None, **kw):
+    gdn = _gdn()
+    dev = torch.device("cuda:0")
+    d = dtype or x["q"].dtype
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].to(dev)
+    s0 = None if x["initial_state"] is None else x["initial_state"].to(dev)
+    o, fin = gdn.chunk_gated_delta_rule(x["q"].to(dev, d), x["k"].to(dev, d), x["v"].to(dev, d),
+                                        x["g"].to(dev), x["beta"].to(dev), scale=x["scale"],
+                                        initial_state=s0, cu_seqlens=cu,
+                                        use_qk_l2norm_in_kernel=x["use_l2norm"], **kw)
+    torch.cuda.synchronize()
+    return o, fin
+
+
+def oracle_full(x):
+    return oracle.recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
+                            use_l2norm=x["use_l2norm"], initial_state=x["initial_state"],
+                            cu_seqlens=None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu().numpy())
+
+
+def check_full(x, dtype):
+    _say(f"[parity] {x['workload'].name} dtype={dtype} lens={x['lens'][:8]}")
+    o, fin = run_gpu(x, dtype)
+    o_ref, f_ref = oracle_full(x)
+    eo = float(np.abs(o.float().cpu().numpy().astype(np.float64) - o_ref).max()) if o.numel() else 0.0
+    ef = float(np.abs(fin.cpu().numpy().astype(np.float64) - f_ref).max()) if fin.numel() else 0.0
+    to, tf = TOL[dtype]
+    _say(f"    max|do|={eo:.3e} (bar {to})  max|dS|={ef:.3e} (bar {tf})")
+    assert eo <= to and ef <= tf
+    return eo, ef
+
+
+SMALL = {
+    "tiny": WORKLOADS["tiny"],
+    "gva_ragged": scaled(WORKLOADS["gva"], "gva_ragged", B=2, T=300, H=2, HV=4),
+    "varlen_mix": scaled(WORKLOADS["varlen"], "varlen_mix", H=2, HV=4,
+                         lengths=(1, 64, 65, 127, 0, 200, 3, 129)),
+    "long_slow": scaled(WORKLOADS["long"], "long_slow", T=1000, H=1, HV=2),
+    "wide_stable": scaled(WORKLOADS["wide_stable"], "wide_small", B=3, T=257, H=2, HV=4),
+    "k64_v128": scaled(WORKLOADS["gva"], "k64_v128", B=2, T=190, H=2, HV=4, K=64, V=128),
+    "k128_v64": scaled(WORKLOADS["gva"], "k128_v64", B=2, T=130, H=1, HV=3, K=128, V=64),
+}
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(name, dtype):
+    x = make_inputs(SMALL[name], seed=0, io_dtype=torch.float32)
+    check_full(x, dtype)
+
+
+def test_final_state_aliases_initial_state():
+    x = make_inputs(SMALL["gva_ragged"], seed=1, io_dtype=torch.float32)
+    gdn = _gdn()
+    dev = torch.device("cuda:0")
+    s = x["initial_state"].to(dev).clone()
+    o, fin = gdn.chunk_gated_delta_rule(x["q"].to(dev, torch.bfloat16), x["k"].to(dev, torch.bfloat16),
+                                        x["v"].to(dev, torch.bfloat16), x["g"].to(dev), x["beta"].to(dev),
+                                        scale=x["scale"], initial_state=s, final_state=s,
+                                        use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    o2, fin2 = run_gpu(x, torch.bfloat16)
+    assert fin.data_ptr() == s.data_ptr()
+    assert torch.equal(o, o2) and torch.equal(s, fin2)
+
+
+def test_no_final_state_and_no_initial_state():
+    x = make_inputs(SMALL["tiny"], seed=2, io_dtype=torch.float32)
+    o, fin = run_gpu(x, torch.bfloat16, output_final_state=False)
+    assert fin is None
+    o_ref, _ = oracle_full(x)
+    assert float(np.abs(o.float().cpu().numpy() - o_ref).max()) <= 2e-2
+
+
+def test_deterministic_bitwise():
+    x = make_inputs(SMALL["varlen_mix"], seed=3, io_dtype=torch.float32)
+    o1, f1 = run_gpu(x, torch.bfloat16)
+    o2, f2 = run_gpu(x, torch.bfloat16)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_varlen_sequences_are_isolated():
+    """NaN in one packed sequence stays inside that sequence."""
+    x = make_inputs(SMALL["varlen_mix"], seed=4, io_dtype=torch.float32)
+    cu = x["cu_seqlens"].tolist()
+    o1, f1 = run_gpu(x, torch.bfloat16)
+    bad = 5   # the 200-token sequence
+    x["v"][0, cu[bad] + 7] = float("nan")
+    o2, f2 = run_gpu(x, torch.bfloat16)
+    for n in range(len(cu) - 1):
+        s = slice(cu[n], cu[n + 1])
+        if n == bad:
+            assert torch.isnan(o2[0, cu[bad] + 7:cu[bad + 1]]).any()
+            assert torch.isnan(f2[n]).any()
+        else:
+            assert torch.equal(o1[0, s], o2[0, s]) and torch.equal(f1[n], f2[n])
+
+
+def test_outputs_fully_written():
+    x = make_inputs(SMALL["varlen_mix"], seed=5, io_dtype=torch.float32)
+    T, HV, V = x["v"].shape[1], x["v"].shape[2], x["v"].shape[3]
+    out = torch.full((1, T, HV, V), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    fin = torch.full(x["initial_state"].shape, float("nan"), device="cuda:0")
+    o, f = run_gpu(x, torch.bfloat16, out=out, final_state=fin)
+    assert not torch.isnan(o).any() and not torch.isnan(f).any()
+
+
+def test_empty_batch():
+    w = scaled(WORKLOADS["varlen"], "empty", H=2, HV=4, lengths=(0, 0, 0))
+    x = make_inputs(w, seed=6, io_dtype=torch.float32)
+    o, f = run_gpu(x, torch.bfloat16)
+    assert o.numel() == 0
+    assert torch.equal(f.cpu(), x["initial_state"])
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: sampled units, same launch configuration as the bench.
+# ---------------------------------------------------------------------------
+FULL = {"gva": (WORKLOADS["gva"], 6), "varlen": (WORKLOADS["varlen"], 6),
+        "long": (WORKLOADS["long"], 1), "wide_stable": (WORKLOADS["wide_stable"], 4)}
+
+
+def _sample_units(x, count, seed=0):
+    N, HV = x["N"], x["workload"].HV
+    rng = np.random.default_rng(seed)
+    units = {0, N * HV - 1}
+    lens = x["lens"]
+    units.add(int(np.argmax(lens)) * HV + HV // 2)
+    while len(units) < count:
+        units.add(int(rng.integers(0, N * HV)))
+    return sorted(units)[:max(count, 2)]
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_parity_full_size_sampled(name):
+    w, count = FULL[name]
+    _say(f"[parity-full] {name}: generating on the GPU")
+    x = make_inputs(w, seed=0, device="cuda:0")
+    o, fin = run_gpu(x, torch.bfloat16)
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all()
+    units = _sample_units(x, count)
+    HV = w.HV
+    G = HV // w.H
+    cu = x["cu_seqlens"]
+    starts = ([int(c) for c in cu.tolist()] if cu is not None else [n * w.T for n in range(x["N"] + 1)])
+    worst_o = worst_f = 0.0
+    for u in units:
+        n, j = divmod(u, HV)
+        t0, t1 = starts[n], starts[n + 1]
+        jk = j // G
+
+        def sl(t, head):
+            return t.reshape(-1, *t.shape[2:])[t0:t1, head:head + 1].unsqueeze(0).cpu()
+        s0 = None if x["initial_state"] is None else x["initial_state"][n:n + 1, j:j + 1].cpu()
+        o_ref, f_ref = oracle.recurrent(sl(x["q"], jk), sl(x["k"], jk), sl(x["v"], j),
+                                        sl(x["g"], j),
+                                        sl(x["beta"], j), scale=x["scale"], use_l2norm=x["use_l2norm"],
+                                        initial_state=s0, nthreads=8)
+        og = o.reshape(-1, HV, w.V)[t0:t1, j].float().cpu().numpy()
+        eo = float(np.abs(og - o_ref[0, :, 0]).max()) if t1 > t0 else 0.0
+        ef = float(np.abs(fin[n, j].cpu().numpy() - f_ref[0, 0]).max())
+        worst_o, worst_f = max(worst_o, eo), max(worst_f, ef)
+        _say(f"    unit n={n} j={j} len={t1 - t0}: max|do|={eo:.3e} max|dS|={ef:.3e}")
+    assert worst_o <= 2e-2 and worst_f <= 1e-2
