@@ -164,9 +164,7 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out
         initial_state = initial_state.contiguous()
     shape = make_shape(B, T, H, HV, K, V, N, _DTYPES[q.dtype])
     need = gdn_chunk_fwd_workspace_bytes(shape)
-    if need == 0:
-        raise GdnError(-4 if (HV % H or K not in (64, 128) or V not in (64, 128)) else -2)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, T, HV, V), dtype=q.dtype, device=q.device)

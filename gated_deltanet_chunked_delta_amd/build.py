@@ -11,8 +11,9 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = [os.path.join(PKG, "csrc", "gdn_kernels.hip"), os.path.join(PKG, "csrc", "gdn_api.cpp")]
-HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(PKG, "csrc", "gdn_internal.h")]
+SOURCES = [os.path.join(PKG, "csrc", "gdn_fused.hip"), os.path.join(PKG, "csrc", "gdn_api.cpp")]
+HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(PKG, "csrc", "gdn_internal.h"),
+           os.path.join(PKG, "csrc", "gdn_device.h")]
 
 # Packed fp32 VALU instructions are kept out of the generated code.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -14,25 +14,11 @@
 
 namespace gdn {
 
-int64_t chunk_records(int B, int T, int N, bool varlen) {
-    const int64_t per_seq = ((int64_t)T + kChunk - 1) / kChunk;
-    if (!varlen) return (int64_t)B * per_seq;
-    // sum over sequences of ceil(len/64) <= floor(T/64) + N
-    return (int64_t)T / kChunk + N;
-}
-
 int elem_bytes(int dtype) { return dtype == GDN_BF16 ? 2 : dtype == GDN_F32 ? 4 : 0; }
 
 }  // namespace gdn
 
 namespace {
-
-struct Layout {
-    size_t seq_chunk_off, chunk_seq, decay, wneg, qs, kt, ut, pm, total;
-    int64_t nc_max;
-};
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int check_shape(const gdn_shape *s) {
     if (!s) return GDN_ERR_NULL;
@@ -46,30 +32,8 @@ int check_shape(const gdn_shape *s) {
     return GDN_OK;
 }
 
-// One layout serves both batch modes: with B == 1 the record count is the
-// larger of the two bounds.
-Layout layout_of(const gdn_shape &s) {
-    Layout L{};
-    int64_t nc = gdn::chunk_records(s.B, s.T, s.N, false);
-    if (s.B == 1) {
-        const int64_t nv = gdn::chunk_records(s.B, s.T, s.N, true);
-        if (nv > nc) nc = nv;
-    }
-    L.nc_max = nc;
-    const size_t eb = (size_t)gdn::elem_bytes(s.dtype);
-    const size_t recs = (size_t)nc * (size_t)s.HV;
-    size_t off = 0;
-    L.seq_chunk_off = off; off = align256(off + sizeof(int32_t) * ((size_t)s.N + 1));
-    L.chunk_seq = off;     off = align256(off + sizeof(int32_t) * (size_t)nc);
-    L.decay = off;         off = align256(off + sizeof(float) * recs);
-    L.wneg = off;          off = align256(off + eb * recs * 64 * (size_t)s.K);
-    L.qs = off;            off = align256(off + eb * recs * 64 * (size_t)s.K);
-    L.kt = off;            off = align256(off + eb * recs * 64 * (size_t)s.K);
-    L.ut = off;            off = align256(off + eb * recs * 64 * (size_t)s.V);
-    L.pm = off;            off = align256(off + eb * recs * 64 * 64);
-    L.total = off;
-    return L;
-}
+// Workspace the forward pass needs: none for the fused kernel.
+size_t workspace_of(const gdn_shape &) { return 0; }
 
 // Kernel timing hook (gdn_profile_enable / gdn_profile_read): HIP events
 // recorded on the caller's stream around each kernel of every forward pass.
@@ -155,8 +119,7 @@ int gdn_profile_read(int max_kinds, const char **names, double *total_ms, int64_
 
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape) {
     if (check_shape(shape) != GDN_OK) return 0;
-    if ((int64_t)layout_of(*shape).nc_max * shape->HV > INT_MAX) return 0;
-    return layout_of(*shape).total;
+    return workspace_of(*shape);
 }
 
 int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
@@ -170,9 +133,8 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     if (varlen ? s.B != 1 : s.N != s.B) return GDN_ERR_SHAPE;
     const bool any_tokens = (int64_t)s.B * s.T > 0;
     if (any_tokens && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
-    const Layout L = layout_of(s);
-    if (L.nc_max * s.HV > INT_MAX) return GDN_ERR_SHAPE;
-    if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255u) != 0)
+    const size_t need = workspace_of(s);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0))
         return GDN_ERR_WORKSPACE;
 
     gdn::Params p{};
@@ -192,18 +154,8 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     p.K = s.K;
     p.V = s.V;
     p.N = s.N;
-    p.nc_max = (int)L.nc_max;
     p.scale = scale;
     p.use_l2norm = use_l2norm ? 1 : 0;
-    char *ws = (char *)workspace;
-    p.seq_chunk_off = (int32_t *)(ws + L.seq_chunk_off);
-    p.chunk_seq = (int32_t *)(ws + L.chunk_seq);
-    p.decay = (float *)(ws + L.decay);
-    p.wneg = ws + L.wneg;
-    p.qs = ws + L.qs;
-    p.kt = ws + L.kt;
-    p.ut = ws + L.ut;
-    p.pm = ws + L.pm;
     hipError_t err;
     {
         std::lock_guard<std::mutex> lock(g_prof.mu);

@@ -23,28 +23,12 @@ struct Params {
     float *final_state;              // [N, HV, K, V] or null
     // sizes
     int B, T, H, HV, K, V, N;
-    int nc_max;                      // chunk records allotted in the workspace
     float scale;
     int use_l2norm;
-    // workspace regions
-    int32_t *seq_chunk_off;          // [N+1]  (varlen) first chunk record of each sequence
-    int32_t *chunk_seq;              // [nc_max] (varlen) sequence of each chunk record
-    float *decay;                    // [nc_max, HV]     exp(gamma_last)
-    void *wneg;                      // [nc_max, HV, 64, K]  -W
-    void *qs;                        // [nc_max, HV, 64, K]  scale rho e^gamma Q
-    void *kt;                        // [nc_max, HV, K, 64]  (diag(r e^{gamma_L - gamma}) K)^T
-    void *ut;                        // [nc_max, HV, V, 64]  U^T
-    void *pm;                        // [nc_max, HV, 64, 64] gated causal scale rho r Q K^T
 };
 
-// Chunk records allotted for a problem (an upper bound of the real count).
-int64_t chunk_records(int B, int T, int N, bool varlen);
-
-// Bytes per element for a dtype code (2 = bf16, 4 = fp32), 0 if unknown.
-int elem_bytes(int dtype);
-
 // The kernels of one forward pass, for the timing hook.
-enum KernelKind { kIndexKernel = 0, kPrepKernel = 1, kScanKernel = 2, kNumKernelKinds = 3 };
+enum KernelKind { kFusedKernel = 0, kNumKernelKinds = 1 };
 const char *kernel_name(int kind);
 
 // Timing hook: when given, the launch sequence calls begin/end around each
@@ -57,5 +41,8 @@ struct Profiler {
 
 // Enqueues the whole forward pass.  Returns the HIP error of the launches.
 hipError_t launch_forward(const Params &p, int dtype, hipStream_t stream, Profiler *prof);
+
+// The fused kernel's launch (gdn_fused.hip).
+hipError_t launch_fused(const Params &p, int dtype, hipStream_t stream);
 
 }  // namespace gdn

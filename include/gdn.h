@@ -55,7 +55,7 @@ typedef enum gdn_status {
                                  B != 1 with cu_seqlens) */
     GDN_ERR_DTYPE = -3,       /* unknown dtype code */
     GDN_ERR_UNSUPPORTED = -4, /* K or V not in {64, 128}, or HV not a multiple of H */
-    GDN_ERR_WORKSPACE = -5,   /* workspace NULL while needed, or smaller than required */
+    GDN_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or too small while one is needed */
     GDN_ERR_LAUNCH = -6       /* the HIP runtime reported an error at launch */
 } gdn_status;
 
@@ -77,8 +77,9 @@ typedef struct gdn_shape {
     int32_t dtype;
 } gdn_shape;
 
-/* Bytes of device workspace gdn_chunk_fwd needs for `shape` (0 on invalid
- * shapes).  Depends only on the sizes and the dtype. */
+/* Bytes of device workspace gdn_chunk_fwd needs for `shape`; depends only on
+ * the sizes and the dtype.  0 means none is needed (workspace may then be
+ * NULL); invalid shapes also give 0, and gdn_chunk_fwd reports why. */
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape);
 
 /* Chunked gated delta rule forward pass (prefill).
@@ -98,7 +99,8 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape);
  *                 must not overlap any other argument.
  *   shape         sizes, see gdn_shape (host pointer)
  *   workspace     device scratch of at least gdn_chunk_fwd_workspace_bytes
- *                 bytes (256-byte aligned); contents on entry are ignored
+ *                 bytes (256-byte aligned; may be NULL when that is 0);
+ *                 contents on entry are ignored
  *   stream        hipStream_t to enqueue on (NULL = the default stream)
  *
  * `out` must not overlap any input.  Sequences of length 0 produce no rows and
