@@ -15,9 +15,12 @@ SOURCES = [os.path.join(PKG, "csrc", "gdn_fused.hip"), os.path.join(PKG, "csrc",
 HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(PKG, "csrc", "gdn_internal.h"),
            os.path.join(PKG, "csrc", "gdn_device.h")]
 
-# Packed fp32 VALU instructions are kept out of the generated code.
+# Packed fp32 VALU instructions are kept out of the generated code.  MFMA
+# accumulators are kept in VGPRs: the kernels consume every accumulator with
+# VALU code, and the AGPR form costs a copy in and out of each product.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def build(verbose: bool = False) -> str:

@@ -83,7 +83,7 @@ template <typename E, int K, int VW, int NB> struct FusedLds {
     E p[64][64 + PE];         // P; blocks (0,1) and (2,3) zeroed, others above unused
     E d[64][16 + PE];         // D_b row r at 16*b + r
     float adiag[4][272];      // diagonal 16x16 blocks of A, row r at 16*r (fp32)
-    float gam[64], beta[64], nk2[64], nq2[64];   // gamma, beta, |k|^2, |q|^2
+    float gam[64], beta[64], rk[64], rq[64];   // gamma, beta, L2-norm factors of k and q
     float bz[64], oq[64], kf[64];   // beta e^gamma r,  scale rho e^gamma,  r e^{gamma_L - gamma}
     float decay;                    // e^{gamma_L}
 };
@@ -104,7 +104,10 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
     static_assert(V % VW == 0 && (NW == 2 || NW == 4), "workgroup shape");
     __shared__ FusedLds<E, K, VW, NB> s;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index is uniform inside a wave; say so, so that per-wave choices
+    // compile to scalar branches instead of exec-mask juggling
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, grp = lane >> 4;
 
     // Workgroup -> (sequence n, key head jk, value head j, column slice).  Ids
@@ -245,16 +248,13 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
             }
             return f;
         };
-        f32x4 zk[CPW][4], zq[CPW][4];   // zk: Z_k (token rows); zq: (Q h)^T (value rows, token columns)
+        f32x4 zk[CPW][4];   // Z_k = K h (token rows)
         f32x4 gk[RT][4], gq[RT][4], gqq[RT];
         {
 #pragma unroll
             for (int ct = 0; ct < CPW; ++ct)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    zk[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    zq[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                for (int t = 0; t < 4; ++t) zk[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < RT; ++i) {
 #pragma unroll
@@ -264,9 +264,9 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                 }
                 gqq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll 1
+#pragma unroll
             for (int s2 = 0; s2 < KS; ++s2) {
-                // state rows 32*s2 .. 32*s2+31: B operand of K h, A operand of h^T Q^T
+                // state rows 32*s2 .. 32*s2+31: B operand of K h
                 v8 hb[CPW];
 #pragma unroll
                 for (int ct = 0; ct < CPW; ++ct)
@@ -275,19 +275,13 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                         hb[ct][e] = to_e<E>(h[ct][2 * s2][e]);
                         hb[ct][4 + e] = to_e<E>(h[ct][2 * s2 + 1][e]);
                     }
-                v8 fk[4], fq[4];
+                v8 fk[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    fk[t] = frag(kaddr, t, s2);
-                    fq[t] = frag(qaddr, t, s2);
-                }
+                for (int t = 0; t < 4; ++t) fk[t] = frag(kaddr, t, s2);
 #pragma unroll
                 for (int ct = 0; ct < CPW; ++ct)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        zk[ct][t] = mma(fk[t], hb[ct], zk[ct][t]);
-                        zq[ct][t] = mma(hb[ct], fq[t], zq[ct][t]);
-                    }
+                    for (int t = 0; t < 4; ++t) zk[ct][t] = mma(fk[t], hb[ct], zk[ct][t]);
 #pragma unroll
                 for (int i = 0; i < RT; ++i) {
                     const int itk = itk_of(i), itq = itq_of(i);
@@ -302,8 +296,8 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                 }
             }
         }
-        // squared norms from the diagonal tiles: lane (i = l16, j = 4*grp + e)
-        // holds entry (j, i); the diagonal is e = l16 - 4*grp
+        // L2-norm factors from the diagonal tiles' squared norms: lane
+        // (i = l16, j = 4*grp + e) holds entry (j, i); the diagonal is e = l16 - 4*grp
         {
             const int e = l16 - 4 * grp;
             if (e >= 0 && e < 4) {
@@ -313,20 +307,19 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
 #pragma unroll
                     for (int jt = 1; jt < 4; ++jt)
                         if (jt == itk_of(i)) dk = gk[i][jt];
-                    s.nk2[16 * itk_of(i) + l16] = dk[e];
-                    s.nq2[16 * itq_of(i) + l16] = gqq[i][e];
+                    s.rk[16 * itk_of(i) + l16] = p.use_l2norm ? rsqrtf(dk[e] + 1e-6f) : 1.f;
+                    s.rq[16 * itq_of(i) + l16] = p.use_l2norm ? rsqrtf(gqq[i][e] + 1e-6f) : 1.f;
                 }
             }
         }
         lds_barrier();
 
-        // ---- per-token factors; Gram epilogue (gate, scale, mask) ----------
-        auto rnorm = [&](float n2) { return p.use_l2norm ? 1.f / sqrtf(n2 + 1e-6f) : 1.f; };
+        // ---- per-token factors; Gram epilogue; diagonal inverses ----------
         if (wave == 0) {
-            const float gi = s.gam[lane], gl = s.gam[63], ri = rnorm(s.nk2[lane]);
+            const float gi = s.gam[lane], gl = s.gam[63], ri = s.rk[lane];
             const float egi = __expf(gi);
             s.bz[lane] = s.beta[lane] * egi * ri;
-            s.oq[lane] = p.scale * rnorm(s.nq2[lane]) * egi;
+            s.oq[lane] = p.scale * s.rq[lane] * egi;
             s.kf[lane] = ri * __expf(gl - gi);
             if (lane == 0) s.decay = __expf(gl);
         }
@@ -334,16 +327,18 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
         for (int ii = 0; ii < RT; ++ii) {
             // K K^T tiles: lane holds column i = 16*itk + l16, rows j = 16*jt + 4*grp + e
             const int itk = itk_of(ii), i = 16 * itk + l16;
-            const float gi = s.gam[i], bri = s.beta[i] * rnorm(s.nk2[i]);
+            const float gi = s.gam[i], bri = s.beta[i] * s.rk[i];
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
                 if (jt > itk) continue;
                 const int j0 = 16 * jt + 4 * grp;
-                const f32x4 gj = *(const f32x4 *)&s.gam[j0], nj = *(const f32x4 *)&s.nk2[j0];
+                const f32x4 gj = *(const f32x4 *)&s.gam[j0], rj = *(const f32x4 *)&s.rk[j0];
                 f32x4 a;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    a[e] = (i > j0 + e) ? bri * rnorm(nj[e]) * __expf(gi - gj[e]) * gk[ii][jt][e] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const float v = bri * rj[e] * __expf(gi - gj[e]) * gk[ii][jt][e];
+                    a[e] = (jt < itk || i > j0 + e) ? v : 0.f;
+                }
                 if (jt == itk) {
                     *(f32x4 *)&s.adiag[itk][16 * l16 + 4 * grp] = a;
                 } else {
@@ -358,16 +353,18 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
         for (int ii = 0; ii < RT; ++ii) {
             // Q K^T tiles: lane holds column i = 16*itq + l16, rows j
             const int itq = itq_of(ii), i = 16 * itq + l16;
-            const float gi = s.gam[i], sri = p.scale * rnorm(s.nq2[i]);
+            const float gi = s.gam[i], sri = p.scale * s.rq[i];
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
                 if (jt > itq) continue;
                 const int j0 = 16 * jt + 4 * grp;
-                const f32x4 gj = *(const f32x4 *)&s.gam[j0], nj = *(const f32x4 *)&s.nk2[j0];
+                const f32x4 gj = *(const f32x4 *)&s.gam[j0], rj = *(const f32x4 *)&s.rk[j0];
                 v4 o;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = to_e<E>((i >= j0 + e) ? sri * rnorm(nj[e]) * __expf(gi - gj[e]) * gq[ii][jt][e] : 0.f);
+                for (int e = 0; e < 4; ++e) {
+                    const float v = sri * rj[e] * __expf(gi - gj[e]) * gq[ii][jt][e];
+                    o[e] = to_e<E>((jt < itq || i >= j0 + e) ? v : 0.f);
+                }
                 *(v4 *)&s.p[i][j0] = o;
             }
         }
@@ -375,36 +372,42 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
             const int t = idx >> 8, e = idx & 255;
             s.p[32 * t + (e >> 4)][32 * t + 16 + (e & 15)] = to_e<E>(0.f);
         }
+        // Each wave inverts the diagonal blocks it just wrote (no barrier: a
+        // wave's own LDS writes are visible to its later reads).  Lane
+        // (group b, column cc); the 16 lanes of group b solve block itk for
+        // b < RT (RT = 1 or 2); rows are prefetched one step ahead.
+        {
+            const int b = grp, cc = l16;
+            if (b < RT) {
+                const float *A = s.adiag[itk_of(b)];
+                float x[16];
+                f32x4 cur[4] = {}, nxt[4] = {};
+                x[0] = (cc == 0) ? 1.f : 0.f;
+                cur[0] = *(const f32x4 *)&A[16 * 1];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) {
+                    if (r + 1 < 16) {
+#pragma unroll
+                        for (int m4 = 0; m4 < (r + 4) / 4; ++m4) nxt[m4] = *(const f32x4 *)&A[16 * (r + 1) + 4 * m4];
+                    }
+                    float acc0 = (r == cc) ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+                    for (int m = 0; m < r; ++m) {
+                        if (m & 1) acc1 -= cur[m >> 2][m & 3] * x[m];
+                        else acc0 -= cur[m >> 2][m & 3] * x[m];
+                    }
+                    x[r] = acc0 + acc1;
+#pragma unroll
+                    for (int m4 = 0; m4 < 4; ++m4) cur[m4] = nxt[m4];
+                    asm volatile("" ::: "memory");   // keep later rows' loads out of this step
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s.d[16 * itk_of(b) + r][cc] = to_e<E>(x[r]);
+            }
+        }
         lds_barrier();
 
-        // ---- diagonal inverses (wave 0); X = beta v - bz Z_k ---------------
-        if (wave == 0) {
-            const int b = grp, cc = l16;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc0 = (r == cc) ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-                for (int m4 = 0; m4 < (r + 3) / 4; ++m4) {
-                    const f32x4 a = *(const f32x4 *)&s.adiag[b][16 * r + 4 * m4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int m = 4 * m4 + e;
-                        if (m < r) {
-                            if (e & 1) acc1 -= a[e] * x[m];
-                            else acc0 -= a[e] * x[m];
-                        }
-                    }
-                }
-                x[r] = acc0 + acc1;
-                // keep the row loads of the next step from being hoisted here:
-                // hoisting all 120 entries would cost 120 registers for the
-                // whole kernel
-                asm volatile("" ::: "memory");
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s.d[16 * b + r][cc] = to_e<E>(x[r]);
-        }
+        // ---- the h-dependent chain: X, V_new, O, next h --------------------
         auto vaddr = [&](int row, int col) { return &vb[sw_off<E, VW>(row, col)]; };
 #pragma unroll
         for (int ct = 0; ct < CPW; ++ct) {
@@ -418,9 +421,6 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                 for (int e = 0; e < 4; ++e) zk[ct][ti][e] = be[e] * to_f(vv[e]) - bz[e] * zk[ct][ti][e];
             }
         }
-        lds_barrier();
-
-        // ---- the h-dependent chain: V_new, O, next h ----------------------
         const float dec = s.decay;
 #pragma unroll
         for (int ct = 0; ct < CPW; ++ct) {
@@ -455,18 +455,34 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                 }
             }
             // O^T = (Q h)^T diag(oq) + V_new^T P^T: lane holds token i = 16*ti + l16
-            // and value columns c0 + 4*grp .. +3
+            // and value columns c0 + 4*grp .. +3.  (Q h)^T = h^T Q^T uses the
+            // state fragments as the A operand and Q's as the B operand.
+            f32x4 zq[4] = {};
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+                v8 hb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hb[e] = to_e<E>(h[ct][2 * s2][e]);
+                    hb[4 + e] = to_e<E>(h[ct][2 * s2 + 1][e]);
+                }
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) zq[ti] = mma(hb, frag(qaddr, ti, s2), zq[ti]);
+            }
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 const int i = 16 * ti + l16;
-                f32x4 o = zq[ct][ti] * s.oq[i];
+                f32x4 o = zq[ti] * s.oq[i];
 #pragma unroll
                 for (int s2 = 0; s2 <= ti / 2; ++s2) o = mma(vnb[s2], ld4x2<E>(&s.p[i][32 * s2 + 4 * grp]), o);
                 if (i < L) {
                     v4 ov;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) ov[e] = to_e<E>(o[e]);
-                    *(v4 *)&og[((size_t)(t0 + i) * p.HV + j) * V + vcol0 + c0 + 4 * grp] = ov;
+                    // 4 consecutive columns: 8 (bf16) or 16 (fp32) bytes, aligned
+                    v4 *dst = (v4 *)__builtin_assume_aligned(&og[((size_t)(t0 + i) * p.HV + j) * V + vcol0 + c0 + 4 * grp],
+                                                            sizeof(v4));
+                    *dst = ov;
                 }
             }
             // h <- e^{gamma_L} h + K^T (kf V_new); K^T fragments by transpose loads
