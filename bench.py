@@ -21,6 +21,27 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
+
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a
+# 1 GiB copy; see profiles/*_hbm_traffic.md), keyed by a hash of the kernel
+# sources and build flags they were measured on.  Any change to the kernel changes
+# the hash, and the bench then reports traffic as null until it is measured again.
+MEASURED_TRAFFIC = {
+    # fused_kernel, GVA workload: FETCH 151,700 KiB x 2.000 + WRITE 139,264 KiB x 1.000
+    "a764d04c786ce8ff": {"gva": 453287936},
+}
+KERNEL_SOURCES = ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused.hip",
+                  "gated_deltanet_chunked_delta_amd/csrc/gdn_device.h",
+                  "gated_deltanet_chunked_delta_amd/csrc/gdn_internal.h",
+                  "gated_deltanet_chunked_delta_amd/build.py"]
+
+
+def kernel_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA
 
@@ -34,6 +55,9 @@ def parse():
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle units for the CPU baseline (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device-to-device copy of this many MiB "
+                         "(a reference kernel of known traffic for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -126,6 +150,15 @@ def main():
     prof = gdn.gdn_profile_read()
     gdn.gdn_profile_enable(False)
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     tokens = sum(x["lens"])
     ms = (t1 - t0) * 1e3 / args.steps
     value = tokens / (ms / 1e3)
@@ -135,9 +168,11 @@ def main():
     dom_us = kernels[dom]["avg_us"]
     # the fused kernel is the whole path: its algorithmic bytes are the path's
     ach = pb / (dom_us * 1e-6) / 1e9
+    khash = kernel_hash()
+    traffic = MEASURED_TRAFFIC.get(khash, {}).get(w.name) if args.dtype == "bf16" else None
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-            "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2)}
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2), "kernel_hash": khash}
     path_us = sum(v["avg_us"] for v in kernels.values())
     flops = path_flops(w, x)
     path = {"algorithmic_bytes": pb, "algorithmic_flops": flops, "kernel_us": round(path_us, 2),

@@ -112,6 +112,10 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// 2^x by the hardware exponential (v_exp_f32).  Tiny results may flush to
+// zero, which is the right limit for the decay factors it is used for.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Sequence offsets are read clamped to [0, T]: a malformed cu_seqlens then
 // yields wrong rows, never an access outside the token range.
 __device__ __forceinline__ int cu_at(const int32_t *cu, int n, int T) { return min(max(cu[n], 0), T); }

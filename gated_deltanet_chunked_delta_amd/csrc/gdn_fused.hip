@@ -226,7 +226,7 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                 const float y = __shfl_up(x, o);
                 if (lane >= o) x += y;
             }
-            s.gam[lane] = x;
+            s.gam[lane] = x * 1.4426950408889634f;   // gamma in log2 units: e^{a-b} = 2^{a2-b2}
             s.beta[lane] = s.bb[buf][lane];
         }
         // This wave's Gram tiles, all transposed (C[j][i]): K K^T row tiles
@@ -287,10 +287,12 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                     const int itk = itk_of(i), itq = itq_of(i);
                     // this wave's B operands, selected by address (no register indexing)
                     const v8 bk = frag(kaddr, itk, s2), bq = frag(qaddr, itq, s2);
+                    // all four column tiles, also those above the diagonal: a few
+                    // wasted products cost less than predicated accumulators
 #pragma unroll
                     for (int jt = 0; jt < 4; ++jt) {
-                        if (jt <= itk) gk[i][jt] = mma(fk[jt], bk, gk[i][jt]);
-                        if (jt <= itq) gq[i][jt] = mma(fk[jt], bq, gq[i][jt]);
+                        gk[i][jt] = mma(fk[jt], bk, gk[i][jt]);
+                        gq[i][jt] = mma(fk[jt], bq, gq[i][jt]);
                     }
                     gqq[i] = mma(bq, bq, gqq[i]);
                 }
@@ -317,11 +319,11 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
         // ---- per-token factors; Gram epilogue; diagonal inverses ----------
         if (wave == 0) {
             const float gi = s.gam[lane], gl = s.gam[63], ri = s.rk[lane];
-            const float egi = __expf(gi);
+            const float egi = fast_exp2(gi);
             s.bz[lane] = s.beta[lane] * egi * ri;
             s.oq[lane] = p.scale * s.rq[lane] * egi;
-            s.kf[lane] = ri * __expf(gl - gi);
-            if (lane == 0) s.decay = __expf(gl);
+            s.kf[lane] = ri * fast_exp2(gl - gi);
+            if (lane == 0) s.decay = fast_exp2(gl);
         }
 #pragma unroll
         for (int ii = 0; ii < RT; ++ii) {
@@ -336,7 +338,7 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                 f32x4 a;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = bri * rj[e] * __expf(gi - gj[e]) * gk[ii][jt][e];
+                    const float v = bri * rj[e] * fast_exp2(gi - gj[e]) * gk[ii][jt][e];
                     a[e] = (jt < itk || i > j0 + e) ? v : 0.f;
                 }
                 if (jt == itk) {
@@ -362,7 +364,7 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                 v4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = sri * rj[e] * __expf(gi - gj[e]) * gq[ii][jt][e];
+                    const float v = sri * rj[e] * fast_exp2(gi - gj[e]) * gq[ii][jt][e];
                     o[e] = to_e<E>((jt < itq || i >= j0 + e) ? v : 0.f);
                 }
                 *(v4 *)&s.p[i][j0] = o;
