@@ -8,8 +8,11 @@ fused gating kernel on the page "[Qwen3.5][Feature] support fla triton kernel
 for qwen3.5" (FastDeploy PR #7024), section "Usage or Command", item 5,
 defines them).
 
-Draw order (one torch.Generator, seeded): [sequence lengths], q, k, v, a, b,
-A_log, dt_bias, initial_state.  q/k/v are drawn in float32 and rounded to
+Draw order (one torch.Generator on the target device, seeded): q, k, v, a, b,
+A_log, dt_bias, initial_state; packed workloads first draw their sequence
+lengths from a separate CPU generator with the same seed.  (CPU and GPU
+generators produce different streams: a workload drawn on the GPU has the same
+shapes and lengths as on the CPU but other values.)  q/k/v are drawn in float32 and rounded to
 bfloat16 (round to nearest even); the float32 check mode uses those same
 bf16-representable values stored as float32, so one oracle run serves both.
 "N(0, s)" below means standard deviation s.
@@ -100,8 +103,11 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", io_dtype=torch.bfloat1
         if w.lengths is not None:
             lens = list(w.lengths)
         else:
-            lens = torch.randint(w.min_len, w.max_len + 1, (w.n_seqs,), generator=gen,
-                                 device=dev).tolist()
+            # lengths come from a CPU generator of their own, so that a packed
+            # workload has the same sequence lengths whichever device draws the values
+            lgen = torch.Generator()
+            lgen.manual_seed(seed)
+            lens = torch.randint(w.min_len, w.max_len + 1, (w.n_seqs,), generator=lgen).tolist()
         N = len(lens)
         B, T = 1, int(sum(lens))
         cu = torch.zeros(N + 1, dtype=torch.int32)
