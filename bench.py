@@ -31,6 +31,7 @@ MEASURED_TRAFFIC = {
     "a764d04c786ce8ff": {"gva": 453287936},
 }
 KERNEL_SOURCES = ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused.hip",
+                  "gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip",
                   "gated_deltanet_chunked_delta_amd/csrc/gdn_device.h",
                   "gated_deltanet_chunked_delta_amd/csrc/gdn_internal.h",
                   "gated_deltanet_chunked_delta_amd/build.py"]

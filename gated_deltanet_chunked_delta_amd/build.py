@@ -11,7 +11,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = [os.path.join(PKG, "csrc", "gdn_fused.hip"), os.path.join(PKG, "csrc", "gdn_api.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", "gdn_fused.hip"), os.path.join(PKG, "csrc", "gdn_fused_ws.hip"),
+           os.path.join(PKG, "csrc", "gdn_api.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(PKG, "csrc", "gdn_internal.h"),
            os.path.join(PKG, "csrc", "gdn_device.h")]
 

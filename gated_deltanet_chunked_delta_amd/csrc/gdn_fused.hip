@@ -557,7 +557,7 @@ const char *kernel_name(int kind) { return kind == kFusedKernel ? "fused_kernel"
 
 hipError_t launch_forward(const Params &p, int dtype, hipStream_t stream, Profiler *prof) {
     if (prof) prof->begin(kFusedKernel, stream);
-    const hipError_t err = launch_fused(p, dtype, stream);
+    const hipError_t err = dtype == 0 ? launch_fused_ws(p, stream) : launch_fused(p, dtype, stream);
     if (prof) prof->end(kFusedKernel, stream);
     return err;
 }

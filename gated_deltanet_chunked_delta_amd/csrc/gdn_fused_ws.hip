@@ -1,0 +1,580 @@
+// Warp-specialized fused forward pass (bf16) for gfx950.
+//
+// Same mathematics as the single-role kernel in gdn_fused.hip (the step list
+// of the page "NPU Training Operators - GDN", operator-semantics section, in
+// the chunk form written out at the top of that file), scheduled differently:
+// a workgroup has 8 waves in two roles.
+//   waves 0-3  chain waves: each owns 16 state columns and runs everything
+//              that depends on the state h: Z = K h, (Q h)^T, X, the block
+//              forward substitution for V_new, the output and the state update.
+//   waves 4-7  prep waves: everything that does not depend on h, one chunk
+//              ahead: the asynchronous copies of the raw rows, the gate cumsum,
+//              the Gram tiles and row norms, their gated epilogue, the
+//              diagonal-block inverses and the per-token factors.
+// A chain wave and a prep wave share each SIMD, so the hardware interleaves
+// the serial state chain of chunk c with the preparation of chunk c+1.
+//
+// Step c (two workgroup barriers), with n = c + 1 the chunk being prepared:
+//   A(c)  prep:  issue the copies of chunk c+2; gate cumsum, Gram tiles and
+//                row norms of chunk n
+//         chain: V_new, output rows and the next state for chunk c
+//   B(c)  prep:  Gram epilogue (-A, P), diagonal inverses D_b and per-token
+//                factors of chunk n; wait for its own copies of chunk c+2
+//         chain: Z, (Q h)^T and X of chunk n
+// Buffers: raw k rows in a ring of three chunks (the chain reads chunk c's K
+// in A(c) while chunk c+2 streams in), raw q/v/g/beta and the prep outputs
+// double-buffered by chunk parity.
+//
+// Rows past the end of a sequence are copies of its last row; the cumsum wave
+// reads their g and beta as 0, which makes their rows of A, X and V_new zero
+// and leaves gamma_L at the last real token, so they contribute nothing.
+#include "gdn_device.h"
+
+namespace gdn {
+namespace {
+
+using namespace dev;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous global -> LDS copies: lane l's bytes land at lds + l * size.
+// They are issued from inline assembly on purpose: the compiler does not track
+// them, so it neither waits for them before unrelated LDS reads nor at the
+// LDS fences of the barriers.  The code that consumes a copy waits for it
+// explicitly (wait_vmem, then a barrier).  Vector memory counters retire in
+// order, so the compiler's own counter waits stay correct (at worst they wait
+// longer).
+__device__ __forceinline__ unsigned lds_base(void *lds) {
+    return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void *)lds);
+}
+__device__ __forceinline__ void lds_copy16(const void *g, void *lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_base(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void *g, void *lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(lds_base(lds)) : "memory", "m0");
+}
+// Wait until this wave's vector memory operations (its copies) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4, 8 inside each row of 16 lanes (zero fill), then the running totals
+// of rows 0 and 0..1 broadcast into the later rows.
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+    x += dpp_mov<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_mov<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_mov<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_mov<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_mov<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_mov<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+template <int N> struct IC { static constexpr int value = N; };
+
+// XOR swizzle of the 16-byte segments of a row of NSEG segments.
+template <int NSEG> __device__ __forceinline__ int swz(int row) {
+    static_assert(NSEG == 8 || NSEG % 16 == 0, "row length");
+    return NSEG >= 16 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int W> __device__ __forceinline__ int sw_off(int row, int col) {
+    constexpr int NSEG = W / 8;
+    return row * W + (((col >> 3) ^ swz<NSEG>(row)) << 3) + (col & 7);
+}
+
+// Per-chunk results of the prep waves that the chain waves read.
+struct alignas(16) PrepOut {
+    bf16 alo[64][68];         // -A in the off-diagonal 16x16 blocks below the diagonal
+    bf16 p[64][72];           // P, columns in the key-slot order (see pcol); blocks (0,1), (2,3) zero
+    bf16 dt[4][16][16];       // D_b transposed: dt[b][j][i] = D_b[i][j]
+    float gam[64];            // gate cumsum, log2 units
+    float beta[64];
+    float bg[64];             // beta e^gamma
+    float oq[64];             // scale rho e^gamma
+    float kf[64];             // r e^{gamma_L - gamma}
+    float decay;              // e^{gamma_L}
+};
+
+// Column of token j in PrepOut::p.  The output product reads P as the B
+// operand of a 16x16x32 product whose lane-group g holds tokens
+// 32 s + 4 g + e and 32 s + 16 + 4 g + e (e = 0..3); storing those eight
+// columns next to each other makes each operand one 16-byte read.
+__device__ __forceinline__ constexpr int pcol(int jt, int g) {   // first column of tile jt, group g
+    return 32 * (jt >> 1) + 8 * g + 4 * (jt & 1);
+}
+
+template <int K, int VW> struct WsLds {
+    bf16 kb[3][64 * K];       // raw k rows (swizzled), ring of three chunks
+    bf16 qb[2][64 * K];       // raw q rows (swizzled)
+    bf16 vb[2][64 * VW];      // raw v rows of this slice (swizzled)
+    float gb[2][64], bb[2][64];
+    PrepOut po[2];
+    float adiag[4][16 * 20];  // prep: diagonal blocks of A, fp32, transposed (A_ij at 20 j + i)
+    float rk[64], rq[64];     // L2-norm factors of the chunk being prepared
+};
+
+// The state h (K x V per value head) is held by the chain waves as K/16 tiles
+// of 16 key rows x 16 value columns in the accumulator layout (lane: value
+// column l16, tile rows 4 grp + e).  Tile mt row r stands for key dimension
+//   kappa(mt, r) = 32 (mt / 2) + 8 (r / 4) + 4 (mt % 2) + r % 4,
+// so that the eight key dimensions a lane group contributes to one 32-wide
+// reduction step (rows 4 grp + e of tiles 2s and 2s+1) are consecutive:
+// 32 s + 8 grp + 0..7.  Raw k/q fragments are then single 16-byte LDS reads.
+// Every product that involves h (Z = K h, (Q h)^T, K^T V_new) uses the same
+// assignment, and the state is read and written through it.
+__device__ __forceinline__ constexpr int kappa(int mt, int r) {
+    return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3);
+}
+
+template <int K, int V>
+__global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
+    typedef bf16 E;
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+    constexpr int VW = 64, VEC = 8;
+    constexpr int NSK = K / VEC, NSV = VW / VEC;
+    constexpr int KT = K / 16, KS = K / 32;
+    constexpr int KROW = 2 * K, VROW = 2 * VW;   // bytes per raw row in LDS
+    static_assert(sizeof(WsLds<K, VW>) <= 160 * 1024, "LDS budget");
+    __shared__ WsLds<K, VW> s;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_chain = wave < 4;
+    const int cw = wave & 3;   // chain: column tile; prep: Gram row tile / copy share
+    const int l16 = lane & 15, grp = lane >> 4;
+
+    // Workgroup -> (sequence n, key head jk, value head j, value slice).  The
+    // workgroups of one (n, jk) share q/k through L2 and sit on one XCD.
+    const int G = p.HV / p.H;
+    constexpr int VS = V / VW;
+    const int per_group = G * VS;
+    const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+    const int member = slot % per_group;
+    const int group = (slot / per_group) * 8 + xcd;
+    if (group >= p.N * p.H) return;
+    const int n = group / p.H, jk = group % p.H;
+    const int j = jk * G + member / VS;
+    const int vcol0 = (member % VS) * VW;
+
+    int64_t tok0;
+    int len;
+    if (p.cu_seqlens) {
+        tok0 = cu_at(p.cu_seqlens, n, p.T);
+        len = max(cu_at(p.cu_seqlens, n + 1, p.T) - (int)tok0, 0);
+    } else {
+        tok0 = (int64_t)n * p.T;
+        len = p.T;
+    }
+    const int nchunks = (len + 63) / 64;
+
+    const E *__restrict__ qg = (const E *)p.q;
+    const E *__restrict__ kg = (const E *)p.k;
+    const E *__restrict__ vg = (const E *)p.v;
+    E *__restrict__ og = (E *)p.out;
+    const size_t kq_row = (size_t)p.H * K, v_row = (size_t)p.HV * V;
+
+    // ---- per-lane LDS byte offsets, fixed for the whole kernel -------------
+    // raw k/q fragment of row tile t, step s2: row 16 t + l16, key slots
+    // 32 s2 + 8 grp .. +7 (one swizzled 16-byte segment)
+    int fo[KS];
+    {
+        const int sw = swz<NSK>(l16);   // the swizzle of row 16 t + l16 does not depend on t
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) fo[s2] = l16 * KROW + (((4 * s2 + grp) ^ sw) << 4);
+    }
+    // transpose reads of K^T for state tile mt: lane (l16, grp) addresses token
+    // row r0 + 4 grp + l16/4, key dims kappa(mt, 4 (l16 % 4)) .. +3
+    int to[KT / 2];
+    {
+        const int rr = 4 * grp + (l16 >> 2), sw = swz<NSK>(rr);
+#pragma unroll
+        for (int m2 = 0; m2 < KT / 2; ++m2) to[m2] = rr * KROW + (((4 * m2 + (l16 & 3)) ^ sw) << 4);
+    }
+    // transpose read of the v tile: token row 16 ti + 4 grp + l16/4, value
+    // columns c0 + 4 (l16 % 4) .. +3 of this wave's 16 columns
+    const int c0 = 16 * cw;
+    const int vo = (4 * grp + (l16 >> 2)) * VROW +
+                   (((2 * cw + ((l16 & 3) >> 1)) ^ swz<NSV>(4 * grp + (l16 >> 2))) << 4) + 8 * (l16 & 1);
+
+    auto frag = [&](const E *buf, int t, int s2) {
+        return *(const v8 *)((const char *)buf + fo[s2] + t * 16 * KROW);
+    };
+    auto tr = [&](const void *pt) { return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)pt); };
+
+    // ---- chain state ------------------------------------------------------
+    f32x4 h[KT];
+    const size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0;
+    if (is_chain && p.initial_state) {
+        const float *__restrict__ s0 = p.initial_state + sbase;
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[mt][e] = s0[(size_t)kappa(mt, 4 * grp + e) * V + c0 + l16];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) h[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Registers carried across the barriers, shared by the two roles (the
+    // roles are exclusive, so one set serves both):
+    //   chain: cr[0..3] = X of the next chunk, C layout [token][value]
+    //          cr[4..7] = (Q h)^T of the next chunk, C layout [value][token]
+    //   prep:  cr[0..3] = K K^T tiles, cr[4..7] = Q K^T tiles of the chunk
+    //          being prepared (transposed, column tiles 0..3)
+    f32x4 cr[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cr[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 *const xz = cr, *const zq = cr + 4, *const gk = cr, *const gq = cr + 4;
+
+    // Prep: the four prep waves share chunk c's copies.
+    auto issue = [&](int c) {
+        const int64_t t0 = tok0 + 64LL * c;
+        const int last = min(64, len - 64 * c) - 1;
+        E *kd = s.kb[c % 3], *qd = s.qb[c & 1], *vd = s.vb[c & 1];
+        const E *kc = kg + (size_t)t0 * kq_row + (size_t)jk * K;
+        const E *qc = qg + (size_t)t0 * kq_row + (size_t)jk * K;
+        const E *vc = vg + (size_t)t0 * v_row + (size_t)j * V + vcol0;
+#pragma unroll
+        for (int i = 0; i < NSK / 4; ++i) {
+            const int t = cw + 4 * i;
+            const int P = 64 * t + lane, row = P / NSK, seg = (P % NSK) ^ swz<NSK>(row);
+            const unsigned off = (unsigned)min(row, last) * (unsigned)kq_row + seg * VEC;
+            lds_copy16(kc + off, kd + 64 * t * VEC);
+            lds_copy16(qc + off, qd + 64 * t * VEC);
+        }
+#pragma unroll
+        for (int i = 0; i < NSV / 4; ++i) {
+            const int t = cw + 4 * i;
+            const int P = 64 * t + lane, row = P / NSV, seg = (P % NSV) ^ swz<NSV>(row);
+            lds_copy16(vc + (unsigned)min(row, last) * (unsigned)v_row + seg * VEC, vd + 64 * t * VEC);
+        }
+        if (cw == 3) {
+            const size_t o = (size_t)(t0 + min(lane, last)) * p.HV + j;
+            lds_copy4(p.g + o, &s.gb[c & 1][0]);
+            lds_copy4(p.beta + o, &s.bb[c & 1][0]);
+        }
+    };
+
+    if (!is_chain && nchunks > 0) {
+        issue(0);
+        wait_vmem();
+    }
+    // P blocks (0,1) and (2,3) are read by the output product but never
+    // written by the epilogue: zero them once in both buffers.
+    if (is_chain) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int idx = 256 * q4 + tid, b2 = idx >> 9, blk = (idx >> 8) & 1, r = (idx >> 4) & 15, jj = idx & 15;
+            s.po[b2].p[32 * blk + r][pcol(2 * blk + 1, jj >> 2) + (jj & 3)] = (E)0.f;
+        }
+    }
+    lds_barrier();
+
+    for (int c = -1; c < nchunks; ++c) {
+        const int cn = c + 1;
+        const bool prep_next = cn < nchunks;
+        // ============================ phase A ================================
+        if (!is_chain) {
+            if (c + 2 < nchunks) issue(c + 2);
+            if (prep_next) {
+                const int pb = cn & 1;
+                const E *kb = s.kb[cn % 3], *qb = s.qb[pb];
+                // Transposed Gram tiles C[j][i]: K K^T of row tile itk = cw and
+                // Q K^T of row tile itq = 3 - cw against column tiles jt <= the
+                // row tile, and Q Q^T's diagonal tile for the norms of q.  The
+                // body is specialized per wave so that it is straight-line code.
+                auto gram = [&](auto itk_c) {
+                    constexpr int itk = decltype(itk_c)::value, itq = 3 - itk;
+                    f32x4 gqq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt) {
+                        gk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        gq[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) {
+                        v8 fk[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) fk[t] = frag(kb, t, s2);
+                        const v8 bq = frag(qb, itq, s2);
+#pragma unroll
+                        for (int jt = 0; jt < 4; ++jt) {
+                            if (jt <= itk) gk[jt] = mma(fk[jt], fk[itk], gk[jt]);
+                            if (jt <= itq) gq[jt] = mma(fk[jt], bq, gq[jt]);
+                        }
+                        gqq = mma(bq, bq, gqq);
+                    }
+                    // squared row norms from the diagonal tiles
+                    const int e = l16 - 4 * grp;
+                    if (e >= 0 && e < 4) {
+                        s.rk[16 * itk + l16] = p.use_l2norm ? rsqrtf(gk[itk][e] + 1e-6f) : 1.f;
+                        s.rq[16 * itq + l16] = p.use_l2norm ? rsqrtf(gqq[e] + 1e-6f) : 1.f;
+                    }
+                };
+                switch (cw) {
+                    case 0: gram(IC<0>()); break;
+                    case 1: gram(IC<1>()); break;
+                    case 2: gram(IC<2>()); break;
+                    default: gram(IC<3>()); break;
+                }
+            }
+        } else {
+            if (c >= 0) {
+                // chain: V_new, output and next state for chunk c
+                const PrepOut &po = s.po[c & 1];
+                const char *kb = (const char *)s.kb[c % 3];
+                const int64_t t0 = tok0 + 64LL * c;
+                const int L = min(64, len - 64 * c);
+                v4 vb16[4];
+                f32x4 vnf[4];
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi) {
+                    f32x4 rr = xz[bi];
+#pragma unroll
+                    for (int m = 0; m < bi; ++m)
+                        rr = mma_k16(*(const v4 *)&po.alo[16 * bi + l16][16 * m + 4 * grp], vb16[m], rr);
+                    v4 rbv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rbv[e] = (E)rr[e];
+                    // D_bi (row l16, columns 4 grp..+3) by a transpose read of D_bi^T
+                    const v4 dfr = tr(&po.dt[bi][4 * grp + (l16 >> 2)][4 * (l16 & 3)]);
+                    vnf[bi] = mma_k16(dfr, rbv, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vb16[bi][e] = (E)vnf[bi][e];
+                }
+                v8 vnb[2], vkb[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const f32x4 k0 = *(const f32x4 *)&po.kf[32 * s2 + 4 * grp];
+                    const f32x4 k1 = *(const f32x4 *)&po.kf[32 * s2 + 16 + 4 * grp];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        vnb[s2][e] = vb16[2 * s2][e];
+                        vnb[s2][4 + e] = vb16[2 * s2 + 1][e];
+                        vkb[s2][e] = (E)(k0[e] * vnf[2 * s2][e]);
+                        vkb[s2][4 + e] = (E)(k1[e] * vnf[2 * s2 + 1][e]);
+                    }
+                }
+                // O^T tiles [value][token]: (Q h)^T scaled per token, plus (P V_new)^T
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    const int i = 16 * ti + l16;
+                    f32x4 o = zq[ti] * po.oq[i];
+#pragma unroll
+                    for (int s2 = 0; s2 <= ti / 2; ++s2) o = mma(vnb[s2], *(const v8 *)&po.p[i][pcol(2 * s2, grp)], o);
+                    if (i < L) {
+                        v4 ov;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ov[e] = (E)o[e];
+                        E *dst = og + ((size_t)(t0 + i) * p.HV + j) * V + vcol0 + c0 + 4 * grp;
+                        *(v4 *)__builtin_assume_aligned(dst, 8) = ov;
+                    }
+                }
+                // h <- e^{gamma_L} h + K^T diag(kf) V_new, K^T by transpose loads
+                const float dec = po.decay;
+#pragma unroll
+                for (int mt = 0; mt < KT; ++mt) {
+                    f32x4 acc = h[mt] * dec;
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const char *pa = kb + to[mt >> 1] + 8 * (mt & 1) + 32 * s2 * KROW;
+                        const v4 a0 = tr(pa), a1 = tr(pa + 16 * KROW);
+                        v8 a;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            a[e] = a0[e];
+                            a[4 + e] = a1[e];
+                        }
+                        acc = mma(a, vkb[s2], acc);
+                    }
+                    h[mt] = acc;
+                }
+            }
+            if (cw == 0 && prep_next) {
+                // gate cumsum of chunk cn in log2 units, beta and beta e^gamma;
+                // rows past the end of the sequence read 0
+                const int pb = cn & 1, L = min(64, len - 64 * cn);
+                const float x = wave_inclusive_scan(lane < L ? s.gb[pb][lane] : 0.f) * 1.4426950408889634f;
+                const float b = lane < L ? s.bb[pb][lane] : 0.f;
+                s.po[pb].gam[lane] = x;
+                s.po[pb].beta[lane] = b;
+                s.po[pb].bg[lane] = b * fast_exp2(x);
+            }
+        }
+        lds_barrier();
+        // ============================ phase B ================================
+        if (!is_chain) {
+            if (prep_next) {
+                const int pb = cn & 1;
+                PrepOut &po = s.po[pb];
+                auto epilogue = [&](auto itk_c) {
+                    constexpr int itk = decltype(itk_c)::value, itq = 3 - itk;
+                    // every LDS read of the epilogue comes before its first store
+                    f32x4 gj[4], rj[4];
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt) {
+                        gj[jt] = *(const f32x4 *)&po.gam[16 * jt + 4 * grp];
+                        rj[jt] = *(const f32x4 *)&s.rk[16 * jt + 4 * grp];
+                    }
+                    const f32x4 bd = *(const f32x4 *)&po.beta[16 * itk + 4 * grp];
+                    const int ik = 16 * itk + l16, iq = 16 * itq + l16;
+                    const float gik = po.gam[ik], rik = s.rk[ik], bik = po.beta[ik];
+                    const float giq = po.gam[iq], sriq = p.scale * s.rq[iq];
+                    {   // diagonal tile of K K^T -> A_itk,itk (fp32, transposed).  The raw
+                        // Gram tile is symmetric, so the lane's values serve as rows
+                        // i = 16 itk + 4 grp + e of column j = 16 itk + l16, which makes
+                        // the transposed store one vector per lane.
+                        f32x4 a;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = bd[e] * rj[itk][e] * rik * fast_exp2(gj[itk][e] - gik) * gk[itk][e];
+                            a[e] = (4 * grp + e > l16) ? v : 0.f;
+                        }
+                        *(f32x4 *)&s.adiag[itk][20 * l16 + 4 * grp] = a;
+                    }
+                    {   // off-diagonal tiles of K K^T in row tile itk -> -A (bf16)
+                        const float bri = bik * rik;
+#pragma unroll
+                        for (int jt = 0; jt < itk; ++jt) {
+                            v4 o;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                o[e] = (E)(-(bri * rj[jt][e] * fast_exp2(gik - gj[jt][e]) * gk[jt][e]));
+                            *(v4 *)&po.alo[ik][16 * jt + 4 * grp] = o;
+                        }
+                    }
+                    {   // Q K^T row tile itq -> P
+#pragma unroll
+                        for (int jt = 0; jt <= itq; ++jt) {
+                            v4 o;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float v = sriq * rj[jt][e] * fast_exp2(giq - gj[jt][e]) * gq[jt][e];
+                                o[e] = (E)((jt < itq || iq >= 16 * jt + 4 * grp + e) ? v : 0.f);
+                            }
+                            *(v4 *)&po.p[iq][pcol(jt, grp)] = o;
+                        }
+                    }
+                };
+                switch (cw) {
+                    case 0: epilogue(IC<0>()); break;
+                    case 1: epilogue(IC<1>()); break;
+                    case 2: epilogue(IC<2>()); break;
+                    default: epilogue(IC<3>()); break;
+                }
+                // D_cw = (I + A_cw,cw)^-1 by column-oriented forward substitution,
+                // lane = column of D: once x_m is final it updates every later
+                // row, so each step has up to 15 independent updates.  Columns
+                // of A stream in a few steps ahead of their use.
+                if (grp == 0) {
+                    const float *AT = s.adiag[cw];
+                    const int cc = l16;
+                    constexpr int PF = 3;
+                    float x[16];
+                    f32x4 col[15][4];
+                    auto load_col = [&](int m) {
+#pragma unroll
+                        for (int c4 = (m + 1) / 4; c4 < 4; ++c4) col[m][c4] = *(const f32x4 *)&AT[20 * m + 4 * c4];
+                    };
+#pragma unroll
+                    for (int m = 0; m < PF; ++m) load_col(m);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+                    for (int m = 0; m < 15; ++m) {
+                        if (m + PF < 15) load_col(m + PF);
+#pragma unroll
+                        for (int r = m + 1; r < 16; ++r) x[r] -= col[m][r >> 2][r & 3] * x[m];
+                        asm volatile("" ::: "memory");
+                    }
+                    // column cc of D is row cc of D^T: two 16-byte stores
+                    v8 d0, d1;
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        d0[r] = (E)x[r];
+                        d1[r] = (E)x[8 + r];
+                    }
+                    *(v8 *)&po.dt[cw][cc][0] = d0;
+                    *(v8 *)&po.dt[cw][cc][8] = d1;
+                }
+            }
+            wait_vmem();   // this wave's copies of chunk c+2
+        } else if (prep_next) {
+            // chain: Z = K h, (Q h)^T and X of chunk cn
+            const int pb = cn & 1;
+            const E *kb = s.kb[cn % 3], *qb = s.qb[pb];
+            const char *vb = (const char *)s.vb[pb];
+            const PrepOut &po = s.po[pb];
+            f32x4 zk[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                zk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                zq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+                v8 hb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hb[e] = (E)h[2 * s2][e];
+                    hb[4 + e] = (E)h[2 * s2 + 1][e];
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    zk[t] = mma(frag(kb, t, s2), hb, zk[t]);
+                    zq[t] = mma(hb, frag(qb, t, s2), zq[t]);
+                }
+            }
+            // X = diag(beta) V - diag(beta e^gamma r) Z
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                const v4 vv = tr(vb + vo + 16 * ti * VROW);
+                const int r0 = 16 * ti + 4 * grp;
+                const f32x4 be = *(const f32x4 *)&po.beta[r0];
+                const f32x4 bg = *(const f32x4 *)&po.bg[r0];
+                const f32x4 rk = *(const f32x4 *)&s.rk[r0];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xz[ti][e] = be[e] * (float)vv[e] - (bg[e] * rk[e]) * zk[ti][e];
+            }
+            if (cw == 1) {   // per-token factors of chunk cn (lane = token)
+                PrepOut &pw = s.po[pb];
+                const float gi = pw.gam[lane], gl = pw.gam[63];
+                pw.oq[lane] = p.scale * s.rq[lane] * fast_exp2(gi);
+                pw.kf[lane] = s.rk[lane] * fast_exp2(gl - gi);
+                if (lane == 0) pw.decay = fast_exp2(gl);
+            }
+        }
+        lds_barrier();
+    }
+
+    if (is_chain && p.final_state) {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                p.final_state[sbase + (size_t)kappa(mt, 4 * grp + e) * V + c0 + l16] = h[mt][e];
+    }
+}
+
+}  // namespace
+
+// One workgroup of 512 threads per (sequence, value head, 64 value columns).
+hipError_t launch_fused_ws(const Params &p, hipStream_t st) {
+    constexpr int VW = 64;
+    const int groups = p.N * p.H;
+    if (groups == 0) return hipSuccess;
+    const int per_group = (p.HV / p.H) * (p.V / VW);
+    const unsigned grid = (unsigned)((groups + 7) / 8) * 8 * per_group;
+    if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64><<<grid, 512, 0, st>>>(p);
+    else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128><<<grid, 512, 0, st>>>(p);
+    else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64><<<grid, 512, 0, st>>>(p);
+    else fused_ws_kernel<128, 128><<<grid, 512, 0, st>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

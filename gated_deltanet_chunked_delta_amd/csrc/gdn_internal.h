@@ -42,7 +42,9 @@ struct Profiler {
 // Enqueues the whole forward pass.  Returns the HIP error of the launches.
 hipError_t launch_forward(const Params &p, int dtype, hipStream_t stream, Profiler *prof);
 
-// The fused kernel's launch (gdn_fused.hip).
+// The single-role fused kernel's launch (gdn_fused.hip).
 hipError_t launch_fused(const Params &p, int dtype, hipStream_t stream);
+// The warp-specialized bf16 kernel's launch (gdn_fused_ws.hip).
+hipError_t launch_fused_ws(const Params &p, hipStream_t stream);
 
 }  // namespace gdn
