@@ -14,18 +14,19 @@
 // A chain wave and a prep wave share each SIMD, so the hardware interleaves
 // the serial state chain of chunk c with the preparation of chunk c+1.
 //
-// Step c (two workgroup barriers), with n = c + 1 the chunk being prepared:
-//   A(c)  prep:  issue the copies of chunk c+2; gate cumsum, Gram tiles and
-//                row norms of chunk n
-//         chain: V_new, output rows and the next state for chunk c
-//   B(c)  prep:  Gram epilogue (-A, P), diagonal inverses D_b and per-token
-//                factors of chunk n; wait for its own copies of chunk c+2
-//         chain: Z, (Q h)^T and X of chunk n
-// Buffers: raw k rows in a ring of three chunks (the chain reads chunk c's K
-// in A(c) while chunk c+2 streams in), raw q/v/g/beta and the prep outputs
+// Step c ends with the only workgroup barrier of the step:
+//   prep:  issue the copies of chunk c+2; for chunk c+1: gate cumsum, Gram
+//          tiles, row norms, gated epilogue (-A, P), diagonal inverses D_b,
+//          per-token factors; wait for its own copies of chunk c+2
+//   chain: X, V_new, output rows and the next state for chunk c, then
+//          Z = K h and (Q h)^T of chunk c+1 with the new state
+// Each prep wave computes every norm and cumsum value it needs itself, so
+// the prep waves never wait for each other inside a step.  Buffers: raw k and
+// v rows in rings of three chunks (the chain reads chunk c's while c+1's is
+// resident and c+2's streams in), raw q/g/beta and the prep outputs
 // double-buffered by chunk parity.
 //
-// Rows past the end of a sequence are copies of its last row; the cumsum wave
+// Rows past the end of a sequence are copies of its last row; the cumsum
 // reads their g and beta as 0, which makes their rows of A, X and V_new zero
 // and leaves gamma_L at the last real token, so they contribute nothing.
 #include "gdn_device.h"
@@ -76,6 +77,15 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
 
 template <int N> struct IC { static constexpr int value = N; };
 
+// Orders LDS writes of some lanes of a wave before LDS reads of other lanes of
+// the same wave.  The hardware keeps a wave's LDS accesses in order; this only
+// stops the compiler from moving the reads above the writes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // XOR swizzle of the 16-byte segments of a row of NSEG segments.
 template <int NSEG> __device__ __forceinline__ int swz(int row) {
     static_assert(NSEG == 8 || NSEG % 16 == 0, "row length");
@@ -94,7 +104,7 @@ struct alignas(16) PrepOut {
     float gam[64];            // gate cumsum, log2 units
     float beta[64];
     float bg[64];             // beta e^gamma
-    float oq[64];             // scale rho e^gamma
+    float rk[64], rq[64];     // L2-norm factors r of k, rho of q (1 without the norm)
     float kf[64];             // r e^{gamma_L - gamma}
     float decay;              // e^{gamma_L}
 };
@@ -110,11 +120,11 @@ __device__ __forceinline__ constexpr int pcol(int jt, int g) {   // first column
 template <int K, int VW> struct WsLds {
     bf16 kb[3][64 * K];       // raw k rows (swizzled), ring of three chunks
     bf16 qb[2][64 * K];       // raw q rows (swizzled)
-    bf16 vb[2][64 * VW];      // raw v rows of this slice (swizzled)
+    bf16 vb[3][64 * VW];      // raw v rows of this slice (swizzled), ring of three chunks
     float gb[2][64], bb[2][64];
     PrepOut po[2];
-    float adiag[4][16 * 20];  // prep: diagonal blocks of A, fp32, transposed (A_ij at 20 j + i)
-    float rk[64], rq[64];     // L2-norm factors of the chunk being prepared
+    float adiag[4][16 * 20];  // per prep wave: its diagonal block of A, fp32, transposed (A_ij at 20 j + i)
+    float stg[4][3][64];      // per prep wave: gamma, beta, r of the chunk being prepared
 };
 
 // The state h (K x V per value head) is held by the chain waves as K/16 tiles
@@ -220,22 +230,19 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt) h[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // Registers carried across the barriers, shared by the two roles (the
-    // roles are exclusive, so one set serves both):
-    //   chain: cr[0..3] = X of the next chunk, C layout [token][value]
-    //          cr[4..7] = (Q h)^T of the next chunk, C layout [value][token]
-    //   prep:  cr[0..3] = K K^T tiles, cr[4..7] = Q K^T tiles of the chunk
-    //          being prepared (transposed, column tiles 0..3)
-    f32x4 cr[8];
+    // Chain: Z = K h and (Q h)^T of the next chunk, carried across the barrier.
+    f32x4 zk[4], zq[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) cr[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 *const xz = cr, *const zq = cr + 4, *const gk = cr, *const gq = cr + 4;
+    for (int t = 0; t < 4; ++t) {
+        zk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        zq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // Prep: the four prep waves share chunk c's copies.
     auto issue = [&](int c) {
         const int64_t t0 = tok0 + 64LL * c;
         const int last = min(64, len - 64 * c) - 1;
-        E *kd = s.kb[c % 3], *qd = s.qb[c & 1], *vd = s.vb[c & 1];
+        E *kd = s.kb[c % 3], *qd = s.qb[c & 1], *vd = s.vb[c % 3];
         const E *kc = kg + (size_t)t0 * kq_row + (size_t)jk * K;
         const E *qc = qg + (size_t)t0 * kq_row + (size_t)jk * K;
         const E *vc = vg + (size_t)t0 * v_row + (size_t)j * V + vcol0;
@@ -275,27 +282,46 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
     }
     lds_barrier();
 
-    for (int c = -1; c < nchunks; ++c) {
-        const int cn = c + 1;
-        const bool prep_next = cn < nchunks;
-        // ============================ phase A ================================
-        if (!is_chain) {
+    // The two roles run separate loops with the same number of barriers, so
+    // that neither carries the other's registers.
+    if (!is_chain) {
+        for (int c = -1; c < nchunks; ++c) {
+            const int cn = c + 1;
+            // ======================= prep: chunk cn ==========================
             if (c + 2 < nchunks) issue(c + 2);
-            if (prep_next) {
-                const int pb = cn & 1;
+            if (cn < nchunks) {
+                const int pb = cn & 1, L = min(64, len - 64 * cn);
+                PrepOut &po = s.po[pb];
+                float *sg = s.stg[cw][0], *sb = s.stg[cw][1], *sr = s.stg[cw][2];
+                // gate cumsum in log2 units (lane = token); rows past the end read 0
+                {
+                    const float b = lane < L ? s.bb[pb][lane] : 0.f;
+                    const float x = wave_inclusive_scan(lane < L ? s.gb[pb][lane] : 0.f) * 1.4426950408889634f;
+                    sg[lane] = x;
+                    sb[lane] = b;
+                    if (cw == 0) {
+                        po.gam[lane] = x;
+                        po.beta[lane] = b;
+                        po.bg[lane] = b * fast_exp2(x);
+                    }
+                }
                 const E *kb = s.kb[cn % 3], *qb = s.qb[pb];
                 // Transposed Gram tiles C[j][i]: K K^T of row tile itk = cw and
                 // Q K^T of row tile itq = 3 - cw against column tiles jt <= the
-                // row tile, and Q Q^T's diagonal tile for the norms of q.  The
-                // body is specialized per wave so that it is straight-line code.
-                auto gram = [&](auto itk_c) {
+                // row tile, Q Q^T's diagonal tile of row tile itq, and the other
+                // diagonal tiles of K K^T for the norms of every k row.  Specialized
+                // per wave so that it is straight-line code.
+                auto prep = [&](auto itk_c) {
                     constexpr int itk = decltype(itk_c)::value, itq = 3 - itk;
-                    f32x4 gqq = f32x4{0.f, 0.f, 0.f, 0.f};
+                    f32x4 gk[4], gq[4], gqq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int jt = 0; jt < 4; ++jt) {
                         gk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
                         gq[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
+                    f32x4 gd[4];   // diagonal tiles of K K^T outside row tile itk
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) gd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s2 = 0; s2 < KS; ++s2) {
                         v8 fk[4];
@@ -306,125 +332,32 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                         for (int jt = 0; jt < 4; ++jt) {
                             if (jt <= itk) gk[jt] = mma(fk[jt], fk[itk], gk[jt]);
                             if (jt <= itq) gq[jt] = mma(fk[jt], bq, gq[jt]);
+                            if (jt != itk) gd[jt] = mma(fk[jt], fk[jt], gd[jt]);
                         }
                         gqq = mma(bq, bq, gqq);
                     }
-                    // squared row norms from the diagonal tiles
-                    const int e = l16 - 4 * grp;
-                    if (e >= 0 && e < 4) {
-                        s.rk[16 * itk + l16] = p.use_l2norm ? rsqrtf(gk[itk][e] + 1e-6f) : 1.f;
-                        s.rq[16 * itq + l16] = p.use_l2norm ? rsqrtf(gqq[e] + 1e-6f) : 1.f;
-                    }
-                };
-                switch (cw) {
-                    case 0: gram(IC<0>()); break;
-                    case 1: gram(IC<1>()); break;
-                    case 2: gram(IC<2>()); break;
-                    default: gram(IC<3>()); break;
-                }
-            }
-        } else {
-            if (c >= 0) {
-                // chain: V_new, output and next state for chunk c
-                const PrepOut &po = s.po[c & 1];
-                const char *kb = (const char *)s.kb[c % 3];
-                const int64_t t0 = tok0 + 64LL * c;
-                const int L = min(64, len - 64 * c);
-                v4 vb16[4];
-                f32x4 vnf[4];
+                    gd[itk] = gk[itk];
+                    // norms from the diagonals: lane (l16, l16 / 4) holds row l16 at e = l16 % 4
+                    {
+                        const int e = l16 - 4 * grp;
+                        if (e >= 0 && e < 4) {
 #pragma unroll
-                for (int bi = 0; bi < 4; ++bi) {
-                    f32x4 rr = xz[bi];
-#pragma unroll
-                    for (int m = 0; m < bi; ++m)
-                        rr = mma_k16(*(const v4 *)&po.alo[16 * bi + l16][16 * m + 4 * grp], vb16[m], rr);
-                    v4 rbv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) rbv[e] = (E)rr[e];
-                    // D_bi (row l16, columns 4 grp..+3) by a transpose read of D_bi^T
-                    const v4 dfr = tr(&po.dt[bi][4 * grp + (l16 >> 2)][4 * (l16 & 3)]);
-                    vnf[bi] = mma_k16(dfr, rbv, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) vb16[bi][e] = (E)vnf[bi][e];
-                }
-                v8 vnb[2], vkb[2];
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const f32x4 k0 = *(const f32x4 *)&po.kf[32 * s2 + 4 * grp];
-                    const f32x4 k1 = *(const f32x4 *)&po.kf[32 * s2 + 16 + 4 * grp];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        vnb[s2][e] = vb16[2 * s2][e];
-                        vnb[s2][4 + e] = vb16[2 * s2 + 1][e];
-                        vkb[s2][e] = (E)(k0[e] * vnf[2 * s2][e]);
-                        vkb[s2][4 + e] = (E)(k1[e] * vnf[2 * s2 + 1][e]);
-                    }
-                }
-                // O^T tiles [value][token]: (Q h)^T scaled per token, plus (P V_new)^T
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    const int i = 16 * ti + l16;
-                    f32x4 o = zq[ti] * po.oq[i];
-#pragma unroll
-                    for (int s2 = 0; s2 <= ti / 2; ++s2) o = mma(vnb[s2], *(const v8 *)&po.p[i][pcol(2 * s2, grp)], o);
-                    if (i < L) {
-                        v4 ov;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) ov[e] = (E)o[e];
-                        E *dst = og + ((size_t)(t0 + i) * p.HV + j) * V + vcol0 + c0 + 4 * grp;
-                        *(v4 *)__builtin_assume_aligned(dst, 8) = ov;
-                    }
-                }
-                // h <- e^{gamma_L} h + K^T diag(kf) V_new, K^T by transpose loads
-                const float dec = po.decay;
-#pragma unroll
-                for (int mt = 0; mt < KT; ++mt) {
-                    f32x4 acc = h[mt] * dec;
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        const char *pa = kb + to[mt >> 1] + 8 * (mt & 1) + 32 * s2 * KROW;
-                        const v4 a0 = tr(pa), a1 = tr(pa + 16 * KROW);
-                        v8 a;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            a[e] = a0[e];
-                            a[4 + e] = a1[e];
+                            for (int t = 0; t < 4; ++t) sr[16 * t + l16] = p.use_l2norm ? rsqrtf(gd[t][e] + 1e-6f) : 1.f;
+                            po.rq[16 * itq + l16] = p.use_l2norm ? rsqrtf(gqq[e] + 1e-6f) : 1.f;
                         }
-                        acc = mma(a, vkb[s2], acc);
                     }
-                    h[mt] = acc;
-                }
-            }
-            if (cw == 0 && prep_next) {
-                // gate cumsum of chunk cn in log2 units, beta and beta e^gamma;
-                // rows past the end of the sequence read 0
-                const int pb = cn & 1, L = min(64, len - 64 * cn);
-                const float x = wave_inclusive_scan(lane < L ? s.gb[pb][lane] : 0.f) * 1.4426950408889634f;
-                const float b = lane < L ? s.bb[pb][lane] : 0.f;
-                s.po[pb].gam[lane] = x;
-                s.po[pb].beta[lane] = b;
-                s.po[pb].bg[lane] = b * fast_exp2(x);
-            }
-        }
-        lds_barrier();
-        // ============================ phase B ================================
-        if (!is_chain) {
-            if (prep_next) {
-                const int pb = cn & 1;
-                PrepOut &po = s.po[pb];
-                auto epilogue = [&](auto itk_c) {
-                    constexpr int itk = decltype(itk_c)::value, itq = 3 - itk;
-                    // every LDS read of the epilogue comes before its first store
+                    wave_lds_sync();   // the staged gamma / beta / r come from other lanes
+                    // epilogue (the staged gamma / beta / r were written by this wave)
                     f32x4 gj[4], rj[4];
 #pragma unroll
                     for (int jt = 0; jt < 4; ++jt) {
-                        gj[jt] = *(const f32x4 *)&po.gam[16 * jt + 4 * grp];
-                        rj[jt] = *(const f32x4 *)&s.rk[16 * jt + 4 * grp];
+                        gj[jt] = *(const f32x4 *)&sg[16 * jt + 4 * grp];
+                        rj[jt] = *(const f32x4 *)&sr[16 * jt + 4 * grp];
                     }
-                    const f32x4 bd = *(const f32x4 *)&po.beta[16 * itk + 4 * grp];
+                    const f32x4 bd = *(const f32x4 *)&sb[16 * itk + 4 * grp];
                     const int ik = 16 * itk + l16, iq = 16 * itq + l16;
-                    const float gik = po.gam[ik], rik = s.rk[ik], bik = po.beta[ik];
-                    const float giq = po.gam[iq], sriq = p.scale * s.rq[iq];
+                    const float gik = sg[ik], rik = sr[ik], bik = sb[ik];
+                    const float giq = sg[iq];
                     {   // diagonal tile of K K^T -> A_itk,itk (fp32, transposed).  The raw
                         // Gram tile is symmetric, so the lane's values serve as rows
                         // i = 16 itk + 4 grp + e of column j = 16 itk + l16, which makes
@@ -435,7 +368,8 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                             const float v = bd[e] * rj[itk][e] * rik * fast_exp2(gj[itk][e] - gik) * gk[itk][e];
                             a[e] = (4 * grp + e > l16) ? v : 0.f;
                         }
-                        *(f32x4 *)&s.adiag[itk][20 * l16 + 4 * grp] = a;
+                        *(f32x4 *)&s.adiag[cw][20 * l16 + 4 * grp] = a;
+                        wave_lds_sync();   // read back across lanes by the solve
                     }
                     {   // off-diagonal tiles of K K^T in row tile itk -> -A (bf16)
                         const float bri = bik * rik;
@@ -448,13 +382,16 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                             *(v4 *)&po.alo[ik][16 * jt + 4 * grp] = o;
                         }
                     }
-                    {   // Q K^T row tile itq -> P
+                    {   // Q K^T row tile itq -> P; rho of row iq from the Q Q^T diagonal
+                        // (lane (l16, grp) reads the value lane (l16, l16 / 4) holds)
+                        const float qq = __shfl(gqq[l16 & 3], (l16 >> 2) * 16 + l16);
+                        const float srq = p.scale * (p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f);
 #pragma unroll
                         for (int jt = 0; jt <= itq; ++jt) {
                             v4 o;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float v = sriq * rj[jt][e] * fast_exp2(giq - gj[jt][e]) * gq[jt][e];
+                                const float v = srq * rj[jt][e] * fast_exp2(giq - gj[jt][e]) * gq[jt][e];
                                 o[e] = (E)((jt < itq || iq >= 16 * jt + 4 * grp + e) ? v : 0.f);
                             }
                             *(v4 *)&po.p[iq][pcol(jt, grp)] = o;
@@ -462,10 +399,16 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                     }
                 };
                 switch (cw) {
-                    case 0: epilogue(IC<0>()); break;
-                    case 1: epilogue(IC<1>()); break;
-                    case 2: epilogue(IC<2>()); break;
-                    default: epilogue(IC<3>()); break;
+                    case 0: prep(IC<0>()); break;
+                    case 1: prep(IC<1>()); break;
+                    case 2: prep(IC<2>()); break;
+                    default: prep(IC<3>()); break;
+                }
+                if (cw == 0) {   // r, and r e^{gamma_L - gamma}, e^{gamma_L} for the chain
+                    const float gi = sg[lane], gl = sg[63], ri = sr[lane];
+                    po.rk[lane] = ri;
+                    po.kf[lane] = ri * fast_exp2(gl - gi);
+                    if (lane == 0) po.decay = fast_exp2(gl);
                 }
                 // D_cw = (I + A_cw,cw)^-1 by column-oriented forward substitution,
                 // lane = column of D: once x_m is final it updates every later
@@ -504,13 +447,102 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                 }
             }
             wait_vmem();   // this wave's copies of chunk c+2
-        } else if (prep_next) {
-            // chain: Z = K h, (Q h)^T and X of chunk cn
-            const int pb = cn & 1;
-            const E *kb = s.kb[cn % 3], *qb = s.qb[pb];
-            const char *vb = (const char *)s.vb[pb];
-            const PrepOut &po = s.po[pb];
-            f32x4 zk[4];
+            lds_barrier();
+        }
+        return;
+    }
+
+    for (int c = -1; c < nchunks; ++c) {
+        const int cn = c + 1;
+        // ======================= chain: chunk c ==========================
+        if (c >= 0) {
+            const PrepOut &po = s.po[c & 1];
+            const char *kb = (const char *)s.kb[c % 3];
+            const char *vb = (const char *)s.vb[c % 3];
+            const int64_t t0 = tok0 + 64LL * c;
+            const int L = min(64, len - 64 * c);
+            // X = diag(beta) V - diag(beta e^gamma r) Z
+            f32x4 xz[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                const v4 vv = tr(vb + vo + 16 * ti * VROW);
+                const int r0 = 16 * ti + 4 * grp;
+                const f32x4 be = *(const f32x4 *)&po.beta[r0];
+                const f32x4 bg = *(const f32x4 *)&po.bg[r0];
+                const f32x4 rk = *(const f32x4 *)&po.rk[r0];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xz[ti][e] = be[e] * (float)vv[e] - (bg[e] * rk[e]) * zk[ti][e];
+            }
+            // V_new by block forward substitution
+            v4 vb16[4];
+            f32x4 vnf[4];
+#pragma unroll
+            for (int bi = 0; bi < 4; ++bi) {
+                f32x4 rr = xz[bi];
+#pragma unroll
+                for (int m = 0; m < bi; ++m)
+                    rr = mma_k16(*(const v4 *)&po.alo[16 * bi + l16][16 * m + 4 * grp], vb16[m], rr);
+                v4 rbv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rbv[e] = (E)rr[e];
+                // D_bi (row l16, columns 4 grp..+3) by a transpose read of D_bi^T
+                const v4 dfr = tr(&po.dt[bi][4 * grp + (l16 >> 2)][4 * (l16 & 3)]);
+                vnf[bi] = mma_k16(dfr, rbv, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vb16[bi][e] = (E)vnf[bi][e];
+            }
+            v8 vnb[2], vkb[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const f32x4 k0 = *(const f32x4 *)&po.kf[32 * s2 + 4 * grp];
+                const f32x4 k1 = *(const f32x4 *)&po.kf[32 * s2 + 16 + 4 * grp];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vnb[s2][e] = vb16[2 * s2][e];
+                    vnb[s2][4 + e] = vb16[2 * s2 + 1][e];
+                    vkb[s2][e] = (E)(k0[e] * vnf[2 * s2][e]);
+                    vkb[s2][4 + e] = (E)(k1[e] * vnf[2 * s2 + 1][e]);
+                }
+            }
+            // O^T tiles [value][token]: (Q h)^T scaled by scale rho e^gamma per
+            // token, plus (P V_new)^T
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                const int i = 16 * ti + l16;
+                f32x4 o = zq[ti] * (p.scale * po.rq[i] * fast_exp2(po.gam[i]));
+#pragma unroll
+                for (int s2 = 0; s2 <= ti / 2; ++s2) o = mma(vnb[s2], *(const v8 *)&po.p[i][pcol(2 * s2, grp)], o);
+                if (i < L) {
+                    v4 ov;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ov[e] = (E)o[e];
+                    E *dst = og + ((size_t)(t0 + i) * p.HV + j) * V + vcol0 + c0 + 4 * grp;
+                    *(v4 *)__builtin_assume_aligned(dst, 8) = ov;
+                }
+            }
+            // h <- e^{gamma_L} h + K^T diag(kf) V_new, K^T by transpose loads
+            const float dec = po.decay;
+#pragma unroll
+            for (int mt = 0; mt < KT; ++mt) {
+                f32x4 acc = h[mt] * dec;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const char *pa = kb + to[mt >> 1] + 8 * (mt & 1) + 32 * s2 * KROW;
+                    const v4 a0 = tr(pa), a1 = tr(pa + 16 * KROW);
+                    v8 a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        a[e] = a0[e];
+                        a[4 + e] = a1[e];
+                    }
+                    acc = mma(a, vkb[s2], acc);
+                }
+                h[mt] = acc;
+            }
+        }
+        if (cn < nchunks) {
+            // Z = K h and (Q h)^T of chunk cn with the updated state
+            const E *kb = s.kb[cn % 3], *qb = s.qb[cn & 1];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 zk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -530,29 +562,11 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                     zq[t] = mma(hb, frag(qb, t, s2), zq[t]);
                 }
             }
-            // X = diag(beta) V - diag(beta e^gamma r) Z
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                const v4 vv = tr(vb + vo + 16 * ti * VROW);
-                const int r0 = 16 * ti + 4 * grp;
-                const f32x4 be = *(const f32x4 *)&po.beta[r0];
-                const f32x4 bg = *(const f32x4 *)&po.bg[r0];
-                const f32x4 rk = *(const f32x4 *)&s.rk[r0];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xz[ti][e] = be[e] * (float)vv[e] - (bg[e] * rk[e]) * zk[ti][e];
-            }
-            if (cw == 1) {   // per-token factors of chunk cn (lane = token)
-                PrepOut &pw = s.po[pb];
-                const float gi = pw.gam[lane], gl = pw.gam[63];
-                pw.oq[lane] = p.scale * s.rq[lane] * fast_exp2(gi);
-                pw.kf[lane] = s.rk[lane] * fast_exp2(gl - gi);
-                if (lane == 0) pw.decay = fast_exp2(gl);
-            }
         }
         lds_barrier();
     }
 
-    if (is_chain && p.final_state) {
+    if (p.final_state) {
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
