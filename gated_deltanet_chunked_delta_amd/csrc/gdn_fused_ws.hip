@@ -3,32 +3,32 @@
 // Same mathematics as the single-role kernel in gdn_fused.hip (the step list
 // of the page "NPU Training Operators - GDN", operator-semantics section, in
 // the chunk form written out at the top of that file), scheduled differently:
-// a workgroup has 8 waves in two roles.
-//   waves 0-3  chain waves: each owns 16 state columns and runs everything
-//              that depends on the state h: Z = K h, (Q h)^T, X, the block
-//              forward substitution for V_new, the output and the state update.
-//   waves 4-7  prep waves: everything that does not depend on h, one chunk
-//              ahead: the asynchronous copies of the raw rows, the gate cumsum,
-//              the Gram tiles and row norms, their gated epilogue, the
-//              diagonal-block inverses and the per-token factors.
-// A chain wave and a prep wave share each SIMD, so the hardware interleaves
-// the serial state chain of chunk c with the preparation of chunk c+1.
+// a workgroup has 12 waves, three per SIMD, in three roles.
+//   waves 0-3   chain waves: each owns 16 state columns and runs everything
+//               that depends on the state h: X, the block forward substitution
+//               for V_new, the output, the state update, and Z = K h and
+//               (Q h)^T of the next chunk.
+//   waves 4-7   K-prep waves, one chunk ahead: gate cumsum, K K^T Gram tiles of
+//               row tile w and the norms of the k rows of tiles 0..w, the
+//               gated -A tiles, the diagonal-block inverse D_w; wave 7, which
+//               has every norm, also the per-token state factors.
+//   waves 8-11  Q-prep waves, one chunk ahead: the asynchronous copies of the
+//               raw rows (two chunks ahead), gate cumsum, Q K^T Gram tiles of
+//               row tile w, the norms of its q rows and of the k rows of tiles
+//               0..w, the gated P tiles.
+// The SIMDs interleave the serial state chain of chunk c with the
+// preparation of chunk c+1.  Each step ends with the only workgroup barrier
+// of the step; every prep wave computes the cumsum and norm values it needs
+// itself, so the prep waves never wait for each other inside a step.
 //
-// Step c ends with the only workgroup barrier of the step:
-//   prep:  issue the copies of chunk c+2; for chunk c+1: gate cumsum, Gram
-//          tiles, row norms, gated epilogue (-A, P), diagonal inverses D_b,
-//          per-token factors; wait for its own copies of chunk c+2
-//   chain: X, V_new, output rows and the next state for chunk c, then
-//          Z = K h and (Q h)^T of chunk c+1 with the new state
-// Each prep wave computes every norm and cumsum value it needs itself, so
-// the prep waves never wait for each other inside a step.  Buffers: raw k and
-// v rows in rings of three chunks (the chain reads chunk c's while c+1's is
-// resident and c+2's streams in), raw q/g/beta and the prep outputs
-// double-buffered by chunk parity.
-//
-// Rows past the end of a sequence are copies of its last row; the cumsum
-// reads their g and beta as 0, which makes their rows of A, X and V_new zero
-// and leaves gamma_L at the last real token, so they contribute nothing.
+// Buffers: raw k and v rows in rings of three chunks (the chain reads chunk
+// c's while c+1's is resident and c+2's streams in), raw q/g/beta and the prep
+// outputs double-buffered by chunk parity.  Rows past the end of a sequence
+// are copies of its last row; the cumsum reads their g and beta as 0, which
+// makes their rows of A, X and V_new zero and leaves gamma_L at the last real
+// token, so they contribute nothing.
+#include <stddef.h>
+
 #include "gdn_device.h"
 
 namespace gdn {
@@ -45,16 +45,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 // explicitly (wait_vmem, then a barrier).  Vector memory counters retire in
 // order, so the compiler's own counter waits stay correct (at worst they wait
 // longer).
-__device__ __forceinline__ unsigned lds_base(void *lds) {
-    return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void *)lds);
-}
-__device__ __forceinline__ void lds_copy16(const void *g, void *lds) {
+__device__ __forceinline__ void lds_copy16(const void *g, unsigned lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_base(lds)) : "memory", "m0");
+                 :: "v"(g), "s"(lds) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_copy4(const void *g, void *lds) {
+__device__ __forceinline__ void lds_copy4(const void *g, unsigned lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(g), "s"(lds_base(lds)) : "memory", "m0");
+                 :: "v"(g), "s"(lds) : "memory", "m0");
 }
 // Wait until this wave's vector memory operations (its copies) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -103,8 +100,8 @@ struct alignas(16) PrepOut {
     bf16 dt[4][16][16];       // D_b transposed: dt[b][j][i] = D_b[i][j]
     float gam[64];            // gate cumsum, log2 units
     float beta[64];
-    float bg[64];             // beta e^gamma
-    float rk[64], rq[64];     // L2-norm factors r of k, rho of q (1 without the norm)
+    float bgr[64];            // beta e^gamma r
+    float rq[64];             // L2-norm factor rho of q (1 without the norm)
     float kf[64];             // r e^{gamma_L - gamma}
     float decay;              // e^{gamma_L}
 };
@@ -123,8 +120,9 @@ template <int K, int VW> struct WsLds {
     bf16 vb[3][64 * VW];      // raw v rows of this slice (swizzled), ring of three chunks
     float gb[2][64], bb[2][64];
     PrepOut po[2];
-    float adiag[4][16 * 20];  // per prep wave: its diagonal block of A, fp32, transposed (A_ij at 20 j + i)
-    float stg[4][3][64];      // per prep wave: gamma, beta, r of the chunk being prepared
+    float adiag[4][16 * 20];  // per K-prep wave: its diagonal block of A, fp32, transposed (A_ij at 20 j + i)
+    float stk[4][3][64];      // per K-prep wave: gamma, beta, r of the chunk being prepared
+    float stq[4][2][64];      // per Q-prep wave: gamma, r of the chunk being prepared
 };
 
 // The state h (K x V per value head) is held by the chain waves as K/16 tiles
@@ -141,22 +139,23 @@ __device__ __forceinline__ constexpr int kappa(int mt, int r) {
 }
 
 template <int K, int V>
-__global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
+__global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     typedef bf16 E;
     typedef bf16x8 v8;
     typedef bf16x4 v4;
     typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+    typedef WsLds<K, 64> Lds;
     constexpr int VW = 64, VEC = 8;
     constexpr int NSK = K / VEC, NSV = VW / VEC;
     constexpr int KT = K / 16, KS = K / 32;
     constexpr int KROW = 2 * K, VROW = 2 * VW;   // bytes per raw row in LDS
-    static_assert(sizeof(WsLds<K, VW>) <= 160 * 1024, "LDS budget");
-    __shared__ WsLds<K, VW> s;
+    static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget");
+    __shared__ Lds s;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool is_chain = wave < 4;
-    const int cw = wave & 3;   // chain: column tile; prep: Gram row tile / copy share
+    const int role = wave >> 2;   // 0 chain, 1 K-prep, 2 Q-prep
+    const int w4 = wave & 3;      // chain: column tile; prep: row tile
     const int l16 = lane & 15, grp = lane >> 4;
 
     // Workgroup -> (sequence n, key head jk, value head j, value slice).  The
@@ -189,7 +188,6 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
     E *__restrict__ og = (E *)p.out;
     const size_t kq_row = (size_t)p.H * K, v_row = (size_t)p.HV * V;
 
-    // ---- per-lane LDS byte offsets, fixed for the whole kernel -------------
     // raw k/q fragment of row tile t, step s2: row 16 t + l16, key slots
     // 32 s2 + 8 grp .. +7 (one swizzled 16-byte segment)
     int fo[KS];
@@ -198,82 +196,83 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) fo[s2] = l16 * KROW + (((4 * s2 + grp) ^ sw) << 4);
     }
-    // transpose reads of K^T for state tile mt: lane (l16, grp) addresses token
-    // row r0 + 4 grp + l16/4, key dims kappa(mt, 4 (l16 % 4)) .. +3
-    int to[KT / 2];
-    {
-        const int rr = 4 * grp + (l16 >> 2), sw = swz<NSK>(rr);
-#pragma unroll
-        for (int m2 = 0; m2 < KT / 2; ++m2) to[m2] = rr * KROW + (((4 * m2 + (l16 & 3)) ^ sw) << 4);
-    }
-    // transpose read of the v tile: token row 16 ti + 4 grp + l16/4, value
-    // columns c0 + 4 (l16 % 4) .. +3 of this wave's 16 columns
-    const int c0 = 16 * cw;
-    const int vo = (4 * grp + (l16 >> 2)) * VROW +
-                   (((2 * cw + ((l16 & 3) >> 1)) ^ swz<NSV>(4 * grp + (l16 >> 2))) << 4) + 8 * (l16 & 1);
-
     auto frag = [&](const E *buf, int t, int s2) {
         return *(const v8 *)((const char *)buf + fo[s2] + t * 16 * KROW);
     };
     auto tr = [&](const void *pt) { return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)pt); };
 
-    // ---- chain state ------------------------------------------------------
-    f32x4 h[KT];
-    const size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0;
-    if (is_chain && p.initial_state) {
-        const float *__restrict__ s0 = p.initial_state + sbase;
-#pragma unroll
-        for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h[mt][e] = s0[(size_t)kappa(mt, 4 * grp + e) * V + c0 + l16];
-    } else {
-#pragma unroll
-        for (int mt = 0; mt < KT; ++mt) h[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // Chain: Z = K h and (Q h)^T of the next chunk, carried across the barrier.
-    f32x4 zk[4], zq[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        zk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        zq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    // gate cumsum of chunk c in log2 units (lane = token), and beta; rows past
+    // the end of the sequence read 0
+    auto cumsum = [&](int c, float &gam, float &b) {
+        const int L = min(64, len - 64 * c);
+        b = lane < L ? s.bb[c & 1][lane] : 0.f;
+        gam = wave_inclusive_scan(lane < L ? s.gb[c & 1][lane] : 0.f) * 1.4426950408889634f;
+    };
 
-    // Prep: the four prep waves share chunk c's copies.
+    // ---- asynchronous copies (Q-prep waves) --------------------------------
+    // LDS destinations are byte addresses (wave-uniform); the per-lane source
+    // offsets inside a full chunk are fixed, only the last chunk of a sequence
+    // clamps its rows.
+    const unsigned lds0 = (unsigned)(size_t)(lds_void *)&s;
+    unsigned kqo[NSK / 4], vvo[NSV / 4];
+#pragma unroll
+    for (int i = 0; i < NSK / 4; ++i) {
+        const int P = 64 * (w4 + 4 * i) + lane, row = P / NSK;
+        kqo[i] = (unsigned)row * (unsigned)kq_row + (((P % NSK) ^ swz<NSK>(row)) * VEC);
+    }
+#pragma unroll
+    for (int i = 0; i < NSV / 4; ++i) {
+        const int P = 64 * (w4 + 4 * i) + lane, row = P / NSV;
+        vvo[i] = (unsigned)row * (unsigned)v_row + (((P % NSV) ^ swz<NSV>(row)) * VEC);
+    }
     auto issue = [&](int c) {
         const int64_t t0 = tok0 + 64LL * c;
         const int last = min(64, len - 64 * c) - 1;
-        E *kd = s.kb[c % 3], *qd = s.qb[c & 1], *vd = s.vb[c % 3];
+        const unsigned kl = lds0 + offsetof(Lds, kb) + (c % 3) * (64 * K * 2);
+        const unsigned ql = lds0 + offsetof(Lds, qb) + (c & 1) * (64 * K * 2);
+        const unsigned vl = lds0 + offsetof(Lds, vb) + (c % 3) * (64 * VW * 2);
         const E *kc = kg + (size_t)t0 * kq_row + (size_t)jk * K;
         const E *qc = qg + (size_t)t0 * kq_row + (size_t)jk * K;
         const E *vc = vg + (size_t)t0 * v_row + (size_t)j * V + vcol0;
+        if (last == 63) {
 #pragma unroll
-        for (int i = 0; i < NSK / 4; ++i) {
-            const int t = cw + 4 * i;
-            const int P = 64 * t + lane, row = P / NSK, seg = (P % NSK) ^ swz<NSK>(row);
-            const unsigned off = (unsigned)min(row, last) * (unsigned)kq_row + seg * VEC;
-            lds_copy16(kc + off, kd + 64 * t * VEC);
-            lds_copy16(qc + off, qd + 64 * t * VEC);
-        }
+            for (int i = 0; i < NSK / 4; ++i) {
+                const unsigned d = 1024u * (w4 + 4 * i);
+                lds_copy16(kc + kqo[i], kl + d);
+                lds_copy16(qc + kqo[i], ql + d);
+            }
 #pragma unroll
-        for (int i = 0; i < NSV / 4; ++i) {
-            const int t = cw + 4 * i;
-            const int P = 64 * t + lane, row = P / NSV, seg = (P % NSV) ^ swz<NSV>(row);
-            lds_copy16(vc + (unsigned)min(row, last) * (unsigned)v_row + seg * VEC, vd + 64 * t * VEC);
+            for (int i = 0; i < NSV / 4; ++i) lds_copy16(vc + vvo[i], vl + 1024u * (w4 + 4 * i));
+        } else {
+#pragma unroll
+            for (int i = 0; i < NSK / 4; ++i) {
+                const int t = w4 + 4 * i;
+                const int P = 64 * t + lane, row = P / NSK, seg = (P % NSK) ^ swz<NSK>(row);
+                const unsigned off = (unsigned)min(row, last) * (unsigned)kq_row + seg * VEC;
+                lds_copy16(kc + off, kl + 1024u * t);
+                lds_copy16(qc + off, ql + 1024u * t);
+            }
+#pragma unroll
+            for (int i = 0; i < NSV / 4; ++i) {
+                const int t = w4 + 4 * i;
+                const int P = 64 * t + lane, row = P / NSV, seg = (P % NSV) ^ swz<NSV>(row);
+                lds_copy16(vc + (unsigned)min(row, last) * (unsigned)v_row + seg * VEC, vl + 1024u * t);
+            }
         }
-        if (cw == 3) {
+        if (w4 == 3) {
             const size_t o = (size_t)(t0 + min(lane, last)) * p.HV + j;
-            lds_copy4(p.g + o, &s.gb[c & 1][0]);
-            lds_copy4(p.beta + o, &s.bb[c & 1][0]);
+            lds_copy4(p.g + o, lds0 + offsetof(Lds, gb) + (c & 1) * 256);
+            lds_copy4(p.beta + o, lds0 + offsetof(Lds, bb) + (c & 1) * 256);
         }
     };
 
-    if (!is_chain && nchunks > 0) {
+    if (role == 2 && nchunks > 0) {
         issue(0);
         wait_vmem();
     }
     // P blocks (0,1) and (2,3) are read by the output product but never
     // written by the epilogue: zero them once in both buffers.
-    if (is_chain) {
+    if (role == 0) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int idx = 256 * q4 + tid, b2 = idx >> 9, blk = (idx >> 8) & 1, r = (idx >> 4) & 15, jj = idx & 15;
@@ -282,96 +281,164 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
     }
     lds_barrier();
 
-    // The two roles run separate loops with the same number of barriers, so
-    // that neither carries the other's registers.
-    if (!is_chain) {
+    // The three roles run separate loops with the same number of barriers, so
+    // that none carries another's registers.
+    if (role == 2) {
+        // ============================ Q-prep ==================================
         for (int c = -1; c < nchunks; ++c) {
             const int cn = c + 1;
-            // ======================= prep: chunk cn ==========================
             if (c + 2 < nchunks) issue(c + 2);
             if (cn < nchunks) {
-                const int pb = cn & 1, L = min(64, len - 64 * cn);
-                PrepOut &po = s.po[pb];
-                float *sg = s.stg[cw][0], *sb = s.stg[cw][1], *sr = s.stg[cw][2];
-                // gate cumsum in log2 units (lane = token); rows past the end read 0
+                PrepOut &po = s.po[cn & 1];
+                float *sg = s.stq[w4][0], *sr = s.stq[w4][1];
                 {
-                    const float b = lane < L ? s.bb[pb][lane] : 0.f;
-                    const float x = wave_inclusive_scan(lane < L ? s.gb[pb][lane] : 0.f) * 1.4426950408889634f;
-                    sg[lane] = x;
-                    sb[lane] = b;
-                    if (cw == 0) {
-                        po.gam[lane] = x;
-                        po.beta[lane] = b;
-                        po.bg[lane] = b * fast_exp2(x);
-                    }
+                    float gam, b;
+                    cumsum(cn, gam, b);
+                    sg[lane] = gam;
                 }
-                const E *kb = s.kb[cn % 3], *qb = s.qb[pb];
-                // Transposed Gram tiles C[j][i]: K K^T of row tile itk = cw and
-                // Q K^T of row tile itq = 3 - cw against column tiles jt <= the
-                // row tile, Q Q^T's diagonal tile of row tile itq, and the other
-                // diagonal tiles of K K^T for the norms of every k row.  Specialized
-                // per wave so that it is straight-line code.
-                auto prep = [&](auto itk_c) {
-                    constexpr int itk = decltype(itk_c)::value, itq = 3 - itk;
-                    f32x4 gk[4], gq[4], gqq = f32x4{0.f, 0.f, 0.f, 0.f};
+                const E *kb = s.kb[cn % 3], *qb = s.qb[cn & 1];
+                // Transposed Gram tiles C[j][i] = k_j . q_i of row tile itq = w4
+                // against column tiles jt <= itq, Q Q^T's diagonal tile, and the
+                // diagonal tiles of K K^T for the norms of every k row
+                auto qprep = [&](auto itq_c) {
+                    constexpr int itq = decltype(itq_c)::value;
+                    f32x4 gq[itq + 1], gd[itq + 1], gqq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) {
-                        gk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int jt = 0; jt <= itq; ++jt) {
                         gq[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        gd[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
-                    f32x4 gd[4];   // diagonal tiles of K K^T outside row tile itk
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) gd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s2 = 0; s2 < KS; ++s2) {
-                        v8 fk[4];
+                        v8 fk[itq + 1];
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) fk[t] = frag(kb, t, s2);
+                        for (int t = 0; t <= itq; ++t) fk[t] = frag(kb, t, s2);
                         const v8 bq = frag(qb, itq, s2);
 #pragma unroll
-                        for (int jt = 0; jt < 4; ++jt) {
-                            if (jt <= itk) gk[jt] = mma(fk[jt], fk[itk], gk[jt]);
-                            if (jt <= itq) gq[jt] = mma(fk[jt], bq, gq[jt]);
-                            if (jt != itk) gd[jt] = mma(fk[jt], fk[jt], gd[jt]);
+                        for (int jt = 0; jt <= itq; ++jt) {
+                            gq[jt] = mma(fk[jt], bq, gq[jt]);
+                            gd[jt] = mma(fk[jt], fk[jt], gd[jt]);
                         }
                         gqq = mma(bq, bq, gqq);
                     }
-                    gd[itk] = gk[itk];
-                    // norms from the diagonals: lane (l16, l16 / 4) holds row l16 at e = l16 % 4
+                    // norms of the k rows of tiles 0..itq from the diagonals: lane
+                    // (l16, l16 / 4) holds row l16 at e = l16 % 4
                     {
                         const int e = l16 - 4 * grp;
                         if (e >= 0 && e < 4) {
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) sr[16 * t + l16] = p.use_l2norm ? rsqrtf(gd[t][e] + 1e-6f) : 1.f;
-                            po.rq[16 * itq + l16] = p.use_l2norm ? rsqrtf(gqq[e] + 1e-6f) : 1.f;
+                            for (int t = 0; t <= itq; ++t) sr[16 * t + l16] = p.use_l2norm ? rsqrtf(gd[t][e] + 1e-6f) : 1.f;
+                        }
+                    }
+                    const float qq = __shfl(gqq[l16 & 3], (l16 >> 2) * 16 + l16);
+                    const float rho = p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f;
+                    if (grp == 0) po.rq[16 * itq + l16] = rho;
+                    wave_lds_sync();   // the staged gamma and r come from other lanes
+                    const int iq = 16 * itq + l16;
+                    const float giq = sg[iq], srq = p.scale * rho;
+                    f32x4 gj[itq + 1], rj[itq + 1];
+#pragma unroll
+                    for (int jt = 0; jt <= itq; ++jt) {
+                        gj[jt] = *(const f32x4 *)&sg[16 * jt + 4 * grp];
+                        rj[jt] = *(const f32x4 *)&sr[16 * jt + 4 * grp];
+                    }
+#pragma unroll
+                    for (int jt = 0; jt <= itq; ++jt) {
+                        v4 o;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = srq * rj[jt][e] * fast_exp2(giq - gj[jt][e]) * gq[jt][e];
+                            o[e] = (E)((jt < itq || iq >= 16 * jt + 4 * grp + e) ? v : 0.f);
+                        }
+                        *(v4 *)&po.p[iq][pcol(jt, grp)] = o;
+                    }
+                };
+                switch (w4) {
+                    case 0: qprep(IC<0>()); break;
+                    case 1: qprep(IC<1>()); break;
+                    case 2: qprep(IC<2>()); break;
+                    default: qprep(IC<3>()); break;
+                }
+            }
+            wait_vmem();   // this wave's copies of chunk c+2
+            lds_barrier();
+        }
+        return;
+    }
+
+    if (role == 1) {
+        // ============================ K-prep ==================================
+        for (int c = -1; c < nchunks; ++c) {
+            const int cn = c + 1;
+            if (cn < nchunks) {
+                PrepOut &po = s.po[cn & 1];
+                float *sg = s.stk[w4][0], *sb = s.stk[w4][1], *sr = s.stk[w4][2];
+                {
+                    float gam, b;
+                    cumsum(cn, gam, b);
+                    sg[lane] = gam;
+                    sb[lane] = b;
+                    if (w4 == 0) {
+                        po.gam[lane] = gam;
+                        po.beta[lane] = b;
+                    }
+                }
+                const E *kb = s.kb[cn % 3];
+                // Transposed Gram tiles C[j][i] = k_j . k_i of row tile itk = w4
+                // against column tiles jt <= itk, and the other diagonal tiles
+                // for the norms of every k row
+                auto kprep = [&](auto itk_c) {
+                    constexpr int itk = decltype(itk_c)::value;
+                    f32x4 gk[itk + 1], gd[itk + 1];
+#pragma unroll
+                    for (int jt = 0; jt <= itk; ++jt) {
+                        gk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        gd[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) {
+                        v8 fk[itk + 1];
+#pragma unroll
+                        for (int t = 0; t <= itk; ++t) fk[t] = frag(kb, t, s2);
+#pragma unroll
+                        for (int jt = 0; jt <= itk; ++jt) {
+                            gk[jt] = mma(fk[jt], fk[itk], gk[jt]);
+                            if (jt < itk) gd[jt] = mma(fk[jt], fk[jt], gd[jt]);
+                        }
+                    }
+                    gd[itk] = gk[itk];
+                    // norms of the rows of tiles 0..itk from the diagonals: lane
+                    // (l16, l16 / 4) holds row l16 at e = l16 % 4
+                    {
+                        const int e = l16 - 4 * grp;
+                        if (e >= 0 && e < 4) {
+#pragma unroll
+                            for (int t = 0; t <= itk; ++t) sr[16 * t + l16] = p.use_l2norm ? rsqrtf(gd[t][e] + 1e-6f) : 1.f;
                         }
                     }
                     wave_lds_sync();   // the staged gamma / beta / r come from other lanes
-                    // epilogue (the staged gamma / beta / r were written by this wave)
-                    f32x4 gj[4], rj[4];
+                    f32x4 gj[itk + 1], rj[itk + 1];
 #pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) {
+                    for (int jt = 0; jt <= itk; ++jt) {
                         gj[jt] = *(const f32x4 *)&sg[16 * jt + 4 * grp];
                         rj[jt] = *(const f32x4 *)&sr[16 * jt + 4 * grp];
                     }
                     const f32x4 bd = *(const f32x4 *)&sb[16 * itk + 4 * grp];
-                    const int ik = 16 * itk + l16, iq = 16 * itq + l16;
+                    const int ik = 16 * itk + l16;
                     const float gik = sg[ik], rik = sr[ik], bik = sb[ik];
-                    const float giq = sg[iq];
-                    {   // diagonal tile of K K^T -> A_itk,itk (fp32, transposed).  The raw
-                        // Gram tile is symmetric, so the lane's values serve as rows
-                        // i = 16 itk + 4 grp + e of column j = 16 itk + l16, which makes
-                        // the transposed store one vector per lane.
+                    {   // diagonal tile -> A_itk,itk (fp32, transposed).  The raw Gram
+                        // tile is symmetric, so the lane's values serve as rows
+                        // i = 16 itk + 4 grp + e of column j = 16 itk + l16, which
+                        // makes the transposed store one vector per lane.
                         f32x4 a;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float v = bd[e] * rj[itk][e] * rik * fast_exp2(gj[itk][e] - gik) * gk[itk][e];
                             a[e] = (4 * grp + e > l16) ? v : 0.f;
                         }
-                        *(f32x4 *)&s.adiag[cw][20 * l16 + 4 * grp] = a;
-                        wave_lds_sync();   // read back across lanes by the solve
+                        *(f32x4 *)&s.adiag[w4][20 * l16 + 4 * grp] = a;
                     }
-                    {   // off-diagonal tiles of K K^T in row tile itk -> -A (bf16)
+                    {   // off-diagonal tiles of row tile itk -> -A (bf16)
                         const float bri = bik * rik;
 #pragma unroll
                         for (int jt = 0; jt < itk; ++jt) {
@@ -382,40 +449,26 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                             *(v4 *)&po.alo[ik][16 * jt + 4 * grp] = o;
                         }
                     }
-                    {   // Q K^T row tile itq -> P; rho of row iq from the Q Q^T diagonal
-                        // (lane (l16, grp) reads the value lane (l16, l16 / 4) holds)
-                        const float qq = __shfl(gqq[l16 & 3], (l16 >> 2) * 16 + l16);
-                        const float srq = p.scale * (p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f);
-#pragma unroll
-                        for (int jt = 0; jt <= itq; ++jt) {
-                            v4 o;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float v = srq * rj[jt][e] * fast_exp2(giq - gj[jt][e]) * gq[jt][e];
-                                o[e] = (E)((jt < itq || iq >= 16 * jt + 4 * grp + e) ? v : 0.f);
-                            }
-                            *(v4 *)&po.p[iq][pcol(jt, grp)] = o;
-                        }
-                    }
+                    wave_lds_sync();   // A_itk,itk is read back across lanes by the solve
                 };
-                switch (cw) {
-                    case 0: prep(IC<0>()); break;
-                    case 1: prep(IC<1>()); break;
-                    case 2: prep(IC<2>()); break;
-                    default: prep(IC<3>()); break;
+                switch (w4) {
+                    case 0: kprep(IC<0>()); break;
+                    case 1: kprep(IC<1>()); break;
+                    case 2: kprep(IC<2>()); break;
+                    default: kprep(IC<3>()); break;
                 }
-                if (cw == 0) {   // r, and r e^{gamma_L - gamma}, e^{gamma_L} for the chain
+                if (w4 == 3) {   // beta e^gamma r, r e^{gamma_L - gamma}, e^{gamma_L} for the chain
                     const float gi = sg[lane], gl = sg[63], ri = sr[lane];
-                    po.rk[lane] = ri;
+                    po.bgr[lane] = sb[lane] * fast_exp2(gi) * ri;
                     po.kf[lane] = ri * fast_exp2(gl - gi);
                     if (lane == 0) po.decay = fast_exp2(gl);
                 }
-                // D_cw = (I + A_cw,cw)^-1 by column-oriented forward substitution,
+                // D_w = (I + A_w,w)^-1 by column-oriented forward substitution,
                 // lane = column of D: once x_m is final it updates every later
                 // row, so each step has up to 15 independent updates.  Columns
                 // of A stream in a few steps ahead of their use.
                 if (grp == 0) {
-                    const float *AT = s.adiag[cw];
+                    const float *AT = s.adiag[w4];
                     const int cc = l16;
                     constexpr int PF = 3;
                     float x[16];
@@ -442,19 +495,55 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                         d0[r] = (E)x[r];
                         d1[r] = (E)x[8 + r];
                     }
-                    *(v8 *)&po.dt[cw][cc][0] = d0;
-                    *(v8 *)&po.dt[cw][cc][8] = d1;
+                    *(v8 *)&po.dt[w4][cc][0] = d0;
+                    *(v8 *)&po.dt[w4][cc][8] = d1;
                 }
             }
-            wait_vmem();   // this wave's copies of chunk c+2
             lds_barrier();
         }
         return;
     }
 
+    // ============================== chain ====================================
+    // The chain is the serial part: it takes the SIMD's issue slots first, the
+    // prep waves fill the gaps.
+    __builtin_amdgcn_s_setprio(3);
+    // transpose reads of K^T for state tile mt: lane (l16, grp) addresses token
+    // row r0 + 4 grp + l16/4, key dims kappa(mt, 4 (l16 % 4)) .. +3
+    int to[KT / 2];
+    {
+        const int rr = 4 * grp + (l16 >> 2), sw = swz<NSK>(rr);
+#pragma unroll
+        for (int m2 = 0; m2 < KT / 2; ++m2) to[m2] = rr * KROW + (((4 * m2 + (l16 & 3)) ^ sw) << 4);
+    }
+    // transpose read of the v tile: token row 16 ti + 4 grp + l16/4, value
+    // columns c0 + 4 (l16 % 4) .. +3 of this wave's 16 columns
+    const int c0 = 16 * w4;
+    const int vo = (4 * grp + (l16 >> 2)) * VROW +
+                   (((2 * w4 + ((l16 & 3) >> 1)) ^ swz<NSV>(4 * grp + (l16 >> 2))) << 4) + 8 * (l16 & 1);
+
+    f32x4 h[KT];
+    const size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0;
+    if (p.initial_state) {
+        const float *__restrict__ s0 = p.initial_state + sbase;
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[mt][e] = s0[(size_t)kappa(mt, 4 * grp + e) * V + c0 + l16];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) h[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Z = K h and (Q h)^T of the next chunk, carried across the barrier.
+    f32x4 zk[4], zq[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        zk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        zq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     for (int c = -1; c < nchunks; ++c) {
         const int cn = c + 1;
-        // ======================= chain: chunk c ==========================
         if (c >= 0) {
             const PrepOut &po = s.po[c & 1];
             const char *kb = (const char *)s.kb[c % 3];
@@ -468,29 +557,31 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                 const v4 vv = tr(vb + vo + 16 * ti * VROW);
                 const int r0 = 16 * ti + 4 * grp;
                 const f32x4 be = *(const f32x4 *)&po.beta[r0];
-                const f32x4 bg = *(const f32x4 *)&po.bg[r0];
-                const f32x4 rk = *(const f32x4 *)&po.rk[r0];
+                const f32x4 bgr = *(const f32x4 *)&po.bgr[r0];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) xz[ti][e] = be[e] * (float)vv[e] - (bg[e] * rk[e]) * zk[ti][e];
+                for (int e = 0; e < 4; ++e) xz[ti][e] = be[e] * (float)vv[e] - bgr[e] * zk[ti][e];
             }
-            // V_new by block forward substitution
+            // V_new by block forward substitution, right-looking: as soon as
+            // block m is final it is applied to every later block, so the
+            // updates of different blocks overlap and only one product per block
+            // sits on the dependency chain.
             v4 vb16[4];
             f32x4 vnf[4];
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi) {
-                f32x4 rr = xz[bi];
-#pragma unroll
-                for (int m = 0; m < bi; ++m)
-                    rr = mma_k16(*(const v4 *)&po.alo[16 * bi + l16][16 * m + 4 * grp], vb16[m], rr);
+            for (int m = 0; m < 4; ++m) {
                 v4 rbv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rbv[e] = (E)rr[e];
-                // D_bi (row l16, columns 4 grp..+3) by a transpose read of D_bi^T
-                const v4 dfr = tr(&po.dt[bi][4 * grp + (l16 >> 2)][4 * (l16 & 3)]);
-                vnf[bi] = mma_k16(dfr, rbv, f32x4{0.f, 0.f, 0.f, 0.f});
+                for (int e = 0; e < 4; ++e) rbv[e] = (E)xz[m][e];
+                // D_m (row l16, columns 4 grp..+3) by a transpose read of D_m^T
+                const v4 dfr = tr(&po.dt[m][4 * grp + (l16 >> 2)][4 * (l16 & 3)]);
+                vnf[m] = mma_k16(dfr, rbv, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vb16[bi][e] = (E)vnf[bi][e];
+                for (int e = 0; e < 4; ++e) vb16[m][e] = (E)vnf[m][e];
+#pragma unroll
+                for (int bi = m + 1; bi < 4; ++bi)
+                    xz[bi] = mma_k16(*(const v4 *)&po.alo[16 * bi + l16][16 * m + 4 * grp], vb16[m], xz[bi]);
             }
+            // V_new for the output product, diag(kf) V_new for the state
             v8 vnb[2], vkb[2];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
@@ -505,22 +596,17 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                 }
             }
             // O^T tiles [value][token]: (Q h)^T scaled by scale rho e^gamma per
-            // token, plus (P V_new)^T
+            // token, plus (P V_new)^T; and h <- e^{gamma_L} h + K^T diag(kf) V_new
+            // (K^T by transpose loads).  The two are independent, so they sit in
+            // one branch-free block and the scheduler interleaves them.
+            f32x4 o[4];
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 const int i = 16 * ti + l16;
-                f32x4 o = zq[ti] * (p.scale * po.rq[i] * fast_exp2(po.gam[i]));
+                o[ti] = zq[ti] * (p.scale * po.rq[i] * fast_exp2(po.gam[i]));
 #pragma unroll
-                for (int s2 = 0; s2 <= ti / 2; ++s2) o = mma(vnb[s2], *(const v8 *)&po.p[i][pcol(2 * s2, grp)], o);
-                if (i < L) {
-                    v4 ov;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ov[e] = (E)o[e];
-                    E *dst = og + ((size_t)(t0 + i) * p.HV + j) * V + vcol0 + c0 + 4 * grp;
-                    *(v4 *)__builtin_assume_aligned(dst, 8) = ov;
-                }
+                for (int s2 = 0; s2 <= ti / 2; ++s2) o[ti] = mma(vnb[s2], *(const v8 *)&po.p[i][pcol(2 * s2, grp)], o[ti]);
             }
-            // h <- e^{gamma_L} h + K^T diag(kf) V_new, K^T by transpose loads
             const float dec = po.decay;
 #pragma unroll
             for (int mt = 0; mt < KT; ++mt) {
@@ -538,6 +624,27 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
                     acc = mma(a, vkb[s2], acc);
                 }
                 h[mt] = acc;
+            }
+            E *dst = og + ((size_t)t0 * p.HV + j) * V + vcol0 + c0 + 4 * grp;
+            const size_t orow = (size_t)p.HV * V;
+            if (L == 64) {
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    v4 ov;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ov[e] = (E)o[ti][e];
+                    *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = ov;
+                }
+            } else {
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    if (16 * ti + l16 < L) {
+                        v4 ov;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ov[e] = (E)o[ti][e];
+                        *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = ov;
+                    }
+                }
             }
         }
         if (cn < nchunks) {
@@ -577,17 +684,17 @@ __global__ void __launch_bounds__(512) fused_ws_kernel(Params p) {
 
 }  // namespace
 
-// One workgroup of 512 threads per (sequence, value head, 64 value columns).
+// One workgroup of 768 threads per (sequence, value head, 64 value columns).
 hipError_t launch_fused_ws(const Params &p, hipStream_t st) {
     constexpr int VW = 64;
     const int groups = p.N * p.H;
     if (groups == 0) return hipSuccess;
     const int per_group = (p.HV / p.H) * (p.V / VW);
     const unsigned grid = (unsigned)((groups + 7) / 8) * 8 * per_group;
-    if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64><<<grid, 512, 0, st>>>(p);
-    else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128><<<grid, 512, 0, st>>>(p);
-    else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64><<<grid, 512, 0, st>>>(p);
-    else fused_ws_kernel<128, 128><<<grid, 512, 0, st>>>(p);
+    if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64><<<grid, 768, 0, st>>>(p);
+    else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128><<<grid, 768, 0, st>>>(p);
+    else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64><<<grid, 768, 0, st>>>(p);
+    else fused_ws_kernel<128, 128><<<grid, 768, 0, st>>>(p);
     return hipGetLastError();
 }
 
