@@ -27,8 +27,8 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # sources and build flags they were measured on.  Any change to the kernel changes
 # the hash, and the bench then reports traffic as null until it is measured again.
 MEASURED_TRAFFIC = {
-    # fused_kernel, GVA workload: FETCH 151,700 KiB x 2.000 + WRITE 139,264 KiB x 1.000
-    "a764d04c786ce8ff": {"gva": 453287936},
+    # fused_ws_kernel, GVA workload: FETCH 151,995 KiB x 2.000 + WRITE 139,776 KiB x 1.000
+    "9f2388541522e1dc": {"gva": 454416384},
 }
 KERNEL_SOURCES = ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused.hip",
                   "gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip",
@@ -44,14 +44,15 @@ def kernel_hash():
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+SETTLE_S = 0.1                 # untimed launches before the warmup steps (clock settling)
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gva")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle units for the CPU baseline (0 = auto)")
@@ -138,6 +139,16 @@ def main():
         if st != 0:
             raise gdn.GdnError(st)
 
+    # Settle: the clocks of a freshly busy GPU take ~100 launches of this size
+    # to reach their steady state (kernel times dip and recover meanwhile), so
+    # untimed launches run for at least SETTLE_S seconds before the W warmup steps.
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(10):
+            step()
+        settle += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -183,7 +194,7 @@ def main():
                                                          flops / (MFMA_PEAK_TFLOPS[args.dtype] * 1e12)))}
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} T={T} N={N} H={w.H} HV={w.HV} K={w.K} V={w.V} "
                                f"l2norm={w.use_l2norm} initial_state={w.init}",

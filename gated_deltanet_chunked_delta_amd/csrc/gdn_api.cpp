@@ -56,8 +56,10 @@ struct EventProfiler : gdn::Profiler {
             pool.pop_back();
             return e;
         }
+        // No system-scope fence: the timing events must not flush caches
+        // between the launches they bracket.
         hipEvent_t e = nullptr;
-        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
         return e;
     }
     void begin(int kind, hipStream_t st) override {

@@ -538,27 +538,25 @@ hipError_t launch_fused_cfg(const Params &p, hipStream_t st) {
 
 }  // namespace
 
-// Column slice per workgroup: bf16 uses 64 columns on 4 waves; the fp32
-// check mode uses 32 columns on 2 waves so that its LDS fits one CU.
+// The fp32 check mode: 32 columns per workgroup on 2 waves, so that its LDS
+// fits one CU.  (bf16 runs the warp-specialized kernel of gdn_fused_ws.hip.)
 hipError_t launch_fused(const Params &p, int dtype, hipStream_t st) {
-    if (dtype == 0) {
-        if (p.K == 64 && p.V == 64) return launch_fused_cfg<bf16, 64, 64, 4, 1>(p, st);
-        if (p.K == 64 && p.V == 128) return launch_fused_cfg<bf16, 64, 128, 4, 1>(p, st);
-        if (p.K == 128 && p.V == 64) return launch_fused_cfg<bf16, 128, 64, 4, 1>(p, st);
-        return launch_fused_cfg<bf16, 128, 128, 4, 1>(p, st);
-    }
+    (void)dtype;
     if (p.K == 64 && p.V == 64) return launch_fused_cfg<float, 64, 64, 2, 1>(p, st);
     if (p.K == 64 && p.V == 128) return launch_fused_cfg<float, 64, 128, 2, 1>(p, st);
     if (p.K == 128 && p.V == 64) return launch_fused_cfg<float, 128, 64, 2, 1>(p, st);
     return launch_fused_cfg<float, 128, 128, 2, 1>(p, st);
 }
 
-const char *kernel_name(int kind) { return kind == kFusedKernel ? "fused_kernel" : "?"; }
+const char *kernel_name(int kind) {
+    return kind == kFusedKernel ? "fused_kernel" : kind == kFusedWsKernel ? "fused_ws_kernel" : "?";
+}
 
 hipError_t launch_forward(const Params &p, int dtype, hipStream_t stream, Profiler *prof) {
-    if (prof) prof->begin(kFusedKernel, stream);
+    const int kind = dtype == 0 ? kFusedWsKernel : kFusedKernel;
+    if (prof) prof->begin(kind, stream);
     const hipError_t err = dtype == 0 ? launch_fused_ws(p, stream) : launch_fused(p, dtype, stream);
-    if (prof) prof->end(kFusedKernel, stream);
+    if (prof) prof->end(kind, stream);
     return err;
 }
 

@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI host code (gdn_api.cpp) and the HIP
-// kernels (gdn_kernels.hip).  Not part of the public ABI.
+// kernels (gdn_fused.hip, gdn_fused_ws.hip).  Not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -28,7 +28,9 @@ struct Params {
 };
 
 // The kernels of one forward pass, for the timing hook.
-enum KernelKind { kFusedKernel = 0, kNumKernelKinds = 1 };
+// fused_kernel: single-role kernel (the fp32 check mode); fused_ws_kernel:
+// warp-specialized kernel (bf16).
+enum KernelKind { kFusedKernel = 0, kFusedWsKernel = 1, kNumKernelKinds = 2 };
 const char *kernel_name(int kind);
 
 // Timing hook: when given, the launch sequence calls begin/end around each
