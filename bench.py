@@ -107,6 +107,100 @@ def cpu_baseline(x, units_wanted):
             "seconds": dt}
 
 
+DECODE_METRIC = "fused recurrent GDN decode tokens/s on 1 MI355X (one token per sequence, pool-indexed state)"
+
+
+def decode_bytes(w, n_valid, eb):
+    """Algorithmic HBM bytes of one decode step: each valid row reads q, k (per
+    key head), v, g, beta and its K x V fp32 state, writes o and the state;
+    padded rows write o; every row reads its slot index."""
+    N = w.N
+    return (n_valid * (2 * w.H * w.K * eb + w.HV * w.V * eb + 8 * w.HV + 8 * w.HV * w.K * w.V)
+            + N * w.HV * w.V * eb + 4 * N)
+
+
+def run_decode(args):
+    import torch
+    import gated_deltanet_chunked_delta_amd as gdn
+    from workloads import DECODE_WORKLOADS, make_decode_inputs
+
+    w = DECODE_WORKLOADS[args.workload]
+    dtype = torch.bfloat16 if args.dtype == "bf16" else torch.float32
+    eb = 2 if args.dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
+    x = make_decode_inputs(w, seed=0, device=dev, io_dtype=dtype)
+    n_valid = int((x["idx"] >= 0).sum())
+    shape = gdn.make_decode_shape(w.N, w.H, w.HV, w.K, w.V, w.pool_size,
+                                  gdn.GDN_BF16 if eb == 2 else gdn.GDN_F32)
+    out = torch.empty((w.N, w.HV, w.V), dtype=dtype, device=dev)
+    pool = x["pool"]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    pool_cpu0 = pool.cpu() if not args.no_cpu_baseline else None
+
+    def step():
+        st = gdn.gdn_recurrent_update(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["use_l2norm"],
+                                      pool, x["idx"], out, shape, stream=stream)
+        if st != 0:
+            raise gdn.GdnError(st)
+
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(10):
+            step()
+        settle += 10
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gdn.gdn_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = gdn.gdn_profile_read()
+    gdn.gdn_profile_enable(False)
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in prof.items() if n}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    dom_us = kernels[dom]["avg_us"]
+    pb = decode_bytes(w, n_valid, eb)
+    ach = pb / (dom_us * 1e-6) / 1e9
+    res = {
+        "metric": DECODE_METRIC, "value": round(n_valid / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: N={w.N} (valid {n_valid}) H={w.H} HV={w.HV} K={w.K} V={w.V} "
+                               f"pool={w.pool_size} l2norm={w.use_l2norm}",
+                   "tokens": n_valid, "global_batch": w.N, "seq_len": 1, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2)},
+        "kernels": {k: {kk: round(vv, 2) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        valid = (x["idx"] >= 0).cpu()
+        sel = torch.nonzero(valid).flatten()
+        cpu = lambda t: t.cpu()[sel].unsqueeze(1)
+        s0 = pool_cpu0[x["idx"].cpu()[sel].long()]
+        t2 = time.perf_counter()
+        oracle.recurrent(cpu(x["q"]), cpu(x["k"]), cpu(x["v"]), cpu(x["g"]), cpu(x["beta"]), scale=x["scale"],
+                         use_l2norm=x["use_l2norm"], initial_state=s0, nthreads=ncpu)
+        dt = time.perf_counter() - t2
+        res["cpu_baseline"] = {"value": round(len(sel) / dt, 1), "unit": "tokens/s", "cores": ncpu,
+                               "kind": "oracle",
+                               "sample": f"the whole step: {len(sel)} rows x {w.HV} value heads, fp64 token "
+                                         f"recurrence from the initial pool ({dt:.3f} s wall)"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -114,6 +208,11 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    from workloads import DECODE_WORKLOADS
+    if args.workload in DECODE_WORKLOADS:
+        run_decode(args)
+        return
 
     import torch
     import gated_deltanet_chunked_delta_amd as gdn

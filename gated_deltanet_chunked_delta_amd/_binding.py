@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK = 0
 GDN_BF16 = 0
 GDN_F32 = 1
-EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_profile_enable", "gdn_profile_read",
-            "gdn_status_str")
+EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_recurrent_update", "gdn_profile_enable",
+            "gdn_profile_read", "gdn_status_str")
 
 _DTYPES = {torch.bfloat16: GDN_BF16, torch.float32: GDN_F32}
 
@@ -27,6 +27,12 @@ class gdn_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class gdn_decode_shape(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("H", ctypes.c_int32), ("HV", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("pool_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -55,6 +61,9 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P, P,
                                   ctypes.POINTER(gdn_shape), P, ctypes.c_size_t, P]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_recurrent_update.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P,
+                                         ctypes.POINTER(gdn_decode_shape), P]
+    lib.gdn_recurrent_update.restype = ctypes.c_int
     lib.gdn_profile_enable.argtypes = [ctypes.c_int]
     lib.gdn_profile_enable.restype = ctypes.c_int
     lib.gdn_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -177,3 +186,62 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out
     if st != GDN_OK:
         raise GdnError(st)
     return out, final_state
+
+
+def make_decode_shape(N, H, HV, K, V, pool_size, dtype) -> gdn_decode_shape:
+    return gdn_decode_shape(int(N), int(H), int(HV), int(K), int(V), int(pool_size), int(dtype))
+
+
+def gdn_recurrent_update(q, k, v, g, beta, scale, use_l2norm, state_pool, state_indices, out,
+                         shape: gdn_decode_shape, stream=None) -> int:
+    """Direct call of the C decode entry point; returns the status code."""
+    lib = load_library()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    return int(lib.gdn_recurrent_update(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                                        int(bool(use_l2norm)), _ptr(state_pool), _ptr(state_indices),
+                                        _ptr(out), ctypes.byref(shape), ctypes.c_void_p(int(stream))))
+
+
+def fused_recurrent_gated_delta_rule_update(q, k, v, g, beta, state_pool, state_indices, scale=None,
+                                            use_qk_l2norm_in_kernel=False, out=None):
+    """One decode step per sequence with an in-place, pool-indexed state.
+
+    q, k [N,H,K] or [N,1,H,K]; v [N,HV,V] or [N,1,HV,V] (bf16, or fp32 for the
+    check mode); g, beta [N,HV] or [N,1,HV] fp32; state_pool [P,HV,K,V] fp32,
+    updated in place; state_indices [N] int32 on the device (an entry outside
+    [0, P), e.g. -1, marks a padding row: its slot is untouched and its output
+    row is zero).  Returns o with v's shape.
+    """
+    squeeze = q.dim() == 4
+    if squeeze:
+        _check(q.shape[1] == 1 and k.shape == q.shape and v.dim() == 4 and v.shape[1] == 1,
+               "decode takes one token per sequence: [N,1,...] layouts need T == 1")
+    qs, ks, vs = (t.reshape(t.shape[0], t.shape[-2], t.shape[-1]) for t in (q, k, v))
+    N, H, K = qs.shape
+    HV, V = vs.shape[1], vs.shape[2]
+    _check(ks.shape == qs.shape and vs.shape[0] == N, "q, k must be [N,H,K] and v [N,HV,V]")
+    _check(qs.dtype in _DTYPES and ks.dtype == qs.dtype and vs.dtype == qs.dtype,
+           "q, k, v must share one dtype (bfloat16 or float32)")
+    gs, bs = g.reshape(N, HV), beta.reshape(N, HV)
+    _check(tuple(gs.shape) == (N, HV) and gs.dtype == torch.float32, "g must be float32 [N,HV]")
+    _check(tuple(bs.shape) == (N, HV) and bs.dtype == torch.float32, "beta must be float32 [N,HV]")
+    _check(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (HV, K, V)
+           and state_pool.dtype == torch.float32 and state_pool.is_contiguous(),
+           f"state_pool must be a contiguous float32 [P,{HV},{K},{V}]")
+    _check(tuple(state_indices.shape) == (N,) and state_indices.dtype == torch.int32,
+           "state_indices must be int32 [N]")
+    _check(qs.is_cuda, "tensors must be on a GPU device (there is no CPU path)")
+    for name, t in (("k", ks), ("v", vs), ("g", gs), ("beta", bs), ("state_pool", state_pool),
+                    ("state_indices", state_indices)):
+        _check(t.device == qs.device, f"{name} must be on {qs.device}")
+    if scale is None:
+        scale = K ** -0.5
+    qs, ks, vs, gs, bs, idx = (t.contiguous() for t in (qs, ks, vs, gs, bs, state_indices))
+    if out is None:
+        out = torch.empty((N, HV, V), dtype=qs.dtype, device=qs.device)
+    shape = make_decode_shape(N, H, HV, K, V, state_pool.shape[0], _DTYPES[qs.dtype])
+    st = gdn_recurrent_update(qs, ks, vs, gs, bs, scale, use_qk_l2norm_in_kernel, state_pool, idx, out, shape)
+    if st != GDN_OK:
+        raise GdnError(st)
+    return out.reshape(v.shape) if squeeze else out

@@ -166,6 +166,44 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+int gdn_recurrent_update(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         float scale, int use_l2norm, float *state_pool, const int32_t *state_indices,
+                         void *out, const gdn_decode_shape *shape, void *stream) {
+    if (!shape) return GDN_ERR_NULL;
+    const gdn_decode_shape &s = *shape;
+    if (s.N < 0 || s.H <= 0 || s.HV <= 0 || s.pool_size < 0) return GDN_ERR_SHAPE;
+    if (gdn::elem_bytes(s.dtype) == 0) return GDN_ERR_DTYPE;
+    if ((s.K != 64 && s.K != 128) || (s.V != 64 && s.V != 128) || s.HV % s.H != 0) return GDN_ERR_UNSUPPORTED;
+    if (s.N > 0 && s.pool_size < 1) return GDN_ERR_SHAPE;
+    // grid size and every index the kernel forms stay in range
+    if ((int64_t)s.N * s.HV * (s.V / 64) > INT_MAX) return GDN_ERR_SHAPE;
+    if (s.N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out)) return GDN_ERR_NULL;
+
+    gdn::DecodeParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.state_pool = state_pool;
+    p.state_indices = state_indices;
+    p.out = out;
+    p.N = s.N;
+    p.H = s.H;
+    p.HV = s.HV;
+    p.K = s.K;
+    p.V = s.V;
+    p.pool_size = s.pool_size;
+    p.scale = scale;
+    p.use_l2norm = use_l2norm ? 1 : 0;
+    hipError_t err;
+    {
+        std::lock_guard<std::mutex> lock(g_prof.mu);
+        err = gdn::launch_recurrent(p, s.dtype, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
+    }
+    return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 const char *gdn_status_str(int status) {
     switch (status) {
         case GDN_OK: return "GDN_OK";

@@ -549,7 +549,12 @@ hipError_t launch_fused(const Params &p, int dtype, hipStream_t st) {
 }
 
 const char *kernel_name(int kind) {
-    return kind == kFusedKernel ? "fused_kernel" : kind == kFusedWsKernel ? "fused_ws_kernel" : "?";
+    switch (kind) {
+        case kFusedKernel: return "fused_kernel";
+        case kFusedWsKernel: return "fused_ws_kernel";
+        case kRecurrentKernel: return "recurrent_update_kernel";
+        default: return "?";
+    }
 }
 
 hipError_t launch_forward(const Params &p, int dtype, hipStream_t stream, Profiler *prof) {

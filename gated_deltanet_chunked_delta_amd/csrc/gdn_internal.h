@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host code (gdn_api.cpp) and the HIP
-// kernels (gdn_fused.hip, gdn_fused_ws.hip).  Not part of the public ABI.
+// kernels (gdn_fused.hip, gdn_fused_ws.hip, gdn_recurrent.hip).  Not part of
+// the public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -28,9 +29,10 @@ struct Params {
 };
 
 // The kernels of one forward pass, for the timing hook.
-// fused_kernel: single-role kernel (the fp32 check mode); fused_ws_kernel:
-// warp-specialized kernel (bf16).
-enum KernelKind { kFusedKernel = 0, kFusedWsKernel = 1, kNumKernelKinds = 2 };
+// fused_kernel: single-role prefill kernel (the fp32 check mode);
+// fused_ws_kernel: warp-specialized prefill kernel (bf16);
+// recurrent_update_kernel: the decode step.
+enum KernelKind { kFusedKernel = 0, kFusedWsKernel = 1, kRecurrentKernel = 2, kNumKernelKinds = 3 };
 const char *kernel_name(int kind);
 
 // Timing hook: when given, the launch sequence calls begin/end around each
@@ -43,6 +45,21 @@ struct Profiler {
 
 // Enqueues the whole forward pass.  Returns the HIP error of the launches.
 hipError_t launch_forward(const Params &p, int dtype, hipStream_t stream, Profiler *prof);
+
+// Everything a decode-step launch needs.  Pointers are device pointers.
+struct DecodeParams {
+    const void *q, *k, *v;           // [N, H, K], [N, H, K], [N, HV, V]
+    const float *g, *beta;           // [N, HV]
+    float *state_pool;               // [pool_size, HV, K, V], updated in place
+    const int32_t *state_indices;    // [N]
+    void *out;                       // [N, HV, V]
+    int N, H, HV, K, V, pool_size;
+    float scale;
+    int use_l2norm;
+};
+
+// Enqueues the decode step (gdn_recurrent.hip).
+hipError_t launch_recurrent(const DecodeParams &p, int dtype, hipStream_t stream, Profiler *prof);
 
 // The single-role fused kernel's launch (gdn_fused.hip).
 hipError_t launch_fused(const Params &p, int dtype, hipStream_t stream);

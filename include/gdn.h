@@ -114,18 +114,66 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v,
                   const gdn_shape *shape, void *workspace, size_t workspace_bytes,
                   void *stream);
 
+/* Sizes of a decode step (one token per sequence).
+ *   N         : sequences in the step (rows of q/k/v/out)
+ *   H, HV     : key/query heads and value heads, as in gdn_shape
+ *   K, V      : head dimensions, each 64 or 128
+ *   pool_size : slots in the state pool
+ *   dtype     : gdn_dtype of q, k, v and out */
+typedef struct gdn_decode_shape {
+    int32_t N, H, HV, K, V, pool_size;
+    int32_t dtype;
+} gdn_decode_shape;
+
+/* Fused recurrent decode step with an in-place, pool-indexed state: for every
+ * sequence n with a valid slot s = state_indices[n] and every value head j,
+ * one token of the recurrence above is applied to pool[s, j]:
+ *
+ *   S = pool[s, j];  S = exp(g[n, j]) S;  S = S + kh (beta[n, j] (v[n, j] - S^T kh))^T
+ *   out[n, j] = scale S^T qh;  pool[s, j] = S
+ *
+ * This is the decode path that the FastDeploy PR #7024 page lists as its
+ * fused recurrent kernel (file table: standard and pool-index interfaces with
+ * a PAD_SLOT_ID = -1 sentinel) and calls in "Usage or Command", item 2
+ * (q, k, v, g, beta, ssm_pool [max_seqs, HV, K, V] updated in place,
+ * ssm_indices [N] int32); the LightLLM page "gdn.py" calls the same operation
+ * with ssm_state_indices and an in-place final state (_gdn_decode_kernel).
+ *
+ *   q, k          [N, H, K]      dtype    read (a [B, 1, H, K] prefill layout with B = N)
+ *   v             [N, HV, V]     dtype    read
+ *   g, beta       [N, HV]        fp32     read
+ *   scale, use_l2norm            as for gdn_chunk_fwd
+ *   state_pool    [pool_size, HV, K, V]  fp32  read and written in place
+ *   state_indices [N] int32               read on the device; an entry outside
+ *                 [0, pool_size) (the sentinel -1 included) marks a padding row:
+ *                 its pool slot is neither read nor written and its out row is
+ *                 written as zeros.  Two valid rows must not name the same slot.
+ *   out           [N, HV, V]     dtype    written (every element)
+ *   shape         sizes (host pointer); stream as for gdn_chunk_fwd
+ *
+ * No workspace.  out must not overlap any input or the pool.
+ * Returns GDN_OK or a negative gdn_status (GDN_ERR_NULL, GDN_ERR_SHAPE for
+ * negative sizes or pool_size < 1 with N > 0, GDN_ERR_DTYPE,
+ * GDN_ERR_UNSUPPORTED as for gdn_chunk_fwd, GDN_ERR_LAUNCH). */
+int gdn_recurrent_update(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta,
+                         float scale, int use_l2norm,
+                         float *state_pool, const int32_t *state_indices,
+                         void *out, const gdn_decode_shape *shape, void *stream);
+
 /* Kernel timing hook, for measurement.  While enabled, every gdn_chunk_fwd
- * call records HIP events on its stream just before and just after each
- * kernel it enqueues (events are created on first use and reused).
+ * and gdn_recurrent_update call records HIP events on its stream just before
+ * and just after each kernel it enqueues (events are created on first use and
+ * reused).
  * gdn_profile_enable(1) starts recording, gdn_profile_enable(0) stops; both
  * discard what was accumulated so far.  Returns GDN_OK. */
 int gdn_profile_enable(int enable);
 
 /* Waits for the recorded events, adds the duration of each recorded launch to
- * its kernel's total and reports, for up to max_kinds kernels of the forward
- * pass (in launch order): a static name, the accumulated milliseconds and the
- * number of launches.  Any output pointer may be NULL.  Returns the number of
- * kernel kinds the forward pass has.  Host-blocking (it synchronises on the
+ * its kernel's total and reports, for up to max_kinds kernel kinds of the
+ * library: a static name, the accumulated milliseconds and the number of
+ * launches.  Any output pointer may be NULL.  Returns the number of kernel
+ * kinds.  Host-blocking (it synchronises on the
  * events), so call it outside a timed region. */
 int gdn_profile_read(int max_kinds, const char **names, double *total_ms, int64_t *launches);
 

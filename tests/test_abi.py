@@ -93,3 +93,43 @@ def test_python_wrapper_rejects_cpu_tensors_and_bad_shapes():
         gdn.chunk_gated_delta_rule(q, q, v, g, g)
     with pytest.raises(ValueError):   # beta with H heads instead of HV
         gdn.chunk_gated_delta_rule(q, q, v, g, torch.zeros(1, 8, 2))
+
+
+def _dcall(shape, ptrs=FAKE):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    return lib.gdn_recurrent_update(P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), 1.0, 1, P(ptrs), P(ptrs),
+                                    P(ptrs), None if shape is None else ctypes.byref(shape), None)
+
+
+@pytest.mark.parametrize("shape,want", [
+    (None, -1),                                                  # no shape
+    (gdn.make_decode_shape(-1, 2, 4, 128, 128, 8, 0), -2),       # negative N
+    (gdn.make_decode_shape(4, 2, 4, 128, 128, 0, 0), -2),        # empty pool with rows
+    (gdn.make_decode_shape(4, 2, 4, 128, 128, 8, 9), -3),        # unknown dtype
+    (gdn.make_decode_shape(4, 2, 4, 96, 128, 8, 0), -4),         # K not supported
+    (gdn.make_decode_shape(4, 3, 4, 128, 128, 8, 0), -4),        # HV % H != 0
+])
+def test_decode_argument_errors(shape, want):
+    assert _dcall(shape) == want
+
+
+def test_decode_null_and_empty():
+    assert _dcall(gdn.make_decode_shape(4, 2, 4, 128, 128, 8, 0), ptrs=0) == -1
+    # no rows: nothing to read or launch, NULL buffers allowed
+    assert _dcall(gdn.make_decode_shape(0, 2, 4, 128, 128, 0, 0), ptrs=0) == 0
+
+
+def test_decode_wrapper_rejects_cpu_tensors_and_bad_shapes():
+    import torch
+    q = torch.zeros(3, 2, 64, dtype=torch.bfloat16)
+    v = torch.zeros(3, 4, 64, dtype=torch.bfloat16)
+    g = torch.zeros(3, 4)
+    pool = torch.zeros(5, 4, 64, 64)
+    idx = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError):   # CPU tensors: there is no CPU path
+        gdn.fused_recurrent_gated_delta_rule_update(q, q, v, g, g, pool, idx)
+    with pytest.raises(ValueError):   # pool with the wrong head count
+        gdn.fused_recurrent_gated_delta_rule_update(q, q, v, g, g, torch.zeros(5, 2, 64, 64), idx)
+    with pytest.raises(ValueError):   # int64 indices
+        gdn.fused_recurrent_gated_delta_rule_update(q, q, v, g, g, pool, idx.long())

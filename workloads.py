@@ -144,3 +144,67 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", io_dtype=torch.bfloat1
     return dict(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), initial_state=s0,
                 cu_seqlens=cu, scale=w.eff_scale, use_l2norm=w.use_l2norm, lens=lens,
                 N=N, workload=w)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: N sequences, one token each, states in a pool."""
+    name: str
+    N: int
+    H: int
+    HV: int
+    K: int
+    V: int
+    pool_size: int
+    n_pad: int = 0                 # rows marked -1 (padding)
+    use_l2norm: bool = True
+    scale: Optional[float] = None
+    a_log_hi: float = math.log(16.0)
+    state_std: float = 0.05
+
+    @property
+    def eff_scale(self) -> float:
+        return self.scale if self.scale is not None else self.K ** -0.5
+
+
+# A serving-style decode batch of the GVA model shape: 256 running sequences in
+# a 512-slot state pool, 8 padded rows.
+DECODE_WORKLOADS = {
+    "decode": DecodeWorkload("decode", N=256, H=16, HV=32, K=128, V=128, pool_size=512, n_pad=8),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: int = 0, device="cpu", io_dtype=torch.bfloat16):
+    """Draws one decode step: q, k [N,H,K], v [N,HV,V] (bf16 values), g, beta
+    [N,HV] by the same gating law as make_inputs, a state pool [P,HV,K,V]
+    ~ N(0, state_std) and int32 slot indices (a random injective map into the
+    pool, the first n_pad rows set to -1).  Values come from a generator on
+    ``device``; the indices from a CPU generator of their own."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    f32 = torch.float32
+
+    def randn(*shape, std=1.0):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=f32) * std
+
+    def io(x):
+        return x.to(torch.bfloat16).to(io_dtype)
+
+    N, H, HV, K, V = w.N, w.H, w.HV, w.K, w.V
+    q = io(randn(N, H, K))
+    k = io(randn(N, H, K))
+    v = io(randn(N, HV, V))
+    a = randn(N, HV)
+    b = randn(N, HV)
+    a_log = torch.rand(HV, generator=gen, device=dev, dtype=f32) * w.a_log_hi
+    dt_bias = torch.rand(HV, generator=gen, device=dev, dtype=f32)
+    g = -torch.exp(a_log) * torch.nn.functional.softplus(a + dt_bias)
+    beta = torch.sigmoid(b)
+    pool = randn(w.pool_size, HV, K, V, std=w.state_std)
+    igen = torch.Generator()
+    igen.manual_seed(seed)
+    idx = torch.randperm(w.pool_size, generator=igen)[:N].to(torch.int32)
+    idx[: w.n_pad] = -1
+    return dict(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), pool=pool, idx=idx.to(dev),
+                scale=w.eff_scale, use_l2norm=w.use_l2norm, workload=w)
