@@ -23,26 +23,45 @@ if ROOT not in sys.path:
 METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a
-# 1 GiB copy; see profiles/*_hbm_traffic.md), keyed by a hash of the kernel
-# sources and build flags they were measured on.  Any change to the kernel changes
-# the hash, and the bench then reports traffic as null until it is measured again.
+# 1 GiB copy; see profiles/*_hbm_traffic.md), keyed by a hash of the measured
+# kernel's source, the device headers and the compile flags.  Any change to them
+# changes the hash, and the bench then reports traffic as null until it is
+# measured again.
 MEASURED_TRAFFIC = {
-    # fused_ws_kernel, GVA workload: FETCH 151,995 KiB x 2.000 + WRITE 139,776 KiB x 1.000
-    "9f2388541522e1dc": {"gva": 454416384},
+    # fused_ws_kernel, GVA prefill: FETCH 151,990.4 KiB x 2.000 + WRITE 139,776.1 KiB x 1.000
+    "ffa5f8891dce8144": {"gva": 454407040},
+    # recurrent_update_kernel, decode: FETCH 257,463.5 KiB x 2.000 + WRITE 510,371.4 KiB x 1.000
+    "297124bdeebd41ed": {"decode": 1049905536},
 }
-KERNEL_SOURCES = ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused.hip",
-                  "gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip",
-                  "gated_deltanet_chunked_delta_amd/csrc/gdn_device.h",
-                  "gated_deltanet_chunked_delta_amd/csrc/gdn_internal.h",
-                  "gated_deltanet_chunked_delta_amd/build.py"]
+KERNEL_SOURCES = {
+    "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
+    "decode": ["gated_deltanet_chunked_delta_amd/csrc/gdn_recurrent.hip"],
+}
+DEVICE_HEADERS = ["gated_deltanet_chunked_delta_amd/csrc/gdn_device.h",
+                  "gated_deltanet_chunked_delta_amd/csrc/gdn_internal.h"]
 
 
-def kernel_hash():
+def kernel_hash(kind):
     import hashlib
+    from gated_deltanet_chunked_delta_amd import build as gbuild
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind] + DEVICE_HEADERS:
         h.update(open(os.path.join(ROOT, f), "rb").read())
+    h.update(" ".join(gbuild.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
+
+
+def copy_calibration(mib, dev):
+    """One plain device copy of known size, the reference kernel for the byte
+    counters (run only when asked, after the timed region)."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 SETTLE_S = 0.1                 # untimed launches before the warmup steps (clock settling)
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA
@@ -162,6 +181,8 @@ def run_decode(args):
     t1 = time.perf_counter()
     prof = gdn.gdn_profile_read()
     gdn.gdn_profile_enable(False)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, dev)
 
     ms = (t1 - t0) * 1e3 / args.steps
     kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in prof.items() if n}
@@ -169,6 +190,8 @@ def run_decode(args):
     dom_us = kernels[dom]["avg_us"]
     pb = decode_bytes(w, n_valid, eb)
     ach = pb / (dom_us * 1e-6) / 1e9
+    khash = kernel_hash("decode")
+    traffic = MEASURED_TRAFFIC.get(khash, {}).get(w.name) if args.dtype == "bf16" else None
     res = {
         "metric": DECODE_METRIC, "value": round(n_valid / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4),
@@ -178,8 +201,9 @@ def run_decode(args):
                                f"pool={w.pool_size} l2norm={w.use_l2norm}",
                    "tokens": n_valid, "global_batch": w.N, "seq_len": 1, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2)},
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2),
+                     "kernel_hash": khash},
         "kernels": {k: {kk: round(vv, 2) if isinstance(vv, float) else vv for kk, vv in v.items()}
                     for k, v in kernels.items()},
     }
@@ -262,13 +286,7 @@ def main():
     gdn.gdn_profile_enable(False)
 
     if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(args.copy_calibration_mib, dev)
 
     tokens = sum(x["lens"])
     ms = (t1 - t0) * 1e3 / args.steps
@@ -279,7 +297,7 @@ def main():
     dom_us = kernels[dom]["avg_us"]
     # the fused kernel is the whole path: its algorithmic bytes are the path's
     ach = pb / (dom_us * 1e-6) / 1e9
-    khash = kernel_hash()
+    khash = kernel_hash("prefill")
     traffic = MEASURED_TRAFFIC.get(khash, {}).get(w.name) if args.dtype == "bf16" else None
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -176,8 +176,9 @@ int gdn_recurrent_update(const void *q, const void *k, const void *v, const floa
     if ((s.K != 64 && s.K != 128) || (s.V != 64 && s.V != 128) || s.HV % s.H != 0) return GDN_ERR_UNSUPPORTED;
     if (s.N > 0 && s.pool_size < 1) return GDN_ERR_SHAPE;
     // grid size and every index the kernel forms stay in range
-    if ((int64_t)s.N * s.HV * (s.V / 64) > INT_MAX) return GDN_ERR_SHAPE;
+    if ((int64_t)s.N * s.HV > INT_MAX) return GDN_ERR_SHAPE;
     if (s.N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out)) return GDN_ERR_NULL;
+    if (s.N > 0 && ((uintptr_t)state_pool & 15) != 0) return GDN_ERR_ALIGN;
 
     gdn::DecodeParams p{};
     p.q = q;
@@ -213,6 +214,7 @@ const char *gdn_status_str(int status) {
         case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: K/V not in {64,128} or HV % H != 0";
         case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: a kernel launch failed";
+        case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is not aligned as its argument requires";
         default: return "unknown gdn_status";
     }
 }

@@ -18,12 +18,16 @@
 //
 // The step is bound by HBM: every (sequence, value head) reads and writes its
 // K x V fp32 state once (2 * 4 K V bytes) and touches only K + K + V other
-// elements.  A workgroup of K/32 waves handles 64 state columns of one
-// (sequence, value head): lane = column, each wave holds 32 rows of its column
-// in registers between the read and the write (the waves' partial inner
-// products are combined through LDS), and every state access is a coalesced
-// 256-byte row of 64 columns.  Few registers per wave let 8 waves share a
-// SIMD, which keeps enough state reads in flight to approach the HBM rate.
+// elements.  One workgroup of K/8 waves owns the whole state of one
+// (sequence, value head).  A lane holds four adjacent columns (one 16-byte
+// piece) of 8 / (64 / (V/4)) rows, so one wave-wide access covers 64 / (V/4)
+// full rows (1 KiB); each wave keeps its 8 rows in registers between the read
+// and the write.  The inner products over rows are summed across the lanes
+// that share columns, then across the waves through LDS.  Fewer than 64
+// registers per lane let 8 waves share a SIMD, which keeps enough state reads
+// in flight to approach the HBM rate.  The state is touched exactly once each
+// way, so its loads and stores are marked non-temporal (streamed past the
+// caches rather than kept in them).
 #include "gdn_device.h"
 
 namespace gdn {
@@ -38,37 +42,42 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 template <typename E, int K, int V>
-__global__ void __launch_bounds__(64 * (K / 32)) recurrent_update_kernel(DecodeParams p) {
-    constexpr int VB = 64;                     // state columns per workgroup
-    constexpr int NW = K / 32;                 // waves per workgroup
-    constexpr int KH = 32;                     // state rows per wave
+__global__ void __launch_bounds__(64 * (K / 8)) recurrent_update_kernel(DecodeParams p) {
+    constexpr int NW = K / 8;                  // waves per workgroup (8 rows each)
+    constexpr int LPR = V / 4;                 // lanes per state row (4 columns each)
+    constexpr int RPI = 64 / LPR;              // state rows per wave-wide access
+    constexpr int RW = K / NW;                 // state rows per wave
+    constexpr int NI = RW / RPI;               // 16-byte state pieces per lane
+    static_assert(NI >= 1 && RW % RPI == 0, "unsupported head size");
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's 32 rows
-    const int vs = blockIdx.x % (V / VB), nj = blockIdx.x / (V / VB);
-    const int n = nj / p.HV, j = nj % p.HV, jk = j / (p.HV / p.H);
-    const int c = vs * VB + lane;
-    E *__restrict__ out = (E *)p.out + ((size_t)n * p.HV + j) * V + c;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c4 = (lane % LPR) * 4;           // this lane's first column
+    const int rl = lane / LPR;                 // its row within an access
+    const int nj = blockIdx.x, n = nj / p.HV, j = nj % p.HV, jk = j / (p.HV / p.H);
+    const size_t nh = (size_t)n * p.HV + j;
+    E *__restrict__ out = (E *)p.out + nh * V;
     const int slot = p.state_indices[n];
     if (slot < 0 || slot >= p.pool_size) {   // padding row: the pool slot is not touched
-        if (wv == 0) *out = to_e<E>(0.f);
+        if (tid < V) out[tid] = to_e<E>(0.f);
         return;
     }
-    // the state block of (slot, j) is uniform; lanes add 32-bit column offsets
-    float *__restrict__ S = p.state_pool + ((size_t)slot * p.HV + j) * K * V + (size_t)wv * KH * V;
+    // the lane's rows are wv*RW + i*RPI + rl, i < NI, at columns c4 .. c4+3
+    f32x4 *__restrict__ S =
+        (f32x4 *)(p.state_pool + (((size_t)slot * p.HV + j) * K + wv * RW + rl) * V + c4);
+    f32x4 s[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) s[i] = __builtin_nontemporal_load(S + i * RPI * V / 4);
 
-    // key and query rows (raw) in LDS; squared norms and their dot product by
-    // a workgroup reduction.  ku is a second copy of the key row for the
-    // update: reading it from a separate array keeps the compiler from holding
-    // the first reads of ks in registers across the column.
-    __shared__ float ks[K], qs[K], ku[K];
-    __shared__ float part[NW][3][64];
-    const E *kp = (const E *)p.k + ((size_t)n * p.H + jk) * K;
-    const E *qp = (const E *)p.q + ((size_t)n * p.H + jk) * K;
+    // key and query rows (raw) in LDS; squared norms and k.q by a workgroup
+    // reduction, combined after the barrier that publishes the rows
+    __shared__ __attribute__((aligned(16))) float ks[K], qs[K];
+    __shared__ float pn[NW][3];
+    __shared__ f32x4 pa[NW][V / 4], pb[NW][V / 4];
     float kk = 0.f, qq = 0.f, kq = 0.f;
-    if (tid < K) {   // one key element per thread
-        const float kv = to_f(kp[tid]), qv = to_f(qp[tid]);
+    if (tid < K) {
+        const float kv = to_f(((const E *)p.k)[((size_t)n * p.H + jk) * K + tid]);
+        const float qv = to_f(((const E *)p.q)[((size_t)n * p.H + jk) * K + tid]);
         ks[tid] = kv;
-        ku[tid] = kv;
         qs[tid] = qv;
         kk = kv * kv;
         qq = qv * qv;
@@ -78,60 +87,77 @@ __global__ void __launch_bounds__(64 * (K / 32)) recurrent_update_kernel(DecodeP
     qq = wave_sum(qq);
     kq = wave_sum(kq);
     if (lane == 0) {
-        part[wv][0][0] = kk;
-        part[wv][1][0] = qq;
-        part[wv][2][0] = kq;
+        pn[wv][0] = kk;
+        pn[wv][1] = qq;
+        pn[wv][2] = kq;
     }
-    // this wave's 32 rows of the column, read once
-    float s[KH];
-#pragma unroll
-    for (int r = 0; r < KH; ++r) s[r] = S[r * V + c];
     __syncthreads();
-    kk = qq = kq = 0.f;
+    // partial S^T k and S^T q over this lane's rows
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        kk += part[w][0][0];
-        qq += part[w][1][0];
-        kq += part[w][2][0];
+    for (int i = 0; i < NI; ++i) {
+        const int r = wv * RW + i * RPI + rl;
+        a += s[i] * ks[r];
+        b += s[i] * qs[r];
     }
+    // lanes holding the same columns (different rows) first, then the waves
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] += __shfl_xor(a[e], o);
+            b[e] += __shfl_xor(b[e], o);
+        }
+    }
+    if (rl == 0) {
+        pa[wv][lane] = a;
+        pb[wv][lane] = b;
+    }
+    __syncthreads();
+    // a few threads finish the sums over the waves (2V column sums, 3 norms)
+    __shared__ __attribute__((aligned(16))) float fin[2][V];
+    __shared__ float fn[3];
+    if (tid < 2 * V) {
+        const int col = tid % V;
+        const float *src = (const float *)(tid < V ? &pa[0][0] : &pb[0][0]);
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x += src[w * V + col];
+        fin[tid / V][col] = x;
+    } else if (tid < 2 * V + 3) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x += pn[w][tid - 2 * V];
+        fn[tid - 2 * V] = x;
+    }
+    __syncthreads();
+    a = *(const f32x4 *)&fin[0][c4];
+    b = *(const f32x4 *)&fin[1][c4];
+    kk = fn[0];
+    qq = fn[1];
+    kq = fn[2];
     const float rk = p.use_l2norm ? rsqrtf(kk + 1e-6f) : 1.f;
     const float rq = p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f;
-    const float *kr = ks + wv * KH, *qr = qs + wv * KH;
-    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-#pragma unroll
-    for (int r = 0; r < KH; r += 2) {
-        a0 += s[r] * kr[r];
-        a1 += s[r + 1] * kr[r + 1];
-        b0 += s[r] * qr[r];
-        b1 += s[r + 1] * qr[r + 1];
-    }
-    // partial S^T k and S^T q of these rows, combined across the waves
-    __syncthreads();   // the first reads of part are done before it is rewritten
-    part[wv][0][lane] = a0 + a1;
-    part[wv][1][lane] = b0 + b1;
-    __syncthreads();
-    float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        a += part[w][0][lane];
-        b += part[w][1][lane];
-    }
-    a *= rk;
-    b *= rq;
-    const size_t nh = (size_t)n * p.HV + j;
     const float eg = __expf(p.g[nh]), bt = p.beta[nh];
-    const float u = to_f(((const E *)p.v)[nh * V + c]) - eg * a;
-    const float bu = bt * u * rk;              // beta u times the key norm factor
-    const float *kw = ku + wv * KH;
+    const E *vp = (const E *)p.v + nh * V + c4;
+    f32x4 u;
 #pragma unroll
-    for (int r = 0; r < KH; ++r) S[r * V + c] = eg * s[r] + bu * kw[r];
-    if (wv == 0) *out = to_e<E>(p.scale * (eg * b + bt * (kq * rk * rq) * u));
+    for (int e = 0; e < 4; ++e) u[e] = to_f(vp[e]) - eg * rk * a[e];
+    const f32x4 bu = u * (bt * rk);            // beta u times the key norm factor
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        __builtin_nontemporal_store(eg * s[i] + bu * ks[wv * RW + i * RPI + rl], S + i * RPI * V / 4);
+    if (wv == 0 && rl == 0) {
+        const float cq = bt * kq * rk * rq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[c4 + e] = to_e<E>(p.scale * (eg * rq * b[e] + cq * u[e]));
+    }
 }
 
 template <typename E, int K, int V>
 hipError_t launch_cfg(const DecodeParams &p, hipStream_t st) {
-    const unsigned grid = (unsigned)((size_t)p.N * p.HV * (V / 64));
-    recurrent_update_kernel<E, K, V><<<grid, 64 * (K / 32), 0, st>>>(p);
+    const unsigned grid = (unsigned)((size_t)p.N * p.HV);
+    recurrent_update_kernel<E, K, V><<<grid, 64 * (K / 8), 0, st>>>(p);
     return hipGetLastError();
 }
 

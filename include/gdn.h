@@ -56,7 +56,8 @@ typedef enum gdn_status {
     GDN_ERR_DTYPE = -3,       /* unknown dtype code */
     GDN_ERR_UNSUPPORTED = -4, /* K or V not in {64, 128}, or HV not a multiple of H */
     GDN_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or too small while one is needed */
-    GDN_ERR_LAUNCH = -6       /* the HIP runtime reported an error at launch */
+    GDN_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
+    GDN_ERR_ALIGN = -7        /* a pointer lacks the alignment its argument requires */
 } gdn_status;
 
 /* Element type of q, k, v and out.  g, beta and both states are always fp32.
@@ -144,6 +145,7 @@ typedef struct gdn_decode_shape {
  *   g, beta       [N, HV]        fp32     read
  *   scale, use_l2norm            as for gdn_chunk_fwd
  *   state_pool    [pool_size, HV, K, V]  fp32  read and written in place
+ *                 (16-byte aligned: the state moves in 16-byte pieces)
  *   state_indices [N] int32               read on the device; an entry outside
  *                 [0, pool_size) (the sentinel -1 included) marks a padding row:
  *                 its pool slot is neither read nor written and its out row is
@@ -154,7 +156,8 @@ typedef struct gdn_decode_shape {
  * No workspace.  out must not overlap any input or the pool.
  * Returns GDN_OK or a negative gdn_status (GDN_ERR_NULL, GDN_ERR_SHAPE for
  * negative sizes or pool_size < 1 with N > 0, GDN_ERR_DTYPE,
- * GDN_ERR_UNSUPPORTED as for gdn_chunk_fwd, GDN_ERR_LAUNCH). */
+ * GDN_ERR_UNSUPPORTED as for gdn_chunk_fwd, GDN_ERR_ALIGN for a state_pool
+ * that is not 16-byte aligned, GDN_ERR_LAUNCH). */
 int gdn_recurrent_update(const void *q, const void *k, const void *v,
                          const float *g, const float *beta,
                          float scale, int use_l2norm,

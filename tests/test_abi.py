@@ -79,7 +79,7 @@ def test_null_tensor_errors():
 
 
 def test_status_strings():
-    for st in range(-6, 1):
+    for st in range(-7, 1):
         assert gdn.gdn_status_str(st).startswith("GDN_")
     assert gdn.gdn_status_str(-99) == "unknown gdn_status"
 
@@ -112,6 +112,14 @@ def _dcall(shape, ptrs=FAKE):
 ])
 def test_decode_argument_errors(shape, want):
     assert _dcall(shape) == want
+
+
+def test_decode_misaligned_pool():
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    shape = gdn.make_decode_shape(4, 2, 4, 128, 128, 8, 0)
+    assert lib.gdn_recurrent_update(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1.0, 1, P(FAKE + 4), P(FAKE),
+                                    P(FAKE), ctypes.byref(shape), None) == -7
 
 
 def test_decode_null_and_empty():
