@@ -15,6 +15,9 @@ Two implementations live here:
   one unit at a time, exposing the per-chunk intermediates.  It reaches the
   same result up to rounding order and is used to check the recurrence and to
   debug.
+* ``gating`` -- g and beta from A_log, dt_bias, a, b in float64 (``gating.py``),
+  and ``recurrent_gated``, the recurrence fed with those gates rounded to
+  float32 (the gates' type on the page that defines them).
 
 Parity is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``
 (hand-derived worked example, closed forms, invariants, the matrix-product
@@ -133,3 +136,15 @@ def recurrent(q, k, v, g, beta, scale=None, use_l2norm=False, initial_state=None
         n, j = divmod(int(uu), HV)
         o[cu[n]:cu[n + 1], j, :] = out[out_row[i]:out_row[i] + ul[i]]
     return o.reshape(B, T, HV, V), fin.reshape(N, HV, K, V)
+
+
+from .gating import gating, sigmoid, softplus  # noqa: E402
+
+
+def recurrent_gated(q, k, v, A_log, dt_bias, a, b, **kw):
+    """``recurrent`` with g and beta computed from the raw gate inputs: a, b
+    [B,T,HV] (or [N,HV] rows of one step each when q is [N,1,H,K]), A_log,
+    dt_bias [HV].  The gates are rounded to float32 before the recurrence, as
+    the gating operator returns them."""
+    g, beta = gating(A_log, dt_bias, a, b)
+    return recurrent(q, k, v, g.astype(np.float32), beta.astype(np.float32), **kw)
