@@ -28,10 +28,10 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # changes the hash, and the bench then reports traffic as null until it is
 # measured again.
 MEASURED_TRAFFIC = {
-    # fused_ws_kernel, GVA prefill: FETCH 151,990.4 KiB x 2.000 + WRITE 139,776.1 KiB x 1.000
-    "ffa5f8891dce8144": {"gva": 454407040},
-    # recurrent_update_kernel, decode: FETCH 257,463.5 KiB x 2.000 + WRITE 510,371.4 KiB x 1.000
-    "297124bdeebd41ed": {"decode": 1049905536},
+    # fused_ws_kernel, GVA prefill: FETCH 151,990.75 KiB x 2.000 + WRITE 139,776.2 KiB x 1.000
+    "2ac7ce49817c0cf4": {"gva": 454407872},
+    # recurrent_update_kernel, decode: FETCH 257,459.0 KiB x 2.000 + WRITE 510,368.6 KiB x 1.000
+    "b2ce57f1b13d562c": {"decode": 1049893504},
 }
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
@@ -76,20 +76,31 @@ def parse():
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle units for the CPU baseline (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gating", default="tensors", choices=["tensors", "fused", "separate"],
+                    help="tensors: g and beta are inputs (computed once by the gating kernel before timing); "
+                         "fused: the kernel computes them from A_log, dt_bias, a, b; separate: each step runs "
+                         "the gating kernel, then the kernel with g and beta")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for hardware byte counters)")
     return ap.parse_args()
 
 
-def path_bytes(w, x, eb):
+def gate_bytes(rows, HV, eb, fused):
+    """Gate inputs read by the chunk or decode kernel: g and beta (fp32) per
+    row and value head, or with in-kernel gating a and b (eb bytes) per row and
+    value head plus A_log and dt_bias per value head."""
+    return rows * HV * 2 * eb + 8 * HV if fused else rows * HV * 8
+
+
+def path_bytes(w, x, eb, fused=False):
     """Algorithmic HBM bytes of one forward pass: every input read once and
-    every output written once (q, k per key head; v, g, beta, o per value
+    every output written once (q, k per key head; v, the gates, o per value
     head; the initial and final states)."""
     T_tot = sum(x["lens"])
     N, H, HV, K, V = x["N"], w.H, w.HV, w.K, w.V
     s_in = N * HV * K * V * 4 if x["initial_state"] is not None else 0
-    return (2 * T_tot * H * K * eb + T_tot * HV * V * eb + 2 * T_tot * HV * 4 + T_tot * HV * V * eb
+    return (2 * T_tot * H * K * eb + T_tot * HV * V * eb + gate_bytes(T_tot, HV, eb, fused) + T_tot * HV * V * eb
             + s_in + N * HV * K * V * 4)
 
 
@@ -111,31 +122,32 @@ def cpu_baseline(x, units_wanted):
     units = np.unique(np.linspace(0, N * HV - 1, U).round().astype(np.int64))
     threads = int(min(ncpu, len(units)))
     cpu = lambda t: None if t is None else t.cpu()
-    args = [cpu(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    args = [cpu(x[n]) for n in ("q", "k", "v")]
+    raw = [cpu(x[n]) for n in ("A_log", "dt_bias", "a", "b")]
     s0 = cpu(x["initial_state"])
     cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu().numpy()
     t0 = time.perf_counter()
-    oracle.recurrent(*args, scale=x["scale"], use_l2norm=x["use_l2norm"], initial_state=s0, cu_seqlens=cu,
-                     units=units, nthreads=threads)
+    oracle.recurrent_gated(*args, *raw, scale=x["scale"], use_l2norm=x["use_l2norm"], initial_state=s0,
+                           cu_seqlens=cu, units=units, nthreads=threads)
     dt = time.perf_counter() - t0
     lens = x["lens"]
     unit_tokens = sum(lens[int(u) // HV] for u in units)
     return {"value": unit_tokens / HV / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(units)} of {N * HV} (sequence, value head) units of the same inputs "
-                      f"({unit_tokens} unit-tokens, fp64 token recurrence, {dt:.2f} s wall)",
+                      f"({unit_tokens} unit-tokens, fp64 gates and token recurrence, {dt:.2f} s wall)",
             "seconds": dt}
 
 
 DECODE_METRIC = "fused recurrent GDN decode tokens/s on 1 MI355X (one token per sequence, pool-indexed state)"
 
 
-def decode_bytes(w, n_valid, eb):
+def decode_bytes(w, n_valid, eb, fused=False):
     """Algorithmic HBM bytes of one decode step: each valid row reads q, k (per
-    key head), v, g, beta and its K x V fp32 state, writes o and the state;
+    key head), v, its gates and its K x V fp32 state, writes o and the state;
     padded rows write o; every row reads its slot index."""
     N = w.N
-    return (n_valid * (2 * w.H * w.K * eb + w.HV * w.V * eb + 8 * w.HV + 8 * w.HV * w.K * w.V)
-            + N * w.HV * w.V * eb + 4 * N)
+    return (n_valid * (2 * w.H * w.K * eb + w.HV * w.V * eb + 8 * w.HV * w.K * w.V)
+            + gate_bytes(n_valid, w.HV, eb, fused) + N * w.HV * w.V * eb + 4 * N)
 
 
 def run_decode(args):
@@ -149,6 +161,12 @@ def run_decode(args):
     dev = torch.device("cuda:0")
     x = make_decode_inputs(w, seed=0, device=dev, io_dtype=dtype)
     n_valid = int((x["idx"] >= 0).sum())
+    gates = gdn.make_gates(x["A_log"], x["dt_bias"], x["a"], x["b"])
+    gt = torch.empty((w.N, w.HV), dtype=torch.float32, device=dev)
+    bt = torch.empty_like(gt)
+    gdt = gdn.GDN_BF16 if eb == 2 else gdn.GDN_F32
+    if args.gating == "tensors":
+        x["g"], x["beta"] = gdn.fused_gdn_gating(x["A_log"], x["a"], x["b"], x["dt_bias"])
     shape = gdn.make_decode_shape(w.N, w.H, w.HV, w.K, w.V, w.pool_size,
                                   gdn.GDN_BF16 if eb == 2 else gdn.GDN_F32)
     out = torch.empty((w.N, w.HV, w.V), dtype=dtype, device=dev)
@@ -157,8 +175,18 @@ def run_decode(args):
     pool_cpu0 = pool.cpu() if not args.no_cpu_baseline else None
 
     def step():
-        st = gdn.gdn_recurrent_update(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["use_l2norm"],
-                                      pool, x["idx"], out, shape, stream=stream)
+        if args.gating == "fused":
+            st = gdn.gdn_recurrent_update_gated(x["q"], x["k"], x["v"], gates, x["scale"], x["use_l2norm"],
+                                                pool, x["idx"], out, shape, stream=stream)
+        else:
+            g, beta = x.get("g"), x.get("beta")
+            if args.gating == "separate":
+                st = gdn.gdn_gating(gates, w.N, w.HV, gdt, gt, bt, stream=stream)
+                if st != 0:
+                    raise gdn.GdnError(st)
+                g, beta = gt, bt
+            st = gdn.gdn_recurrent_update(x["q"], x["k"], x["v"], g, beta, x["scale"], x["use_l2norm"],
+                                          pool, x["idx"], out, shape, stream=stream)
         if st != 0:
             raise gdn.GdnError(st)
 
@@ -188,17 +216,18 @@ def run_decode(args):
     kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in prof.items() if n}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dom_us = kernels[dom]["avg_us"]
-    pb = decode_bytes(w, n_valid, eb)
+    pb = decode_bytes(w, n_valid, eb, fused=args.gating == "fused")
     ach = pb / (dom_us * 1e-6) / 1e9
     khash = kernel_hash("decode")
-    traffic = MEASURED_TRAFFIC.get(khash, {}).get(w.name) if args.dtype == "bf16" else None
+    traffic = (MEASURED_TRAFFIC.get(khash, {}).get(w.name)
+               if args.dtype == "bf16" and args.gating == "tensors" else None)
     res = {
         "metric": DECODE_METRIC, "value": round(n_valid / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: N={w.N} (valid {n_valid}) H={w.H} HV={w.HV} K={w.K} V={w.V} "
-                               f"pool={w.pool_size} l2norm={w.use_l2norm}",
+                               f"pool={w.pool_size} l2norm={w.use_l2norm} gating={args.gating}",
                    "tokens": n_valid, "global_batch": w.N, "seq_len": 1, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -215,13 +244,14 @@ def run_decode(args):
         cpu = lambda t: t.cpu()[sel].unsqueeze(1)
         s0 = pool_cpu0[x["idx"].cpu()[sel].long()]
         t2 = time.perf_counter()
-        oracle.recurrent(cpu(x["q"]), cpu(x["k"]), cpu(x["v"]), cpu(x["g"]), cpu(x["beta"]), scale=x["scale"],
-                         use_l2norm=x["use_l2norm"], initial_state=s0, nthreads=ncpu)
+        oracle.recurrent_gated(cpu(x["q"]), cpu(x["k"]), cpu(x["v"]), x["A_log"].cpu(), x["dt_bias"].cpu(),
+                               cpu(x["a"]), cpu(x["b"]), scale=x["scale"], use_l2norm=x["use_l2norm"],
+                               initial_state=s0, nthreads=ncpu)
         dt = time.perf_counter() - t2
         res["cpu_baseline"] = {"value": round(len(sel) / dt, 1), "unit": "tokens/s", "cores": ncpu,
                                "kind": "oracle",
-                               "sample": f"the whole step: {len(sel)} rows x {w.HV} value heads, fp64 token "
-                                         f"recurrence from the initial pool ({dt:.3f} s wall)"}
+                               "sample": f"the whole step: {len(sel)} rows x {w.HV} value heads, fp64 gates "
+                                         f"and token recurrence from the initial pool ({dt:.3f} s wall)"}
     print(json.dumps(res), flush=True)
 
 
@@ -249,6 +279,12 @@ def main():
     x = make_inputs(w, seed=0, device=dev, io_dtype=dtype)
     B, T = x["q"].shape[0], x["q"].shape[1]
     N = x["N"]
+    gates = gdn.make_gates(x["A_log"], x["dt_bias"], x["a"], x["b"])
+    gt = torch.empty((B, T, w.HV), dtype=torch.float32, device=dev)
+    bt = torch.empty_like(gt)
+    gdt = gdn.GDN_BF16 if eb == 2 else gdn.GDN_F32
+    if args.gating == "tensors":
+        x["g"], x["beta"] = gdn.fused_gdn_gating(x["A_log"], x["a"], x["b"], x["dt_bias"])
     shape = gdn.make_shape(B, T, w.H, w.HV, w.K, w.V, N, gdn.GDN_BF16 if eb == 2 else gdn.GDN_F32)
     need = gdn.gdn_chunk_fwd_workspace_bytes(shape)
     ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
@@ -257,8 +293,18 @@ def main():
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def step():
-        st = gdn.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["use_l2norm"],
-                               x["initial_state"], x["cu_seqlens"], out, fin, shape, ws, stream=stream)
+        if args.gating == "fused":
+            st = gdn.gdn_chunk_fwd_gated(x["q"], x["k"], x["v"], gates, x["scale"], x["use_l2norm"],
+                                         x["initial_state"], x["cu_seqlens"], out, fin, shape, ws, stream=stream)
+        else:
+            g, beta = x.get("g"), x.get("beta")
+            if args.gating == "separate":
+                st = gdn.gdn_gating(gates, B * T, w.HV, gdt, gt, bt, stream=stream)
+                if st != 0:
+                    raise gdn.GdnError(st)
+                g, beta = gt, bt
+            st = gdn.gdn_chunk_fwd(x["q"], x["k"], x["v"], g, beta, x["scale"], x["use_l2norm"],
+                                   x["initial_state"], x["cu_seqlens"], out, fin, shape, ws, stream=stream)
         if st != 0:
             raise gdn.GdnError(st)
 
@@ -291,14 +337,15 @@ def main():
     tokens = sum(x["lens"])
     ms = (t1 - t0) * 1e3 / args.steps
     value = tokens / (ms / 1e3)
-    pb = path_bytes(w, x, eb)
+    pb = path_bytes(w, x, eb, fused=args.gating == "fused")
     kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in prof.items() if n}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dom_us = kernels[dom]["avg_us"]
     # the fused kernel is the whole path: its algorithmic bytes are the path's
     ach = pb / (dom_us * 1e-6) / 1e9
     khash = kernel_hash("prefill")
-    traffic = MEASURED_TRAFFIC.get(khash, {}).get(w.name) if args.dtype == "bf16" else None
+    traffic = (MEASURED_TRAFFIC.get(khash, {}).get(w.name)
+               if args.dtype == "bf16" and args.gating == "tensors" else None)
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2), "kernel_hash": khash}
@@ -314,7 +361,7 @@ def main():
         "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} T={T} N={N} H={w.H} HV={w.HV} K={w.K} V={w.V} "
-                               f"l2norm={w.use_l2norm} initial_state={w.init}",
+                               f"l2norm={w.use_l2norm} initial_state={w.init} gating={args.gating}",
                    "tokens": tokens, "global_batch": N, "seq_len": T if N == B else None,
                    "parallelism": "single GPU"},
         "roofline": roof, "path": path,

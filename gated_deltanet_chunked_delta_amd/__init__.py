@@ -1,15 +1,19 @@
-"""MI355X-native gated delta rule: chunked prefill and fused recurrent decode.
+"""MI355X-native gated delta rule: chunked prefill, fused recurrent decode and
+the gate computation.
 
 The compute path is the C-ABI library ``libgdn.so`` (hand-written HIP kernels
 for gfx950, declared in ``include/gdn.h``); this package only marshals
 arguments to it.
 """
 from ._binding import (EXPORTED, GDN_BF16, GDN_F32, GDN_OK, LIB_PATH, GdnError, chunk_gated_delta_rule,
-                       fused_recurrent_gated_delta_rule_update, gdn_chunk_fwd, gdn_chunk_fwd_workspace_bytes,
-                       gdn_decode_shape, gdn_profile_enable, gdn_profile_read, gdn_recurrent_update,
-                       gdn_shape, gdn_status_str, load_library, make_decode_shape, make_shape)
+                       fused_gdn_gating, fused_recurrent_gated_delta_rule_update, gdn_chunk_fwd,
+                       gdn_chunk_fwd_gated, gdn_chunk_fwd_workspace_bytes, gdn_decode_shape, gdn_gates,
+                       gdn_gating, gdn_profile_enable, gdn_profile_read, gdn_recurrent_update,
+                       gdn_recurrent_update_gated, gdn_shape, gdn_status_str, load_library, make_decode_shape,
+                       make_gates, make_shape)
 
 __all__ = ["EXPORTED", "GDN_BF16", "GDN_F32", "GDN_OK", "LIB_PATH", "GdnError", "chunk_gated_delta_rule",
-           "fused_recurrent_gated_delta_rule_update", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes",
-           "gdn_decode_shape", "gdn_profile_enable", "gdn_profile_read", "gdn_recurrent_update", "gdn_shape",
-           "gdn_status_str", "load_library", "make_decode_shape", "make_shape"]
+           "fused_gdn_gating", "fused_recurrent_gated_delta_rule_update", "gdn_chunk_fwd", "gdn_chunk_fwd_gated",
+           "gdn_chunk_fwd_workspace_bytes", "gdn_decode_shape", "gdn_gates", "gdn_gating", "gdn_profile_enable",
+           "gdn_profile_read", "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_shape",
+           "gdn_status_str", "load_library", "make_decode_shape", "make_gates", "make_shape"]

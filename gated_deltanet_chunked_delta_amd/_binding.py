@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK = 0
 GDN_BF16 = 0
 GDN_F32 = 1
-EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_recurrent_update", "gdn_profile_enable",
-            "gdn_profile_read", "gdn_status_str")
+EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_workspace_bytes", "gdn_gating",
+            "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_profile_enable", "gdn_profile_read",
+            "gdn_status_str")
 
 _DTYPES = {torch.bfloat16: GDN_BF16, torch.float32: GDN_F32}
 
@@ -33,6 +34,11 @@ class gdn_decode_shape(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("H", ctypes.c_int32), ("HV", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("pool_size", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
+
+
+class gdn_gates(ctypes.Structure):
+    _fields_ = [("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("a", ctypes.c_void_p),
+                ("b", ctypes.c_void_p)]
 
 
 class GdnError(RuntimeError):
@@ -64,6 +70,15 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_recurrent_update.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P,
                                          ctypes.POINTER(gdn_decode_shape), P]
     lib.gdn_recurrent_update.restype = ctypes.c_int
+    G = ctypes.POINTER(gdn_gates)
+    lib.gdn_chunk_fwd_gated.argtypes = [P, P, P, G, ctypes.c_float, ctypes.c_int, P, P, P, P,
+                                        ctypes.POINTER(gdn_shape), P, ctypes.c_size_t, P]
+    lib.gdn_chunk_fwd_gated.restype = ctypes.c_int
+    lib.gdn_recurrent_update_gated.argtypes = [P, P, P, G, ctypes.c_float, ctypes.c_int, P, P, P,
+                                               ctypes.POINTER(gdn_decode_shape), P]
+    lib.gdn_recurrent_update_gated.restype = ctypes.c_int
+    lib.gdn_gating.argtypes = [G, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    lib.gdn_gating.restype = ctypes.c_int
     lib.gdn_profile_enable.argtypes = [ctypes.c_int]
     lib.gdn_profile_enable.restype = ctypes.c_int
     lib.gdn_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -133,9 +148,9 @@ def _check(cond, msg):
         raise ValueError(msg)
 
 
-def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None, initial_state=None, output_final_state=True,
                            cu_seqlens=None, use_qk_l2norm_in_kernel=False, workspace=None, out=None,
-                           final_state=None):
+                           final_state=None, A_log=None, dt_bias=None, a_raw=None, b_raw=None):
     """Forward chunked gated delta rule on the GPU.
 
     q, k [B,T,H,K] and v [B,T,HV,V] (bf16, or fp32 for the check mode);
@@ -144,6 +159,10 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out
     ``(o [B,T,HV,V], final_state [N,HV,K,V] fp32 or None)``.  ``scale=None``
     means 1/sqrt(K).  Optional preallocated ``workspace`` (uint8),
     ``out`` and ``final_state`` are used as given.
+
+    Instead of g and beta, the raw gate inputs A_log, dt_bias [HV] fp32 and
+    a_raw, b_raw [B,T,HV] (q's dtype) may be given; the kernel then computes
+    g = -exp(A_log) softplus(a_raw + dt_bias) and beta = sigmoid(b_raw).
     """
     _check(q.dim() == 4 and k.shape == q.shape, "q and k must be [B,T,H,K] of equal shape")
     B, T, H, K = q.shape
@@ -151,9 +170,15 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out
     HV, V = v.shape[2], v.shape[3]
     _check(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype,
            "q, k, v must share one dtype (bfloat16 or float32)")
-    _check(tuple(g.shape) == (B, T, HV) and g.dtype == torch.float32, "g must be float32 [B,T,HV]")
-    _check(tuple(beta.shape) == (B, T, HV) and beta.dtype == torch.float32, "beta must be float32 [B,T,HV]")
+    gated = g is None and beta is None
     _check(q.is_cuda, "tensors must be on a GPU device (there is no CPU path)")
+    if gated:
+        A_log, dt_bias, a_raw, b_raw = _gate_inputs(A_log, dt_bias, a_raw, b_raw, (B, T, HV), q.dtype, q.device)
+    else:
+        _check(g is not None and beta is not None and all(t is None for t in (A_log, dt_bias, a_raw, b_raw)),
+               "give either g and beta or the raw gate inputs")
+        _check(tuple(g.shape) == (B, T, HV) and g.dtype == torch.float32, "g must be float32 [B,T,HV]")
+        _check(tuple(beta.shape) == (B, T, HV) and beta.dtype == torch.float32, "beta must be float32 [B,T,HV]")
     for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state),
                     ("cu_seqlens", cu_seqlens)):
         _check(t is None or t.device == q.device, f"{name} must be on {q.device}")
@@ -168,7 +193,9 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out
                f"initial_state must be float32 [{N},{HV},{K},{V}]")
     if scale is None:
         scale = K ** -0.5
-    q, k, v, g, beta = (t.contiguous() for t in (q, k, v, g, beta))
+    q, k, v = (t.contiguous() for t in (q, k, v))
+    if not gated:
+        g, beta = g.contiguous(), beta.contiguous()
     if initial_state is not None:
         initial_state = initial_state.contiguous()
     shape = make_shape(B, T, H, HV, K, V, N, _DTYPES[q.dtype])
@@ -181,8 +208,12 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out
         final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=q.device)
     if not output_final_state:
         final_state = None
-    st = gdn_chunk_fwd(q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, initial_state, cu_seqlens, out,
-                       final_state, shape, workspace)
+    if gated:
+        st = gdn_chunk_fwd_gated(q, k, v, make_gates(A_log, dt_bias, a_raw, b_raw), scale, use_qk_l2norm_in_kernel,
+                                 initial_state, cu_seqlens, out, final_state, shape, workspace)
+    else:
+        st = gdn_chunk_fwd(q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, initial_state, cu_seqlens, out,
+                           final_state, shape, workspace)
     if st != GDN_OK:
         raise GdnError(st)
     return out, final_state
@@ -204,7 +235,8 @@ def gdn_recurrent_update(q, k, v, g, beta, scale, use_l2norm, state_pool, state_
 
 
 def fused_recurrent_gated_delta_rule_update(q, k, v, g, beta, state_pool, state_indices, scale=None,
-                                            use_qk_l2norm_in_kernel=False, out=None):
+                                            use_qk_l2norm_in_kernel=False, out=None, A_log=None, dt_bias=None,
+                                            a_raw=None, b_raw=None):
     """One decode step per sequence with an in-place, pool-indexed state.
 
     q, k [N,H,K] or [N,1,H,K]; v [N,HV,V] or [N,1,HV,V] (bf16, or fp32 for the
@@ -212,6 +244,9 @@ def fused_recurrent_gated_delta_rule_update(q, k, v, g, beta, state_pool, state_
     updated in place; state_indices [N] int32 on the device (an entry outside
     [0, P), e.g. -1, marks a padding row: its slot is untouched and its output
     row is zero).  Returns o with v's shape.
+
+    With g = beta = None, the raw gate inputs A_log, dt_bias [HV] fp32 and
+    a_raw, b_raw [N,HV] or [N,1,HV] (q's dtype) give the gates in the kernel.
     """
     squeeze = q.dim() == 4
     if squeeze:
@@ -223,9 +258,16 @@ def fused_recurrent_gated_delta_rule_update(q, k, v, g, beta, state_pool, state_
     _check(ks.shape == qs.shape and vs.shape[0] == N, "q, k must be [N,H,K] and v [N,HV,V]")
     _check(qs.dtype in _DTYPES and ks.dtype == qs.dtype and vs.dtype == qs.dtype,
            "q, k, v must share one dtype (bfloat16 or float32)")
-    gs, bs = g.reshape(N, HV), beta.reshape(N, HV)
-    _check(tuple(gs.shape) == (N, HV) and gs.dtype == torch.float32, "g must be float32 [N,HV]")
-    _check(tuple(bs.shape) == (N, HV) and bs.dtype == torch.float32, "beta must be float32 [N,HV]")
+    gated = g is None and beta is None
+    if gated:
+        A_log, dt_bias, a_raw, b_raw = _gate_inputs(A_log, dt_bias, a_raw, b_raw, (N, HV), qs.dtype, qs.device)
+        gs = bs = None
+    else:
+        _check(g is not None and beta is not None and all(t is None for t in (A_log, dt_bias, a_raw, b_raw)),
+               "give either g and beta or the raw gate inputs")
+        gs, bs = g.reshape(N, HV), beta.reshape(N, HV)
+        _check(tuple(gs.shape) == (N, HV) and gs.dtype == torch.float32, "g must be float32 [N,HV]")
+        _check(tuple(bs.shape) == (N, HV) and bs.dtype == torch.float32, "beta must be float32 [N,HV]")
     _check(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (HV, K, V)
            and state_pool.dtype == torch.float32 and state_pool.is_contiguous(),
            f"state_pool must be a contiguous float32 [P,{HV},{K},{V}]")
@@ -234,14 +276,98 @@ def fused_recurrent_gated_delta_rule_update(q, k, v, g, beta, state_pool, state_
     _check(qs.is_cuda, "tensors must be on a GPU device (there is no CPU path)")
     for name, t in (("k", ks), ("v", vs), ("g", gs), ("beta", bs), ("state_pool", state_pool),
                     ("state_indices", state_indices)):
-        _check(t.device == qs.device, f"{name} must be on {qs.device}")
+        _check(t is None or t.device == qs.device, f"{name} must be on {qs.device}")
     if scale is None:
         scale = K ** -0.5
-    qs, ks, vs, gs, bs, idx = (t.contiguous() for t in (qs, ks, vs, gs, bs, state_indices))
+    qs, ks, vs, idx = (t.contiguous() for t in (qs, ks, vs, state_indices))
+    if not gated:
+        gs, bs = gs.contiguous(), bs.contiguous()
     if out is None:
         out = torch.empty((N, HV, V), dtype=qs.dtype, device=qs.device)
     shape = make_decode_shape(N, H, HV, K, V, state_pool.shape[0], _DTYPES[qs.dtype])
-    st = gdn_recurrent_update(qs, ks, vs, gs, bs, scale, use_qk_l2norm_in_kernel, state_pool, idx, out, shape)
+    if gated:
+        st = gdn_recurrent_update_gated(qs, ks, vs, make_gates(A_log, dt_bias, a_raw, b_raw), scale,
+                                        use_qk_l2norm_in_kernel, state_pool, idx, out, shape)
+    else:
+        st = gdn_recurrent_update(qs, ks, vs, gs, bs, scale, use_qk_l2norm_in_kernel, state_pool, idx, out,
+                                  shape)
     if st != GDN_OK:
         raise GdnError(st)
     return out.reshape(v.shape) if squeeze else out
+
+
+def make_gates(A_log, dt_bias, a, b) -> gdn_gates:
+    """The raw gate inputs as a gdn_gates struct of device pointers (the
+    tensors must stay alive while the struct is in use)."""
+    return gdn_gates(*(None if t is None else t.data_ptr() for t in (A_log, dt_bias, a, b)))
+
+
+def _stream(t, stream):
+    return ctypes.c_void_p(int(torch.cuda.current_stream(t.device).cuda_stream if stream is None else stream))
+
+
+def gdn_gating(gates: gdn_gates, rows, HV, dtype, g, beta, stream=None, device=None) -> int:
+    """Direct call of the C gating entry point; returns the status code."""
+    lib = load_library()
+    if stream is None:
+        stream = torch.cuda.current_stream(device if device is not None else g.device).cuda_stream
+    return int(lib.gdn_gating(ctypes.byref(gates), int(rows), int(HV), int(dtype), _ptr(g), _ptr(beta),
+                              ctypes.c_void_p(int(stream))))
+
+
+def gdn_chunk_fwd_gated(q, k, v, gates: gdn_gates, scale, use_l2norm, initial_state, cu_seqlens, out,
+                        final_state, shape: gdn_shape, workspace, workspace_bytes=None, stream=None) -> int:
+    """Direct call of the C prefill entry point with in-kernel gating."""
+    lib = load_library()
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return int(lib.gdn_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(gates), float(scale),
+                                       int(bool(use_l2norm)), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
+                                       _ptr(final_state), ctypes.byref(shape), _ptr(workspace),
+                                       int(workspace_bytes), _stream(q, stream)))
+
+
+def gdn_recurrent_update_gated(q, k, v, gates: gdn_gates, scale, use_l2norm, state_pool, state_indices, out,
+                               shape: gdn_decode_shape, stream=None) -> int:
+    """Direct call of the C decode entry point with in-kernel gating."""
+    lib = load_library()
+    return int(lib.gdn_recurrent_update_gated(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(gates), float(scale),
+                                              int(bool(use_l2norm)), _ptr(state_pool), _ptr(state_indices),
+                                              _ptr(out), ctypes.byref(shape), _stream(q, stream)))
+
+
+def _gate_inputs(A_log, dt_bias, a, b, rows_shape, io_dtype, device):
+    """Checks the raw gate inputs against a [rows..., HV] layout and returns
+    contiguous copies (a, b reshaped to rows x HV)."""
+    HV = rows_shape[-1]
+    _check(all(t is not None for t in (A_log, dt_bias, a, b)),
+           "in-kernel gating needs all of A_log, dt_bias, a_raw, b_raw")
+    _check(tuple(A_log.shape) == (HV,) and tuple(dt_bias.shape) == (HV,) and A_log.dtype == torch.float32
+           and dt_bias.dtype == torch.float32, f"A_log and dt_bias must be float32 [{HV}]")
+    n = 1
+    for d in rows_shape:
+        n *= d
+    _check(a.numel() == n and b.numel() == n and a.dtype == io_dtype and b.dtype == io_dtype,
+           f"a_raw and b_raw must hold {tuple(rows_shape)} elements of q's dtype")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("a_raw", a), ("b_raw", b)):
+        _check(t.device == device, f"{name} must be on {device}")
+    return A_log.contiguous(), dt_bias.contiguous(), a.contiguous(), b.contiguous()
+
+
+def fused_gdn_gating(A_log, a, b, dt_bias):
+    """g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b) on the GPU.
+
+    A_log, dt_bias [HV] float32; a, b [..., HV] bfloat16 or float32.
+    Returns (g, beta), float32 with a's shape."""
+    _check(a.is_cuda, "tensors must be on a GPU device (there is no CPU path)")
+    _check(a.dtype in _DTYPES and b.dtype == a.dtype and tuple(b.shape) == tuple(a.shape) and a.dim() >= 1,
+           "a and b must share one shape [..., HV] and dtype (bfloat16 or float32)")
+    HV = a.shape[-1]
+    A_log, dt_bias, ac, bc = _gate_inputs(A_log, dt_bias, a, b, tuple(a.shape), a.dtype, a.device)
+    g = torch.empty(a.shape, dtype=torch.float32, device=a.device)
+    beta = torch.empty_like(g)
+    gates = make_gates(A_log, dt_bias, ac, bc)
+    st = gdn_gating(gates, a.numel() // HV, HV, _DTYPES[a.dtype], g, beta)
+    if st != GDN_OK:
+        raise GdnError(st)
+    return g, beta

@@ -96,6 +96,114 @@ struct EventProfiler : gdn::Profiler {
 
 EventProfiler g_prof;
 
+const gdn_gates kNoGates = {nullptr, nullptr, nullptr, nullptr};
+
+// Raw gate inputs: all four pointers given, a and b 4-byte aligned.
+int check_gates(const gdn_gates &gt) {
+    if (!gt.A_log || !gt.dt_bias || !gt.a || !gt.b) return GDN_ERR_NULL;
+    if ((((uintptr_t)gt.a | (uintptr_t)gt.b) & 3u) != 0) return GDN_ERR_ALIGN;
+    return GDN_OK;
+}
+
+// The prefill entry points: g / beta given (gates == null) or gates computed
+// in the kernel from the raw inputs (gates != null).
+int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+              const gdn_gates *gates, float scale, int use_l2norm, const float *initial_state,
+              const int32_t *cu_seqlens, void *out, float *final_state, const gdn_shape *shape, void *workspace,
+              size_t workspace_bytes, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN_OK) return st;
+    const gdn_shape &s = *shape;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen ? s.B != 1 : s.N != s.B) return GDN_ERR_SHAPE;
+    const bool any_tokens = (int64_t)s.B * s.T > 0;
+    if (any_tokens && (!q || !k || !v || !out)) return GDN_ERR_NULL;
+    if (any_tokens && !gates && (!g || !beta)) return GDN_ERR_NULL;
+    if (any_tokens && gates) {
+        const int gs = check_gates(*gates);
+        if (gs != GDN_OK) return gs;
+        // bf16 gate inputs are read through their aligned 4-byte word, whose
+        // half is the same for every token only when HV is even
+        if (s.dtype == GDN_BF16 && s.HV % 2 != 0) return GDN_ERR_UNSUPPORTED;
+    }
+    const size_t need = workspace_of(s);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0))
+        return GDN_ERR_WORKSPACE;
+
+    gdn::Params p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    if (any_tokens && gates) p.gates = gdn::Gates{gates->A_log, gates->dt_bias, gates->a, gates->b};
+    p.initial_state = initial_state;
+    p.cu_seqlens = cu_seqlens;
+    p.out = out;
+    p.final_state = final_state;
+    p.B = s.B;
+    p.T = s.T;
+    p.H = s.H;
+    p.HV = s.HV;
+    p.K = s.K;
+    p.V = s.V;
+    p.N = s.N;
+    p.scale = scale;
+    p.use_l2norm = use_l2norm ? 1 : 0;
+    hipError_t err;
+    {
+        std::lock_guard<std::mutex> lock(g_prof.mu);
+        err = gdn::launch_forward(p, s.dtype, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
+    }
+    return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+// The decode entry points, as chunk_fwd.
+int recurrent_update(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                     const gdn_gates *gates, float scale, int use_l2norm, float *state_pool,
+                     const int32_t *state_indices, void *out, const gdn_decode_shape *shape, void *stream) {
+    if (!shape) return GDN_ERR_NULL;
+    const gdn_decode_shape &s = *shape;
+    if (s.N < 0 || s.H <= 0 || s.HV <= 0 || s.pool_size < 0) return GDN_ERR_SHAPE;
+    if (gdn::elem_bytes(s.dtype) == 0) return GDN_ERR_DTYPE;
+    if ((s.K != 64 && s.K != 128) || (s.V != 64 && s.V != 128) || s.HV % s.H != 0) return GDN_ERR_UNSUPPORTED;
+    if (s.N > 0 && s.pool_size < 1) return GDN_ERR_SHAPE;
+    // grid size and every index the kernel forms stay in range
+    if ((int64_t)s.N * s.HV > INT_MAX) return GDN_ERR_SHAPE;
+    if (s.N > 0 && (!q || !k || !v || !state_pool || !state_indices || !out)) return GDN_ERR_NULL;
+    if (s.N > 0 && !gates && (!g || !beta)) return GDN_ERR_NULL;
+    if (s.N > 0 && gates) {
+        const int gs = check_gates(*gates);
+        if (gs != GDN_OK) return gs;
+    }
+    if (s.N > 0 && ((uintptr_t)state_pool & 15) != 0) return GDN_ERR_ALIGN;
+
+    gdn::DecodeParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    if (s.N > 0 && gates) p.gates = gdn::Gates{gates->A_log, gates->dt_bias, gates->a, gates->b};
+    p.state_pool = state_pool;
+    p.state_indices = state_indices;
+    p.out = out;
+    p.N = s.N;
+    p.H = s.H;
+    p.HV = s.HV;
+    p.K = s.K;
+    p.V = s.V;
+    p.pool_size = s.pool_size;
+    p.scale = scale;
+    p.use_l2norm = use_l2norm ? 1 : 0;
+    hipError_t err;
+    {
+        std::lock_guard<std::mutex> lock(g_prof.mu);
+        err = gdn::launch_recurrent(p, s.dtype, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
+    }
+    return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,79 +236,45 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                   float scale, int use_l2norm, const float *initial_state, const int32_t *cu_seqlens,
                   void *out, float *final_state, const gdn_shape *shape, void *workspace,
                   size_t workspace_bytes, void *stream) {
-    const int st = check_shape(shape);
-    if (st != GDN_OK) return st;
-    const gdn_shape &s = *shape;
-    const bool varlen = cu_seqlens != nullptr;
-    if (varlen ? s.B != 1 : s.N != s.B) return GDN_ERR_SHAPE;
-    const bool any_tokens = (int64_t)s.B * s.T > 0;
-    if (any_tokens && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
-    const size_t need = workspace_of(s);
-    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0))
-        return GDN_ERR_WORKSPACE;
+    return chunk_fwd(q, k, v, g, beta, nullptr, scale, use_l2norm, initial_state, cu_seqlens, out, final_state,
+                     shape, workspace, workspace_bytes, stream);
+}
 
-    gdn::Params p{};
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.g = g;
-    p.beta = beta;
-    p.initial_state = initial_state;
-    p.cu_seqlens = cu_seqlens;
-    p.out = out;
-    p.final_state = final_state;
-    p.B = s.B;
-    p.T = s.T;
-    p.H = s.H;
-    p.HV = s.HV;
-    p.K = s.K;
-    p.V = s.V;
-    p.N = s.N;
-    p.scale = scale;
-    p.use_l2norm = use_l2norm ? 1 : 0;
-    hipError_t err;
-    {
-        std::lock_guard<std::mutex> lock(g_prof.mu);
-        err = gdn::launch_forward(p, s.dtype, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
-    }
-    return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v, const gdn_gates *gates, float scale,
+                        int use_l2norm, const float *initial_state, const int32_t *cu_seqlens, void *out,
+                        float *final_state, const gdn_shape *shape, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+    return chunk_fwd(q, k, v, nullptr, nullptr, gates ? gates : &kNoGates, scale, use_l2norm, initial_state,
+                     cu_seqlens, out, final_state, shape, workspace, workspace_bytes, stream);
 }
 
 int gdn_recurrent_update(const void *q, const void *k, const void *v, const float *g, const float *beta,
                          float scale, int use_l2norm, float *state_pool, const int32_t *state_indices,
                          void *out, const gdn_decode_shape *shape, void *stream) {
-    if (!shape) return GDN_ERR_NULL;
-    const gdn_decode_shape &s = *shape;
-    if (s.N < 0 || s.H <= 0 || s.HV <= 0 || s.pool_size < 0) return GDN_ERR_SHAPE;
-    if (gdn::elem_bytes(s.dtype) == 0) return GDN_ERR_DTYPE;
-    if ((s.K != 64 && s.K != 128) || (s.V != 64 && s.V != 128) || s.HV % s.H != 0) return GDN_ERR_UNSUPPORTED;
-    if (s.N > 0 && s.pool_size < 1) return GDN_ERR_SHAPE;
-    // grid size and every index the kernel forms stay in range
-    if ((int64_t)s.N * s.HV > INT_MAX) return GDN_ERR_SHAPE;
-    if (s.N > 0 && (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out)) return GDN_ERR_NULL;
-    if (s.N > 0 && ((uintptr_t)state_pool & 15) != 0) return GDN_ERR_ALIGN;
+    return recurrent_update(q, k, v, g, beta, nullptr, scale, use_l2norm, state_pool, state_indices, out, shape,
+                            stream);
+}
 
-    gdn::DecodeParams p{};
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.g = g;
-    p.beta = beta;
-    p.state_pool = state_pool;
-    p.state_indices = state_indices;
-    p.out = out;
-    p.N = s.N;
-    p.H = s.H;
-    p.HV = s.HV;
-    p.K = s.K;
-    p.V = s.V;
-    p.pool_size = s.pool_size;
-    p.scale = scale;
-    p.use_l2norm = use_l2norm ? 1 : 0;
+int gdn_recurrent_update_gated(const void *q, const void *k, const void *v, const gdn_gates *gates, float scale,
+                               int use_l2norm, float *state_pool, const int32_t *state_indices, void *out,
+                               const gdn_decode_shape *shape, void *stream) {
+    return recurrent_update(q, k, v, nullptr, nullptr, gates ? gates : &kNoGates, scale, use_l2norm, state_pool,
+                            state_indices, out, shape, stream);
+}
+
+int gdn_gating(const gdn_gates *gates, int64_t rows, int32_t HV, int32_t dtype, float *g, float *beta,
+               void *stream) {
+    if (rows < 0 || HV <= 0 || rows > ((int64_t)1 << 62) / HV) return GDN_ERR_SHAPE;
+    if (gdn::elem_bytes(dtype) == 0) return GDN_ERR_DTYPE;
+    if (rows == 0) return GDN_OK;
+    if (!gates || !g || !beta) return GDN_ERR_NULL;
+    const int st = check_gates(*gates);
+    if (st != GDN_OK) return st;
+    const gdn::Gates gt{gates->A_log, gates->dt_bias, gates->a, gates->b};
     hipError_t err;
     {
         std::lock_guard<std::mutex> lock(g_prof.mu);
-        err = gdn::launch_recurrent(p, s.dtype, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
+        err = gdn::launch_gating(gt, rows, HV, dtype, g, beta, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
     }
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }

@@ -35,6 +35,38 @@ template <> __device__ __forceinline__ float to_e<float>(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 
+// Gates from the raw projections (the fused gating operator of the FastDeploy
+// PR #7024 page, "Usage or Command" item 5): g = -exp(A_log) softplus(a +
+// dt_bias) with negA = -exp(A_log), beta = sigmoid(b).  Every kernel uses
+// these two functions, so in-kernel gates equal the stand-alone kernel's bit
+// for bit.  They run on the hardware exp2 / log2 / reciprocal (about one ulp
+// each):
+//   softplus(x) = max(x, 0) + log1p(e),  e = e^-|x| in (0, 1],
+//   log1p(e)    = ln(u) e / (u - 1),  u = 1 + e  (exact when u = 1: e),
+// the rewrite that cancels the rounding of u (Goldberg, "What every computer
+// scientist should know about floating-point arithmetic", on log1p), and
+//   sigmoid(b)  = 1 / (1 + e^-b),
+// which goes to 0 or 1 in the tails (the reciprocal of inf is 0).
+__device__ __forceinline__ float gate_g(float a, float negA, float dt_bias) {
+    const float x = a + dt_bias;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+    const float u = 1.f + e;
+    const float l1p = u == 1.f ? e : __builtin_amdgcn_logf(u) * 0.6931471805599453f * e * __builtin_amdgcn_rcpf(u - 1.f);
+    return negA * (fmaxf(x, 0.f) + l1p);
+}
+__device__ __forceinline__ float gate_beta(float b) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-b * 1.4426950408889634f));
+}
+
+// One raw gate input of element type E from the 4-byte word that holds it: a
+// bf16 sits in the low or high half (hi) of its aligned word.
+template <typename E> __device__ __forceinline__ float gate_raw(float word, bool hi);
+template <> __device__ __forceinline__ float gate_raw<float>(float word, bool) { return word; }
+template <> __device__ __forceinline__ float gate_raw<bf16>(float word, bool hi) {
+    const unsigned w = __float_as_uint(word);
+    return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
+}
+
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -135,6 +135,14 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
     }
     const int nchunks = (len + 63) / 64;
 
+    // Raw gate inputs, when given: the head's constants, and which half of its
+    // aligned 4-byte word a bf16 input occupies (HV is even, so the half is
+    // the parity of j for every token).
+    const bool gated = p.gates.A_log != nullptr;
+    const float negA = gated ? -expf(p.gates.A_log[j]) : 0.f;
+    const float dtb = gated ? p.gates.dt_bias[j] : 0.f;
+    const bool ghi = sizeof(E) == 2 && (j & 1);
+
     const E *__restrict__ qg = (const E *)p.q;
     const E *__restrict__ kg = (const E *)p.k;
     const E *__restrict__ vg = (const E *)p.v;
@@ -186,8 +194,14 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
         }
         if (wave == NW - 1) {
             const size_t o = (size_t)(t0 + min(lane, last)) * p.HV + j;
-            lds_copy4(p.g + o, &s.gb[buf][0]);
-            lds_copy4(p.beta + o, &s.bb[buf][0]);
+            if (gated) {   // the aligned word that holds the raw input
+                const size_t wo = (o * sizeof(E)) & ~(size_t)3;
+                lds_copy4((const char *)p.gates.a + wo, &s.gb[buf][0]);
+                lds_copy4((const char *)p.gates.b + wo, &s.bb[buf][0]);
+            } else {
+                lds_copy4(p.g + o, &s.gb[buf][0]);
+                lds_copy4(p.beta + o, &s.bb[buf][0]);
+            }
         }
     };
 
@@ -220,14 +234,18 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
 
         // ---- gate cumsum; Z = [K; Q] h, Gram tiles, squared row norms ------
         if (wave == 0) {
-            float x = s.gb[buf][lane];
+            float x = s.gb[buf][lane], bt = s.bb[buf][lane];
+            if (gated) {   // gates from the raw inputs; rows past the end read 0
+                x = lane < L ? gate_g(gate_raw<E>(x, ghi), negA, dtb) : 0.f;
+                bt = lane < L ? gate_beta(gate_raw<E>(bt, ghi)) : 0.f;
+            }
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const float y = __shfl_up(x, o);
                 if (lane >= o) x += y;
             }
             s.gam[lane] = x * 1.4426950408889634f;   // gamma in log2 units: e^{a-b} = 2^{a2-b2}
-            s.beta[lane] = s.bb[buf][lane];
+            s.beta[lane] = bt;
         }
         // This wave's Gram tiles, all transposed (C[j][i]): K K^T row tiles
         // itk = wave + NW*i (columns jt <= itk), Q K^T row tiles itq = 3 - itk
@@ -553,6 +571,7 @@ const char *kernel_name(int kind) {
         case kFusedKernel: return "fused_kernel";
         case kFusedWsKernel: return "fused_ws_kernel";
         case kRecurrentKernel: return "recurrent_update_kernel";
+        case kGatingKernel: return "gating_kernel";
         default: return "?";
     }
 }

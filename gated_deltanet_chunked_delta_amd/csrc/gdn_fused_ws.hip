@@ -27,7 +27,14 @@
 // are copies of its last row; the cumsum reads their g and beta as 0, which
 // makes their rows of A, X and V_new zero and leaves gamma_L at the last real
 // token, so they contribute nothing.
+//
+// In-kernel gating: the copying wave fetches the raw gate words of chunk c+3
+// (their own ring) and, at the start of the next step, turns those of chunk
+// c+2 into g and beta in the g/beta ring, so every gate is computed once and
+// off the step's barrier-to-barrier path.
 #include <stddef.h>
+
+#include <type_traits>
 
 #include "gdn_device.h"
 
@@ -124,6 +131,10 @@ template <int K, int VW> struct WsLds {
     float stk[4][3][64];      // per K-prep wave: gamma, beta, r of the chunk being prepared
     float stq[4][2][64];      // per Q-prep wave: gamma, r of the chunk being prepared
 };
+// With in-kernel gating: the raw gate words, by chunk parity, after the rest.
+template <int K, int VW> struct WsLdsGated : WsLds<K, VW> {
+    float ra[2][64], rb[2][64];
+};
 
 // The state h (K x V per value head) is held by the chain waves as K/16 tiles
 // of 16 key rows x 16 value columns in the accumulator layout (lane: value
@@ -138,13 +149,16 @@ __device__ __forceinline__ constexpr int kappa(int mt, int r) {
     return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3);
 }
 
-template <int K, int V>
+// GATED: the gates come from the raw inputs (p.gates) instead of p.g / p.beta.
+// A template parameter, so that the kernel without in-kernel gating carries
+// none of its code.
+template <int K, int V, bool GATED>
 __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     typedef bf16 E;
     typedef bf16x8 v8;
     typedef bf16x4 v4;
     typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-    typedef WsLds<K, 64> Lds;
+    typedef typename std::conditional<GATED, WsLdsGated<K, 64>, WsLds<K, 64>>::type Lds;
     constexpr int VW = 64, VEC = 8;
     constexpr int NSK = K / VEC, NSV = VW / VEC;
     constexpr int KT = K / 16, KS = K / 32;
@@ -182,6 +196,14 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     }
     const int nchunks = (len + 63) / 64;
 
+    // Raw gate inputs, when given: the head's constants, and which half of its
+    // aligned 4-byte word a bf16 input occupies (HV is even, so the half is
+    // the parity of j for every token).
+    constexpr bool gated = GATED;
+    const float negA = gated ? -expf(p.gates.A_log[j]) : 0.f;
+    const float dtb = gated ? p.gates.dt_bias[j] : 0.f;
+    const bool ghi = sizeof(E) == 2 && (j & 1);
+
     const E *__restrict__ qg = (const E *)p.q;
     const E *__restrict__ kg = (const E *)p.k;
     const E *__restrict__ vg = (const E *)p.v;
@@ -207,6 +229,15 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         const int L = min(64, len - 64 * c);
         b = lane < L ? s.bb[c & 1][lane] : 0.f;
         gam = wave_inclusive_scan(lane < L ? s.gb[c & 1][lane] : 0.f) * 1.4426950408889634f;
+    };
+    // With raw gate inputs, the copying wave turns the landed raw words of
+    // chunk c into g and beta (one wave computes each gate once).
+    auto gate_chunk = [&](int c) {
+        if constexpr (GATED) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");   // after the copies' wait
+            s.gb[c & 1][lane] = gate_g(gate_raw<E>(s.ra[c & 1][lane], ghi), negA, dtb);
+            s.bb[c & 1][lane] = gate_beta(gate_raw<E>(s.rb[c & 1][lane], ghi));
+        }
     };
 
     // ---- asynchronous copies (Q-prep waves) --------------------------------
@@ -259,16 +290,32 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                 lds_copy16(vc + (unsigned)min(row, last) * (unsigned)v_row + seg * VEC, vl + 1024u * t);
             }
         }
-        if (w4 == 3) {
+        if (w4 == 3 && !gated) {
             const size_t o = (size_t)(t0 + min(lane, last)) * p.HV + j;
             lds_copy4(p.g + o, lds0 + offsetof(Lds, gb) + (c & 1) * 256);
             lds_copy4(p.beta + o, lds0 + offsetof(Lds, bb) + (c & 1) * 256);
         }
     };
+    // raw gate words of chunk c (in-kernel gating; the copying wave only):
+    // the aligned 4-byte word that holds each token's input
+    auto issue_gates = [&](int c) {
+        if constexpr (GATED) {
+            const int64_t t0 = tok0 + 64LL * c;
+            const int last = min(64, len - 64 * c) - 1;
+            const size_t wo = (((size_t)(t0 + min(lane, last)) * p.HV + j) * sizeof(E)) & ~(size_t)3;
+            lds_copy4((const char *)p.gates.a + wo, (unsigned)(size_t)(lds_void *)&s.ra[c & 1][0]);
+            lds_copy4((const char *)p.gates.b + wo, (unsigned)(size_t)(lds_void *)&s.rb[c & 1][0]);
+        }
+    };
 
     if (role == 2 && nchunks > 0) {
         issue(0);
+        if (gated && w4 == 3) {
+            issue_gates(0);
+            if (nchunks > 1) issue_gates(1);
+        }
         wait_vmem();
+        if (gated && w4 == 3) gate_chunk(0);
     }
     // P blocks (0,1) and (2,3) are read by the output product but never
     // written by the epilogue: zero them once in both buffers.
@@ -288,6 +335,10 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         for (int c = -1; c < nchunks; ++c) {
             const int cn = c + 1;
             if (c + 2 < nchunks) issue(c + 2);
+            if (gated && w4 == 3) {
+                if (c + 2 < nchunks) gate_chunk(c + 2);   // its raw words landed before the last barrier
+                if (c + 3 < nchunks) issue_gates(c + 3);
+            }
             if (cn < nchunks) {
                 PrepOut &po = s.po[cn & 1];
                 float *sg = s.stq[w4][0], *sr = s.stq[w4][1];
@@ -691,10 +742,17 @@ hipError_t launch_fused_ws(const Params &p, hipStream_t st) {
     if (groups == 0) return hipSuccess;
     const int per_group = (p.HV / p.H) * (p.V / VW);
     const unsigned grid = (unsigned)((groups + 7) / 8) * 8 * per_group;
-    if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64><<<grid, 768, 0, st>>>(p);
-    else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128><<<grid, 768, 0, st>>>(p);
-    else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64><<<grid, 768, 0, st>>>(p);
-    else fused_ws_kernel<128, 128><<<grid, 768, 0, st>>>(p);
+    if (p.gates.A_log) {
+        if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, true><<<grid, 768, 0, st>>>(p);
+        else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, true><<<grid, 768, 0, st>>>(p);
+        else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, true><<<grid, 768, 0, st>>>(p);
+        else fused_ws_kernel<128, 128, true><<<grid, 768, 0, st>>>(p);
+    } else {
+        if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, false><<<grid, 768, 0, st>>>(p);
+        else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, false><<<grid, 768, 0, st>>>(p);
+        else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, false><<<grid, 768, 0, st>>>(p);
+        else fused_ws_kernel<128, 128, false><<<grid, 768, 0, st>>>(p);
+    }
     return hipGetLastError();
 }
 

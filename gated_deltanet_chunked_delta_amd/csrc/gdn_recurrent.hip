@@ -138,7 +138,15 @@ __global__ void __launch_bounds__(64 * (K / 8)) recurrent_update_kernel(DecodePa
     kq = fn[2];
     const float rk = p.use_l2norm ? rsqrtf(kk + 1e-6f) : 1.f;
     const float rq = p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f;
-    const float eg = __expf(p.g[nh]), bt = p.beta[nh];
+    float gv, bt;
+    if (p.gates.A_log) {   // gates from the raw inputs
+        gv = gate_g(to_f(((const E *)p.gates.a)[nh]), -expf(p.gates.A_log[j]), p.gates.dt_bias[j]);
+        bt = gate_beta(to_f(((const E *)p.gates.b)[nh]));
+    } else {
+        gv = p.g[nh];
+        bt = p.beta[nh];
+    }
+    const float eg = __expf(gv);
     const E *vp = (const E *)p.v + nh * V + c4;
     f32x4 u;
 #pragma unroll

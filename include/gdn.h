@@ -164,8 +164,63 @@ int gdn_recurrent_update(const void *q, const void *k, const void *v,
                          float *state_pool, const int32_t *state_indices,
                          void *out, const gdn_decode_shape *shape, void *stream);
 
-/* Kernel timing hook, for measurement.  While enabled, every gdn_chunk_fwd
- * and gdn_recurrent_update call records HIP events on its stream just before
+/* Raw gate inputs, for the entry points that compute the gates themselves:
+ *
+ *   g    = -exp(A_log[j]) * softplus(a[r, j] + dt_bias[j])
+ *   beta = sigmoid(b[r, j])
+ *
+ * per row r (token) and value head j, in fp32: the fused gating operator of
+ * the FastDeploy PR #7024 page (file table and "Usage or Command", item 5),
+ * which the LightLLM page "gdn.py" also hands to its decode kernel as A_log,
+ * dt_bias, a_raw, b_raw.  softplus(x) = ln(1 + e^x), sigmoid(x) = 1/(1 + e^-x).
+ *
+ *   A_log, dt_bias  [HV]       fp32   read (device pointers)
+ *   a, b            [rows, HV] dtype  read (device pointers; the dtype of the
+ *                   call's q/k/v: bf16, or fp32 in the check mode), 4-byte
+ *                   aligned */
+typedef struct gdn_gates {
+    const float *A_log;
+    const float *dt_bias;
+    const void *a;
+    const void *b;
+} gdn_gates;
+
+/* The stand-alone gate computation: g and beta [rows, HV] fp32 (written, every
+ * element) from `gates` with a, b of type `dtype`.  For callers that keep the
+ * gates as tensors (the un-fused prefill of the LightLLM page calls the gating
+ * operator, then the chunked kernel).
+ * Returns GDN_OK, GDN_ERR_NULL (gates, a pointer of it, g or beta NULL with
+ * rows > 0), GDN_ERR_SHAPE (rows < 0, HV <= 0, rows * HV beyond 2^62),
+ * GDN_ERR_DTYPE, GDN_ERR_LAUNCH. */
+int gdn_gating(const gdn_gates *gates, int64_t rows, int32_t HV, int32_t dtype,
+               float *g, float *beta, void *stream);
+
+/* gdn_chunk_fwd with the gates computed in the kernel from `gates` (rows =
+ * B * T) instead of read from g and beta: the same result as gdn_gating
+ * followed by gdn_chunk_fwd, up to rounding, with no g / beta tensors in
+ * memory and one launch.  All other arguments as for gdn_chunk_fwd.  With bf16
+ * inputs HV must be even (GDN_ERR_UNSUPPORTED otherwise: the kernel reads
+ * each bf16 gate input through the aligned 4-byte word that holds it); a and
+ * b must be 4-byte aligned (GDN_ERR_ALIGN). */
+int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v,
+                        const gdn_gates *gates,
+                        float scale, int use_l2norm,
+                        const float *initial_state, const int32_t *cu_seqlens,
+                        void *out, float *final_state,
+                        const gdn_shape *shape, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* gdn_recurrent_update with the gates computed in the kernel from `gates`
+ * (rows = N; a padding row's inputs are not read), as the LightLLM page's
+ * decode call does.  All other arguments as for gdn_recurrent_update. */
+int gdn_recurrent_update_gated(const void *q, const void *k, const void *v,
+                               const gdn_gates *gates,
+                               float scale, int use_l2norm,
+                               float *state_pool, const int32_t *state_indices,
+                               void *out, const gdn_decode_shape *shape, void *stream);
+
+/* Kernel timing hook, for measurement.  While enabled, every call of the
+ * entry points above records HIP events on its stream just before
  * and just after each kernel it enqueues (events are created on first use and
  * reused).
  * gdn_profile_enable(1) starts recording, gdn_profile_enable(0) stops; both

@@ -148,3 +148,15 @@ def recurrent_gated(q, k, v, A_log, dt_bias, a, b, **kw):
     the gating operator returns them."""
     g, beta = gating(A_log, dt_bias, a, b)
     return recurrent(q, k, v, g.astype(np.float32), beta.astype(np.float32), **kw)
+
+
+def add_gates(x):
+    """Adds g and beta (float32 tensors on the device of x["a"]) computed from
+    the raw gate inputs of an input dict of ``workloads`` -- the un-fused
+    entry points take them as inputs.  Returns x."""
+    import torch
+    g, beta = gating(x["A_log"], x["dt_bias"], x["a"], x["b"])
+    dev = x["a"].device
+    x["g"] = torch.from_numpy(g.astype(np.float32)).to(dev)
+    x["beta"] = torch.from_numpy(beta.astype(np.float32)).to(dev)
+    return x

@@ -114,6 +114,72 @@ def test_decode_argument_errors(shape, want):
     assert _dcall(shape) == want
 
 
+def _gates(A=FAKE, dt=FAKE, a=FAKE, b=FAKE):
+    return gdn.gdn_gates(A, dt, a, b)
+
+
+@pytest.mark.parametrize("gates,HV,dtype,want", [
+    (None, 4, 0, -1),                        # no gates struct
+    (dict(a=0), 4, 0, -1),                   # a missing
+    (dict(A=0), 4, 0, -1),                   # A_log missing
+    (dict(b=FAKE + 2), 4, 0, -7),            # b not 4-byte aligned
+    ({}, 3, 0, -4),                          # bf16 gate inputs with odd HV
+    ({}, 3, 9, -3),                          # unknown dtype
+])
+def test_prefill_gated_argument_errors(gates, HV, dtype, want):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    shape = gdn.make_shape(2, 64, 1, HV, 128, 128, 2, dtype)
+    gs = None if gates is None else ctypes.byref(_gates(**gates))
+    assert lib.gdn_chunk_fwd_gated(P(FAKE), P(FAKE), P(FAKE), gs, 1.0, 1, None, None, P(FAKE), P(FAKE),
+                                   ctypes.byref(shape), None, 0, None) == want
+
+
+def test_gated_odd_hv_fp32_and_empty_are_accepted_on_the_host():
+    # fp32 gate inputs have no word-sharing restriction; with no tokens and no
+    # sequences nothing is launched, so FAKE pointers are never touched
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    shape = gdn.make_shape(0, 0, 1, 3, 128, 128, 0, 1)
+    assert lib.gdn_chunk_fwd_gated(P(FAKE), P(FAKE), P(FAKE), ctypes.byref(_gates()), 1.0, 1, None, None,
+                                   P(FAKE), None, ctypes.byref(shape), None, 0, None) == 0
+
+
+@pytest.mark.parametrize("gates,want", [(None, -1), (dict(dt=0), -1), (dict(a=FAKE + 1), -7)])
+def test_decode_gated_argument_errors(gates, want):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    shape = gdn.make_decode_shape(4, 2, 4, 128, 128, 8, 0)
+    gs = None if gates is None else ctypes.byref(_gates(**gates))
+    assert lib.gdn_recurrent_update_gated(P(FAKE), P(FAKE), P(FAKE), gs, 1.0, 1, P(FAKE), P(FAKE), P(FAKE),
+                                          ctypes.byref(shape), None) == want
+
+
+@pytest.mark.parametrize("rows,HV,dtype,gates,want", [
+    (-1, 4, 0, {}, -2), (4, 0, 0, {}, -2), (1 << 61, 4, 0, {}, -2), (4, 4, 5, {}, -3),
+    (4, 4, 0, None, -1), (4, 4, 0, dict(b=0), -1), (4, 4, 0, dict(a=FAKE + 2), -7),
+    (0, 4, 0, None, 0),                       # nothing to compute
+])
+def test_gating_argument_errors(rows, HV, dtype, gates, want):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    gs = None if gates is None else ctypes.byref(_gates(**gates))
+    assert lib.gdn_gating(gs, rows, HV, dtype, P(FAKE), P(FAKE), None) == want
+
+
+def test_gating_wrappers_reject_cpu_tensors_and_mixed_gates():
+    import torch
+    a = torch.zeros(3, 4, dtype=torch.bfloat16)
+    A = torch.zeros(4)
+    with pytest.raises(ValueError):
+        gdn.fused_gdn_gating(A, a, a, A)
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    v = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    g = torch.zeros(1, 8, 2)
+    with pytest.raises(ValueError):   # g and raw gates together
+        gdn.chunk_gated_delta_rule(q, q, v, g, g, A_log=torch.zeros(2))
+
+
 def test_decode_misaligned_pool():
     lib = gdn.load_library()
     P = ctypes.c_void_p

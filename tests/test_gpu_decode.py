@@ -38,7 +38,7 @@ def make_case(w, N, pool_size, pad_rows, seed=0):
     drawn N(0, 0.05) and slot indices: a random injective map of the rows to
     the pool, with the rows in pad_rows marked -1 (and the last of them, if
     any, pointed past the pool instead)."""
-    x = make_inputs(scaled(w, w.name + "_decode", B=N, T=1, init="none"), seed=seed)
+    x = oracle.add_gates(make_inputs(scaled(w, w.name + "_decode", B=N, T=1, init="none"), seed=seed))
     gen = torch.Generator().manual_seed(seed + 1)
     pool = torch.randn(pool_size, w.HV, w.K, w.V, generator=gen) * 0.05
     idx = torch.randperm(pool_size, generator=gen)[:N].to(torch.int32)
@@ -106,7 +106,7 @@ def test_decode_steps_follow_the_recurrence():
     gdn = _gdn()
     w = scaled(WORKLOADS["gva"], "gva_steps", H=2, HV=4)
     N, P, T = 6, 8, 4
-    x = make_inputs(scaled(w, "gva_steps", B=N, T=T, init="none"), seed=3)
+    x = oracle.add_gates(make_inputs(scaled(w, "gva_steps", B=N, T=T, init="none"), seed=3))
     gen = torch.Generator().manual_seed(4)
     pool = torch.randn(P, w.HV, w.K, w.V, generator=gen) * 0.05
     idx = torch.tensor([5, 1, -1, 0, 7, 3], dtype=torch.int32)
@@ -138,7 +138,7 @@ def test_decode_continues_prefill():
     gdn = _gdn()
     w = scaled(WORKLOADS["gva"], "gva_cont", H=2, HV=4)
     B, T = 3, 130
-    x = make_inputs(scaled(w, "gva_cont", B=B, T=T), seed=5)
+    x = oracle.add_gates(make_inputs(scaled(w, "gva_cont", B=B, T=T), seed=5))
     d = lambda t: t.to(DEV)
     o_full, f_full = gdn.chunk_gated_delta_rule(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), d(x["beta"]),
                                                 scale=x["scale"], initial_state=d(x["initial_state"]),

@@ -78,12 +78,12 @@ SMALL = {
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_parity_small(name, dtype):
-    x = make_inputs(SMALL[name], seed=0, io_dtype=torch.float32)
+    x = oracle.add_gates(make_inputs(SMALL[name], seed=0, io_dtype=torch.float32))
     check_full(x, dtype)
 
 
 def test_final_state_aliases_initial_state():
-    x = make_inputs(SMALL["gva_ragged"], seed=1, io_dtype=torch.float32)
+    x = oracle.add_gates(make_inputs(SMALL["gva_ragged"], seed=1, io_dtype=torch.float32))
     gdn = _gdn()
     dev = torch.device("cuda:0")
     s = x["initial_state"].to(dev).clone()
@@ -98,7 +98,7 @@ def test_final_state_aliases_initial_state():
 
 
 def test_no_final_state_and_no_initial_state():
-    x = make_inputs(SMALL["tiny"], seed=2, io_dtype=torch.float32)
+    x = oracle.add_gates(make_inputs(SMALL["tiny"], seed=2, io_dtype=torch.float32))
     o, fin = run_gpu(x, torch.bfloat16, output_final_state=False)
     assert fin is None
     o_ref, _ = oracle_full(x)
@@ -106,7 +106,7 @@ def test_no_final_state_and_no_initial_state():
 
 
 def test_deterministic_bitwise():
-    x = make_inputs(SMALL["varlen_mix"], seed=3, io_dtype=torch.float32)
+    x = oracle.add_gates(make_inputs(SMALL["varlen_mix"], seed=3, io_dtype=torch.float32))
     o1, f1 = run_gpu(x, torch.bfloat16)
     o2, f2 = run_gpu(x, torch.bfloat16)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
@@ -114,7 +114,7 @@ def test_deterministic_bitwise():
 
 def test_varlen_sequences_are_isolated():
     """NaN in one packed sequence stays inside that sequence."""
-    x = make_inputs(SMALL["varlen_mix"], seed=4, io_dtype=torch.float32)
+    x = oracle.add_gates(make_inputs(SMALL["varlen_mix"], seed=4, io_dtype=torch.float32))
     cu = x["cu_seqlens"].tolist()
     o1, f1 = run_gpu(x, torch.bfloat16)
     bad = 5   # the 200-token sequence
@@ -130,7 +130,7 @@ def test_varlen_sequences_are_isolated():
 
 
 def test_outputs_fully_written():
-    x = make_inputs(SMALL["varlen_mix"], seed=5, io_dtype=torch.float32)
+    x = oracle.add_gates(make_inputs(SMALL["varlen_mix"], seed=5, io_dtype=torch.float32))
     T, HV, V = x["v"].shape[1], x["v"].shape[2], x["v"].shape[3]
     out = torch.full((1, T, HV, V), float("nan"), dtype=torch.bfloat16, device="cuda:0")
     fin = torch.full(x["initial_state"].shape, float("nan"), device="cuda:0")
@@ -140,7 +140,7 @@ def test_outputs_fully_written():
 
 def test_empty_batch():
     w = scaled(WORKLOADS["varlen"], "empty", H=2, HV=4, lengths=(0, 0, 0))
-    x = make_inputs(w, seed=6, io_dtype=torch.float32)
+    x = oracle.add_gates(make_inputs(w, seed=6, io_dtype=torch.float32))
     o, f = run_gpu(x, torch.bfloat16)
     assert o.numel() == 0
     assert torch.equal(f.cpu(), x["initial_state"])
@@ -168,7 +168,7 @@ def _sample_units(x, count, seed=0):
 def test_parity_full_size_sampled(name):
     w, count = FULL[name]
     _say(f"[parity-full] {name}: generating on the GPU")
-    x = make_inputs(w, seed=0, device="cuda:0")
+    x = oracle.add_gates(make_inputs(w, seed=0, device="cuda:0"))
     o, fin = run_gpu(x, torch.bfloat16)
     assert torch.isfinite(o).all() and torch.isfinite(fin).all()
     units = _sample_units(x, count)

@@ -60,7 +60,7 @@ def _case():
     # tiny-workload distributions, GVA and an initial state so every mutant has
     # something to break; 128 tokens keep the numpy loop fast
     w = scaled(WORKLOADS["gva"], "mut", B=1, T=128, H=2, HV=4, K=32, V=32)
-    x = make_inputs(w, seed=0, io_dtype=torch.float32)
+    x = oracle.add_gates(make_inputs(w, seed=0, io_dtype=torch.float32))
     f = lambda t: t[0].numpy().astype(np.float64)
     return x, f(x["q"]), f(x["k"]), f(x["v"]), f(x["g"]), f(x["beta"]), x["initial_state"][0].numpy()
 

@@ -2,19 +2,21 @@
 
 This module is shared by the oracle-side tests and the GPU-side tests and
 benchmark.  It holds none of the method's arithmetic: it only draws random
-tensors and applies the gating law that produces the g and beta inputs
-(g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b), in float32, as the
-fused gating kernel on the page "[Qwen3.5][Feature] support fla triton kernel
-for qwen3.5" (FastDeploy PR #7024), section "Usage or Command", item 5,
-defines them).
+tensors.  The gates are drawn as their raw inputs (a, b per token and value
+head, A_log and dt_bias per value head); g and beta follow from them by the
+gating law (g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b), the
+fused gating operator of the page "[Qwen3.5][Feature] support fla triton
+kernel for qwen3.5" (FastDeploy PR #7024), "Usage or Command", item 5), which
+each side computes itself: the oracle in float64, the GPU path in its kernels.
 
 Draw order (one torch.Generator on the target device, seeded): q, k, v, a, b,
 A_log, dt_bias, initial_state; packed workloads first draw their sequence
 lengths from a separate CPU generator with the same seed.  (CPU and GPU
 generators produce different streams: a workload drawn on the GPU has the same
-shapes and lengths as on the CPU but other values.)  q/k/v are drawn in float32 and rounded to
-bfloat16 (round to nearest even); the float32 check mode uses those same
-bf16-representable values stored as float32, so one oracle run serves both.
+shapes and lengths as on the CPU but other values.)  q/k/v and a/b are drawn
+in float32 and rounded to bfloat16 (round to nearest even), the type a model's
+projections produce; the float32 check mode uses those same bf16-representable
+values stored as float32, so one oracle run serves both.
 "N(0, s)" below means standard deviation s.
 """
 from __future__ import annotations
@@ -90,10 +92,11 @@ def scaled(w: Workload, name: str, **kw) -> Workload:
 def make_inputs(w: Workload, seed: int = 0, device="cpu", io_dtype=torch.bfloat16):
     """Draws one batch of inputs for workload ``w``.
 
-    Returns a dict with q, k [B,T,H,K] and v [B,T,HV,V] in ``io_dtype``
-    (bf16 values; float32 holds the same values), g, beta [B,T,HV] float32,
-    initial_state [N,HV,K,V] float32 or None, cu_seqlens [N+1] int32 or None,
-    scale, use_l2norm, and the sequence lengths as a Python list.
+    Returns a dict with q, k [B,T,H,K], v [B,T,HV,V] and the raw gate inputs
+    a, b [B,T,HV] in ``io_dtype`` (bf16 values; float32 holds the same
+    values), A_log, dt_bias [HV] float32, initial_state [N,HV,K,V] float32 or
+    None, cu_seqlens [N+1] int32 or None, scale, use_l2norm, and the sequence
+    lengths as a Python list.
     """
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -129,19 +132,17 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", io_dtype=torch.bfloat1
     q = io(randn(B, T, H, K, std=w.qk_std))
     k = io(randn(B, T, H, K, std=w.qk_std))
     v = io(randn(B, T, HV, V))
-    a = randn(B, T, HV)
-    b = randn(B, T, HV, std=w.b_std)
+    a = io(randn(B, T, HV))
+    b = io(randn(B, T, HV, std=w.b_std))
     a_log = torch.rand(HV, generator=gen, device=dev, dtype=f32) * w.a_log_hi
     dt_bias = torch.rand(HV, generator=gen, device=dev, dtype=f32)
-    g = -torch.exp(a_log) * torch.nn.functional.softplus(a + dt_bias)
-    beta = torch.sigmoid(b)
     if w.init == "none":
         s0 = None
     else:
         s0 = randn(N, HV, K, V, std=w.init_std)
         if w.init == "odd":
             s0[0::2] = 0.0
-    return dict(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), initial_state=s0,
+    return dict(q=q, k=k, v=v, a=a, b=b, A_log=a_log, dt_bias=dt_bias, initial_state=s0,
                 cu_seqlens=cu, scale=w.eff_scale, use_l2norm=w.use_l2norm, lens=lens,
                 N=N, workload=w)
 
@@ -175,8 +176,8 @@ DECODE_WORKLOADS = {
 
 
 def make_decode_inputs(w: DecodeWorkload, seed: int = 0, device="cpu", io_dtype=torch.bfloat16):
-    """Draws one decode step: q, k [N,H,K], v [N,HV,V] (bf16 values), g, beta
-    [N,HV] by the same gating law as make_inputs, a state pool [P,HV,K,V]
+    """Draws one decode step: q, k [N,H,K], v [N,HV,V] and the raw gate inputs
+    a, b [N,HV] (bf16 values), A_log, dt_bias [HV] float32, a state pool [P,HV,K,V]
     ~ N(0, state_std) and int32 slot indices (a random injective map into the
     pool, the first n_pad rows set to -1).  Values come from a generator on
     ``device``; the indices from a CPU generator of their own."""
@@ -195,16 +196,14 @@ def make_decode_inputs(w: DecodeWorkload, seed: int = 0, device="cpu", io_dtype=
     q = io(randn(N, H, K))
     k = io(randn(N, H, K))
     v = io(randn(N, HV, V))
-    a = randn(N, HV)
-    b = randn(N, HV)
+    a = io(randn(N, HV))
+    b = io(randn(N, HV))
     a_log = torch.rand(HV, generator=gen, device=dev, dtype=f32) * w.a_log_hi
     dt_bias = torch.rand(HV, generator=gen, device=dev, dtype=f32)
-    g = -torch.exp(a_log) * torch.nn.functional.softplus(a + dt_bias)
-    beta = torch.sigmoid(b)
     pool = randn(w.pool_size, HV, K, V, std=w.state_std)
     igen = torch.Generator()
     igen.manual_seed(seed)
     idx = torch.randperm(w.pool_size, generator=igen)[:N].to(torch.int32)
     idx[: w.n_pad] = -1
-    return dict(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), pool=pool, idx=idx.to(dev),
+    return dict(q=q, k=k, v=v, a=a, b=b, A_log=a_log, dt_bias=dt_bias, pool=pool, idx=idx.to(dev),
                 scale=w.eff_scale, use_l2norm=w.use_l2norm, workload=w)
