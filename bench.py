@@ -143,10 +143,12 @@ DECODE_METRIC = "fused recurrent GDN decode tokens/s on 1 MI355X (one token per 
 
 def decode_bytes(w, n_valid, eb, fused=False):
     """Algorithmic HBM bytes of one decode step: each valid row reads q, k (per
-    key head), v, its gates and its K x V fp32 state, writes o and the state;
-    padded rows write o; every row reads its slot index."""
+    key head), v, its gates and its K x V state (fp32 or bf16), writes o and
+    the state; padded rows write o; every row reads its slot index."""
+    import torch
     N = w.N
-    return (n_valid * (2 * w.H * w.K * eb + w.HV * w.V * eb + 8 * w.HV * w.K * w.V)
+    sb = 2 if w.pool_dtype == torch.bfloat16 else 4
+    return (n_valid * (2 * w.H * w.K * eb + w.HV * w.V * eb + 2 * sb * w.HV * w.K * w.V)
             + gate_bytes(n_valid, w.HV, eb, fused) + N * w.HV * w.V * eb + 4 * N)
 
 
@@ -174,8 +176,20 @@ def run_decode(args):
     stream = torch.cuda.current_stream(dev).cuda_stream
     pool_cpu0 = pool.cpu() if not args.no_cpu_baseline else None
 
+    spool = gdn.make_state_pool(pool, x["idx"]) if pool.dtype == torch.bfloat16 else None
+
     def step():
-        if args.gating == "fused":
+        if spool is not None:   # a bf16 pool: the pool entry point
+            g, beta = x.get("g"), x.get("beta")
+            if args.gating == "separate":
+                st = gdn.gdn_gating(gates, w.N, w.HV, gdt, gt, bt, stream=stream)
+                if st != 0:
+                    raise gdn.GdnError(st)
+                g, beta = gt, bt
+            st = gdn.gdn_recurrent_update_pool(x["q"], x["k"], x["v"], g, beta,
+                                               gates if args.gating == "fused" else None, x["scale"],
+                                               x["use_l2norm"], spool, out, shape, stream=stream)
+        elif args.gating == "fused":
             st = gdn.gdn_recurrent_update_gated(x["q"], x["k"], x["v"], gates, x["scale"], x["use_l2norm"],
                                                 pool, x["idx"], out, shape, stream=stream)
         else:
@@ -227,7 +241,8 @@ def run_decode(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: N={w.N} (valid {n_valid}) H={w.H} HV={w.HV} K={w.K} V={w.V} "
-                               f"pool={w.pool_size} l2norm={w.use_l2norm} gating={args.gating}",
+                               f"pool={w.pool_size} ({str(w.pool_dtype)[6:]}) l2norm={w.use_l2norm} "
+                               f"gating={args.gating}",
                    "tokens": n_valid, "global_batch": w.N, "seq_len": 1, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK = 0
 GDN_BF16 = 0
 GDN_F32 = 1
-EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_workspace_bytes", "gdn_gating",
-            "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_profile_enable", "gdn_profile_read",
-            "gdn_status_str")
+EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_pool", "gdn_chunk_fwd_workspace_bytes",
+            "gdn_gating", "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_recurrent_update_pool",
+            "gdn_profile_enable", "gdn_profile_read", "gdn_status_str")
 
 _DTYPES = {torch.bfloat16: GDN_BF16, torch.float32: GDN_F32}
 
@@ -39,6 +39,11 @@ class gdn_decode_shape(ctypes.Structure):
 class gdn_gates(ctypes.Structure):
     _fields_ = [("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("a", ctypes.c_void_p),
                 ("b", ctypes.c_void_p)]
+
+
+class gdn_state_pool(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("indices", ctypes.c_void_p), ("pool_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("read_initial", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -79,6 +84,13 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_recurrent_update_gated.restype = ctypes.c_int
     lib.gdn_gating.argtypes = [G, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.gdn_gating.restype = ctypes.c_int
+    SP = ctypes.POINTER(gdn_state_pool)
+    lib.gdn_chunk_fwd_pool.argtypes = [P, P, P, P, P, G, ctypes.c_float, ctypes.c_int, SP, P, P,
+                                       ctypes.POINTER(gdn_shape), P, ctypes.c_size_t, P]
+    lib.gdn_chunk_fwd_pool.restype = ctypes.c_int
+    lib.gdn_recurrent_update_pool.argtypes = [P, P, P, P, P, G, ctypes.c_float, ctypes.c_int, SP, P,
+                                              ctypes.POINTER(gdn_decode_shape), P]
+    lib.gdn_recurrent_update_pool.restype = ctypes.c_int
     lib.gdn_profile_enable.argtypes = [ctypes.c_int]
     lib.gdn_profile_enable.restype = ctypes.c_int
     lib.gdn_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -150,7 +162,8 @@ def _check(cond, msg):
 
 def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None, initial_state=None, output_final_state=True,
                            cu_seqlens=None, use_qk_l2norm_in_kernel=False, workspace=None, out=None,
-                           final_state=None, A_log=None, dt_bias=None, a_raw=None, b_raw=None):
+                           final_state=None, A_log=None, dt_bias=None, a_raw=None, b_raw=None,
+                           ssm_state_pool=None, ssm_state_indices=None, read_initial_state=True):
     """Forward chunked gated delta rule on the GPU.
 
     q, k [B,T,H,K] and v [B,T,HV,V] (bf16, or fp32 for the check mode);
@@ -163,6 +176,12 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None, initial_state
     Instead of g and beta, the raw gate inputs A_log, dt_bias [HV] fp32 and
     a_raw, b_raw [B,T,HV] (q's dtype) may be given; the kernel then computes
     g = -exp(A_log) softplus(a_raw + dt_bias) and beta = sigmoid(b_raw).
+
+    With ``ssm_state_pool`` [P,HV,K,V] (float32 or bfloat16) and
+    ``ssm_state_indices`` [N] int32, sequence n starts from slot
+    ssm_state_indices[n] (from zero if ``read_initial_state`` is False) and its
+    final state is written back to that slot in place; initial_state and
+    final_state are then not used and the call returns ``(o, None)``.
     """
     _check(q.dim() == 4 and k.shape == q.shape, "q and k must be [B,T,H,K] of equal shape")
     B, T, H, K = q.shape
@@ -188,6 +207,17 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None, initial_state
         N = cu_seqlens.shape[0] - 1
     else:
         N = B
+    pooled = ssm_state_pool is not None
+    if pooled:
+        _check(initial_state is None and final_state is None,
+               "with a state pool, initial and final states live in the pool")
+        _check(ssm_state_pool.dim() == 4 and tuple(ssm_state_pool.shape[1:]) == (HV, K, V)
+               and ssm_state_pool.dtype in _DTYPES and ssm_state_pool.is_contiguous()
+               and ssm_state_pool.device == q.device,
+               f"ssm_state_pool must be a contiguous float32/bfloat16 [P,{HV},{K},{V}] on {q.device}")
+        _check(ssm_state_indices is not None and tuple(ssm_state_indices.shape) == (N,)
+               and ssm_state_indices.dtype == torch.int32 and ssm_state_indices.device == q.device,
+               f"ssm_state_indices must be int32 [{N}] on {q.device}")
     if initial_state is not None:
         _check(tuple(initial_state.shape) == (N, HV, K, V) and initial_state.dtype == torch.float32,
                f"initial_state must be float32 [{N},{HV},{K},{V}]")
@@ -204,6 +234,14 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None, initial_state
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, T, HV, V), dtype=q.dtype, device=q.device)
+    if pooled:
+        pool = make_state_pool(ssm_state_pool, ssm_state_indices.contiguous(), read_initial_state)
+        gates = make_gates(A_log, dt_bias, a_raw, b_raw) if gated else None
+        st = gdn_chunk_fwd_pool(q, k, v, g, beta, gates, scale, use_qk_l2norm_in_kernel, pool, cu_seqlens, out,
+                                shape, workspace)
+        if st != GDN_OK:
+            raise GdnError(st)
+        return out, None
     if output_final_state and final_state is None:
         final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=q.device)
     if not output_final_state:
@@ -240,8 +278,8 @@ def fused_recurrent_gated_delta_rule_update(q, k, v, g, beta, state_pool, state_
     """One decode step per sequence with an in-place, pool-indexed state.
 
     q, k [N,H,K] or [N,1,H,K]; v [N,HV,V] or [N,1,HV,V] (bf16, or fp32 for the
-    check mode); g, beta [N,HV] or [N,1,HV] fp32; state_pool [P,HV,K,V] fp32,
-    updated in place; state_indices [N] int32 on the device (an entry outside
+    check mode); g, beta [N,HV] or [N,1,HV] fp32; state_pool [P,HV,K,V] fp32
+    or bf16 (rounded to nearest even when stored), updated in place; state_indices [N] int32 on the device (an entry outside
     [0, P), e.g. -1, marks a padding row: its slot is untouched and its output
     row is zero).  Returns o with v's shape.
 
@@ -269,8 +307,8 @@ def fused_recurrent_gated_delta_rule_update(q, k, v, g, beta, state_pool, state_
         _check(tuple(gs.shape) == (N, HV) and gs.dtype == torch.float32, "g must be float32 [N,HV]")
         _check(tuple(bs.shape) == (N, HV) and bs.dtype == torch.float32, "beta must be float32 [N,HV]")
     _check(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (HV, K, V)
-           and state_pool.dtype == torch.float32 and state_pool.is_contiguous(),
-           f"state_pool must be a contiguous float32 [P,{HV},{K},{V}]")
+           and state_pool.dtype in _DTYPES and state_pool.is_contiguous(),
+           f"state_pool must be a contiguous float32 or bfloat16 [P,{HV},{K},{V}]")
     _check(tuple(state_indices.shape) == (N,) and state_indices.dtype == torch.int32,
            "state_indices must be int32 [N]")
     _check(qs.is_cuda, "tensors must be on a GPU device (there is no CPU path)")
@@ -285,7 +323,11 @@ def fused_recurrent_gated_delta_rule_update(q, k, v, g, beta, state_pool, state_
     if out is None:
         out = torch.empty((N, HV, V), dtype=qs.dtype, device=qs.device)
     shape = make_decode_shape(N, H, HV, K, V, state_pool.shape[0], _DTYPES[qs.dtype])
-    if gated:
+    if state_pool.dtype == torch.bfloat16:
+        gates = make_gates(A_log, dt_bias, a_raw, b_raw) if gated else None
+        st = gdn_recurrent_update_pool(qs, ks, vs, gs, bs, gates, scale, use_qk_l2norm_in_kernel,
+                                       make_state_pool(state_pool, idx), out, shape)
+    elif gated:
         st = gdn_recurrent_update_gated(qs, ks, vs, make_gates(A_log, dt_bias, a_raw, b_raw), scale,
                                         use_qk_l2norm_in_kernel, state_pool, idx, out, shape)
     else:
@@ -371,3 +413,34 @@ def fused_gdn_gating(A_log, a, b, dt_bias):
     if st != GDN_OK:
         raise GdnError(st)
     return g, beta
+
+
+def make_state_pool(data, indices, read_initial=True) -> gdn_state_pool:
+    """A gdn_state_pool struct over a [P,HV,K,V] tensor (float32 or bfloat16)
+    and [N] int32 slot indices (the tensors must stay alive while it is used)."""
+    return gdn_state_pool(data.data_ptr(), indices.data_ptr(), int(data.shape[0]), _DTYPES[data.dtype],
+                          int(bool(read_initial)))
+
+
+def gdn_chunk_fwd_pool(q, k, v, g, beta, gates, scale, use_l2norm, pool: gdn_state_pool, cu_seqlens, out,
+                       shape: gdn_shape, workspace, workspace_bytes=None, stream=None) -> int:
+    """Direct call of the C prefill entry point with a state pool (gates may
+    be None: g and beta are then used)."""
+    lib = load_library()
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return int(lib.gdn_chunk_fwd_pool(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      None if gates is None else ctypes.byref(gates), float(scale),
+                                      int(bool(use_l2norm)), ctypes.byref(pool), _ptr(cu_seqlens), _ptr(out),
+                                      ctypes.byref(shape), _ptr(workspace), int(workspace_bytes),
+                                      _stream(q, stream)))
+
+
+def gdn_recurrent_update_pool(q, k, v, g, beta, gates, scale, use_l2norm, pool: gdn_state_pool, out,
+                              shape: gdn_decode_shape, stream=None) -> int:
+    """Direct call of the C decode entry point with a state pool."""
+    lib = load_library()
+    return int(lib.gdn_recurrent_update_pool(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                             None if gates is None else ctypes.byref(gates), float(scale),
+                                             int(bool(use_l2norm)), ctypes.byref(pool), _ptr(out),
+                                             ctypes.byref(shape), _stream(q, stream)))

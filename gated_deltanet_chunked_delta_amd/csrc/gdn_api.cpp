@@ -105,12 +105,22 @@ int check_gates(const gdn_gates &gt) {
     return GDN_OK;
 }
 
+// A state pool: data, indices given, a known dtype, at least one slot, data
+// aligned for the decode kernel's vector accesses (16 bytes in fp32, 8 in bf16).
+int check_pool(const gdn_state_pool &pl) {
+    if (!pl.data || !pl.indices) return GDN_ERR_NULL;
+    if (pl.dtype != GDN_BF16 && pl.dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (pl.pool_size < 1) return GDN_ERR_SHAPE;
+    if (((uintptr_t)pl.data & (pl.dtype == GDN_BF16 ? 7u : 15u)) != 0) return GDN_ERR_ALIGN;
+    return GDN_OK;
+}
+
 // The prefill entry points: g / beta given (gates == null) or gates computed
 // in the kernel from the raw inputs (gates != null).
 int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
               const gdn_gates *gates, float scale, int use_l2norm, const float *initial_state,
               const int32_t *cu_seqlens, void *out, float *final_state, const gdn_shape *shape, void *workspace,
-              size_t workspace_bytes, void *stream) {
+              size_t workspace_bytes, void *stream, const gdn_state_pool *pool = nullptr) {
     const int st = check_shape(shape);
     if (st != GDN_OK) return st;
     const gdn_shape &s = *shape;
@@ -125,6 +135,10 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
         // bf16 gate inputs are read through their aligned 4-byte word, whose
         // half is the same for every token only when HV is even
         if (s.dtype == GDN_BF16 && s.HV % 2 != 0) return GDN_ERR_UNSUPPORTED;
+    }
+    if (pool && s.N > 0) {
+        const int ps = check_pool(*pool);
+        if (ps != GDN_OK) return ps;
     }
     const size_t need = workspace_of(s);
     if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0))
@@ -150,6 +164,13 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
     p.N = s.N;
     p.scale = scale;
     p.use_l2norm = use_l2norm ? 1 : 0;
+    if (pool && s.N > 0) {
+        p.initial_state = pool->read_initial ? (const float *)pool->data : nullptr;
+        p.final_state = (float *)pool->data;
+        p.state_indices = pool->indices;
+        p.pool_size = pool->pool_size;
+        p.state_bf16 = pool->dtype == GDN_BF16;
+    }
     hipError_t err;
     {
         std::lock_guard<std::mutex> lock(g_prof.mu);
@@ -161,7 +182,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
 // The decode entry points, as chunk_fwd.
 int recurrent_update(const void *q, const void *k, const void *v, const float *g, const float *beta,
                      const gdn_gates *gates, float scale, int use_l2norm, float *state_pool,
-                     const int32_t *state_indices, void *out, const gdn_decode_shape *shape, void *stream) {
+                     const int32_t *state_indices, void *out, const gdn_decode_shape *shape, void *stream,
+                     bool state_bf16 = false) {
     if (!shape) return GDN_ERR_NULL;
     const gdn_decode_shape &s = *shape;
     if (s.N < 0 || s.H <= 0 || s.HV <= 0 || s.pool_size < 0) return GDN_ERR_SHAPE;
@@ -176,7 +198,7 @@ int recurrent_update(const void *q, const void *k, const void *v, const float *g
         const int gs = check_gates(*gates);
         if (gs != GDN_OK) return gs;
     }
-    if (s.N > 0 && ((uintptr_t)state_pool & 15) != 0) return GDN_ERR_ALIGN;
+    if (s.N > 0 && ((uintptr_t)state_pool & (state_bf16 ? 7u : 15u)) != 0) return GDN_ERR_ALIGN;
 
     gdn::DecodeParams p{};
     p.q = q;
@@ -196,6 +218,7 @@ int recurrent_update(const void *q, const void *k, const void *v, const float *g
     p.pool_size = s.pool_size;
     p.scale = scale;
     p.use_l2norm = use_l2norm ? 1 : 0;
+    p.state_bf16 = state_bf16 ? 1 : 0;
     hipError_t err;
     {
         std::lock_guard<std::mutex> lock(g_prof.mu);
@@ -260,6 +283,28 @@ int gdn_recurrent_update_gated(const void *q, const void *k, const void *v, cons
                                const gdn_decode_shape *shape, void *stream) {
     return recurrent_update(q, k, v, nullptr, nullptr, gates ? gates : &kNoGates, scale, use_l2norm, state_pool,
                             state_indices, out, shape, stream);
+}
+
+int gdn_chunk_fwd_pool(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                       const gdn_gates *gates, float scale, int use_l2norm, const gdn_state_pool *pool,
+                       const int32_t *cu_seqlens, void *out, const gdn_shape *shape, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (!pool) return GDN_ERR_NULL;
+    return chunk_fwd(q, k, v, g, beta, gates, scale, use_l2norm, nullptr, cu_seqlens, out, nullptr, shape,
+                     workspace, workspace_bytes, stream, pool);
+}
+
+int gdn_recurrent_update_pool(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                              const gdn_gates *gates, float scale, int use_l2norm, const gdn_state_pool *pool,
+                              void *out, const gdn_decode_shape *shape, void *stream) {
+    if (!pool || !shape) return GDN_ERR_NULL;
+    if (shape->N > 0) {
+        const int ps = check_pool(*pool);
+        if (ps != GDN_OK) return ps;
+        if (shape->pool_size != pool->pool_size) return GDN_ERR_SHAPE;
+    }
+    return recurrent_update(q, k, v, g, beta, gates, scale, use_l2norm, (float *)pool->data, pool->indices, out,
+                            shape, stream, pool->dtype == GDN_BF16);
 }
 
 int gdn_gating(const gdn_gates *gates, int64_t rows, int32_t HV, int32_t dtype, float *g, float *beta,

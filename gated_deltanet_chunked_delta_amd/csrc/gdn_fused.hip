@@ -150,16 +150,28 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
 
     // state: CPW column tiles x KT row tiles, C layout
     f32x4 h[CPW][KT];
-    const size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0;
-    if (p.initial_state) {
+    size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0;
+    bool s_in = p.initial_state != nullptr, s_out = p.final_state != nullptr;
+    if (p.state_indices) {   // state pool: the slot of sequence n (outside the pool: none)
+        const int slot = p.state_indices[n];
+        const bool ok = slot >= 0 && slot < p.pool_size;
+        s_in = s_in && ok;
+        s_out = s_out && ok;
+        sbase = ((size_t)(ok ? slot : 0) * p.HV + j) * K * V + vcol0;
+    }
+    if (s_in) {
         const float *__restrict__ s0 = p.initial_state + sbase;
+        const bf16 *__restrict__ s0h = (const bf16 *)p.initial_state + sbase;
 #pragma unroll
         for (int ct = 0; ct < CPW; ++ct) {
             const int col = 16 * (wave * CPW + ct) + l16;
 #pragma unroll
             for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[ct][mt][e] = s0[(16 * mt + 4 * grp + e) * V + col];
+                for (int e = 0; e < 4; ++e) {
+                    const size_t o = (size_t)(16 * mt + 4 * grp + e) * V + col;
+                    h[ct][mt][e] = p.state_bf16 ? to_f(s0h[o]) : s0[o];
+                }
         }
     } else {
 #pragma unroll
@@ -530,15 +542,20 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
         }
     }
 
-    if (p.final_state) {
+    if (s_out) {
 #pragma unroll
         for (int ct = 0; ct < CPW; ++ct) {
             const int col = 16 * (wave * CPW + ct) + l16;
 #pragma unroll
             for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    p.final_state[sbase + (size_t)(16 * mt + 4 * grp + e) * V + col] = h[ct][mt][e];
+                for (int e = 0; e < 4; ++e) {
+                    const size_t o = sbase + (size_t)(16 * mt + 4 * grp + e) * V + col;
+                    if (p.state_bf16)
+                        ((bf16 *)p.final_state)[o] = (bf16)h[ct][mt][e];
+                    else
+                        p.final_state[o] = h[ct][mt][e];
+                }
         }
     }
 }

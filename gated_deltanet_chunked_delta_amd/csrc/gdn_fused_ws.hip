@@ -150,9 +150,10 @@ __device__ __forceinline__ constexpr int kappa(int mt, int r) {
 }
 
 // GATED: the gates come from the raw inputs (p.gates) instead of p.g / p.beta.
-// A template parameter, so that the kernel without in-kernel gating carries
-// none of its code.
-template <int K, int V, bool GATED>
+// POOL: the states live in a slot-indexed pool and/or are stored as bf16
+// (p.state_indices, p.state_bf16).  Template parameters, so that the plain
+// kernel carries none of their code.
+template <int K, int V, bool GATED, bool POOL>
 __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     typedef bf16 E;
     typedef bf16x8 v8;
@@ -574,8 +575,22 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                    (((2 * w4 + ((l16 & 3) >> 1)) ^ swz<NSV>(4 * grp + (l16 >> 2))) << 4) + 8 * (l16 & 1);
 
     f32x4 h[KT];
-    const size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0;
-    if (p.initial_state) {
+    size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0;
+    bool s_in = p.initial_state != nullptr, s_out = p.final_state != nullptr;
+    if (POOL && p.state_indices) {   // state pool: the slot of sequence n (outside the pool: none)
+        const int slot = p.state_indices[n];
+        const bool ok = slot >= 0 && slot < p.pool_size;
+        s_in = s_in && ok;
+        s_out = s_out && ok;
+        sbase = ((size_t)(ok ? slot : 0) * p.HV + j) * K * V + vcol0;
+    }
+    if (POOL && s_in && p.state_bf16) {
+        const bf16 *__restrict__ s0 = (const bf16 *)p.initial_state + sbase;
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[mt][e] = to_f(s0[(size_t)kappa(mt, 4 * grp + e) * V + c0 + l16]);
+    } else if (s_in) {
         const float *__restrict__ s0 = p.initial_state + sbase;
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
@@ -724,13 +739,28 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         lds_barrier();
     }
 
-    if (p.final_state) {
+    if (POOL && s_out && p.state_bf16) {
+        bf16 *__restrict__ sf = (bf16 *)p.final_state + sbase;
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sf[(size_t)kappa(mt, 4 * grp + e) * V + c0 + l16] = (bf16)h[mt][e];
+    } else if (s_out) {
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 p.final_state[sbase + (size_t)kappa(mt, 4 * grp + e) * V + c0 + l16] = h[mt][e];
     }
+}
+
+template <bool GATED, bool POOL>
+hipError_t launch_ws_kv(const Params &p, unsigned grid, hipStream_t st) {
+    if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, GATED, POOL><<<grid, 768, 0, st>>>(p);
+    else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, GATED, POOL><<<grid, 768, 0, st>>>(p);
+    else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, GATED, POOL><<<grid, 768, 0, st>>>(p);
+    else fused_ws_kernel<128, 128, GATED, POOL><<<grid, 768, 0, st>>>(p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -742,18 +772,11 @@ hipError_t launch_fused_ws(const Params &p, hipStream_t st) {
     if (groups == 0) return hipSuccess;
     const int per_group = (p.HV / p.H) * (p.V / VW);
     const unsigned grid = (unsigned)((groups + 7) / 8) * 8 * per_group;
-    if (p.gates.A_log) {
-        if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, true><<<grid, 768, 0, st>>>(p);
-        else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, true><<<grid, 768, 0, st>>>(p);
-        else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, true><<<grid, 768, 0, st>>>(p);
-        else fused_ws_kernel<128, 128, true><<<grid, 768, 0, st>>>(p);
-    } else {
-        if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, false><<<grid, 768, 0, st>>>(p);
-        else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, false><<<grid, 768, 0, st>>>(p);
-        else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, false><<<grid, 768, 0, st>>>(p);
-        else fused_ws_kernel<128, 128, false><<<grid, 768, 0, st>>>(p);
-    }
-    return hipGetLastError();
+    const bool gated = p.gates.A_log != nullptr, pool = p.state_indices != nullptr || p.state_bf16;
+    if (gated && pool) return launch_ws_kv<true, true>(p, grid, st);
+    if (gated) return launch_ws_kv<true, false>(p, grid, st);
+    if (pool) return launch_ws_kv<false, true>(p, grid, st);
+    return launch_ws_kv<false, false>(p, grid, st);
 }
 
 }  // namespace gdn

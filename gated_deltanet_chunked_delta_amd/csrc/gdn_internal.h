@@ -35,6 +35,13 @@ struct Params {
     float scale;
     int use_l2norm;
     Gates gates;                     // used instead of g, beta when gates.A_log != null
+    // State pool: when state_indices is non-null, initial_state and
+    // final_state point at one pool [pool_size, HV, K, V] and sequence n uses
+    // slot state_indices[n] (a slot outside the pool: zero start, no store).
+    // state_bf16: the states (pool or not) are stored as bf16.
+    const int32_t *state_indices;
+    int pool_size;
+    int state_bf16;
 };
 
 // The kernels of one forward pass, for the timing hook.
@@ -62,12 +69,13 @@ struct DecodeParams {
     const void *q, *k, *v;           // [N, H, K], [N, H, K], [N, HV, V]
     const float *g, *beta;           // [N, HV]
     Gates gates;                     // used instead of g, beta when gates.A_log != null
-    float *state_pool;               // [pool_size, HV, K, V], updated in place
+    float *state_pool;               // [pool_size, HV, K, V], updated in place (bf16 when state_bf16)
     const int32_t *state_indices;    // [N]
     void *out;                       // [N, HV, V]
     int N, H, HV, K, V, pool_size;
     float scale;
     int use_l2norm;
+    int state_bf16;
 };
 
 // Enqueues the decode step (gdn_recurrent.hip).

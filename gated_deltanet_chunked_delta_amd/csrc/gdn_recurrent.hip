@@ -1,5 +1,5 @@
 // Fused recurrent decode step (one token per sequence) with an in-place,
-// pool-indexed fp32 state, for gfx950.
+// pool-indexed state (fp32, or bf16 rounded to nearest even), for gfx950.
 //
 // For sequence n, value head j and state slot s = state_indices[n] (a slot
 // outside [0, pool_size) marks a padding row), with kh, qh the (optionally
@@ -17,17 +17,17 @@
 // kernel with its ssm_pool / ssm_indices interface).
 //
 // The step is bound by HBM: every (sequence, value head) reads and writes its
-// K x V fp32 state once (2 * 4 K V bytes) and touches only K + K + V other
-// elements.  One workgroup of K/8 waves owns the whole state of one
-// (sequence, value head).  A lane holds four adjacent columns (one 16-byte
-// piece) of 8 / (64 / (V/4)) rows, so one wave-wide access covers 64 / (V/4)
-// full rows (1 KiB); each wave keeps its 8 rows in registers between the read
-// and the write.  The inner products over rows are summed across the lanes
-// that share columns, then across the waves through LDS.  Fewer than 64
-// registers per lane let 8 waves share a SIMD, which keeps enough state reads
-// in flight to approach the HBM rate.  The state is touched exactly once each
-// way, so its loads and stores are marked non-temporal (streamed past the
-// caches rather than kept in them).
+// K x V state once (2 * 4 K V bytes in fp32, half that in a bf16 pool) and
+// touches only K + K + V other elements.  One workgroup of K/8 waves owns the
+// whole state of one (sequence, value head).  A lane holds four adjacent
+// columns (16 bytes in fp32, 8 in bf16) of 8 / (64 / (V/4)) rows, so one
+// wave-wide access covers 64 / (V/4) full rows; each wave keeps its 8 rows in
+// registers (fp32) between the read and the write.  The inner products over
+// rows are summed across the lanes that share columns, then across the waves
+// through LDS.  Fewer than 64 registers per lane let 8 waves share a SIMD,
+// which keeps enough state reads in flight to approach the HBM rate.  The
+// state is touched exactly once each way, so its loads and stores are marked
+// non-temporal (streamed past the caches rather than kept in them).
 #include "gdn_device.h"
 
 namespace gdn {
@@ -41,7 +41,27 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-template <typename E, int K, int V>
+// Four consecutive state elements of type S (fp32 or bf16) as fp32, and back
+// (bf16 rounded to nearest even); non-temporal: each state byte is touched
+// once each way.
+template <typename S> struct State4;
+template <> struct State4<float> {
+    typedef f32x4 T;
+    static __device__ __forceinline__ f32x4 load(const T *p) { return __builtin_nontemporal_load(p); }
+    static __device__ __forceinline__ void store(T *p, f32x4 x) { __builtin_nontemporal_store(x, p); }
+};
+template <> struct State4<bf16> {
+    typedef bf16x4 T;
+    static __device__ __forceinline__ f32x4 load(const T *p) {
+        const bf16x4 x = __builtin_nontemporal_load(p);
+        return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    }
+    static __device__ __forceinline__ void store(T *p, f32x4 x) {
+        __builtin_nontemporal_store(bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}, p);
+    }
+};
+
+template <typename E, typename SE, int K, int V>
 __global__ void __launch_bounds__(64 * (K / 8)) recurrent_update_kernel(DecodeParams p) {
     constexpr int NW = K / 8;                  // waves per workgroup (8 rows each)
     constexpr int LPR = V / 4;                 // lanes per state row (4 columns each)
@@ -62,11 +82,12 @@ __global__ void __launch_bounds__(64 * (K / 8)) recurrent_update_kernel(DecodePa
         return;
     }
     // the lane's rows are wv*RW + i*RPI + rl, i < NI, at columns c4 .. c4+3
-    f32x4 *__restrict__ S =
-        (f32x4 *)(p.state_pool + (((size_t)slot * p.HV + j) * K + wv * RW + rl) * V + c4);
+    typedef State4<SE> SIO;
+    typename SIO::T *__restrict__ S =
+        (typename SIO::T *)((SE *)p.state_pool + (((size_t)slot * p.HV + j) * K + wv * RW + rl) * V + c4);
     f32x4 s[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) s[i] = __builtin_nontemporal_load(S + i * RPI * V / 4);
+    for (int i = 0; i < NI; ++i) s[i] = SIO::load(S + i * RPI * V / 4);
 
     // key and query rows (raw) in LDS; squared norms and k.q by a workgroup
     // reduction, combined after the barrier that publishes the rows
@@ -153,8 +174,7 @@ __global__ void __launch_bounds__(64 * (K / 8)) recurrent_update_kernel(DecodePa
     for (int e = 0; e < 4; ++e) u[e] = to_f(vp[e]) - eg * rk * a[e];
     const f32x4 bu = u * (bt * rk);            // beta u times the key norm factor
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-        __builtin_nontemporal_store(eg * s[i] + bu * ks[wv * RW + i * RPI + rl], S + i * RPI * V / 4);
+    for (int i = 0; i < NI; ++i) SIO::store(S + i * RPI * V / 4, eg * s[i] + bu * ks[wv * RW + i * RPI + rl]);
     if (wv == 0 && rl == 0) {
         const float cq = bt * kq * rk * rq;
 #pragma unroll
@@ -162,19 +182,24 @@ __global__ void __launch_bounds__(64 * (K / 8)) recurrent_update_kernel(DecodePa
     }
 }
 
-template <typename E, int K, int V>
+template <typename E, typename SE, int K, int V>
 hipError_t launch_cfg(const DecodeParams &p, hipStream_t st) {
     const unsigned grid = (unsigned)((size_t)p.N * p.HV);
-    recurrent_update_kernel<E, K, V><<<grid, 64 * (K / 8), 0, st>>>(p);
+    recurrent_update_kernel<E, SE, K, V><<<grid, 64 * (K / 8), 0, st>>>(p);
     return hipGetLastError();
+}
+
+template <typename E, typename SE>
+hipError_t launch_kv(const DecodeParams &p, hipStream_t st) {
+    if (p.K == 64 && p.V == 64) return launch_cfg<E, SE, 64, 64>(p, st);
+    if (p.K == 64 && p.V == 128) return launch_cfg<E, SE, 64, 128>(p, st);
+    if (p.K == 128 && p.V == 64) return launch_cfg<E, SE, 128, 64>(p, st);
+    return launch_cfg<E, SE, 128, 128>(p, st);
 }
 
 template <typename E>
 hipError_t launch_dtype(const DecodeParams &p, hipStream_t st) {
-    if (p.K == 64 && p.V == 64) return launch_cfg<E, 64, 64>(p, st);
-    if (p.K == 64 && p.V == 128) return launch_cfg<E, 64, 128>(p, st);
-    if (p.K == 128 && p.V == 64) return launch_cfg<E, 128, 64>(p, st);
-    return launch_cfg<E, 128, 128>(p, st);
+    return p.state_bf16 ? launch_kv<E, bf16>(p, st) : launch_kv<E, float>(p, st);
 }
 
 }  // namespace

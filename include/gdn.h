@@ -219,6 +219,58 @@ int gdn_recurrent_update_gated(const void *q, const void *k, const void *v,
                                float *state_pool, const int32_t *state_indices,
                                void *out, const gdn_decode_shape *shape, void *stream);
 
+/* A state pool: the recurrent states of the sequences a server keeps, one
+ * slot per sequence, read and updated in place by prefill and decode (the
+ * ssm_pool / ssm_indices interface of the FastDeploy PR #7024 page, "Usage or
+ * Command" item 2, and the ssm_states buffer with b_ssm_buffer_idx and a
+ * bf16 or fp32 state type of the LightLLM page "gdn.py").
+ *
+ *   data          [pool_size, HV, K, V] of dtype (device); 16-byte aligned in
+ *                 fp32, 8-byte in bf16 (GDN_ERR_ALIGN otherwise)
+ *   indices       [N] int32 (device): the slot of sequence n.  A slot outside
+ *                 [0, pool_size) (the PAD_SLOT_ID -1 of the FastDeploy page
+ *                 included) gives the sequence no state: prefill runs it from
+ *                 zero and stores nothing, decode writes a zero output row.
+ *                 Two sequences must not name the same slot.
+ *   pool_size     slots in the pool (>= 1 when N > 0)
+ *   dtype         GDN_F32, or GDN_BF16: states are read as bf16 and the
+ *                 updated state is rounded to bf16 (nearest even) when stored;
+ *                 the arithmetic stays fp32
+ *   read_initial  prefill only: non-zero = each sequence starts from its
+ *                 slot's state; 0 = from zero (the slot is only written), so
+ *                 no dummy zero state is ever read (the FastDeploy page's
+ *                 review comments ask for exactly this flag) */
+typedef struct gdn_state_pool {
+    void *data;
+    const int32_t *indices;
+    int32_t pool_size;
+    int32_t dtype;
+    int32_t read_initial;
+} gdn_state_pool;
+
+/* Prefill with the states in a pool: as gdn_chunk_fwd (or, when gates is
+ * non-NULL, gdn_chunk_fwd_gated, g and beta then unused), with sequence n's
+ * initial state read from and its final state written to slot indices[n] of
+ * the pool, in place.  Returns the statuses of those calls, and GDN_ERR_NULL
+ * (no pool, or no data / indices), GDN_ERR_DTYPE (pool dtype), GDN_ERR_SHAPE
+ * (pool_size < 1) and GDN_ERR_ALIGN for the pool. */
+int gdn_chunk_fwd_pool(const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, const gdn_gates *gates,
+                       float scale, int use_l2norm,
+                       const gdn_state_pool *pool, const int32_t *cu_seqlens, void *out,
+                       const gdn_shape *shape, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Decode with a pool of either state type: as gdn_recurrent_update (or, when
+ * gates is non-NULL, gdn_recurrent_update_gated) on pool->data at the slots
+ * pool->indices; shape->pool_size must equal pool->pool_size (GDN_ERR_SHAPE);
+ * read_initial is ignored (decode always continues the slot's state). */
+int gdn_recurrent_update_pool(const void *q, const void *k, const void *v,
+                              const float *g, const float *beta, const gdn_gates *gates,
+                              float scale, int use_l2norm,
+                              const gdn_state_pool *pool, void *out,
+                              const gdn_decode_shape *shape, void *stream);
+
 /* Kernel timing hook, for measurement.  While enabled, every call of the
  * entry points above records HIP events on its stream just before
  * and just after each kernel it enqueues (events are created on first use and

@@ -160,3 +160,24 @@ def add_gates(x):
     x["g"] = torch.from_numpy(g.astype(np.float32)).to(dev)
     x["beta"] = torch.from_numpy(beta.astype(np.float32)).to(dev)
     return x
+
+
+def recurrent_pool(q, k, v, g, beta, pool, indices, read_initial=True, **kw):
+    """``recurrent`` against a state pool [P,HV,K,V] (any float type): sequence
+    n starts from pool[indices[n]] (from zero when read_initial is false or the
+    slot lies outside [0, P), a sequence with no state) and its final state
+    replaces that slot.  Returns (o, pool_after) with pool_after a float64 copy
+    of the pool holding the final states (unrounded) in the named slots."""
+    import torch
+    pool64 = pool.detach().to("cpu", torch.float64).numpy() if isinstance(pool, torch.Tensor) \
+        else np.asarray(pool, dtype=np.float64)
+    idx = np.asarray(indices.cpu() if isinstance(indices, torch.Tensor) else indices, dtype=np.int64)
+    P = pool64.shape[0]
+    valid = (idx >= 0) & (idx < P)
+    s0 = np.zeros((len(idx),) + pool64.shape[1:], dtype=np.float64)
+    if read_initial:
+        s0[valid] = pool64[idx[valid]]
+    o, fin = recurrent(q, k, v, g, beta, initial_state=s0.astype(np.float32), **kw)
+    after = pool64.copy()
+    after[idx[valid]] = fin[valid]
+    return o, after

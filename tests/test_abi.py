@@ -180,6 +180,39 @@ def test_gating_wrappers_reject_cpu_tensors_and_mixed_gates():
         gdn.chunk_gated_delta_rule(q, q, v, g, g, A_log=torch.zeros(2))
 
 
+def _pool(data=FAKE, idx=FAKE, P=8, dtype=0, read=1):
+    return gdn.gdn_state_pool(data, idx, P, dtype, read)
+
+
+@pytest.mark.parametrize("pool,want", [
+    (None, -1),                                  # no pool struct
+    (dict(data=0), -1), (dict(idx=0), -1),       # pool without data / indices
+    (dict(dtype=7), -3),                         # unknown pool dtype
+    (dict(P=0), -2),                             # empty pool with sequences
+    (dict(data=FAKE + 2, dtype=0), -7),          # a bf16 pool needs 8-byte alignment
+    (dict(data=FAKE + 8, dtype=1), -7),          # an fp32 pool needs 16-byte alignment
+])
+def test_prefill_pool_argument_errors(pool, want):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    shape = gdn.make_shape(2, 64, 1, 2, 128, 128, 2, 0)
+    pl = None if pool is None else ctypes.byref(_pool(**pool))
+    assert lib.gdn_chunk_fwd_pool(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 1.0, 1, pl, None, P(FAKE),
+                                  ctypes.byref(shape), None, 0, None) == want
+
+
+@pytest.mark.parametrize("pool,pool_size,want", [
+    (None, 8, -1), (dict(data=FAKE + 8, dtype=1), 8, -7), (dict(P=8), 9, -2), (dict(dtype=3), 8, -3),
+])
+def test_decode_pool_argument_errors(pool, pool_size, want):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    shape = gdn.make_decode_shape(4, 2, 4, 128, 128, pool_size, 0)
+    pl = None if pool is None else ctypes.byref(_pool(**pool))
+    assert lib.gdn_recurrent_update_pool(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 1.0, 1, pl, P(FAKE),
+                                         ctypes.byref(shape), None) == want
+
+
 def test_decode_misaligned_pool():
     lib = gdn.load_library()
     P = ctypes.c_void_p

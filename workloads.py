@@ -162,6 +162,7 @@ class DecodeWorkload:
     scale: Optional[float] = None
     a_log_hi: float = math.log(16.0)
     state_std: float = 0.05
+    pool_dtype: torch.dtype = torch.float32
 
     @property
     def eff_scale(self) -> float:
@@ -169,16 +170,18 @@ class DecodeWorkload:
 
 
 # A serving-style decode batch of the GVA model shape: 256 running sequences in
-# a 512-slot state pool, 8 padded rows.
+# a 512-slot state pool, 8 padded rows; the same with a bf16 pool.
 DECODE_WORKLOADS = {
     "decode": DecodeWorkload("decode", N=256, H=16, HV=32, K=128, V=128, pool_size=512, n_pad=8),
+    "decode_bf16pool": DecodeWorkload("decode_bf16pool", N=256, H=16, HV=32, K=128, V=128, pool_size=512,
+                                      n_pad=8, pool_dtype=torch.bfloat16),
 }
 
 
 def make_decode_inputs(w: DecodeWorkload, seed: int = 0, device="cpu", io_dtype=torch.bfloat16):
     """Draws one decode step: q, k [N,H,K], v [N,HV,V] and the raw gate inputs
     a, b [N,HV] (bf16 values), A_log, dt_bias [HV] float32, a state pool [P,HV,K,V]
-    ~ N(0, state_std) and int32 slot indices (a random injective map into the
+    of w.pool_dtype ~ N(0, state_std) and int32 slot indices (a random injective map into the
     pool, the first n_pad rows set to -1).  Values come from a generator on
     ``device``; the indices from a CPU generator of their own."""
     dev = torch.device(device)
@@ -200,7 +203,7 @@ def make_decode_inputs(w: DecodeWorkload, seed: int = 0, device="cpu", io_dtype=
     b = io(randn(N, HV))
     a_log = torch.rand(HV, generator=gen, device=dev, dtype=f32) * w.a_log_hi
     dt_bias = torch.rand(HV, generator=gen, device=dev, dtype=f32)
-    pool = randn(w.pool_size, HV, K, V, std=w.state_std)
+    pool = randn(w.pool_size, HV, K, V, std=w.state_std).to(w.pool_dtype)
     igen = torch.Generator()
     igen.manual_seed(seed)
     idx = torch.randperm(w.pool_size, generator=igen)[:N].to(torch.int32)
