@@ -34,8 +34,6 @@
 // off the step's barrier-to-barrier path.
 #include <stddef.h>
 
-#include <type_traits>
-
 #include "gdn_device.h"
 
 namespace gdn {
@@ -127,13 +125,10 @@ template <int K, int VW> struct WsLds {
     bf16 vb[3][64 * VW];      // raw v rows of this slice (swizzled), ring of three chunks
     float gb[2][64], bb[2][64];
     PrepOut po[2];
-    float adiag[4][16 * 20];  // per K-prep wave: its diagonal block of A, fp32, transposed (A_ij at 20 j + i)
+    float adiag[4][16 * 20];  // per K-prep wave: its diagonal block of A, fp32, by column: A_ij at 20 j + 4 (i % 4) + i / 4
     float stk[4][3][64];      // per K-prep wave: gamma, beta, r of the chunk being prepared
     float stq[4][2][64];      // per Q-prep wave: gamma, r of the chunk being prepared
-};
-// With in-kernel gating: the raw gate words, by chunk parity, after the rest.
-template <int K, int VW> struct WsLdsGated : WsLds<K, VW> {
-    float ra[2][64], rb[2][64];
+    float ra[2][64], rb[2][64];  // in-kernel gating: raw gate words by chunk parity (unused otherwise)
 };
 
 // The state h (K x V per value head) is held by the chain waves as K/16 tiles
@@ -159,7 +154,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     typedef bf16x8 v8;
     typedef bf16x4 v4;
     typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-    typedef typename std::conditional<GATED, WsLdsGated<K, 64>, WsLds<K, 64>>::type Lds;
+    typedef WsLds<K, 64> Lds;
     constexpr int VW = 64, VEC = 8;
     constexpr int NSK = K / VEC, NSV = VW / VEC;
     constexpr int KT = K / 16, KS = K / 32;
@@ -349,60 +344,84 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                     sg[lane] = gam;
                 }
                 const E *kb = s.kb[cn % 3], *qb = s.qb[cn & 1];
-                // Transposed Gram tiles C[j][i] = k_j . q_i of row tile itq = w4
-                // against column tiles jt <= itq, Q Q^T's diagonal tile, and the
-                // diagonal tiles of K K^T for the norms of every k row
-                auto qprep = [&](auto itq_c) {
-                    constexpr int itq = decltype(itq_c)::value;
-                    f32x4 gq[itq + 1], gd[itq + 1], gqq = f32x4{0.f, 0.f, 0.f, 0.f};
+                // The ten causal tiles of Q K^T, spread so that no wave waits for
+                // another inside the step; each wave also computes the diagonal
+                // tiles of Q Q^T and K K^T for the norms its tiles need:
+                //   wave 0: rows 0, 1 (tiles (0,0) (1,0) (1,1));  wave 1: row 2;
+                //   wave 2: (3,0) (3,1) (3,2);  wave 3: (3,3)
+                // (7, 7, 7 and 3 tiles, against 3, 5, 7 and 9 for whole row tiles).
+                // Tiles are transposed: C[j][i] = k_j . q_i.
+                auto qprep = [&](auto w_c) {
+                    constexpr int W = decltype(w_c)::value;
+                    constexpr int R0 = W == 0 ? 0 : W == 1 ? 2 : 3, R1 = W == 0 ? 1 : W == 1 ? 2 : 3;
+                    constexpr int J0 = W == 3 ? 3 : 0, J1 = W == 0 ? 1 : W == 3 ? 3 : 2;
+                    constexpr int NR = R1 - R0 + 1, NJ = J1 - J0 + 1;
+                    f32x4 gq[NR][NJ], gd[NJ], gqq[NR];
 #pragma unroll
-                    for (int jt = 0; jt <= itq; ++jt) {
-                        gq[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        gd[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int r = 0; r < NR; ++r) {
+                        gqq[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int jj = 0; jj < NJ; ++jj) gq[r][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
+#pragma unroll
+                    for (int jj = 0; jj < NJ; ++jj) gd[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s2 = 0; s2 < KS; ++s2) {
-                        v8 fk[itq + 1];
+                        v8 fk[NJ], bq[NR];
 #pragma unroll
-                        for (int t = 0; t <= itq; ++t) fk[t] = frag(kb, t, s2);
-                        const v8 bq = frag(qb, itq, s2);
+                        for (int jj = 0; jj < NJ; ++jj) fk[jj] = frag(kb, J0 + jj, s2);
 #pragma unroll
-                        for (int jt = 0; jt <= itq; ++jt) {
-                            gq[jt] = mma(fk[jt], bq, gq[jt]);
-                            gd[jt] = mma(fk[jt], fk[jt], gd[jt]);
+                        for (int r = 0; r < NR; ++r) bq[r] = frag(qb, R0 + r, s2);
+#pragma unroll
+                        for (int jj = 0; jj < NJ; ++jj) {
+                            gd[jj] = mma(fk[jj], fk[jj], gd[jj]);
+#pragma unroll
+                            for (int r = 0; r < NR; ++r)
+                                if (J0 + jj <= R0 + r) gq[r][jj] = mma(fk[jj], bq[r], gq[r][jj]);
                         }
-                        gqq = mma(bq, bq, gqq);
+#pragma unroll
+                        for (int r = 0; r < NR; ++r) gqq[r] = mma(bq[r], bq[r], gqq[r]);
                     }
-                    // norms of the k rows of tiles 0..itq from the diagonals: lane
+                    // norms of the k rows of tiles J0..J1 from the diagonals: lane
                     // (l16, l16 / 4) holds row l16 at e = l16 % 4
                     {
                         const int e = l16 - 4 * grp;
                         if (e >= 0 && e < 4) {
 #pragma unroll
-                            for (int t = 0; t <= itq; ++t) sr[16 * t + l16] = p.use_l2norm ? rsqrtf(gd[t][e] + 1e-6f) : 1.f;
+                            for (int jj = 0; jj < NJ; ++jj)
+                                sr[16 * (J0 + jj) + l16] = p.use_l2norm ? rsqrtf(gd[jj][e] + 1e-6f) : 1.f;
                         }
                     }
-                    const float qq = __shfl(gqq[l16 & 3], (l16 >> 2) * 16 + l16);
-                    const float rho = p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f;
-                    if (grp == 0) po.rq[16 * itq + l16] = rho;
+                    float rho[NR];
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const float qq = __shfl(gqq[r][l16 & 3], (l16 >> 2) * 16 + l16);
+                        rho[r] = p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f;
+                        if (W != 2 && grp == 0) po.rq[16 * (R0 + r) + l16] = rho[r];   // row 3: wave 3 publishes
+                    }
                     wave_lds_sync();   // the staged gamma and r come from other lanes
-                    const int iq = 16 * itq + l16;
-                    const float giq = sg[iq], srq = p.scale * rho;
-                    f32x4 gj[itq + 1], rj[itq + 1];
+                    f32x4 gj[NJ], rj[NJ];
 #pragma unroll
-                    for (int jt = 0; jt <= itq; ++jt) {
-                        gj[jt] = *(const f32x4 *)&sg[16 * jt + 4 * grp];
-                        rj[jt] = *(const f32x4 *)&sr[16 * jt + 4 * grp];
+                    for (int jj = 0; jj < NJ; ++jj) {
+                        gj[jj] = *(const f32x4 *)&sg[16 * (J0 + jj) + 4 * grp];
+                        rj[jj] = *(const f32x4 *)&sr[16 * (J0 + jj) + 4 * grp];
                     }
 #pragma unroll
-                    for (int jt = 0; jt <= itq; ++jt) {
-                        v4 o;
+                    for (int r = 0; r < NR; ++r) {
+                        const int itq = R0 + r, iq = 16 * itq + l16;
+                        const float giq = sg[iq], srq = p.scale * rho[r];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float v = srq * rj[jt][e] * fast_exp2(giq - gj[jt][e]) * gq[jt][e];
-                            o[e] = (E)((jt < itq || iq >= 16 * jt + 4 * grp + e) ? v : 0.f);
+                        for (int jj = 0; jj < NJ; ++jj) {
+                            const int jt = J0 + jj;
+                            if (jt > itq) continue;
+                            v4 o;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float v = srq * rj[jj][e] * fast_exp2(giq - gj[jj][e]) * gq[r][jj][e];
+                                o[e] = (E)((jt < itq || iq >= 16 * jt + 4 * grp + e) ? v : 0.f);
+                            }
+                            *(v4 *)&po.p[iq][pcol(jt, grp)] = o;
                         }
-                        *(v4 *)&po.p[iq][pcol(jt, grp)] = o;
                     }
                 };
                 switch (w4) {
@@ -436,72 +455,92 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                     }
                 }
                 const E *kb = s.kb[cn % 3];
-                // Transposed Gram tiles C[j][i] = k_j . k_i of row tile itk = w4
-                // against column tiles jt <= itk, and the other diagonal tiles
-                // for the norms of every k row
-                auto kprep = [&](auto itk_c) {
-                    constexpr int itk = decltype(itk_c)::value;
-                    f32x4 gk[itk + 1], gd[itk + 1];
+                // The ten lower Gram tiles of K K^T are spread so that no wave
+                // waits for another inside the step: wave W computes its own
+                // diagonal tile (for A_WW and D_W), two off-diagonal tiles (i, j)
+                // and the further diagonal tiles whose norms those need:
+                //   W = 0: (1,0) (2,0), diagonals 0 1 2;  W = 1: (2,1) (3,1), 1 2 3;
+                //   W = 2: (3,0) (3,2), diagonals 0 2 3;  W = 3: diagonal 3 only
+                // (5, 5, 5 and 1 tiles, against 1, 3, 5 and 7 for whole row tiles).
+                // Tiles are transposed: C[j][i] = k_j . k_i.
+                auto kprep = [&](auto w_c) {
+                    constexpr int W = decltype(w_c)::value;
+                    constexpr int NOFF = W == 3 ? 0 : 2;
+                    constexpr int OI0 = W == 0 ? 1 : W == 1 ? 2 : 3, OJ0 = W == 0 ? 0 : W == 1 ? 1 : 0;
+                    constexpr int OI1 = W == 0 ? 2 : 3, OJ1 = W == 0 ? 0 : W == 1 ? 1 : 2;
+                    constexpr int DM = W == 0 ? 0x7 : W == 1 ? 0xE : W == 2 ? 0xD : 0x8;
+                    f32x4 gd[4], go[2];
 #pragma unroll
-                    for (int jt = 0; jt <= itk; ++jt) {
-                        gk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        gd[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
+                    for (int t = 0; t < 4; ++t) gd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    go[0] = go[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s2 = 0; s2 < KS; ++s2) {
-                        v8 fk[itk + 1];
+                        v8 fk[4];
 #pragma unroll
-                        for (int t = 0; t <= itk; ++t) fk[t] = frag(kb, t, s2);
+                        for (int t = 0; t < 4; ++t)
+                            if (DM >> t & 1) fk[t] = frag(kb, t, s2);
 #pragma unroll
-                        for (int jt = 0; jt <= itk; ++jt) {
-                            gk[jt] = mma(fk[jt], fk[itk], gk[jt]);
-                            if (jt < itk) gd[jt] = mma(fk[jt], fk[jt], gd[jt]);
+                        for (int t = 0; t < 4; ++t)
+                            if (DM >> t & 1) gd[t] = mma(fk[t], fk[t], gd[t]);
+                        if (NOFF > 0) {
+                            go[0] = mma(fk[OJ0], fk[OI0], go[0]);
+                            go[1] = mma(fk[OJ1], fk[OI1], go[1]);
                         }
                     }
-                    gd[itk] = gk[itk];
-                    // norms of the rows of tiles 0..itk from the diagonals: lane
+                    // norms of the rows of the computed diagonal tiles: lane
                     // (l16, l16 / 4) holds row l16 at e = l16 % 4
                     {
                         const int e = l16 - 4 * grp;
                         if (e >= 0 && e < 4) {
 #pragma unroll
-                            for (int t = 0; t <= itk; ++t) sr[16 * t + l16] = p.use_l2norm ? rsqrtf(gd[t][e] + 1e-6f) : 1.f;
+                            for (int t = 0; t < 4; ++t)
+                                if (DM >> t & 1) sr[16 * t + l16] = p.use_l2norm ? rsqrtf(gd[t][e] + 1e-6f) : 1.f;
                         }
                     }
                     wave_lds_sync();   // the staged gamma / beta / r come from other lanes
-                    f32x4 gj[itk + 1], rj[itk + 1];
-#pragma unroll
-                    for (int jt = 0; jt <= itk; ++jt) {
-                        gj[jt] = *(const f32x4 *)&sg[16 * jt + 4 * grp];
-                        rj[jt] = *(const f32x4 *)&sr[16 * jt + 4 * grp];
-                    }
-                    const f32x4 bd = *(const f32x4 *)&sb[16 * itk + 4 * grp];
-                    const int ik = 16 * itk + l16;
-                    const float gik = sg[ik], rik = sr[ik], bik = sb[ik];
-                    {   // diagonal tile -> A_itk,itk (fp32, transposed).  The raw Gram
-                        // tile is symmetric, so the lane's values serve as rows
-                        // i = 16 itk + 4 grp + e of column j = 16 itk + l16, which
-                        // makes the transposed store one vector per lane.
-                        f32x4 a;
+                    {   // diagonal tile -> A_WW (fp32, by column).  The raw Gram tile
+                        // is symmetric, so the lane's values serve as rows i = 4 grp + e
+                        // (of the tile) of column j = l16.  Rows are stored in the
+                        // order the solve's lanes take them (i % 4 major), so that
+                        // each solve step reads one vector.
+                        const f32x4 gw = *(const f32x4 *)&sg[16 * W + 4 * grp];
+                        const f32x4 rw = *(const f32x4 *)&sr[16 * W + 4 * grp];
+                        const f32x4 bw = *(const f32x4 *)&sb[16 * W + 4 * grp];
+                        const int ik = 16 * W + l16;
+                        const float gik = sg[ik], rik = sr[ik];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float v = bd[e] * rj[itk][e] * rik * fast_exp2(gj[itk][e] - gik) * gk[itk][e];
-                            a[e] = (4 * grp + e > l16) ? v : 0.f;
-                        }
-                        *(f32x4 *)&s.adiag[w4][20 * l16 + 4 * grp] = a;
-                    }
-                    {   // off-diagonal tiles of row tile itk -> -A (bf16)
-                        const float bri = bik * rik;
-#pragma unroll
-                        for (int jt = 0; jt < itk; ++jt) {
-                            v4 o;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                o[e] = (E)(-(bri * rj[jt][e] * fast_exp2(gik - gj[jt][e]) * gk[jt][e]));
-                            *(v4 *)&po.alo[ik][16 * jt + 4 * grp] = o;
+                            const float v = bw[e] * rw[e] * rik * fast_exp2(gw[e] - gik) * gd[W][e];
+                            s.adiag[W][20 * l16 + 4 * e + grp] = (4 * grp + e > l16) ? v : 0.f;
                         }
                     }
-                    wave_lds_sync();   // A_itk,itk is read back across lanes by the solve
+                    // off-diagonal tiles (i, j) -> -A (bf16): row 16 i + l16,
+                    // columns 16 j + 4 grp + e
+                    auto off = [&](auto oi_c, auto oj_c, const f32x4 &g) {
+                        constexpr int OI = decltype(oi_c)::value, OJ = decltype(oj_c)::value;
+                        const int ik = 16 * OI + l16;
+                        const float gik = sg[ik], bri = sb[ik] * sr[ik];
+                        const f32x4 gj = *(const f32x4 *)&sg[16 * OJ + 4 * grp];
+                        const f32x4 rj = *(const f32x4 *)&sr[16 * OJ + 4 * grp];
+                        v4 o;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[e] = (E)(-(bri * rj[e] * fast_exp2(gik - gj[e]) * g[e]));
+                        *(v4 *)&po.alo[ik][16 * OJ + 4 * grp] = o;
+                    };
+                    if constexpr (NOFF > 0) {
+                        off(IC<OI0>(), IC<OJ0>(), go[0]);
+                        off(IC<OI1>(), IC<OJ1>(), go[1]);
+                    }
+                    // beta e^gamma r, r e^{gamma_L - gamma} for the rows of tile W,
+                    // e^{gamma_L} (wave 0), for the chain
+                    if (grp == 0) {
+                        const int i = 16 * W + l16;
+                        const float gi = sg[i], gl = sg[63], ri = sr[i];
+                        po.bgr[i] = sb[i] * fast_exp2(gi) * ri;
+                        po.kf[i] = ri * fast_exp2(gl - gi);
+                        if (W == 0 && l16 == 0) po.decay = fast_exp2(gl);
+                    }
+                    wave_lds_sync();   // A_WW is read back across lanes by the solve
                 };
                 switch (w4) {
                     case 0: kprep(IC<0>()); break;
@@ -509,46 +548,37 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                     case 2: kprep(IC<2>()); break;
                     default: kprep(IC<3>()); break;
                 }
-                if (w4 == 3) {   // beta e^gamma r, r e^{gamma_L - gamma}, e^{gamma_L} for the chain
-                    const float gi = sg[lane], gl = sg[63], ri = sr[lane];
-                    po.bgr[lane] = sb[lane] * fast_exp2(gi) * ri;
-                    po.kf[lane] = ri * fast_exp2(gl - gi);
-                    if (lane == 0) po.decay = fast_exp2(gl);
-                }
-                // D_w = (I + A_w,w)^-1 by column-oriented forward substitution,
-                // lane = column of D: once x_m is final it updates every later
-                // row, so each step has up to 15 independent updates.  Columns
-                // of A stream in a few steps ahead of their use.
-                if (grp == 0) {
+                // D_w = (I + A_w,w)^-1 by column-oriented forward substitution
+                // with every lane busy: the four lanes of quad c hold column c
+                // of D, lane g of the quad rows g, g+4, g+8, g+12.  Once x_m is
+                // final it is broadcast inside each quad (one DPP move) and
+                // updates every row; A being strictly lower, the rows at or
+                // above m take zeros, so each step is four branch-free FMAs.
+                {
                     const float *AT = s.adiag[w4];
-                    const int cc = l16;
-                    constexpr int PF = 3;
-                    float x[16];
-                    f32x4 col[15][4];
-                    auto load_col = [&](int m) {
+                    const int cc = lane >> 2, gg = lane & 3;
+                    float x[4];
 #pragma unroll
-                        for (int c4 = (m + 1) / 4; c4 < 4; ++c4) col[m][c4] = *(const f32x4 *)&AT[20 * m + 4 * c4];
+                    for (int q = 0; q < 4; ++q) x[q] = (4 * q + gg == cc) ? 1.f : 0.f;
+                    f32x4 col[16];
+#pragma unroll
+                    for (int m = 0; m < 15; ++m) col[m] = *(const f32x4 *)&AT[20 * m + 4 * gg];
+                    auto bcast = [&](auto m_c) {   // x_m from lane m % 4 of the quad
+                        constexpr int m = decltype(m_c)::value, sl = m % 4;
+                        return dpp_mov<sl | (sl << 2) | (sl << 4) | (sl << 6), 0xf>(x[m / 4]);
                     };
+                    auto step = [&](auto m_c) {
+                        constexpr int m = decltype(m_c)::value;
+                        const float xm = bcast(m_c);
 #pragma unroll
-                    for (int m = 0; m < PF; ++m) load_col(m);
+                        for (int q = 0; q < 4; ++q) x[q] -= col[m][q] * xm;
+                    };
+                    step(IC<0>()); step(IC<1>()); step(IC<2>()); step(IC<3>()); step(IC<4>());
+                    step(IC<5>()); step(IC<6>()); step(IC<7>()); step(IC<8>()); step(IC<9>());
+                    step(IC<10>()); step(IC<11>()); step(IC<12>()); step(IC<13>()); step(IC<14>());
+                    // column cc of D is row cc of D^T
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-                    for (int m = 0; m < 15; ++m) {
-                        if (m + PF < 15) load_col(m + PF);
-#pragma unroll
-                        for (int r = m + 1; r < 16; ++r) x[r] -= col[m][r >> 2][r & 3] * x[m];
-                        asm volatile("" ::: "memory");
-                    }
-                    // column cc of D is row cc of D^T: two 16-byte stores
-                    v8 d0, d1;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        d0[r] = (E)x[r];
-                        d1[r] = (E)x[8 + r];
-                    }
-                    *(v8 *)&po.dt[w4][cc][0] = d0;
-                    *(v8 *)&po.dt[w4][cc][8] = d1;
+                    for (int q = 0; q < 4; ++q) po.dt[w4][cc][4 * q + gg] = (E)x[q];
                 }
             }
             lds_barrier();
