@@ -28,10 +28,11 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # changes the hash, and the bench then reports traffic as null until it is
 # measured again.
 MEASURED_TRAFFIC = {
-    # fused_ws_kernel, GVA prefill: FETCH 151,990.75 KiB x 2.000 + WRITE 139,776.2 KiB x 1.000
-    "2ac7ce49817c0cf4": {"gva": 454407872},
-    # recurrent_update_kernel, decode: FETCH 257,459.0 KiB x 2.000 + WRITE 510,368.6 KiB x 1.000
-    "b2ce57f1b13d562c": {"decode": 1049893504},
+    # fused_ws_kernel, GVA prefill: FETCH 151,985.9 KiB x 2.000 + WRITE 139,776.5 KiB x 1.000
+    "a5cfac635656b7e5": {"gva": 454398176},
+    # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,370.0 KiB;
+    # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,011.75 KiB
+    "ff527de4d2c9c570": {"decode": 1049895936, "decode_bf16pool": 529398528},
 }
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
