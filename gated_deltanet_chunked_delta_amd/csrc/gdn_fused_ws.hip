@@ -8,14 +8,16 @@
 //               that depends on the state h: X, the block forward substitution
 //               for V_new, the output, the state update, and Z = K h and
 //               (Q h)^T of the next chunk.
-//   waves 4-7   K-prep waves, one chunk ahead: gate cumsum, K K^T Gram tiles of
-//               row tile w and the norms of the k rows of tiles 0..w, the
-//               gated -A tiles, the diagonal-block inverse D_w; wave 7, which
-//               has every norm, also the per-token state factors.
+//   waves 4-7   K-prep waves, one chunk ahead: gate cumsum; wave w computes
+//               its diagonal K K^T tile (A_ww and the diagonal-block inverse
+//               D_w), two off-diagonal tiles (the gated -A tiles) and the
+//               diagonal tiles whose norms those need, spread so that the four
+//               waves carry 5, 5, 5 and 1 tiles; each publishes the per-token
+//               state factors of its own 16 rows.
 //   waves 8-11  Q-prep waves, one chunk ahead: the asynchronous copies of the
-//               raw rows (two chunks ahead), gate cumsum, Q K^T Gram tiles of
-//               row tile w, the norms of its q rows and of the k rows of tiles
-//               0..w, the gated P tiles.
+//               raw rows (two chunks ahead), gate cumsum, the ten causal Q K^T
+//               tiles spread 7, 7, 7 and 3 tiles per wave (with the Q Q^T and
+//               K K^T diagonals for the norms they need), the gated P tiles.
 // The SIMDs interleave the serial state chain of chunk c with the
 // preparation of chunk c+1.  Each step ends with the only workgroup barrier
 // of the step; every prep wave computes the cumsum and norm values it needs
