@@ -366,15 +366,19 @@ def main():
     kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in prof.items() if n}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dom_us = kernels[dom]["avg_us"]
-    # the fused kernel is the whole path: its algorithmic bytes are the path's
-    ach = pb / (dom_us * 1e-6) / 1e9
+    per_step = lambda k: kernels[k]["avg_us"] * kernels[k]["launches"] / args.steps
+    dom_step_us = per_step(dom)
+    # the fused kernel is the whole path (a split long sequence launches it twice
+    # per step): the path's algorithmic bytes over its time per step
+    ach = pb / (dom_step_us * 1e-6) / 1e9
     khash = kernel_hash("prefill")
     traffic = (MEASURED_TRAFFIC.get(khash, {}).get(w.name)
                if args.dtype == "bf16" and args.gating == "tensors" else None)
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2), "kernel_hash": khash}
-    path_us = sum(v["avg_us"] for v in kernels.values())
+            "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2),
+            "launches_per_step": round(kernels[dom]["launches"] / args.steps, 2), "kernel_hash": khash}
+    path_us = sum(per_step(k) for k in kernels)
     flops = path_flops(w, x)
     path = {"algorithmic_bytes": pb, "algorithmic_flops": flops, "kernel_us": round(path_us, 2),
             "hbm_frac": round(pb / (path_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

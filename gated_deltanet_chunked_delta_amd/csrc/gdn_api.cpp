@@ -32,8 +32,14 @@ int check_shape(const gdn_shape *s) {
     return GDN_OK;
 }
 
-// Workspace the forward pass needs: none for the fused kernel.
-size_t workspace_of(const gdn_shape &) { return 0; }
+// Workspace for the sequence split of few, long, equal-length sequences
+// (gdn_split.hip); 0 when these sizes are not split.  The fused kernel itself
+// needs none.
+gdn::SplitPlan split_of(const gdn_shape &s) {
+    if (s.N != s.B) return gdn::SplitPlan{};
+    return gdn::plan_split(s.B, s.T, s.H, s.HV, s.K, s.V, gdn::elem_bytes(s.dtype));
+}
+size_t workspace_of(const gdn_shape &s) { return split_of(s).bytes; }
 
 // Kernel timing hook (gdn_profile_enable / gdn_profile_read): HIP events
 // recorded on the caller's stream around each kernel of every forward pass.
@@ -140,9 +146,14 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
         const int ps = check_pool(*pool);
         if (ps != GDN_OK) return ps;
     }
-    const size_t need = workspace_of(s);
-    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0))
-        return GDN_ERR_WORKSPACE;
+    // The split runs only where it applies and the caller gave the workspace
+    // for it (256-byte aligned); otherwise the sequences run unsplit.
+    gdn::SplitPlan split;
+    if (!pool && !varlen) {
+        split = split_of(s);
+        if (split.active && (!workspace || workspace_bytes < split.bytes || ((uintptr_t)workspace & 255u) != 0))
+            split.active = false;
+    }
 
     gdn::Params p{};
     p.q = q;
@@ -174,7 +185,9 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
     hipError_t err;
     {
         std::lock_guard<std::mutex> lock(g_prof.mu);
-        err = gdn::launch_forward(p, s.dtype, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
+        gdn::Profiler *prof = g_prof.on ? &g_prof : nullptr;
+        err = split.active ? gdn::launch_split(p, s.dtype, split, workspace, (hipStream_t)stream, prof)
+                           : gdn::launch_forward(p, s.dtype, (hipStream_t)stream, prof);
     }
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }

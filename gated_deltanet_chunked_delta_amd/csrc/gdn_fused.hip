@@ -159,9 +159,11 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
         s_out = s_out && ok;
         sbase = ((size_t)(ok ? slot : 0) * p.HV + j) * K * V + vcol0;
     }
+    // init_shared: one initial state for every sequence
+    const size_t sbase_in = p.init_shared ? (size_t)j * K * V + vcol0 : sbase;
     if (s_in) {
-        const float *__restrict__ s0 = p.initial_state + sbase;
-        const bf16 *__restrict__ s0h = (const bf16 *)p.initial_state + sbase;
+        const float *__restrict__ s0 = p.initial_state + sbase_in;
+        const bf16 *__restrict__ s0h = (const bf16 *)p.initial_state + sbase_in;
 #pragma unroll
         for (int ct = 0; ct < CPW; ++ct) {
             const int col = 16 * (wave * CPW + ct) + l16;
@@ -183,7 +185,8 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
     // Asynchronous copy of chunk c's raw rows into LDS buffer `buf`.  Rows past
     // the sequence end read the last valid row (so every address stays inside
     // the sequence) and are zeroed after arrival.
-    const size_t kq_row = (size_t)p.H * K, v_row = (size_t)p.HV * V;   // elements between token rows
+    // elements between token rows (v_zero: every token reads the one zero row)
+    const size_t kq_row = (size_t)p.H * K, v_row = p.v_zero ? 0 : (size_t)p.HV * V;
     auto issue = [&](int c, int buf) {
         const int64_t t0 = tok0 + 64LL * c;
         const int last = min(64, len - 64 * c) - 1;
@@ -589,6 +592,9 @@ const char *kernel_name(int kind) {
         case kFusedWsKernel: return "fused_ws_kernel";
         case kRecurrentKernel: return "recurrent_update_kernel";
         case kGatingKernel: return "gating_kernel";
+        case kSplitSetupKernel: return "split_setup_kernel";
+        case kSplitCombineKernel: return "split_combine_kernel";
+        case kSplitCorrectKernel: return "split_correct_kernel";
         default: return "?";
     }
 }

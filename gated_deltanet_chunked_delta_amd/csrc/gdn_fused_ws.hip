@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     const E *__restrict__ kg = (const E *)p.k;
     const E *__restrict__ vg = (const E *)p.v;
     E *__restrict__ og = (E *)p.out;
-    const size_t kq_row = (size_t)p.H * K, v_row = (size_t)p.HV * V;
+    const size_t kq_row = (size_t)p.H * K, v_row = (POOL && p.v_zero) ? 0 : (size_t)p.HV * V;
 
     // raw k/q fragment of row tile t, step s2: row 16 t + l16, key slots
     // 32 s2 + 8 grp .. +7 (one swizzled 16-byte segment)
@@ -607,23 +607,24 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                    (((2 * w4 + ((l16 & 3) >> 1)) ^ swz<NSV>(4 * grp + (l16 >> 2))) << 4) + 8 * (l16 & 1);
 
     f32x4 h[KT];
-    size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0;
+    size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0, sbase_in = sbase;
     bool s_in = p.initial_state != nullptr, s_out = p.final_state != nullptr;
     if (POOL && p.state_indices) {   // state pool: the slot of sequence n (outside the pool: none)
         const int slot = p.state_indices[n];
         const bool ok = slot >= 0 && slot < p.pool_size;
         s_in = s_in && ok;
         s_out = s_out && ok;
-        sbase = ((size_t)(ok ? slot : 0) * p.HV + j) * K * V + vcol0;
+        sbase = sbase_in = ((size_t)(ok ? slot : 0) * p.HV + j) * K * V + vcol0;
     }
+    if (POOL && p.init_shared) sbase_in = (size_t)j * K * V + vcol0;   // one initial state for all
     if (POOL && s_in && p.state_bf16) {
-        const bf16 *__restrict__ s0 = (const bf16 *)p.initial_state + sbase;
+        const bf16 *__restrict__ s0 = (const bf16 *)p.initial_state + sbase_in;
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) h[mt][e] = to_f(s0[(size_t)kappa(mt, 4 * grp + e) * V + c0 + l16]);
     } else if (s_in) {
-        const float *__restrict__ s0 = p.initial_state + sbase;
+        const float *__restrict__ s0 = p.initial_state + sbase_in;
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
@@ -804,7 +805,8 @@ hipError_t launch_fused_ws(const Params &p, hipStream_t st) {
     if (groups == 0) return hipSuccess;
     const int per_group = (p.HV / p.H) * (p.V / VW);
     const unsigned grid = (unsigned)((groups + 7) / 8) * 8 * per_group;
-    const bool gated = p.gates.A_log != nullptr, pool = p.state_indices != nullptr || p.state_bf16;
+    const bool gated = p.gates.A_log != nullptr,
+               pool = p.state_indices != nullptr || p.state_bf16 || p.v_zero || p.init_shared;
     if (gated && pool) return launch_ws_kv<true, true>(p, grid, st);
     if (gated) return launch_ws_kv<true, false>(p, grid, st);
     if (pool) return launch_ws_kv<false, true>(p, grid, st);

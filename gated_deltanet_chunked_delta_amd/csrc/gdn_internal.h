@@ -42,6 +42,11 @@ struct Params {
     const int32_t *state_indices;
     int pool_size;
     int state_bf16;
+    // Sequence split (the transfer-map run): v_zero = v points at one zero row
+    // of HV x V elements read for every token; init_shared = initial_state
+    // holds one [HV, K, V] state used by every sequence.
+    int v_zero;
+    int init_shared;
 };
 
 // The kernels of one forward pass, for the timing hook.
@@ -49,8 +54,11 @@ struct Params {
 // fused_ws_kernel: warp-specialized prefill kernel (bf16);
 // recurrent_update_kernel: the decode step;
 // gating_kernel: the stand-alone gate computation.
+// split_setup_kernel, split_combine_kernel, split_correct_kernel: the
+// sequence split of long sequences (gdn_split.hip).
 enum KernelKind { kFusedKernel = 0, kFusedWsKernel = 1, kRecurrentKernel = 2, kGatingKernel = 3,
-                  kNumKernelKinds = 4 };
+                  kSplitSetupKernel = 4, kSplitCombineKernel = 5, kSplitCorrectKernel = 6,
+                  kNumKernelKinds = 7 };
 const char *kernel_name(int kind);
 
 // Timing hook: when given, the launch sequence calls begin/end around each
@@ -85,6 +93,29 @@ hipError_t launch_recurrent(const DecodeParams &p, int dtype, hipStream_t stream
 // gates into g and beta.
 hipError_t launch_gating(const Gates &gt, int64_t rows, int HV, int dtype, float *g, float *beta,
                          hipStream_t stream, Profiler *prof);
+
+// Sequence split (gdn_split.hip).  A batch of few, long, equal-length
+// sequences gives too few workgroups to fill the GPU; each sequence is then
+// cut into S segments of L tokens that run side by side.  The state is affine
+// in a segment's initial state h_a: S_t = S0_t + M_t h_a, with S0_t the state
+// from a zero start and M_t the segment's K x K transfer map so far.  So
+//   1. every segment runs from zero (segment 0 from the true initial state)
+//      -> outputs o0, final states h0;
+//   2. every segment runs again with v = 0 from the identity (K state
+//      columns) -> final maps M and outputs oM_t = scale M_t^T q_t;
+//   3. h_{s+1} = M_s h_s + h0_s in segment order (h_1 = h0_0);
+//   4. o_t += h_s^T oM_t for the tokens of segments s >= 1.
+struct SplitPlan {
+    bool active = false;
+    int S = 1, L = 0;                 // segments per sequence, tokens per segment (multiple of 64)
+    size_t off_cu = 0, off_idx = 0, off_pool = 0, off_map = 0, off_hs = 0, off_om = 0, off_id = 0,
+           off_zero = 0, bytes = 0;   // workspace carve-up (256-byte aligned)
+};
+// The split for these sizes (equal-length sequences only); bytes = 0 when none.
+SplitPlan plan_split(int B, int T, int H, int HV, int K, int V, int elem_bytes);
+// Enqueues the split forward pass of p (cu_seqlens null) with workspace ws.
+hipError_t launch_split(const Params &p, int dtype, const SplitPlan &plan, void *ws, hipStream_t stream,
+                        Profiler *prof);
 
 // The single-role fused kernel's launch (gdn_fused.hip).
 hipError_t launch_fused(const Params &p, int dtype, hipStream_t stream);

@@ -55,7 +55,7 @@ typedef enum gdn_status {
                                  B != 1 with cu_seqlens) */
     GDN_ERR_DTYPE = -3,       /* unknown dtype code */
     GDN_ERR_UNSUPPORTED = -4, /* K or V not in {64, 128}, or HV not a multiple of H */
-    GDN_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or too small while one is needed */
+    GDN_ERR_WORKSPACE = -5,   /* reserved: workspace NULL, misaligned or too small while required */
     GDN_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
     GDN_ERR_ALIGN = -7        /* a pointer lacks the alignment its argument requires */
 } gdn_status;
@@ -78,9 +78,21 @@ typedef struct gdn_shape {
     int32_t dtype;
 } gdn_shape;
 
-/* Bytes of device workspace gdn_chunk_fwd needs for `shape`; depends only on
- * the sizes and the dtype.  0 means none is needed (workspace may then be
- * NULL); invalid shapes also give 0, and gdn_chunk_fwd reports why. */
+/* Bytes of device workspace that let gdn_chunk_fwd (and gdn_chunk_fwd_gated)
+ * split long sequences for `shape`; depends only on the sizes and the dtype.
+ * 0 means the sizes are not split and no workspace is used; invalid shapes
+ * also give 0, and gdn_chunk_fwd reports why.
+ *
+ * The split: a batch of few equal-length sequences (B * HV * V/64 <= 64
+ * workgroups, T >= 2048) is too narrow to fill the GPU, so each sequence is
+ * cut into 2-8 segments that run side by side.  The state is affine in a
+ * segment's initial state (the recurrence below is linear in S), so every
+ * segment runs from zero and, a second time, from the identity with v = 0
+ * (its transfer map); the segment states are then chained in order and each
+ * segment's outputs corrected by one product.  Results equal the unsplit pass
+ * up to rounding.  The workspace holds the maps and the transfer outputs
+ * (about B * T * HV * K elements of dtype plus 3 * B * 8 * HV * K * max(K, V)
+ * floats: ~1 GiB for one 131072-token sequence with HV = 32, K = V = 128). */
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape);
 
 /* Chunked gated delta rule forward pass (prefill).
@@ -99,9 +111,10 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape);
  *                 May alias initial_state exactly (in-place state update);
  *                 must not overlap any other argument.
  *   shape         sizes, see gdn_shape (host pointer)
- *   workspace     device scratch of at least gdn_chunk_fwd_workspace_bytes
- *                 bytes (256-byte aligned; may be NULL when that is 0);
- *                 contents on entry are ignored
+ *   workspace     device scratch of gdn_chunk_fwd_workspace_bytes bytes
+ *                 (256-byte aligned), or NULL: long sequences are split only
+ *                 when it is given and large enough, and otherwise run unsplit
+ *                 (never an error); contents on entry are ignored
  *   stream        hipStream_t to enqueue on (NULL = the default stream)
  *
  * `out` must not overlap any input.  Sequences of length 0 produce no rows and

@@ -54,6 +54,14 @@ def test_workspace_size_and_bad_shapes():
     s2 = gdn.make_shape(4, 4096, 16, 32, 128, 128, 4, gdn.GDN_F32)
     b1, b2 = gdn.gdn_chunk_fwd_workspace_bytes(s1), gdn.gdn_chunk_fwd_workspace_bytes(s2)
     assert 0 <= b1 <= b2
+    assert b1 == b2 == 0                      # 256 workgroups: not split
+    # one long sequence (64 workgroups): split, workspace for 4 segments incl. the
+    # transfer outputs [T, HV, K] of the dtype
+    b3 = gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 131072, 16, 32, 128, 128, 1, gdn.GDN_BF16))
+    b4 = gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 131072, 16, 32, 128, 128, 1, gdn.GDN_F32))
+    assert b3 >= 131072 * 32 * 128 * 2 and b4 >= 131072 * 32 * 128 * 4 and b4 > b3
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 1024, 16, 32, 128, 128, 1, 0)) == 0   # short
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 1, 16, 32, 128, 128, 4, 0)) == 0      # varlen
     assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 16, 32, 96, 128, 4, 0)) == 0
     assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 3, 32, 128, 128, 4, 0)) == 0
     assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 16, 32, 128, 128, 4, 7)) == 0
