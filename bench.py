@@ -29,10 +29,10 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # measured again.
 MEASURED_TRAFFIC = {
     # fused_ws_kernel, GVA prefill: FETCH 151,985.9 KiB x 2.000 + WRITE 139,776.5 KiB x 1.000
-    "d2c025ac15eaa202": {"gva": 454398176},
+    "7cfe1bb0f0a8fdf1": {"gva": 454398176},
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,370.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,011.75 KiB
-    "cbb084bc84402f84": {"decode": 1049895936, "decode_bf16pool": 529398528},
+    "84462a58c8717f5e": {"decode": 1049895936, "decode_bf16pool": 529398528},
 }
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
