@@ -105,10 +105,9 @@ struct alignas(16) PrepOut {
     bf16 alo[64][68];         // -A in the off-diagonal 16x16 blocks below the diagonal
     bf16 p[64][72];           // P, columns in the key-slot order (see pcol); blocks (0,1), (2,3) zero
     bf16 dt[4][16][16];       // D_b transposed: dt[b][j][i] = D_b[i][j]
-    float gam[64];            // gate cumsum, log2 units
     float beta[64];
     float bgr[64];            // beta e^gamma r
-    float rq[64];             // L2-norm factor rho of q (1 without the norm)
+    float osc[64];            // output scale of (Q h)^T: scale rho e^gamma
     float kf[64];             // r e^{gamma_L - gamma}
     float decay;              // e^{gamma_L}
 };
@@ -399,7 +398,6 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                     for (int r = 0; r < NR; ++r) {
                         const float qq = __shfl(gqq[r][l16 & 3], (l16 >> 2) * 16 + l16);
                         rho[r] = p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f;
-                        if (W != 2 && grp == 0) po.rq[16 * (R0 + r) + l16] = rho[r];   // row 3: wave 3 publishes
                     }
                     wave_lds_sync();   // the staged gamma and r come from other lanes
                     f32x4 gj[NJ], rj[NJ];
@@ -412,6 +410,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                     for (int r = 0; r < NR; ++r) {
                         const int itq = R0 + r, iq = 16 * itq + l16;
                         const float giq = sg[iq], srq = p.scale * rho[r];
+                        if (W != 2 && grp == 0) po.osc[iq] = srq * fast_exp2(giq);   // row 3: wave 3 publishes
 #pragma unroll
                         for (int jj = 0; jj < NJ; ++jj) {
                             const int jt = J0 + jj;
@@ -451,10 +450,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                     cumsum(cn, gam, b);
                     sg[lane] = gam;
                     sb[lane] = b;
-                    if (w4 == 0) {
-                        po.gam[lane] = gam;
-                        po.beta[lane] = b;
-                    }
+                    if (w4 == 0) po.beta[lane] = b;
                 }
                 const E *kb = s.kb[cn % 3];
                 // The ten lower Gram tiles of K K^T are spread so that no wave
@@ -702,7 +698,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 const int i = 16 * ti + l16;
-                o[ti] = zq[ti] * (p.scale * po.rq[i] * fast_exp2(po.gam[i]));
+                o[ti] = zq[ti] * po.osc[i];
 #pragma unroll
                 for (int s2 = 0; s2 <= ti / 2; ++s2) o[ti] = mma(vnb[s2], *(const v8 *)&po.p[i][pcol(2 * s2, grp)], o[ti]);
             }
