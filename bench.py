@@ -28,8 +28,8 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # changes the hash, and the bench then reports traffic as null until it is
 # measured again.
 MEASURED_TRAFFIC = {
-    # fused_ws_kernel, GVA prefill: FETCH 151,985.9 KiB x 2.000 + WRITE 139,776.5 KiB x 1.000
-    "7cfe1bb0f0a8fdf1": {"gva": 454398176},
+    # fused_ws_kernel, GVA prefill: FETCH 151,985.6 KiB x 2.000 + WRITE 139,776.1 KiB x 1.000
+    "54b35e5aaa83fde3": {"gva": 454397120},
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,370.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,011.75 KiB
     "84462a58c8717f5e": {"decode": 1049895936, "decode_bf16pool": 529398528},
