@@ -18,6 +18,7 @@ GDN_OK = 0
 GDN_BF16 = 0
 GDN_F32 = 1
 EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_pool", "gdn_chunk_fwd_workspace_bytes",
+            "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
             "gdn_gating", "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_recurrent_update_pool",
             "gdn_profile_enable", "gdn_profile_read", "gdn_status_str")
 
@@ -72,6 +73,11 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P, P,
                                   ctypes.POINTER(gdn_shape), P, ctypes.c_size_t, P]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(gdn_shape)]
+    lib.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunk_bwd.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P, P, P, P, P, P,
+                                  ctypes.POINTER(gdn_shape), P, ctypes.c_size_t, P]
+    lib.gdn_chunk_bwd.restype = ctypes.c_int
     lib.gdn_recurrent_update.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P,
                                          ctypes.POINTER(gdn_decode_shape), P]
     lib.gdn_recurrent_update.restype = ctypes.c_int
@@ -255,6 +261,79 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None, initial_state
     if st != GDN_OK:
         raise GdnError(st)
     return out, final_state
+
+
+def gdn_chunk_bwd_workspace_bytes(shape: gdn_shape) -> int:
+    return int(load_library().gdn_chunk_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, dout, dht, scale, use_l2norm, initial_state, cu_seqlens, dq, dk, dv, dg,
+                  dbeta, dh0, shape: gdn_shape, workspace, workspace_bytes=None, stream=None) -> int:
+    """Direct call of the C backward entry point; returns the status code."""
+    lib = load_library()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return int(lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(dout), _ptr(dht),
+                                 float(scale), int(bool(use_l2norm)), _ptr(initial_state), _ptr(cu_seqlens),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                                 ctypes.byref(shape), _ptr(workspace), int(workspace_bytes),
+                                 ctypes.c_void_p(int(stream))))
+
+
+def chunk_gated_delta_rule_bwd(q, k, v, g, beta, do, dht=None, scale=None, initial_state=None, cu_seqlens=None,
+                               use_qk_l2norm_in_kernel=False, output_dh0=True, workspace=None):
+    """Backward pass of ``chunk_gated_delta_rule`` (g / beta form) on the GPU.
+
+    Takes the forward inputs, ``do`` (gradient of the output, q's dtype and
+    [B,T,HV,V]) and ``dht`` (gradient of the final state, float32
+    [N,HV,K,V], or None when the final state is unused).  Returns
+    ``(dq, dk, dv, dg, dbeta, dh0)``: dq, dk, dv in q's dtype and shapes of
+    q, k, v; dg, dbeta float32 [B,T,HV]; dh0 float32 [N,HV,K,V] (None when
+    ``output_dh0`` is False).  A preallocated uint8 ``workspace`` of
+    gdn_chunk_bwd_workspace_bytes bytes may be given.
+    """
+    _check(q.dim() == 4 and k.shape == q.shape, "q and k must be [B,T,H,K] of equal shape")
+    B, T, H, K = q.shape
+    _check(v.dim() == 4 and v.shape[:2] == (B, T), "v must be [B,T,HV,V]")
+    HV, V = v.shape[2], v.shape[3]
+    _check(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype and do.dtype == q.dtype,
+           "q, k, v, do must share one dtype (bfloat16 or float32)")
+    _check(q.is_cuda, "tensors must be on a GPU device (there is no CPU path)")
+    _check(tuple(do.shape) == (B, T, HV, V), "do must have v's shape")
+    _check(tuple(g.shape) == (B, T, HV) and g.dtype == torch.float32, "g must be float32 [B,T,HV]")
+    _check(tuple(beta.shape) == (B, T, HV) and beta.dtype == torch.float32, "beta must be float32 [B,T,HV]")
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta), ("do", do), ("dht", dht),
+                    ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)):
+        _check(t is None or t.device == q.device, f"{name} must be on {q.device}")
+    if cu_seqlens is not None:
+        _check(B == 1, "cu_seqlens requires B == 1")
+        _check(cu_seqlens.dim() == 1 and cu_seqlens.dtype == torch.int32, "cu_seqlens must be int32 [N+1]")
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    for name, t in (("initial_state", initial_state), ("dht", dht)):
+        _check(t is None or (tuple(t.shape) == (N, HV, K, V) and t.dtype == torch.float32),
+               f"{name} must be float32 [{N},{HV},{K},{V}]")
+    if scale is None:
+        scale = K ** -0.5
+    q, k, v, g, beta, do = (t.contiguous() for t in (q, k, v, g, beta, do))
+    initial_state = None if initial_state is None else initial_state.contiguous()
+    dht = None if dht is None else dht.contiguous()
+    shape = make_shape(B, T, H, HV, K, V, N, _DTYPES[q.dtype])
+    need = gdn_chunk_bwd_workspace_bytes(shape)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty((B, T, HV), dtype=torch.float32, device=q.device)
+    dbeta = torch.empty_like(dg)
+    dh0 = torch.empty((N, HV, K, V), dtype=torch.float32, device=q.device) if output_dh0 else None
+    st = gdn_chunk_bwd(q, k, v, g, beta, do, dht, scale, use_qk_l2norm_in_kernel, initial_state, cu_seqlens, dq,
+                       dk, dv, dg, dbeta, dh0, shape, workspace)
+    if st != GDN_OK:
+        raise GdnError(st)
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def make_decode_shape(N, H, HV, K, V, pool_size, dtype) -> gdn_decode_shape:

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = [os.path.join(PKG, "csrc", "gdn_fused.hip"), os.path.join(PKG, "csrc", "gdn_fused_ws.hip"),
            os.path.join(PKG, "csrc", "gdn_recurrent.hip"), os.path.join(PKG, "csrc", "gdn_gating.hip"),
-           os.path.join(PKG, "csrc", "gdn_split.hip"),
+           os.path.join(PKG, "csrc", "gdn_split.hip"), os.path.join(PKG, "csrc", "gdn_backward.hip"),
            os.path.join(PKG, "csrc", "gdn_api.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(PKG, "csrc", "gdn_internal.h"),
            os.path.join(PKG, "csrc", "gdn_device.h")]

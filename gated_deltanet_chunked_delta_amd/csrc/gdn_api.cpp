@@ -240,9 +240,80 @@ int recurrent_update(const void *q, const void *k, const void *v, const float *g
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+// The backward pass.  The workspace slots are sized for packed sequences when
+// B == 1 (ceil(T/64) + N chunks bound the chunks of any N sequences of T tokens
+// in all) and for B equal-length sequences otherwise.
+gdn::BwdPlan bwd_plan_of(const gdn_shape &s) {
+    return gdn::plan_backward(s.B, s.T, s.H, s.HV, s.K, s.V, s.N, s.B == 1);
+}
+
+int chunk_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *dout,
+              const float *dht, float scale, int use_l2norm, const float *initial_state, const int32_t *cu_seqlens,
+              void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0, const gdn_shape *shape,
+              void *workspace, size_t workspace_bytes, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN_OK) return st;
+    const gdn_shape &s = *shape;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen ? s.B != 1 : s.N != s.B) return GDN_ERR_SHAPE;
+    const bool any_tokens = (int64_t)s.B * s.T > 0;
+    if (any_tokens && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+        return GDN_ERR_NULL;
+    const gdn::BwdPlan plan = bwd_plan_of(s);
+    if (plan.nc_max < 0 || plan.bytes == 0) return GDN_ERR_SHAPE;
+    if (!workspace || workspace_bytes < plan.bytes || ((uintptr_t)workspace & 255u) != 0) return GDN_ERR_WORKSPACE;
+    if (s.N == 0 || (!any_tokens && !dh0)) return GDN_OK;
+
+    gdn::BwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.dout = dout;
+    p.dht = dht;
+    p.initial_state = initial_state;
+    p.cu_seqlens = cu_seqlens;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dg = dg;
+    p.dbeta = dbeta;
+    p.dh0 = dh0;
+    p.B = s.B;
+    p.T = s.T;
+    p.H = s.H;
+    p.HV = s.HV;
+    p.K = s.K;
+    p.V = s.V;
+    p.N = s.N;
+    p.scale = scale;
+    p.use_l2norm = use_l2norm ? 1 : 0;
+    hipError_t err;
+    {
+        std::lock_guard<std::mutex> lock(g_prof.mu);
+        err = gdn::launch_backward(p, s.dtype, plan, workspace, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
+    }
+    return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape *shape) {
+    if (check_shape(shape) != GDN_OK) return 0;
+    const gdn::BwdPlan plan = bwd_plan_of(*shape);
+    return plan.nc_max < 0 ? 0 : plan.bytes;
+}
+
+int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *dout,
+                  const float *dht, float scale, int use_l2norm, const float *initial_state,
+                  const int32_t *cu_seqlens, void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0,
+                  const gdn_shape *shape, void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_bwd(q, k, v, g, beta, dout, dht, scale, use_l2norm, initial_state, cu_seqlens, dq, dk, dv, dg,
+                     dbeta, dh0, shape, workspace, workspace_bytes, stream);
+}
 
 int gdn_profile_enable(int enable) {
     std::lock_guard<std::mutex> lock(g_prof.mu);

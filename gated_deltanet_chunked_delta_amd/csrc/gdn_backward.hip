@@ -1,0 +1,866 @@
+// Backward pass of the chunked gated delta rule, for gfx950.
+//
+// The page "NPU Training Operators - GDN" lists, beside the forward operators,
+// the backward ones (gradients of q, k, v, the gates g and beta, and of the
+// initial state; the gate gradient by a reverse cumulative sum).  The pages
+// give no equations for them; the ones below are the chain rule applied to the
+// chunked (WY) form of the forward pass.  Per chunk of L <= 64 rows, with
+// gamma the chunk-local inclusive cumsum of g, D_i = exp(gamma_i), qh / kh the
+// (optionally L2-normalised) rows and h the state at the chunk start:
+//
+//   A    = strictly lower, A_ij = beta_i exp(gamma_i - gamma_j) kh_i . kh_j
+//   Tm   = (I + A)^-1
+//   B    = diag(beta) (V - diag(D) Kh h)
+//   Vn   = Tm B                                      (the delta-rule errors)
+//   h'   = D_L h + Kh^T diag(exp(gamma_L - gamma)) Vn
+//   O    = scale (diag(D) Qh h + Pm Vn),  Pm_ij = [j <= i] exp(gamma_i - gamma_j) qh_i . kh_j
+//
+// Going back through a chunk, given dO and dh' (the gradient of h'):
+//
+//   dVn  = scale Pm^T dO + diag(exp(gamma_L - gamma)) Kh dh'
+//   dB   = Tm^T dVn                                  ((I + A) Vn = B)
+//   dh   = D_L dh' + scale Qh^T diag(D) dO - Kh^T diag(beta D) dB
+//   dA   = -dB Vn^T (strictly lower part),  dV = diag(beta) dB
+//   dQh  = scale diag(D) dO h^T + dSqk Kh,    dSqk = [j <= i] exp(gamma_i - gamma_j) scale (dO Vn^T)_ij
+//   dKh  = dSqk^T Qh + F dh'^T - diag(beta) E + Ad Kh + Ad^T Kh
+//          with F = diag(exp(gamma_L - gamma)) Vn, E = diag(D) dB h^T, Ad = dA * beta_i exp(gamma_i - gamma_j)
+//   dbeta_i  = dB_i . V_i - kh_i . E_i + sum_j dA_ij exp(gamma_i - gamma_j) kh_i . kh_j
+//   dgamma_i = qh_i . (scale D_i dO_i h^T) - beta_i kh_i . E_i - kh_i . (F dh'^T)_i
+//              + rowsum_i(Z) - colsum_i(Z),   Z = dSqk * (qh_i . kh_j) + dA * A
+//              + [i = L] (D_L <dh', h> + sum_j kh_j . (F dh'^T)_j)
+//   dg_s     = sum_{i >= s in the chunk} dgamma_i
+//
+// and the L2 norm's backward dx = f (dxh - xh (xh . dxh)), f = 1/sqrt(|x|^2 + 1e-6).
+// The state gradient runs backwards over chunks just as the state runs
+// forwards, so the pass is five launches:
+//   bwd_prep_kernel      per (chunk, value head): gamma, Tm, A / beta and Pm
+//   bwd_fwd_scan_kernel  per (sequence, value head, 32 value columns), forward
+//                        over chunks: the chunk-start states h and Vn
+//   bwd_dh_scan_kernel   per (sequence, value head, 32 value columns), backward
+//                        over chunks: dh' per chunk, dB, the initial-state gradient
+//   bwd_grads_kernel     per (chunk, value head): dq, dk per value head, dv,
+//                        dg, dbeta
+//   bwd_reduce_kernel    dq, dk summed over the value heads of each key head
+// All arithmetic is fp32 on the VALU with operands staged in LDS; the
+// intermediates live in the caller's workspace (layout in BwdPlan).
+#include <hip/hip_runtime.h>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+using namespace dev;
+
+constexpr int kThreads = 256;
+constexpr int kVT = 32;          // value columns per scan workgroup / grads tile
+constexpr int kPadC = kChunk + 1;
+constexpr int kPadT = kVT + 1;
+
+// LDS sizes in floats.
+template <int K>
+constexpr int prep_floats() { return 2 * kChunk * (K + 1) + 2 * kChunk * kPadC + 4 * kChunk; }
+template <int K>
+constexpr int fwd_scan_floats() { return K * kPadT + kChunk * (K + 1) + kChunk * kPadC + 2 * kChunk * kPadT + 3 * kChunk; }
+template <int K>
+constexpr int dh_scan_floats() {
+    return K * kPadT + 2 * kChunk * (K + 1) + 2 * kChunk * kPadC + 3 * kChunk * kPadT + 4 * kChunk;
+}
+// grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the three
+// 64 x 65 matrices of the second phase reuse their space.
+template <int K>
+constexpr int grads_tile_floats() { return 2 * K * kPadT + 4 * kChunk * kPadT; }
+static_assert(grads_tile_floats<64>() >= 3 * kChunk * kPadC, "phase-2 matrices must fit in the tile region");
+template <int K>
+constexpr int grads_floats() { return 2 * kChunk * (K + 1) + grads_tile_floats<K>() + 6 * kChunk + 20; }
+
+__device__ __forceinline__ int tx_of() { return threadIdx.x & 15; }
+__device__ __forceinline__ int ty_of() { return threadIdx.x >> 4; }
+
+// acc[i][j] += sum_{m < KD} fa(ty + 16 i, m) * fb(tx + 16 j, m)
+template <int MR, int NR, int KD, typename FA, typename FB>
+__device__ __forceinline__ void mm(float (&acc)[MR][NR], FA fa, FB fb) {
+    const int tx = tx_of(), ty = ty_of();
+#pragma unroll 4
+    for (int m = 0; m < KD; ++m) {
+        float a[MR], b[NR];
+#pragma unroll
+        for (int i = 0; i < MR; ++i) a[i] = fa(ty + 16 * i, m);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) b[j] = fb(tx + 16 * j, m);
+#pragma unroll
+        for (int i = 0; i < MR; ++i)
+#pragma unroll
+            for (int j = 0; j < NR; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+}
+
+template <int MR, int NR>
+__device__ __forceinline__ void zero(float (&acc)[MR][NR]) {
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int j = 0; j < NR; ++j) acc[i][j] = 0.f;
+}
+
+// Sum over the 16 lanes that share ty (lanes tx = 0..15 of one row group).
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+// The chunk of a chunk index: sequence n, first token t0 (packed index),
+// rows L, and the chunk index c inside its sequence.  Returns false for
+// indices past the last chunk.
+struct ChunkRef {
+    int n, c, t0, L;
+};
+__device__ __forceinline__ bool find_chunk(const BwdParams &p, int cid, ChunkRef &r) {
+    if (!p.cu_seqlens) {
+        const int ncs = (p.T + kChunk - 1) / kChunk;
+        if (ncs == 0 || cid >= p.B * ncs) return false;
+        r.n = cid / ncs;
+        r.c = cid - r.n * ncs;
+        r.t0 = r.n * p.T + r.c * kChunk;
+        r.L = min(kChunk, p.T - r.c * kChunk);
+        return true;
+    }
+    const int *co = p.chunk_offsets;
+    if (cid >= co[p.N]) return false;
+    int lo = 0, hi = p.N;   // co[lo] <= cid < co[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (co[mid] <= cid) lo = mid;
+        else hi = mid;
+    }
+    r.n = lo;
+    r.c = cid - co[lo];
+    const int bos = p.cu_seqlens[lo], eos = p.cu_seqlens[lo + 1];
+    r.t0 = bos + r.c * kChunk;
+    r.L = min(kChunk, eos - r.t0);
+    return true;
+}
+
+// Sequence n's first token, length and first chunk index.
+__device__ __forceinline__ void seq_of(const BwdParams &p, int n, int &bos, int &len, int &cid0) {
+    if (!p.cu_seqlens) {
+        bos = n * p.T;
+        len = p.T;
+        cid0 = n * ((p.T + kChunk - 1) / kChunk);
+    } else {
+        bos = p.cu_seqlens[n];
+        len = p.cu_seqlens[n + 1] - bos;
+        cid0 = p.chunk_offsets[n];
+    }
+}
+
+// Loads L rows of a key-head row set ([T_tot, H, K], rows t0..t0+L-1 of head
+// jk) into dst[64][K+1] as fp32, zero rows past L, and normalises each row
+// (factor into f[r]) when use_l2norm.  Ends with a barrier.
+template <typename E, int K>
+__device__ void load_rows_normed(const E *src, int t0, int L, int H, int jk, int use_l2norm, float *dst, float *f) {
+    for (int e = threadIdx.x; e < kChunk * K; e += kThreads) {
+        const int r = e / K, c = e - r * K;
+        dst[r * (K + 1) + c] = r < L ? to_f(src[((int64_t)(t0 + r) * H + jk) * K + c]) : 0.f;
+    }
+    __syncthreads();
+    // 4 lanes per row
+    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+    float s = 0.f;
+    for (int c = part; c < K; c += 4) {
+        const float x = dst[r * (K + 1) + c];
+        s = fmaf(x, x, s);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    const float fr = use_l2norm ? 1.f / sqrtf(s + 1e-6f) : 1.f;
+    if (use_l2norm)
+        for (int c = part; c < K; c += 4) dst[r * (K + 1) + c] *= fr;
+    if (part == 0) f[r] = fr;
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// chunk offsets of packed sequences: co[n] = sum_{m < n} ceil(len_m / 64)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void bwd_setup_kernel(const int32_t *cu, int N, int32_t *co) {
+    __shared__ int part[kThreads];
+    const int per = (N + kThreads - 1) / kThreads;
+    const int a = min(N, (int)threadIdx.x * per), b = min(N, a + per);
+    int s = 0;
+    for (int n = a; n < b; ++n) s += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    part[threadIdx.x] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < kThreads; ++i) {
+            const int x = part[i];
+            part[i] = run;
+            run += x;
+        }
+        co[N] = run;
+    }
+    __syncthreads();
+    int run = part[threadIdx.x];
+    for (int n = a; n < b; ++n) {
+        co[n] = run;
+        run += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// per (chunk, value head): gamma, Tm = (I + A)^-1, A / beta and Pm
+// ---------------------------------------------------------------------------
+template <typename E, int K>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
+    __shared__ float sm[prep_floats<K>()];
+    float *kh = sm;                          // [64][K+1]
+    float *qh = kh + kChunk * (K + 1);       // [64][K+1]
+    float *A = qh + kChunk * (K + 1);        // [64][65]
+    float *Tm = A + kChunk * kPadC;          // [64][65]
+    float *gam = Tm + kChunk * kPadC;        // [64]
+    float *bet = gam + kChunk;               // [64]
+    float *fk = bet + kChunk;                // [64]
+    float *fq = fk + kChunk;                 // [64]
+
+    ChunkRef cr;
+    if (!find_chunk(p, blockIdx.x, cr)) return;
+    const int j = blockIdx.y, HV = p.HV, jk = j / (HV / p.H);
+    const int cid = blockIdx.x, L = cr.L, t0 = cr.t0;
+
+    if (threadIdx.x == 0) {
+        float run = 0.f;
+        for (int r = 0; r < kChunk; ++r) {
+            if (r < L) run += p.g[(int64_t)(t0 + r) * HV + j];
+            gam[r] = run;
+            bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+        }
+    }
+    load_rows_normed<E, K>((const E *)p.k, t0, L, p.H, jk, p.use_l2norm, kh, fk);
+    load_rows_normed<E, K>((const E *)p.q, t0, L, p.H, jk, p.use_l2norm, qh, fq);
+    if (threadIdx.x < L) p.gam[(int64_t)(t0 + threadIdx.x) * HV + j] = gam[threadIdx.x];
+
+    const int tx = tx_of(), ty = ty_of();
+    float kk[4][4], qk[4][4];
+    zero(kk);
+    zero(qk);
+    mm<4, 4, K>(kk, [&](int r, int m) { return kh[r * (K + 1) + m]; },
+                [&](int c, int m) { return kh[c * (K + 1) + m]; });
+    mm<4, 4, K>(qk, [&](int r, int m) { return qh[r * (K + 1) + m]; },
+                [&](int c, int m) { return kh[c * (K + 1) + m]; });
+    float *ag_out = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
+    float *pm_out = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = ty + 16 * i;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int c = tx + 16 * jj;
+            const float e = (c <= r && r < L) ? __expf(gam[r] - gam[c]) : 0.f;
+            const float ag = c < r ? e * kk[i][jj] : 0.f;
+            A[r * kPadC + c] = bet[r] * ag;
+            ag_out[r * kChunk + c] = ag;
+            pm_out[r * kChunk + c] = e * qk[i][jj];
+        }
+    }
+    __syncthreads();
+
+    // Tm = (I + A)^-1 by forward substitution over rows: Tm_i = e_i - sum_{m<i} A_im Tm_m.
+    // 4 lanes per column, each summing every 4th m.
+    const int col = threadIdx.x >> 2, part = threadIdx.x & 3;
+    for (int i = 0; i < kChunk; ++i) {
+        float s = 0.f;
+        for (int m = col + part; m < i; m += 4) s = fmaf(A[i * kPadC + m], Tm[m * kPadC + col], s);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (part == 0) Tm[i * kPadC + col] = col == i ? 1.f : col < i ? -s : 0.f;
+        __syncthreads();
+    }
+    float *tm_out = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+        const int r = e >> 6, c = e & 63;
+        tm_out[e] = Tm[r * kPadC + c];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// forward over chunks per (sequence, value head, 32 value columns): h, Vn
+// ---------------------------------------------------------------------------
+template <typename E, int K>
+__global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
+    __shared__ float sm[fwd_scan_floats<K>()];
+    float *h = sm;                           // [K][33]
+    float *kh = h + K * kPadT;               // [64][K+1]
+    float *Tm = kh + kChunk * (K + 1);       // [64][65]
+    float *vv = Tm + kChunk * kPadC;         // [64][33]: v, then F
+    float *Bm = vv + kChunk * kPadT;         // [64][33]
+    float *gam = Bm + kChunk * kPadT;        // [64]
+    float *bet = gam + kChunk;               // [64]
+    float *fk = bet + kChunk;                // [64]
+
+    const int HV = p.HV, V = p.V;
+    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int c0 = blockIdx.y * kVT;
+    int bos, len, cid0;
+    seq_of(p, n, bos, len, cid0);
+    const int nc = (len + kChunk - 1) / kChunk;
+    const int tx = tx_of(), ty = ty_of();
+
+    for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
+        const int r = e / kVT, c = e - r * kVT;
+        h[r * kPadT + c] = p.initial_state ? p.initial_state[(((int64_t)n * HV + j) * K + r) * V + c0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int ci = 0; ci < nc; ++ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        float *hs = p.hs + ((int64_t)cid * HV + j) * K * V;
+        for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
+            const int r = e / kVT, c = e - r * kVT;
+            hs[(int64_t)r * V + c0 + c] = h[r * kPadT + c];
+        }
+        const float *tm = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) Tm[(e >> 6) * kPadC + (e & 63)] = tm[e];
+        for (int e = threadIdx.x; e < kChunk * kVT; e += kThreads) {
+            const int r = e / kVT, c = e - r * kVT;
+            vv[r * kPadT + c] = r < L ? to_f(((const E *)p.v)[((int64_t)(t0 + r) * HV + j) * V + c0 + c]) : 0.f;
+        }
+        if (threadIdx.x < kChunk) {
+            const int r = threadIdx.x;
+            gam[r] = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
+            bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+        }
+        load_rows_normed<E, K>((const E *)p.k, t0, L, p.H, jk, p.use_l2norm, kh, fk);
+
+        // B = diag(beta) (V - diag(D) Kh h)
+        {
+            float x[4][2];
+            zero(x);
+            mm<4, 2, K>(x, [&](int r, int m) { return kh[r * (K + 1) + m]; },
+                        [&](int c, int m) { return h[m * kPadT + c]; });
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ty + 16 * i;
+                const float d = __expf(gam[r]);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int c = tx + 16 * jj;
+                    Bm[r * kPadT + c] = bet[r] * (vv[r * kPadT + c] - d * x[i][jj]);
+                }
+            }
+        }
+        __syncthreads();
+        // Vn = Tm B; F = diag(exp(gamma_L - gamma)) Vn into vv
+        {
+            float x[4][2];
+            zero(x);
+            mm<4, 2, kChunk>(x, [&](int r, int m) { return Tm[r * kPadC + m]; },
+                             [&](int c, int m) { return Bm[m * kPadT + c]; });
+            const float gl = gam[L - 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ty + 16 * i;
+                const float f = r < L ? __expf(gl - gam[r]) : 0.f;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int c = tx + 16 * jj;
+                    if (r < L) p.vn[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = x[i][jj];
+                    vv[r * kPadT + c] = f * x[i][jj];
+                }
+            }
+        }
+        __syncthreads();
+        // h <- D_L h + Kh^T F
+        {
+            float x[K / 16][2];
+            zero(x);
+            mm<K / 16, 2, kChunk>(x, [&](int r, int m) { return kh[m * (K + 1) + r]; },
+                                  [&](int c, int m) { return vv[m * kPadT + c]; });
+            const float dl = __expf(gam[L - 1]);
+#pragma unroll
+            for (int i = 0; i < K / 16; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    float &hv = h[(ty + 16 * i) * kPadT + tx + 16 * jj];
+                    hv = fmaf(dl, hv, x[i][jj]);
+                }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward over chunks per (sequence, value head, 32 value columns):
+// dh' per chunk, dB, and the initial-state gradient
+// ---------------------------------------------------------------------------
+template <typename E, int K>
+__global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
+    __shared__ float sm[dh_scan_floats<K>()];
+    float *dh = sm;                          // [K][33]
+    float *kh = dh + K * kPadT;              // [64][K+1]
+    float *qh = kh + kChunk * (K + 1);       // [64][K+1]
+    float *Tm = qh + kChunk * (K + 1);       // [64][65]
+    float *Pm = Tm + kChunk * kPadC;         // [64][65]
+    float *dO = Pm + kChunk * kPadC;         // [64][33]
+    float *dVn = dO + kChunk * kPadT;        // [64][33]
+    float *dB = dVn + kChunk * kPadT;        // [64][33]
+    float *gam = dB + kChunk * kPadT;        // [64]
+    float *bet = gam + kChunk;               // [64]
+    float *fk = bet + kChunk;                // [64]
+    float *fq = fk + kChunk;                 // [64]
+
+    const int HV = p.HV, V = p.V;
+    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int c0 = blockIdx.y * kVT;
+    int bos, len, cid0;
+    seq_of(p, n, bos, len, cid0);
+    const int nc = (len + kChunk - 1) / kChunk;
+    const int tx = tx_of(), ty = ty_of();
+    const float scale = p.scale;
+
+    for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
+        const int r = e / kVT, c = e - r * kVT;
+        dh[r * kPadT + c] = p.dht ? p.dht[(((int64_t)n * HV + j) * K + r) * V + c0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int ci = nc - 1; ci >= 0; --ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        float *dhs = p.dhs + ((int64_t)cid * HV + j) * K * V;
+        for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
+            const int r = e / kVT, c = e - r * kVT;
+            dhs[(int64_t)r * V + c0 + c] = dh[r * kPadT + c];
+        }
+        const float *tm = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+        const float *pm = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+            Tm[(e >> 6) * kPadC + (e & 63)] = tm[e];
+            Pm[(e >> 6) * kPadC + (e & 63)] = pm[e];
+        }
+        for (int e = threadIdx.x; e < kChunk * kVT; e += kThreads) {
+            const int r = e / kVT, c = e - r * kVT;
+            dO[r * kPadT + c] = r < L ? to_f(((const E *)p.dout)[((int64_t)(t0 + r) * HV + j) * V + c0 + c]) : 0.f;
+        }
+        if (threadIdx.x < kChunk) {
+            const int r = threadIdx.x;
+            gam[r] = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
+            bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+        }
+        load_rows_normed<E, K>((const E *)p.k, t0, L, p.H, jk, p.use_l2norm, kh, fk);
+        load_rows_normed<E, K>((const E *)p.q, t0, L, p.H, jk, p.use_l2norm, qh, fq);
+        const float gl = gam[L - 1];
+
+        // dVn = scale Pm^T dO + diag(exp(gamma_L - gamma)) Kh dh'
+        {
+            float a[4][2], b[4][2];
+            zero(a);
+            zero(b);
+            mm<4, 2, kChunk>(a, [&](int r, int m) { return Pm[m * kPadC + r]; },
+                             [&](int c, int m) { return dO[m * kPadT + c]; });
+            mm<4, 2, K>(b, [&](int r, int m) { return kh[r * (K + 1) + m]; },
+                        [&](int c, int m) { return dh[m * kPadT + c]; });
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ty + 16 * i;
+                const float f = r < L ? __expf(gl - gam[r]) : 0.f;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) dVn[r * kPadT + tx + 16 * jj] = scale * a[i][jj] + f * b[i][jj];
+            }
+        }
+        __syncthreads();
+        // dB = Tm^T dVn
+        {
+            float a[4][2];
+            zero(a);
+            mm<4, 2, kChunk>(a, [&](int r, int m) { return Tm[m * kPadC + r]; },
+                             [&](int c, int m) { return dVn[m * kPadT + c]; });
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ty + 16 * i;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int c = tx + 16 * jj;
+                    dB[r * kPadT + c] = a[i][jj];
+                    if (r < L) p.db[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = a[i][jj];
+                }
+            }
+        }
+        __syncthreads();
+        // dh <- D_L dh' + scale Qh^T diag(D) dO - Kh^T diag(beta D) dB
+        {
+            float a[K / 16][2];
+            zero(a);
+            mm<K / 16, 2, kChunk>(a, [&](int r, int m) { return qh[m * (K + 1) + r]; },
+                                  [&](int c, int m) { return scale * __expf(gam[m]) * dO[m * kPadT + c]; });
+            mm<K / 16, 2, kChunk>(a, [&](int r, int m) { return kh[m * (K + 1) + r]; },
+                                  [&](int c, int m) { return -bet[m] * __expf(gam[m]) * dB[m * kPadT + c]; });
+            const float dl = __expf(gl);
+#pragma unroll
+            for (int i = 0; i < K / 16; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    float &x = dh[(ty + 16 * i) * kPadT + tx + 16 * jj];
+                    x = fmaf(dl, x, a[i][jj]);
+                }
+        }
+        __syncthreads();
+    }
+    if (p.dh0)
+        for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
+            const int r = e / kVT, c = e - r * kVT;
+            p.dh0[(((int64_t)n * HV + j) * K + r) * V + c0 + c] = dh[r * kPadT + c];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// per (chunk, value head): dq, dk (per value head), dv, dg, dbeta
+// ---------------------------------------------------------------------------
+template <typename E, int K, int V>
+__global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
+    __shared__ float sm[grads_floats<K>()];
+    float *kh = sm;                          // [64][K+1]
+    float *qh = kh + kChunk * (K + 1);       // [64][K+1]
+    float *tile = qh + kChunk * (K + 1);     // per value tile, then the 64 x 64 matrices
+    float *hT = tile;                        // [K][33]
+    float *dhT = hT + K * kPadT;             // [K][33]
+    float *vnT = dhT + K * kPadT;            // [64][33]
+    float *dbT = vnT + kChunk * kPadT;       // [64][33]
+    float *doT = dbT + kChunk * kPadT;       // [64][33]
+    float *vvT = doT + kChunk * kPadT;       // [64][33]
+    float *dS = tile;                        // [64][65] dSqk (after the value tiles)
+    float *Ad = dS + kChunk * kPadC;         // [64][65]
+    float *Zm = Ad + kChunk * kPadC;         // [64][65]
+    float *rows = tile + grads_tile_floats<K>();   // scalars per row
+    float *gam = rows;                       // [64]
+    float *bet = gam + kChunk;               // [64]
+    float *fk = bet + kChunk;                // [64]
+    float *fq = fk + kChunk;                 // [64]
+    float *dgam = fq + kChunk;               // [64]
+    float *dbet = dgam + kChunk;             // [64]
+    float *red = dbet + kChunk;              // [kThreads / 64] block reduction slots
+
+    ChunkRef cr;
+    if (!find_chunk(p, blockIdx.x, cr)) return;
+    const int j = blockIdx.y, HV = p.HV, jk = j / (HV / p.H);
+    const int cid = blockIdx.x, L = cr.L, t0 = cr.t0;
+    const int tx = tx_of(), ty = ty_of();
+    const float scale = p.scale;
+    constexpr int KR = K / 16;
+
+    if (threadIdx.x < kChunk) {
+        const int r = threadIdx.x;
+        gam[r] = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
+        bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+    }
+    load_rows_normed<E, K>((const E *)p.k, t0, L, p.H, jk, p.use_l2norm, kh, fk);
+    load_rows_normed<E, K>((const E *)p.q, t0, L, p.H, jk, p.use_l2norm, qh, fq);
+
+    float aP[4][4], aA[4][4], dQ[4][KR], aE[4][KR], aF[4][KR];
+    zero(aP);
+    zero(aA);
+    zero(dQ);
+    zero(aE);
+    zero(aF);
+    float sdh = 0.f;      // this thread's part of <dh', h>
+    float sbv = 0.f;      // row (threadIdx.x >> 2): sum_v dB v
+    const float *hs = p.hs + ((int64_t)cid * HV + j) * K * V;
+    const float *dhs = p.dhs + ((int64_t)cid * HV + j) * K * V;
+    for (int c0 = 0; c0 < V; c0 += kVT) {
+        for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
+            const int r = e / kVT, c = e - r * kVT;
+            const float hv = hs[(int64_t)r * V + c0 + c], dv = dhs[(int64_t)r * V + c0 + c];
+            hT[r * kPadT + c] = hv;
+            dhT[r * kPadT + c] = dv;
+            sdh = fmaf(hv, dv, sdh);
+        }
+        for (int e = threadIdx.x; e < kChunk * kVT; e += kThreads) {
+            const int r = e / kVT, c = e - r * kVT;
+            const int64_t at = ((int64_t)(t0 + r) * HV + j) * V + c0 + c;
+            const bool in = r < L;
+            vnT[r * kPadT + c] = in ? p.vn[at] : 0.f;
+            dbT[r * kPadT + c] = in ? p.db[at] : 0.f;
+            doT[r * kPadT + c] = in ? to_f(((const E *)p.dout)[at]) : 0.f;
+            vvT[r * kPadT + c] = in ? to_f(((const E *)p.v)[at]) : 0.f;
+        }
+        __syncthreads();
+        {
+            const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+            float s = 0.f;
+            for (int c = part; c < kVT; c += 4) s = fmaf(dbT[r * kPadT + c], vvT[r * kPadT + c], s);
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            sbv += s;
+            if (r < L)
+                for (int c = part; c < kVT; c += 4)
+                    ((E *)p.dv)[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = to_e<E>(bet[r] * dbT[r * kPadT + c]);
+        }
+        mm<4, 4, kVT>(aP, [&](int r, int m) { return doT[r * kPadT + m]; },
+                      [&](int c, int m) { return vnT[c * kPadT + m]; });
+        mm<4, 4, kVT>(aA, [&](int r, int m) { return dbT[r * kPadT + m]; },
+                      [&](int c, int m) { return vnT[c * kPadT + m]; });
+        mm<4, KR, kVT>(dQ, [&](int r, int m) { return doT[r * kPadT + m]; },
+                       [&](int c, int m) { return hT[c * kPadT + m]; });
+        mm<4, KR, kVT>(aE, [&](int r, int m) { return dbT[r * kPadT + m]; },
+                       [&](int c, int m) { return hT[c * kPadT + m]; });
+        mm<4, KR, kVT>(aF, [&](int r, int m) { return vnT[r * kPadT + m]; },
+                       [&](int c, int m) { return dhT[c * kPadT + m]; });
+        __syncthreads();
+    }
+
+    // <dh', h> over the block
+    {
+        float s = sdh;
+        for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    }
+    const float gl = gam[L - 1];
+    // row scalings and the row dot products with qh / kh
+    float t3sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = ty + 16 * i;
+        const float d = __expf(gam[r]);
+        const float f = r < L ? __expf(gl - gam[r]) : 0.f;
+        float t1 = 0.f, t2 = 0.f, t3 = 0.f;
+#pragma unroll
+        for (int c = 0; c < KR; ++c) {
+            const int col = tx + 16 * c;
+            dQ[i][c] *= scale * d;
+            aE[i][c] *= d;
+            aF[i][c] *= f;
+            t1 = fmaf(qh[r * (K + 1) + col], dQ[i][c], t1);
+            t2 = fmaf(kh[r * (K + 1) + col], aE[i][c], t2);
+            t3 = fmaf(kh[r * (K + 1) + col], aF[i][c], t3);
+        }
+        t1 = sum16(t1);
+        t2 = sum16(t2);
+        t3 = sum16(t3);
+        t3sum += t3;
+        if (tx == 0) {
+            dgam[r] = t1 - bet[r] * t2 - t3;
+            dbet[r] = -t2;
+        }
+    }
+    // dK so far: F dh'^T - diag(beta) E
+    float dK[4][KR];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < KR; ++c) dK[i][c] = aF[i][c] - bet[ty + 16 * i] * aE[i][c];
+
+    // the 64 x 64 matrices: dSqk, Ad and Z = dSqk * (qh . kh) + dA * A
+    const float *pm = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+    const float *ag = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
+    float dbA[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = ty + 16 * i;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int c = tx + 16 * jj;
+            const bool low = c <= r && r < L;
+            const float e = low ? __expf(gam[r] - gam[c]) : 0.f;
+            const float dpm = scale * aP[i][jj];
+            const float dsq = e * dpm;                   // dSqk
+            const float z1 = dpm * pm[r * kChunk + c];   // dPm * Pm
+            const float dA = c < r && r < L ? -aA[i][jj] : 0.f;
+            const float agv = ag[r * kChunk + c];
+            dS[r * kPadC + c] = dsq;
+            Ad[r * kPadC + c] = dA * bet[r] * e;
+            Zm[r * kPadC + c] = z1 + dA * bet[r] * agv;
+            dbA[i] = fmaf(dA, agv, dbA[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float s = sum16(dbA[i]);
+        if (tx == 0) dbet[ty + 16 * i] += s;
+    }
+    __syncthreads();
+    if (threadIdx.x < kChunk) {
+        const int r = threadIdx.x;
+        float rs = 0.f, cs = 0.f;
+        for (int m = 0; m < kChunk; ++m) {
+            rs += Zm[r * kPadC + m];
+            cs += Zm[m * kPadC + r];
+        }
+        dgam[r] += rs - cs;
+    }
+    if ((threadIdx.x & 3) == 0) dbet[threadIdx.x >> 2] += sbv;
+    if (tx == 0) red[4 + ty] = t3sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float s = red[0] + red[1] + red[2] + red[3];
+        float t = 0.f;
+        for (int y = 0; y < 16; ++y) t += red[4 + y];
+        dgam[L - 1] += __expf(gl) * s + t;
+    }
+
+    // dQ += dSqk Kh;  dK += dSqk^T Qh + (Ad + Ad^T) Kh
+    mm<4, KR, kChunk>(dQ, [&](int r, int m) { return dS[r * kPadC + m]; },
+                      [&](int c, int m) { return kh[m * (K + 1) + c]; });
+    mm<4, KR, kChunk>(dK, [&](int r, int m) { return dS[m * kPadC + r]; },
+                      [&](int c, int m) { return qh[m * (K + 1) + c]; });
+    mm<4, KR, kChunk>(dK, [&](int r, int m) { return Ad[r * kPadC + m] + Ad[m * kPadC + r]; },
+                      [&](int c, int m) { return kh[m * (K + 1) + c]; });
+
+    // L2-norm backward and the per-value-head partial dq, dk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = ty + 16 * i;
+        float sq = 0.f, sk = 0.f;
+        if (p.use_l2norm) {
+#pragma unroll
+            for (int c = 0; c < KR; ++c) {
+                sq = fmaf(qh[r * (K + 1) + tx + 16 * c], dQ[i][c], sq);
+                sk = fmaf(kh[r * (K + 1) + tx + 16 * c], dK[i][c], sk);
+            }
+            sq = sum16(sq);
+            sk = sum16(sk);
+        }
+        if (r < L) {
+            float *dq = p.dqp + ((int64_t)(t0 + r) * HV + j) * K;
+            float *dk = p.dkp + ((int64_t)(t0 + r) * HV + j) * K;
+#pragma unroll
+            for (int c = 0; c < KR; ++c) {
+                const int col = tx + 16 * c;
+                dq[col] = fq[r] * (dQ[i][c] - qh[r * (K + 1) + col] * sq);
+                dk[col] = fk[r] * (dK[i][c] - kh[r * (K + 1) + col] * sk);
+            }
+        }
+    }
+    __syncthreads();
+    // dg = reverse cumsum of dgamma inside the chunk; dbeta
+    if (threadIdx.x < L) {
+        const int r = threadIdx.x;
+        float s = 0.f;
+        for (int m = r; m < L; ++m) s += dgam[m];
+        p.dg[(int64_t)(t0 + r) * HV + j] = s;
+        p.dbeta[(int64_t)(t0 + r) * HV + j] = dbet[r];
+    }
+}
+
+// dq, dk [T_tot, H, K] = sum over the G value heads of each key head
+template <typename E>
+__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const float *dqp, const float *dkp, E *dq, E *dk,
+                                                             int64_t total, int H, int G, int K) {
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= total) return;
+    const int64_t row = e / K;   // t * H + jk
+    const int c = (int)(e - row * K);
+    const int64_t t = row / H;
+    const int jk = (int)(row - t * H);
+    float sq = 0.f, sk = 0.f;
+    for (int g = 0; g < G; ++g) {
+        const int64_t at = (t * (int64_t)H * G + (int64_t)jk * G + g) * K + c;
+        sq += dqp[at];
+        sk += dkp[at];
+    }
+    dq[e] = to_e<E>(sq);
+    dk[e] = to_e<E>(sk);
+}
+
+template <typename E, int K, int V>
+hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *prof) {
+    const dim3 blk(kThreads);
+    if (p.cu_seqlens && p.N > 0) {
+        if (prof) prof->begin(kBwdSetupKernel, st);
+        hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), blk, 0, st, p.cu_seqlens, p.N, p.chunk_offsets);
+        if (prof) prof->end(kBwdSetupKernel, st);
+    }
+    if (nc_max > 0) {
+        if (prof) prof->begin(kBwdPrepKernel, st);
+        hipLaunchKernelGGL((bwd_prep_kernel<E, K>), dim3(nc_max, p.HV), blk, 0, st, p);
+        if (prof) prof->end(kBwdPrepKernel, st);
+    }
+    if (p.N > 0) {
+        const dim3 scan_grid(p.N * p.HV, V / kVT);
+        if (nc_max > 0) {
+            if (prof) prof->begin(kBwdFwdScanKernel, st);
+            hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K>), scan_grid, blk, 0, st, p);
+            if (prof) prof->end(kBwdFwdScanKernel, st);
+        }
+        if (prof) prof->begin(kBwdDhScanKernel, st);
+        hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K>), scan_grid, blk, 0, st, p);
+        if (prof) prof->end(kBwdDhScanKernel, st);
+    }
+    if (nc_max > 0) {
+        if (prof) prof->begin(kBwdGradsKernel, st);
+        hipLaunchKernelGGL((bwd_grads_kernel<E, K, V>), dim3(nc_max, p.HV), blk, 0, st, p);
+        if (prof) prof->end(kBwdGradsKernel, st);
+        const int64_t total = (int64_t)p.T_tot * p.H * K;
+        if (total > 0) {
+            if (prof) prof->begin(kBwdReduceKernel, st);
+            hipLaunchKernelGGL(bwd_reduce_kernel<E>, dim3((unsigned)((total + kThreads - 1) / kThreads)), blk, 0, st,
+                               p.dqp, p.dkp, (E *)p.dq, (E *)p.dk, total, p.H, p.HV / p.H, K);
+            if (prof) prof->end(kBwdReduceKernel, st);
+        }
+    }
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_dtype(const BwdParams &p, int nc_max, hipStream_t st, Profiler *prof) {
+    if (p.K == 64) return p.V == 64 ? launch_kv<E, 64, 64>(p, nc_max, st, prof) : launch_kv<E, 64, 128>(p, nc_max, st, prof);
+    return p.V == 64 ? launch_kv<E, 128, 64>(p, nc_max, st, prof) : launch_kv<E, 128, 128>(p, nc_max, st, prof);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+static int bwd_max_chunks(int B, int T, int N, bool varlen) {
+    const int64_t t_tot = (int64_t)B * T;
+    const int64_t nc = varlen ? (t_tot + kChunk - 1) / kChunk + N : (int64_t)B * ((T + kChunk - 1) / kChunk);
+    return nc > INT32_MAX ? -1 : (int)nc;
+}
+
+BwdPlan plan_backward(int B, int T, int H, int HV, int K, int V, int N, bool varlen) {
+    BwdPlan pl;
+    const int64_t t_tot = (int64_t)B * T;
+    pl.nc_max = bwd_max_chunks(B, T, N, varlen);
+    if (pl.nc_max < 0) return pl;
+    const size_t nc = (size_t)pl.nc_max;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    pl.off_co = take(sizeof(int32_t) * (size_t)(N + 1));
+    pl.off_gam = take(sizeof(float) * (size_t)t_tot * HV);
+    pl.off_tm = take(sizeof(float) * nc * HV * kChunk * kChunk);
+    pl.off_ag = take(sizeof(float) * nc * HV * kChunk * kChunk);
+    pl.off_pm = take(sizeof(float) * nc * HV * kChunk * kChunk);
+    pl.off_hs = take(sizeof(float) * nc * HV * K * V);
+    pl.off_dhs = take(sizeof(float) * nc * HV * K * V);
+    pl.off_vn = take(sizeof(float) * (size_t)t_tot * HV * V);
+    pl.off_db = take(sizeof(float) * (size_t)t_tot * HV * V);
+    pl.off_dqp = take(sizeof(float) * (size_t)t_tot * HV * K);
+    pl.off_dkp = take(sizeof(float) * (size_t)t_tot * HV * K);
+    pl.bytes = off;
+    return pl;
+}
+
+hipError_t launch_backward(BwdParams p, int dtype, const BwdPlan &plan, void *ws, hipStream_t stream,
+                           Profiler *prof) {
+    char *w = (char *)ws;
+    p.chunk_offsets = (int32_t *)(w + plan.off_co);
+    p.gam = (float *)(w + plan.off_gam);
+    p.tm = (float *)(w + plan.off_tm);
+    p.ag = (float *)(w + plan.off_ag);
+    p.pm = (float *)(w + plan.off_pm);
+    p.hs = (float *)(w + plan.off_hs);
+    p.dhs = (float *)(w + plan.off_dhs);
+    p.vn = (float *)(w + plan.off_vn);
+    p.db = (float *)(w + plan.off_db);
+    p.dqp = (float *)(w + plan.off_dqp);
+    p.dkp = (float *)(w + plan.off_dkp);
+    p.T_tot = p.B * p.T;
+    const int nc = p.T_tot > 0 ? plan.nc_max : 0;
+    return dtype == 0 ? launch_dtype<bf16>(p, nc, stream, prof) : launch_dtype<float>(p, nc, stream, prof);
+}
+
+}  // namespace gdn

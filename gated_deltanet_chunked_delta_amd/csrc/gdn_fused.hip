@@ -595,6 +595,12 @@ const char *kernel_name(int kind) {
         case kSplitSetupKernel: return "split_setup_kernel";
         case kSplitCombineKernel: return "split_combine_kernel";
         case kSplitCorrectKernel: return "split_correct_kernel";
+        case kBwdSetupKernel: return "bwd_setup_kernel";
+        case kBwdPrepKernel: return "bwd_prep_kernel";
+        case kBwdFwdScanKernel: return "bwd_fwd_scan_kernel";
+        case kBwdDhScanKernel: return "bwd_dh_scan_kernel";
+        case kBwdGradsKernel: return "bwd_grads_kernel";
+        case kBwdReduceKernel: return "bwd_reduce_kernel";
         default: return "?";
     }
 }

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host code (gdn_api.cpp) and the HIP
-// kernels (gdn_fused.hip, gdn_fused_ws.hip, gdn_recurrent.hip, gdn_gating.hip).  Not part of
+// kernels (gdn_fused.hip, gdn_fused_ws.hip, gdn_recurrent.hip, gdn_gating.hip,
+// gdn_split.hip, gdn_backward.hip).  Not part of
 // the public ABI.
 #pragma once
 
@@ -56,9 +57,11 @@ struct Params {
 // gating_kernel: the stand-alone gate computation.
 // split_setup_kernel, split_combine_kernel, split_correct_kernel: the
 // sequence split of long sequences (gdn_split.hip).
+// bwd_*_kernel: the backward pass (gdn_backward.hip).
 enum KernelKind { kFusedKernel = 0, kFusedWsKernel = 1, kRecurrentKernel = 2, kGatingKernel = 3,
                   kSplitSetupKernel = 4, kSplitCombineKernel = 5, kSplitCorrectKernel = 6,
-                  kNumKernelKinds = 7 };
+                  kBwdSetupKernel = 7, kBwdPrepKernel = 8, kBwdFwdScanKernel = 9, kBwdDhScanKernel = 10,
+                  kBwdGradsKernel = 11, kBwdReduceKernel = 12, kNumKernelKinds = 13 };
 const char *kernel_name(int kind);
 
 // Timing hook: when given, the launch sequence calls begin/end around each
@@ -116,6 +119,42 @@ SplitPlan plan_split(int B, int T, int H, int HV, int K, int V, int elem_bytes);
 // Enqueues the split forward pass of p (cu_seqlens null) with workspace ws.
 hipError_t launch_split(const Params &p, int dtype, const SplitPlan &plan, void *ws, hipStream_t stream,
                         Profiler *prof);
+
+// Everything the backward pass needs (gdn_backward.hip).  Pointers are device
+// pointers; the intermediates point into the caller's workspace.
+struct BwdParams {
+    // inputs
+    const void *q, *k, *v;           // [T_tot, H, K], [T_tot, H, K], [T_tot, HV, V]
+    const float *g, *beta;           // [T_tot, HV]
+    const void *dout;                // [T_tot, HV, V], gradient of the output
+    const float *dht;                // [N, HV, K, V] gradient of the final state, or null
+    const float *initial_state;      // [N, HV, K, V] or null
+    const int32_t *cu_seqlens;       // [N+1] or null (equal-length mode)
+    // outputs
+    void *dq, *dk, *dv;              // shapes of q, k, v
+    float *dg, *dbeta;               // [T_tot, HV]
+    float *dh0;                      // [N, HV, K, V] or null
+    // workspace
+    int32_t *chunk_offsets;          // [N+1] first chunk of each packed sequence
+    float *gam;                      // [T_tot, HV] chunk-local cumsum of g
+    float *tm, *ag, *pm;             // [chunks, HV, 64, 64]: (I+A)^-1, A / beta, masked gated Q K^T
+    float *hs, *dhs;                 // [chunks, HV, K, V]: state at chunk start, its gradient at chunk end
+    float *vn, *db;                  // [T_tot, HV, V]: delta-rule errors and their B-gradient
+    float *dqp, *dkp;                // [T_tot, HV, K]: dq, dk per value head
+    // sizes
+    int B, T, H, HV, K, V, N, T_tot;
+    float scale;
+    int use_l2norm;
+};
+// Workspace carve-up of the backward pass (256-byte aligned offsets).
+struct BwdPlan {
+    int nc_max = 0;                   // chunk slots (an upper bound on the chunks of packed sequences)
+    size_t off_co = 0, off_gam = 0, off_tm = 0, off_ag = 0, off_pm = 0, off_hs = 0, off_dhs = 0, off_vn = 0,
+           off_db = 0, off_dqp = 0, off_dkp = 0, bytes = 0;
+};
+BwdPlan plan_backward(int B, int T, int H, int HV, int K, int V, int N, bool varlen);
+hipError_t launch_backward(BwdParams p, int dtype, const BwdPlan &plan, void *ws, hipStream_t stream,
+                           Profiler *prof);
 
 // The single-role fused kernel's launch (gdn_fused.hip).
 hipError_t launch_fused(const Params &p, int dtype, hipStream_t stream);

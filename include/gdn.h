@@ -55,7 +55,7 @@ typedef enum gdn_status {
                                  B != 1 with cu_seqlens) */
     GDN_ERR_DTYPE = -3,       /* unknown dtype code */
     GDN_ERR_UNSUPPORTED = -4, /* K or V not in {64, 128}, or HV not a multiple of H */
-    GDN_ERR_WORKSPACE = -5,   /* reserved: workspace NULL, misaligned or too small while required */
+    GDN_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or too small where required (gdn_chunk_bwd) */
     GDN_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
     GDN_ERR_ALIGN = -7        /* a pointer lacks the alignment its argument requires */
 } gdn_status;
@@ -283,6 +283,50 @@ int gdn_recurrent_update_pool(const void *q, const void *k, const void *v,
                               float scale, int use_l2norm,
                               const gdn_state_pool *pool, void *out,
                               const gdn_decode_shape *shape, void *stream);
+
+/* Bytes of device workspace gdn_chunk_bwd needs for `shape` (0 for invalid
+ * shapes).  The backward pass keeps, per 64-token chunk and value head, the
+ * chunk-start state and its gradient (2 K V floats) and three 64 x 64 fp32
+ * matrices, and per token and value head 2 V + 2 K + 1 floats:
+ * about 1.6 GiB at B = 4, T = 4096, HV = 32, K = V = 128.  Chunk slots are
+ * counted for packed sequences (ceil(T/64) + N) when B == 1, else B ceil(T/64). */
+size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape *shape);
+
+/* Backward pass of gdn_chunk_fwd (training).  The page "NPU Training
+ * Operators - GDN" lists the backward operators next to the forward ones in its
+ * operator-semantics section: the gradients of q, k, v, of the gates g and
+ * beta (the one of g by a reverse cumulative sum over each chunk) and of the
+ * initial state.  Given the forward inputs and the gradients of the forward
+ * outputs, it writes the gradients of the forward inputs:
+ *
+ *   q, k, v, g, beta, scale, use_l2norm, initial_state, cu_seqlens, shape
+ *                 exactly as given to gdn_chunk_fwd (read)
+ *   dout          [B, T, HV, V]  dtype          read; gradient of out
+ *   dht           [N, HV, K, V]  fp32 or NULL   read; gradient of final_state
+ *                 (NULL: the final state is not used, gradient zero)
+ *   dq, dk        [B, T, H, K]   dtype          written (every element); with
+ *                 use_l2norm these are gradients of the raw (unnormalised) rows
+ *   dv            [B, T, HV, V]  dtype          written (every element)
+ *   dg, dbeta     [B, T, HV]     fp32           written (every element)
+ *   dh0           [N, HV, K, V]  fp32 or NULL   written; gradient of
+ *                 initial_state (NULL = not produced)
+ *   workspace     device scratch of gdn_chunk_bwd_workspace_bytes bytes,
+ *                 256-byte aligned (required: GDN_ERR_WORKSPACE otherwise);
+ *                 contents on entry are ignored
+ *   stream        hipStream_t to enqueue on (NULL = the default stream)
+ *
+ * Outputs must not overlap each other, the inputs or the workspace.  All
+ * arithmetic is fp32 whatever dtype is (bf16 inputs are widened, bf16 outputs
+ * rounded to nearest even at the end).  Returns GDN_OK or a negative
+ * gdn_status; checks run on the host before anything is enqueued. */
+int gdn_chunk_bwd(const void *q, const void *k, const void *v,
+                  const float *g, const float *beta,
+                  const void *dout, const float *dht,
+                  float scale, int use_l2norm,
+                  const float *initial_state, const int32_t *cu_seqlens,
+                  void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0,
+                  const gdn_shape *shape, void *workspace, size_t workspace_bytes,
+                  void *stream);
 
 /* Kernel timing hook, for measurement.  While enabled, every call of the
  * entry points above records HIP events on its stream just before

@@ -147,6 +147,22 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", io_dtype=torch.bfloat1
                 N=N, workload=w)
 
 
+def make_grad_inputs(x, seed: int = 1, dht_std: float = 0.1):
+    """Draws the output gradients of a backward pass for the forward inputs
+    ``x`` of ``make_inputs``: do with v's shape, dtype and device (N(0, 1)
+    values rounded to bf16) and dht [N,HV,K,V] float32 ~ N(0, dht_std^2).
+    Adds them to x as x["do"], x["dht"] and returns x."""
+    v = x["v"]
+    dev = v.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    w = x["workload"]
+    do = torch.randn(*v.shape, generator=gen, device=dev, dtype=torch.float32)
+    x["do"] = do.to(torch.bfloat16).to(v.dtype)
+    x["dht"] = torch.randn(x["N"], w.HV, w.K, w.V, generator=gen, device=dev, dtype=torch.float32) * dht_std
+    return x
+
+
 @dataclasses.dataclass(frozen=True)
 class DecodeWorkload:
     """One decode step: N sequences, one token each, states in a pool."""
