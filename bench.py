@@ -1,5 +1,6 @@
 #!/usr/bin/env python3
-"""Throughput of the chunked gated delta rule forward pass on one MI355X.
+"""Throughput of the chunked gated delta rule forward pass on one MI355X
+(``--path bwd``: its backward pass; a decode workload: the decode step).
 
 One step = one full forward pass (every kernel of the path) over one batch of
 seeded synthetic inputs already resident in HBM.  Default workload: the
@@ -90,6 +91,9 @@ def parse():
                     help="tensors: g and beta are inputs (computed once by the gating kernel before timing); "
                          "fused: the kernel computes them from A_log, dt_bias, a, b; separate: each step runs "
                          "the gating kernel, then the kernel with g and beta")
+    ap.add_argument("--path", default="fwd", choices=["fwd", "bwd"],
+                    help="fwd: the forward pass (prefill); bwd: the backward pass (gdn_chunk_bwd) of the "
+                         "same workload, given the output and final-state gradients")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for hardware byte counters)")
@@ -280,6 +284,128 @@ def run_decode(args):
     print(json.dumps(res), flush=True)
 
 
+BWD_METRIC = "chunk GDN backward tokens/s on 1 MI355X (dq, dk, dv, dg, dbeta, dh0)"
+
+
+def bwd_path_bytes(w, x, eb):
+    """Algorithmic HBM bytes of one backward pass: every input read once (q, k
+    per key head; v, do, g, beta per value head; the initial state and the
+    final-state gradient) and every gradient written once (dq, dk per key head;
+    dv, dg, dbeta per value head; dh0)."""
+    T_tot = sum(x["lens"])
+    N, H, HV, K, V = x["N"], w.H, w.HV, w.K, w.V
+    state = N * HV * K * V * 4
+    s_in = state if x["initial_state"] is not None else 0
+    reads = 2 * T_tot * H * K * eb + 2 * T_tot * HV * V * eb + T_tot * HV * 8 + s_in + state
+    writes = 2 * T_tot * H * K * eb + T_tot * HV * V * eb + T_tot * HV * 8 + state
+    return reads + writes
+
+
+def bwd_cpu_baseline(x, groups=2):
+    """The fp64 backward oracle (numpy, token by token) on `groups` (sequence,
+    key head) groups of the same inputs, with all value heads of each group."""
+    import numpy as np
+    from oracle.backward import backward
+    w = x["workload"]
+    G = w.HV // w.H
+    N = x["N"]
+    picks = [(int(n), int(h)) for n, h in zip(np.linspace(0, N - 1, groups).round(),
+                                              np.linspace(0, w.H - 1, groups).round())]
+    toks = 0
+    t0 = time.perf_counter()
+    for n, jk in picks:
+        sl = slice(jk * G, (jk + 1) * G)
+        c = lambda t: t[n:n + 1].cpu()
+        s0 = None if x["initial_state"] is None else x["initial_state"][n:n + 1, sl].cpu()
+        backward(c(x["q"])[:, :, jk:jk + 1], c(x["k"])[:, :, jk:jk + 1], c(x["v"])[:, :, sl],
+                 c(x["g"])[:, :, sl], c(x["beta"])[:, :, sl], c(x["do"])[:, :, sl], dht=x["dht"][n:n + 1, sl].cpu(),
+                 scale=x["scale"], use_l2norm=x["use_l2norm"], initial_state=s0)
+        toks += x["lens"][n] * G
+    dt = time.perf_counter() - t0
+    return {"value": round(toks / w.HV / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(picks)} (sequence, key head) groups x {G} value heads of the same inputs "
+                      f"({toks} unit-tokens, fp64 token-level reverse mode in numpy, {dt:.2f} s wall)"}
+
+
+def run_backward(args):
+    import torch
+    import gated_deltanet_chunked_delta_amd as gdn
+    from workloads import WORKLOADS, make_grad_inputs, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dtype = torch.bfloat16 if args.dtype == "bf16" else torch.float32
+    eb = 2 if args.dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
+    x = make_inputs(w, seed=0, device=dev, io_dtype=dtype)
+    x["g"], x["beta"] = gdn.fused_gdn_gating(x["A_log"], x["a"], x["b"], x["dt_bias"])
+    x = make_grad_inputs(x, seed=100)
+    B, T = x["q"].shape[0], x["q"].shape[1]
+    N = x["N"]
+    shape = gdn.make_shape(B, T, w.H, w.HV, w.K, w.V, N, gdn.GDN_BF16 if eb == 2 else gdn.GDN_F32)
+    ws = torch.empty(gdn.gdn_chunk_bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+    dg = torch.empty((B, T, w.HV), dtype=torch.float32, device=dev)
+    dbeta = torch.empty_like(dg)
+    dh0 = torch.empty((N, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step():
+        st = gdn.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], x["dht"], x["scale"],
+                               x["use_l2norm"], x["initial_state"], x["cu_seqlens"], dq, dk, dv, dg, dbeta, dh0,
+                               shape, ws, stream=stream)
+        if st != 0:
+            raise gdn.GdnError(st)
+
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        step()
+        settle += 1
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gdn.gdn_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = gdn.gdn_profile_read()
+    gdn.gdn_profile_enable(False)
+
+    tokens = sum(x["lens"])
+    ms = (t1 - t0) * 1e3 / args.steps
+    pb = bwd_path_bytes(w, x, eb)
+    kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in prof.items() if n}
+    per_step = lambda k: kernels[k]["avg_us"] * kernels[k]["launches"] / args.steps
+    dom = max(kernels, key=per_step)
+    path_us = sum(per_step(k) for k in kernels)
+    # five kernels share the path: the path's algorithmic bytes over the sum of
+    # their times per step (the dominant kernel's share of that time is given)
+    ach = pb / (path_us * 1e-6) / 1e9
+    res = {
+        "metric": BWD_METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} backward: B={B} T={T} N={N} H={w.H} HV={w.HV} K={w.K} V={w.V} "
+                               f"l2norm={w.use_l2norm} initial_state={w.init} dht=yes",
+                   "tokens": tokens, "global_batch": N, "seq_len": T if N == B else None,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "scope": "path", "kernel": dom, "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_step": pb, "kernel_us_per_step": round(path_us, 2),
+                     "dominant_kernel_share": round(per_step(dom) / path_us, 3)},
+        "kernels": {k: {kk: round(vv, 2) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = bwd_cpu_baseline(x)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -291,6 +417,9 @@ def main():
     from workloads import DECODE_WORKLOADS
     if args.workload in DECODE_WORKLOADS:
         run_decode(args)
+        return
+    if args.path == "bwd":
+        run_backward(args)
         return
 
     import torch

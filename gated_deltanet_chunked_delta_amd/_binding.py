@@ -122,7 +122,7 @@ def gdn_profile_read():
     """Returns {kernel name: (total ms, launches)} accumulated since enabling
     (synchronises on the recorded events)."""
     lib = load_library()
-    n = 8
+    n = int(lib.gdn_profile_read(0, None, None, None))
     names = (ctypes.c_char_p * n)()
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_int64 * n)()

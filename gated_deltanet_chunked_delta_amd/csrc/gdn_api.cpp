@@ -259,6 +259,10 @@ int chunk_bwd(const void *q, const void *k, const void *v, const float *g, const
     const bool any_tokens = (int64_t)s.B * s.T > 0;
     if (any_tokens && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
         return GDN_ERR_NULL;
+    // the kernels read and write every tensor in 16-byte vectors
+    const uintptr_t any = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)dout | (uintptr_t)dq |
+                          (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)dht | (uintptr_t)initial_state | (uintptr_t)dh0;
+    if ((any & 15u) != 0) return GDN_ERR_ALIGN;
     const gdn::BwdPlan plan = bwd_plan_of(s);
     if (plan.nc_max < 0 || plan.bytes == 0) return GDN_ERR_SHAPE;
     if (!workspace || workspace_bytes < plan.bytes || ((uintptr_t)workspace & 255u) != 0) return GDN_ERR_WORKSPACE;

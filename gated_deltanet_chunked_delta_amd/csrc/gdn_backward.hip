@@ -60,7 +60,11 @@ constexpr int kPadT = kVT + 1;
 
 // LDS sizes in floats.
 template <int K>
-constexpr int prep_floats() { return 2 * kChunk * (K + 1) + 2 * kChunk * kPadC + 4 * kChunk; }
+constexpr int prep_q_floats() {   // the q rows, then A [64][65] and Tm [64][64] in the same space
+    return kChunk * (K + 1) > kChunk * kPadC + kChunk * kChunk ? kChunk * (K + 1) : kChunk * kPadC + kChunk * kChunk;
+}
+template <int K>
+constexpr int prep_floats() { return kChunk * (K + 1) + prep_q_floats<K>() + 4 * kChunk; }
 template <int K>
 constexpr int fwd_scan_floats() { return K * kPadT + kChunk * (K + 1) + kChunk * kPadC + 2 * kChunk * kPadT + 3 * kChunk; }
 template <int K>
@@ -158,18 +162,125 @@ __device__ __forceinline__ void seq_of(const BwdParams &p, int n, int &bos, int 
     }
 }
 
-// Loads L rows of a key-head row set ([T_tot, H, K], rows t0..t0+L-1 of head
-// jk) into dst[64][K+1] as fp32, zero rows past L, and normalises each row
-// (factor into f[r]) when use_l2norm.  Ends with a barrier.
-template <typename E, int K>
-__device__ void load_rows_normed(const E *src, int t0, int L, int H, int jk, int use_l2norm, float *dst, float *f) {
-    for (int e = threadIdx.x; e < kChunk * K; e += kThreads) {
-        const int r = e / K, c = e - r * K;
-        dst[r * (K + 1) + c] = r < L ? to_f(src[((int64_t)(t0 + r) * H + jk) * K + c]) : 0.f;
+// Eight consecutive elements (16-byte aligned in bf16, 32 in fp32) as fp32.
+__device__ __forceinline__ void ld8f(const bf16 *p, float (&o)[8]) {
+    const bf16x8 x = *(const bf16x8 *)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (float)x[e];
+}
+__device__ __forceinline__ void ld8f(const float *p, float (&o)[8]) {
+    const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o[e] = a[e];
+        o[4 + e] = b[e];
     }
-    __syncthreads();
-    // 4 lanes per row
-    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+}
+
+template <int K>
+__device__ __forceinline__ void store_state_tile(const float *tile, float *dst, int V, int c0) {
+    constexpr int N4 = K * kVT / 4 / kThreads;
+#pragma unroll
+    for (int u = 0; u < N4; ++u) {
+        const int i = threadIdx.x + kThreads * u, r = i >> 3, c = (i & 7) * 4;
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = tile[r * kPadT + c + e];
+        *(f32x4 *)(dst + (int64_t)r * V + c0 + c) = x;
+    }
+}
+
+// Register-staged copies: load() issues the global loads of one copy,
+// commit() writes them to LDS.  A chunk step issues the loads of the next
+// step before its own arithmetic, so their latency hides behind it.
+//
+// L rows (zero past L) of a key-head row set [T_tot, H, K] at head jk, into
+// dst[64][K+1] as fp32.
+template <typename E, int K>
+struct RowsReg {
+    static constexpr int PER_ROW = K / 8, VPT = kChunk * PER_ROW / kThreads;
+    float v[VPT][8];
+    __device__ __forceinline__ void load(const E *src, int t0, int L, int H, int jk) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int i = threadIdx.x + kThreads * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
+            if (r < L) ld8f(src + ((int64_t)(t0 + r) * H + jk) * K + c, v[u]);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+        }
+    }
+    __device__ __forceinline__ void commit(float *dst) const {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int i = threadIdx.x + kThreads * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[r * (K + 1) + c + e] = v[u][e];
+        }
+    }
+};
+// A 64 x 64 fp32 matrix (contiguous) into dst[64][65].
+struct Mat64Reg {
+    f32x4 v[4];
+    __device__ __forceinline__ void load(const float *src) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const f32x4 *)(src + 4 * (threadIdx.x + kThreads * u));
+    }
+    __device__ __forceinline__ void commit(float *dst) const {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = threadIdx.x + kThreads * u, r = i >> 4, c = (i & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[r * kPadC + c + e] = v[u][e];
+        }
+    }
+};
+// Rows t0..t0+L-1 (zero past L), 32 columns from c0, of a [T_tot, HV, V]
+// tensor at value head j, into dst[64][33] as fp32.
+template <typename E>
+struct TileReg {
+    float v[8];
+    __device__ __forceinline__ void load(const E *src, int t0, int L, int HV, int j, int V, int c0) {
+        const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 8;
+        if (r < L) ld8f(src + ((int64_t)(t0 + r) * HV + j) * V + c0 + c, v);
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    __device__ __forceinline__ void commit(float *dst) const {
+        const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[r * kPadT + c + e] = v[e];
+    }
+};
+// K rows x 32 columns from c0 of a K x V fp32 state (row stride V), into dst[K][33].
+template <int K>
+struct StateTileReg {
+    static constexpr int N4 = K * kVT / 4 / kThreads;
+    f32x4 v[N4];
+    __device__ __forceinline__ void load(const float *src, int V, int c0) {
+#pragma unroll
+        for (int u = 0; u < N4; ++u) {
+            const int i = threadIdx.x + kThreads * u, r = i >> 3, c = (i & 7) * 4;
+            v[u] = *(const f32x4 *)(src + (int64_t)r * V + c0 + c);
+        }
+    }
+    __device__ __forceinline__ void commit(float *dst) const {
+#pragma unroll
+        for (int u = 0; u < N4; ++u) {
+            const int i = threadIdx.x + kThreads * u, r = i >> 3, c = (i & 7) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[r * kPadT + c + e] = v[u][e];
+        }
+    }
+};
+
+// L2-normalises the rows of dst[64][K+1] in place when use_l2norm (factor
+// 1/sqrt(|x|^2 + 1e-6) into f[r], else 1).  Call after a barrier that
+// follows the writes of dst; ends with a barrier.
+template <int K>
+__device__ __forceinline__ void norm_rows(float *dst, float *f, int use_l2norm) {
+    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;   // 4 lanes per row
     float s = 0.f;
     for (int c = part; c < K; c += 4) {
         const float x = dst[r * (K + 1) + c];
@@ -220,9 +331,9 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     __shared__ float sm[prep_floats<K>()];
     float *kh = sm;                          // [64][K+1]
     float *qh = kh + kChunk * (K + 1);       // [64][K+1]
-    float *A = qh + kChunk * (K + 1);        // [64][65]
-    float *Tm = A + kChunk * kPadC;          // [64][65]
-    float *gam = Tm + kChunk * kPadC;        // [64]
+    float *A = qh;                           // [64][65] after the products (qh is dead then)
+    float *Tm = A + kChunk * kPadC;          // [64][64]
+    float *gam = qh + prep_q_floats<K>();   // [64]
     float *bet = gam + kChunk;               // [64]
     float *fk = bet + kChunk;                // [64]
     float *fq = fk + kChunk;                 // [64]
@@ -240,8 +351,16 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
             bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
         }
     }
-    load_rows_normed<E, K>((const E *)p.k, t0, L, p.H, jk, p.use_l2norm, kh, fk);
-    load_rows_normed<E, K>((const E *)p.q, t0, L, p.H, jk, p.use_l2norm, qh, fq);
+    {
+        RowsReg<E, K> rk, rq;
+        rk.load((const E *)p.k, t0, L, p.H, jk);
+        rq.load((const E *)p.q, t0, L, p.H, jk);
+        rk.commit(kh);
+        rq.commit(qh);
+    }
+    __syncthreads();
+    norm_rows<K>(kh, fk, p.use_l2norm);
+    norm_rows<K>(qh, fq, p.use_l2norm);
     if (threadIdx.x < L) p.gam[(int64_t)(t0 + threadIdx.x) * HV + j] = gam[threadIdx.x];
 
     const int tx = tx_of(), ty = ty_of();
@@ -254,6 +373,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
                 [&](int c, int m) { return kh[c * (K + 1) + m]; });
     float *ag_out = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
     float *pm_out = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+    __syncthreads();   // A overwrites qh
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = ty + 16 * i;
@@ -274,16 +394,17 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     const int col = threadIdx.x >> 2, part = threadIdx.x & 3;
     for (int i = 0; i < kChunk; ++i) {
         float s = 0.f;
-        for (int m = col + part; m < i; m += 4) s = fmaf(A[i * kPadC + m], Tm[m * kPadC + col], s);
+        for (int m = col + part; m < i; m += 4) s = fmaf(A[i * kPadC + m], Tm[m * kChunk + col], s);
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
-        if (part == 0) Tm[i * kPadC + col] = col == i ? 1.f : col < i ? -s : 0.f;
+        if (part == 0) Tm[i * kChunk + col] = col == i ? 1.f : col < i ? -s : 0.f;
         __syncthreads();
     }
     float *tm_out = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
-    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
-        const int r = e >> 6, c = e & 63;
-        tm_out[e] = Tm[r * kPadC + c];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = 4 * (threadIdx.x + kThreads * u);
+        *(f32x4 *)(tm_out + i) = f32x4{Tm[i], Tm[i + 1], Tm[i + 2], Tm[i + 3]};
     }
 }
 
@@ -310,30 +431,43 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
     const int nc = (len + kChunk - 1) / kChunk;
     const int tx = tx_of(), ty = ty_of();
 
-    for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
-        const int r = e / kVT, c = e - r * kVT;
-        h[r * kPadT + c] = p.initial_state ? p.initial_state[(((int64_t)n * HV + j) * K + r) * V + c0 + c] : 0.f;
+    if (p.initial_state) {
+        StateTileReg<K> r0;
+        r0.load(p.initial_state + ((int64_t)n * HV + j) * K * V, V, c0);
+        r0.commit(h);
+    } else {
+        for (int e = threadIdx.x; e < K * kVT; e += kThreads) h[(e / kVT) * kPadT + e % kVT] = 0.f;
     }
     __syncthreads();
-    for (int ci = 0; ci < nc; ++ci) {
+    RowsReg<E, K> rk;
+    Mat64Reg rt;
+    TileReg<E> rv;
+    float rg = 0.f, rb = 0.f;
+    auto fetch = [&](int ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
-        float *hs = p.hs + ((int64_t)cid * HV + j) * K * V;
-        for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
-            const int r = e / kVT, c = e - r * kVT;
-            hs[(int64_t)r * V + c0 + c] = h[r * kPadT + c];
-        }
-        const float *tm = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) Tm[(e >> 6) * kPadC + (e & 63)] = tm[e];
-        for (int e = threadIdx.x; e < kChunk * kVT; e += kThreads) {
-            const int r = e / kVT, c = e - r * kVT;
-            vv[r * kPadT + c] = r < L ? to_f(((const E *)p.v)[((int64_t)(t0 + r) * HV + j) * V + c0 + c]) : 0.f;
-        }
+        rk.load((const E *)p.k, t0, L, p.H, jk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rv.load((const E *)p.v, t0, L, HV, j, V, c0);
         if (threadIdx.x < kChunk) {
             const int r = threadIdx.x;
-            gam[r] = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
-            bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+            rg = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
+            rb = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
         }
-        load_rows_normed<E, K>((const E *)p.k, t0, L, p.H, jk, p.use_l2norm, kh, fk);
+    };
+    if (nc > 0) fetch(0);
+    for (int ci = 0; ci < nc; ++ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        store_state_tile<K>(h, p.hs + ((int64_t)cid * HV + j) * K * V, V, c0);
+        rk.commit(kh);
+        rt.commit(Tm);
+        rv.commit(vv);
+        if (threadIdx.x < kChunk) {
+            gam[threadIdx.x] = rg;
+            bet[threadIdx.x] = rb;
+        }
+        __syncthreads();
+        norm_rows<K>(kh, fk, p.use_l2norm);
+        if (ci + 1 < nc) fetch(ci + 1);
 
         // B = diag(beta) (V - diag(D) Kh h)
         {
@@ -421,35 +555,48 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
     const int tx = tx_of(), ty = ty_of();
     const float scale = p.scale;
 
-    for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
-        const int r = e / kVT, c = e - r * kVT;
-        dh[r * kPadT + c] = p.dht ? p.dht[(((int64_t)n * HV + j) * K + r) * V + c0 + c] : 0.f;
+    if (p.dht) {
+        StateTileReg<K> r0;
+        r0.load(p.dht + ((int64_t)n * HV + j) * K * V, V, c0);
+        r0.commit(dh);
+    } else {
+        for (int e = threadIdx.x; e < K * kVT; e += kThreads) dh[(e / kVT) * kPadT + e % kVT] = 0.f;
     }
     __syncthreads();
-    for (int ci = nc - 1; ci >= 0; --ci) {
+    RowsReg<E, K> rk, rq;
+    Mat64Reg rt, rp;
+    TileReg<E> ro;
+    float rg = 0.f, rb = 0.f;
+    auto fetch = [&](int ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
-        float *dhs = p.dhs + ((int64_t)cid * HV + j) * K * V;
-        for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
-            const int r = e / kVT, c = e - r * kVT;
-            dhs[(int64_t)r * V + c0 + c] = dh[r * kPadT + c];
-        }
-        const float *tm = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
-        const float *pm = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
-            Tm[(e >> 6) * kPadC + (e & 63)] = tm[e];
-            Pm[(e >> 6) * kPadC + (e & 63)] = pm[e];
-        }
-        for (int e = threadIdx.x; e < kChunk * kVT; e += kThreads) {
-            const int r = e / kVT, c = e - r * kVT;
-            dO[r * kPadT + c] = r < L ? to_f(((const E *)p.dout)[((int64_t)(t0 + r) * HV + j) * V + c0 + c]) : 0.f;
-        }
+        rk.load((const E *)p.k, t0, L, p.H, jk);
+        rq.load((const E *)p.q, t0, L, p.H, jk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rp.load(p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        ro.load((const E *)p.dout, t0, L, HV, j, V, c0);
         if (threadIdx.x < kChunk) {
             const int r = threadIdx.x;
-            gam[r] = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
-            bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+            rg = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
+            rb = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
         }
-        load_rows_normed<E, K>((const E *)p.k, t0, L, p.H, jk, p.use_l2norm, kh, fk);
-        load_rows_normed<E, K>((const E *)p.q, t0, L, p.H, jk, p.use_l2norm, qh, fq);
+    };
+    if (nc > 0) fetch(nc - 1);
+    for (int ci = nc - 1; ci >= 0; --ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        store_state_tile<K>(dh, p.dhs + ((int64_t)cid * HV + j) * K * V, V, c0);
+        rk.commit(kh);
+        rq.commit(qh);
+        rt.commit(Tm);
+        rp.commit(Pm);
+        ro.commit(dO);
+        if (threadIdx.x < kChunk) {
+            gam[threadIdx.x] = rg;
+            bet[threadIdx.x] = rb;
+        }
+        __syncthreads();
+        norm_rows<K>(kh, fk, p.use_l2norm);
+        norm_rows<K>(qh, fq, p.use_l2norm);
+        if (ci > 0) fetch(ci - 1);
         const float gl = gam[L - 1];
 
         // dVn = scale Pm^T dO + diag(exp(gamma_L - gamma)) Kh dh'
@@ -507,11 +654,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
         }
         __syncthreads();
     }
-    if (p.dh0)
-        for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
-            const int r = e / kVT, c = e - r * kVT;
-            p.dh0[(((int64_t)n * HV + j) * K + r) * V + c0 + c] = dh[r * kPadT + c];
-        }
+    if (p.dh0) store_state_tile<K>(dh, p.dh0 + ((int64_t)n * HV + j) * K * V, V, c0);
 }
 
 // ---------------------------------------------------------------------------
@@ -554,8 +697,30 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
         gam[r] = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
         bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
     }
-    load_rows_normed<E, K>((const E *)p.k, t0, L, p.H, jk, p.use_l2norm, kh, fk);
-    load_rows_normed<E, K>((const E *)p.q, t0, L, p.H, jk, p.use_l2norm, qh, fq);
+    const float *hs = p.hs + ((int64_t)cid * HV + j) * K * V;
+    const float *dhs = p.dhs + ((int64_t)cid * HV + j) * K * V;
+    StateTileReg<K> th, tdh;
+    TileReg<float> tvn, tdb;
+    TileReg<E> tdo, tv;
+    auto fetch = [&](int c0) {
+        th.load(hs, V, c0);
+        tdh.load(dhs, V, c0);
+        tvn.load(p.vn, t0, L, HV, j, V, c0);
+        tdb.load(p.db, t0, L, HV, j, V, c0);
+        tdo.load((const E *)p.dout, t0, L, HV, j, V, c0);
+        tv.load((const E *)p.v, t0, L, HV, j, V, c0);
+    };
+    {
+        RowsReg<E, K> rk, rq;
+        rk.load((const E *)p.k, t0, L, p.H, jk);
+        rq.load((const E *)p.q, t0, L, p.H, jk);
+        fetch(0);
+        rk.commit(kh);
+        rq.commit(qh);
+    }
+    __syncthreads();
+    norm_rows<K>(kh, fk, p.use_l2norm);
+    norm_rows<K>(qh, fq, p.use_l2norm);
 
     float aP[4][4], aA[4][4], dQ[4][KR], aE[4][KR], aF[4][KR];
     zero(aP);
@@ -565,26 +730,25 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
     zero(aF);
     float sdh = 0.f;      // this thread's part of <dh', h>
     float sbv = 0.f;      // row (threadIdx.x >> 2): sum_v dB v
-    const float *hs = p.hs + ((int64_t)cid * HV + j) * K * V;
-    const float *dhs = p.dhs + ((int64_t)cid * HV + j) * K * V;
     for (int c0 = 0; c0 < V; c0 += kVT) {
-        for (int e = threadIdx.x; e < K * kVT; e += kThreads) {
-            const int r = e / kVT, c = e - r * kVT;
-            const float hv = hs[(int64_t)r * V + c0 + c], dv = dhs[(int64_t)r * V + c0 + c];
-            hT[r * kPadT + c] = hv;
-            dhT[r * kPadT + c] = dv;
-            sdh = fmaf(hv, dv, sdh);
-        }
-        for (int e = threadIdx.x; e < kChunk * kVT; e += kThreads) {
-            const int r = e / kVT, c = e - r * kVT;
-            const int64_t at = ((int64_t)(t0 + r) * HV + j) * V + c0 + c;
-            const bool in = r < L;
-            vnT[r * kPadT + c] = in ? p.vn[at] : 0.f;
-            dbT[r * kPadT + c] = in ? p.db[at] : 0.f;
-            doT[r * kPadT + c] = in ? to_f(((const E *)p.dout)[at]) : 0.f;
-            vvT[r * kPadT + c] = in ? to_f(((const E *)p.v)[at]) : 0.f;
-        }
+        th.commit(hT);
+        tdh.commit(dhT);
+        tvn.commit(vnT);
+        tdb.commit(dbT);
+        tdo.commit(doT);
+        tv.commit(vvT);
         __syncthreads();
+        if (c0 + kVT < V) fetch(c0 + kVT);
+        // this thread's part of <dh', h>: the elements it wrote
+        {
+            constexpr int N4 = K * kVT / 4 / kThreads;
+#pragma unroll
+            for (int u = 0; u < N4; ++u) {
+                const int i = threadIdx.x + kThreads * u, r = i >> 3, c = (i & 7) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sdh = fmaf(hT[r * kPadT + c + e], dhT[r * kPadT + c + e], sdh);
+            }
+        }
         {
             const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
             float s = 0.f;

@@ -288,7 +288,7 @@ int gdn_recurrent_update_pool(const void *q, const void *k, const void *v,
  * shapes).  The backward pass keeps, per 64-token chunk and value head, the
  * chunk-start state and its gradient (2 K V floats) and three 64 x 64 fp32
  * matrices, and per token and value head 2 V + 2 K + 1 floats:
- * about 1.6 GiB at B = 4, T = 4096, HV = 32, K = V = 128.  Chunk slots are
+ * about 2.4 GiB at B = 4, T = 4096, HV = 32, K = V = 128.  Chunk slots are
  * counted for packed sequences (ceil(T/64) + N) when B == 1, else B ceil(T/64). */
 size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape *shape);
 
@@ -315,7 +315,9 @@ size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape *shape);
  *                 contents on entry are ignored
  *   stream        hipStream_t to enqueue on (NULL = the default stream)
  *
- * Outputs must not overlap each other, the inputs or the workspace.  All
+ * q, k, v, dout, dq, dk, dv and the three states must be 16-byte aligned
+ * (GDN_ERR_ALIGN otherwise).  Outputs must not overlap each other, the inputs
+ * or the workspace.  All
  * arithmetic is fp32 whatever dtype is (bf16 inputs are widened, bf16 outputs
  * rounded to nearest even at the end).  Returns GDN_OK or a negative
  * gdn_status; checks run on the host before anything is enqueued. */

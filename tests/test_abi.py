@@ -248,3 +248,64 @@ def test_decode_wrapper_rejects_cpu_tensors_and_bad_shapes():
         gdn.fused_recurrent_gated_delta_rule_update(q, q, v, g, g, torch.zeros(5, 2, 64, 64), idx)
     with pytest.raises(ValueError):   # int64 indices
         gdn.fused_recurrent_gated_delta_rule_update(q, q, v, g, g, pool, idx.long())
+
+
+# ---------------------------------------------------------------------------
+# backward entry point
+# ---------------------------------------------------------------------------
+def _bcall(shape, ws=FAKE, ws_bytes=1 << 40, cu=None, ptrs=FAKE, dout=FAKE):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    return lib.gdn_chunk_bwd(P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(dout) if dout else None, None,
+                             1.0, 1, None, None if cu is None else P(cu), P(ptrs), P(ptrs), P(ptrs), P(ptrs),
+                             P(ptrs), None, None if shape is None else ctypes.byref(shape), P(ws) if ws else None,
+                             ws_bytes, None)
+
+
+def test_backward_workspace_size():
+    # equal-length: per chunk and value head 2 K V + 3 * 64 * 64 floats, per
+    # token and value head 2 V + 2 K + 1 floats, N + 1 chunk offsets; each
+    # region rounded up to 256 bytes
+    B, T, H, HV, K, V = 4, 4096, 16, 32, 128, 128
+    got = gdn.gdn_chunk_bwd_workspace_bytes(gdn.make_shape(B, T, H, HV, K, V, B, gdn.GDN_BF16))
+    chunks = B * T // 64
+    want = 256 + 4 * (chunks * HV * (2 * K * V + 3 * 64 * 64) + B * T * HV * (2 * V + 2 * K + 1))
+    assert want <= got <= want + 11 * 256
+    # B == 1: slots for packed sequences, ceil(T/64) + N chunks
+    g1 = gdn.gdn_chunk_bwd_workspace_bytes(gdn.make_shape(1, 1000, 2, 4, 64, 64, 7, gdn.GDN_F32))
+    slots = (1000 + 63) // 64 + 7
+    want1 = 4 * (slots * 4 * (2 * 64 * 64 + 3 * 64 * 64) + 1000 * 4 * (2 * 64 + 2 * 64 + 1))
+    assert want1 <= g1 <= want1 + 12 * 256
+    assert gdn.gdn_chunk_bwd_workspace_bytes(gdn.make_shape(1, 64, 2, 4, 96, 64, 1, 0)) == 0   # K unsupported
+
+
+@pytest.mark.parametrize("shape,ws,ws_bytes,cu,want", [
+    (None, FAKE, 1 << 40, None, -1),
+    (gdn.make_shape(2, 64, 2, 4, 128, 128, 2, 0), None, 0, None, -5),          # no workspace
+    (gdn.make_shape(2, 64, 2, 4, 128, 128, 2, 0), FAKE, 1024, None, -5),       # too small
+    (gdn.make_shape(2, 64, 2, 4, 128, 128, 2, 0), FAKE + 16, 1 << 40, None, -5),   # misaligned
+    (gdn.make_shape(2, 64, 2, 4, 128, 128, 3, 0), FAKE, 1 << 40, None, -2),    # N != B
+    (gdn.make_shape(2, 64, 2, 4, 128, 128, 2, 0), FAKE, 1 << 40, FAKE, -2),    # B != 1 with cu_seqlens
+    (gdn.make_shape(1, 64, 2, 3, 128, 128, 1, 0), FAKE, 1 << 40, None, -4),    # HV % H
+    (gdn.make_shape(1, 64, 2, 4, 128, 128, 1, 5), FAKE, 1 << 40, None, -3),    # dtype
+])
+def test_backward_argument_errors(shape, ws, ws_bytes, cu, want):
+    assert _bcall(shape, ws=ws, ws_bytes=ws_bytes, cu=cu) == want
+
+
+def test_backward_null_and_misaligned_tensor_errors():
+    s = gdn.make_shape(2, 64, 2, 4, 128, 128, 2, 0)
+    assert _bcall(s, dout=0) == -1
+    assert _bcall(s, ptrs=0) == -1
+    assert _bcall(s, dout=FAKE + 8) == -7
+
+
+def test_backward_wrapper_rejects_cpu_tensors_and_bad_shapes():
+    import torch
+    q = torch.zeros(1, 8, 2, 64)
+    v = torch.zeros(1, 8, 4, 64)
+    g = torch.zeros(1, 8, 4)
+    with pytest.raises(ValueError):
+        gdn.chunk_gated_delta_rule_bwd(q, q, v, g, g, v)          # CPU tensors: no CPU path
+    with pytest.raises(ValueError):
+        gdn.chunk_gated_delta_rule_bwd(q, q, v, g, g, v[:, :4])   # do shape
