@@ -66,10 +66,10 @@ constexpr int prep_q_floats() {   // the q rows, then A [64][65] and Tm [64][64]
 template <int K>
 constexpr int prep_floats() { return kChunk * (K + 1) + prep_q_floats<K>() + 4 * kChunk; }
 template <int K>
-constexpr int fwd_scan_floats() { return K * kPadT + kChunk * (K + 1) + kChunk * kPadC + 2 * kChunk * kPadT + 3 * kChunk; }
+constexpr int fwd_scan_floats() { return K * kPadT + kChunk * (K + 1) + kChunk * kPadC + 2 * kChunk * kPadT + 5 * kChunk; }
 template <int K>
 constexpr int dh_scan_floats() {
-    return K * kPadT + 2 * kChunk * (K + 1) + 2 * kChunk * kPadC + 3 * kChunk * kPadT + 4 * kChunk;
+    return K * kPadT + 2 * kChunk * (K + 1) + 2 * kChunk * kPadC + 3 * kChunk * kPadT + 7 * kChunk;
 }
 // grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the three
 // 64 x 65 matrices of the second phase reuse their space.
@@ -79,36 +79,55 @@ static_assert(grads_tile_floats<64>() >= 3 * kChunk * kPadC, "phase-2 matrices m
 template <int K>
 constexpr int grads_floats() { return 2 * kChunk * (K + 1) + grads_tile_floats<K>() + 6 * kChunk + 20; }
 
-__device__ __forceinline__ int tx_of() { return threadIdx.x & 15; }
-__device__ __forceinline__ int ty_of() { return threadIdx.x >> 4; }
-
-// acc[i][j] += sum_{m < KD} fa(ty + 16 i, m) * fb(tx + 16 j, m)
-template <int MR, int NR, int KD, typename FA, typename FB>
-__device__ __forceinline__ void mm(float (&acc)[MR][NR], FA fa, FB fb) {
-    const int tx = tx_of(), ty = ty_of();
-#pragma unroll 4
-    for (int m = 0; m < KD; ++m) {
-        float a[MR], b[NR];
+// Products on the matrix cores: 16 x 16 fp32 tiles by v_mfma_f32_16x16x4f32
+// (fp32 operands, fp32 accumulation, so the pass keeps fp32 accuracy).
+// Inside a wave, lane l holds elements (4 (l >> 4) + e, l & 15), e < 4, of
+// each tile.  A k-step feeds four contraction indices, one per group of 16
+// lanes: group q takes index q KD/4 + s at step s, the same index for both
+// operands, so the assignment only fixes the order of the sum.
+//   acc[t] += sum_{m < KD} fa(ra(t) + (l & 15), m) * fb(cb(t) + (l & 15), m)
+// Operand reads that coincide between tiles (same ra or cb) are shared.  The
+// operands of a group of k-steps are read from LDS into registers before the
+// group's products issue, so one LDS latency is paid per group, not per step.
+template <int NT, int KD, typename RA, typename CB, typename FA, typename FB>
+__device__ __forceinline__ void wmm(f32x4 (&acc)[NT], RA ra, CB cb, FA fa, FB fb) {
+    constexpr int S = KD / 4;
+    constexpr int G0 = NT >= 4 ? 4 : 8;
+    constexpr int G = S <= G0 ? S : (S % G0 == 0 ? G0 : (S % 4 == 0 ? 4 : 1));
+    static_assert(S % G == 0, "k-steps must split into whole groups");
+    const int i = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
 #pragma unroll
-        for (int i = 0; i < MR; ++i) a[i] = fa(ty + 16 * i, m);
+    for (int g = 0; g < S; g += G) {
+        float av[G][NT], bv[G][NT];
 #pragma unroll
-        for (int j = 0; j < NR; ++j) b[j] = fb(tx + 16 * j, m);
+        for (int s = 0; s < G; ++s) {
+            const int m = q * S + g + s;
 #pragma unroll
-        for (int i = 0; i < MR; ++i)
+            for (int t = 0; t < NT; ++t) {
+                av[s][t] = fa(ra(t) + i, m);
+                bv[s][t] = fb(cb(t) + i, m);
+            }
+        }
 #pragma unroll
-            for (int j = 0; j < NR; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int s = 0; s < G; ++s)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s][t], bv[s][t], acc[t], 0, 0, 0);
     }
 }
 
-template <int MR, int NR>
-__device__ __forceinline__ void zero(float (&acc)[MR][NR]) {
+template <int NT>
+__device__ __forceinline__ void zero(f32x4 (&acc)[NT]) {
 #pragma unroll
-    for (int i = 0; i < MR; ++i)
-#pragma unroll
-        for (int j = 0; j < NR; ++j) acc[i][j] = 0.f;
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Sum over the 16 lanes that share ty (lanes tx = 0..15 of one row group).
+// Row and column of element e of this lane in a tile at (r0, c0).
+__device__ __forceinline__ int lrow(int r0, int e) { return r0 + 4 * ((threadIdx.x >> 4) & 3) + e; }
+__device__ __forceinline__ int lcol(int c0) { return c0 + (threadIdx.x & 15); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Sum over the 16 lanes that hold the same tile rows (lanes l & 15 = 0..15).
 __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 1);
     x += __shfl_xor(x, 2);
@@ -162,21 +181,6 @@ __device__ __forceinline__ void seq_of(const BwdParams &p, int n, int &bos, int 
     }
 }
 
-// Eight consecutive elements (16-byte aligned in bf16, 32 in fp32) as fp32.
-__device__ __forceinline__ void ld8f(const bf16 *p, float (&o)[8]) {
-    const bf16x8 x = *(const bf16x8 *)p;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (float)x[e];
-}
-__device__ __forceinline__ void ld8f(const float *p, float (&o)[8]) {
-    const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        o[e] = a[e];
-        o[4 + e] = b[e];
-    }
-}
-
 template <int K>
 __device__ __forceinline__ void store_state_tile(const float *tile, float *dst, int V, int c0) {
     constexpr int N4 = K * kVT / 4 / kThreads;
@@ -199,15 +203,15 @@ __device__ __forceinline__ void store_state_tile(const float *tile, float *dst, 
 template <typename E, int K>
 struct RowsReg {
     static constexpr int PER_ROW = K / 8, VPT = kChunk * PER_ROW / kThreads;
-    float v[VPT][8];
+    typename VT<E>::v8 v[VPT];   // kept in the input type until the LDS write
     __device__ __forceinline__ void load(const E *src, int t0, int L, int H, int jk) {
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
             const int i = threadIdx.x + kThreads * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
-            if (r < L) ld8f(src + ((int64_t)(t0 + r) * H + jk) * K + c, v[u]);
+            if (r < L) v[u] = ld8<E>(src + ((int64_t)(t0 + r) * H + jk) * K + c);
             else
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+                for (int e = 0; e < 8; ++e) v[u][e] = to_e<E>(0.f);
         }
     }
     __device__ __forceinline__ void commit(float *dst) const {
@@ -215,7 +219,7 @@ struct RowsReg {
         for (int u = 0; u < VPT; ++u) {
             const int i = threadIdx.x + kThreads * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dst[r * (K + 1) + c + e] = v[u][e];
+            for (int e = 0; e < 8; ++e) dst[r * (K + 1) + c + e] = to_f(v[u][e]);
         }
     }
 };
@@ -239,18 +243,18 @@ struct Mat64Reg {
 // tensor at value head j, into dst[64][33] as fp32.
 template <typename E>
 struct TileReg {
-    float v[8];
+    typename VT<E>::v8 v;   // kept in the input type until the LDS write
     __device__ __forceinline__ void load(const E *src, int t0, int L, int HV, int j, int V, int c0) {
         const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 8;
-        if (r < L) ld8f(src + ((int64_t)(t0 + r) * HV + j) * V + c0 + c, v);
+        if (r < L) v = ld8<E>(src + ((int64_t)(t0 + r) * HV + j) * V + c0 + c);
         else
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+            for (int e = 0; e < 8; ++e) v[e] = to_e<E>(0.f);
     }
     __device__ __forceinline__ void commit(float *dst) const {
         const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[r * kPadT + c + e] = v[e];
+        for (int e = 0; e < 8; ++e) dst[r * kPadT + c + e] = to_f(v[e]);
     }
 };
 // K rows x 32 columns from c0 of a K x V fp32 state (row stride V), into dst[K][33].
@@ -292,7 +296,35 @@ __device__ __forceinline__ void norm_rows(float *dst, float *f, int use_l2norm) 
     if (use_l2norm)
         for (int c = part; c < K; c += 4) dst[r * (K + 1) + c] *= fr;
     if (part == 0) f[r] = fr;
-    __syncthreads();
+    lds_barrier();
+}
+
+// One block row I of Tm = (I + A)^-1 (16-row blocks, diagonal blocks already
+// in Tm, blocks above the diagonal zero): wave J < I computes
+// T_IJ = -X_I sum_{K<I} A_IK T_KJ, staging the sum in its scratch ysc [16][17].
+// Every thread of the workgroup calls it (it holds two barriers).
+template <int I>
+__device__ __forceinline__ void tm_block_row(const float *A, float *Tm, float *ysc, int w) {
+    if (w < I) {
+        f32x4 y[1];
+        zero(y);
+        wmm<1, 16 * I>(y, [&](int) { return 16 * I; }, [&](int) { return 16 * w; },
+                       [&](int r, int m) { return A[r * kPadC + m]; },
+                       [&](int c, int m) { return Tm[m * kChunk + c]; });
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ysc[lrow(0, e) * 17 + lcol(0)] = y[0][e];
+    }
+    lds_barrier();
+    if (w < I) {
+        f32x4 z[1];
+        zero(z);
+        wmm<1, 16>(z, [&](int) { return 16 * I; }, [&](int) { return 0; },
+                   [&](int r, int m) { return Tm[r * kChunk + 16 * I + m]; },
+                   [&](int c, int m) { return ysc[m * 17 + c]; });
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Tm[lrow(16 * I, e) * kChunk + lcol(16 * w)] = -z[0][e];
+    }
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -363,43 +395,60 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     norm_rows<K>(qh, fq, p.use_l2norm);
     if (threadIdx.x < L) p.gam[(int64_t)(t0 + threadIdx.x) * HV + j] = gam[threadIdx.x];
 
-    const int tx = tx_of(), ty = ty_of();
-    float kk[4][4], qk[4][4];
+    // K K^T and Q K^T: wave w computes rows 16w..16w+15, all four column tiles.
+    const int w = wave_id();
+    auto ra = [&](int) { return 16 * w; };
+    auto cb = [&](int t) { return 16 * t; };
+    f32x4 kk[4], qk[4];
     zero(kk);
     zero(qk);
-    mm<4, 4, K>(kk, [&](int r, int m) { return kh[r * (K + 1) + m]; },
-                [&](int c, int m) { return kh[c * (K + 1) + m]; });
-    mm<4, 4, K>(qk, [&](int r, int m) { return qh[r * (K + 1) + m]; },
-                [&](int c, int m) { return kh[c * (K + 1) + m]; });
+    wmm<4, K>(kk, ra, cb, [&](int r, int m) { return kh[r * (K + 1) + m]; },
+              [&](int c, int m) { return kh[c * (K + 1) + m]; });
+    wmm<4, K>(qk, ra, cb, [&](int r, int m) { return qh[r * (K + 1) + m]; },
+              [&](int c, int m) { return kh[c * (K + 1) + m]; });
     float *ag_out = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
     float *pm_out = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
-    __syncthreads();   // A overwrites qh
+    lds_barrier();   // A overwrites qh
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = ty + 16 * i;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int c = tx + 16 * jj;
-            const float e = (c <= r && r < L) ? __expf(gam[r] - gam[c]) : 0.f;
-            const float ag = c < r ? e * kk[i][jj] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+            const int r = lrow(16 * w, e), c = lcol(16 * t);
+            const float d = (c <= r && r < L) ? __expf(gam[r] - gam[c]) : 0.f;
+            const float ag = c < r ? d * kk[t][e] : 0.f;
             A[r * kPadC + c] = bet[r] * ag;
+            Tm[r * kChunk + c] = 0.f;
             ag_out[r * kChunk + c] = ag;
-            pm_out[r * kChunk + c] = e * qk[i][jj];
+            pm_out[r * kChunk + c] = d * qk[t][e];
         }
-    }
-    __syncthreads();
+    lds_barrier();
 
-    // Tm = (I + A)^-1 by forward substitution over rows: Tm_i = e_i - sum_{m<i} A_im Tm_m.
-    // 4 lanes per column, each summing every 4th m.
-    const int col = threadIdx.x >> 2, part = threadIdx.x & 3;
-    for (int i = 0; i < kChunk; ++i) {
-        float s = 0.f;
-        for (int m = col + part; m < i; m += 4) s = fmaf(A[i * kPadC + m], Tm[m * kChunk + col], s);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        if (part == 0) Tm[i * kChunk + col] = col == i ? 1.f : col < i ? -s : 0.f;
-        __syncthreads();
+    // Tm = (I + A)^-1, blocked by 16.  Wave w inverts the diagonal block
+    // X_w = (I + A_ww)^-1 by forward substitution, X_im = -sum_{j<=m<i} A_im X_mj:
+    // lane (column l & 15, part l >> 4) keeps rows part, part + 4, ... of its column.
+    {
+        const int col = threadIdx.x & 15, part = (threadIdx.x >> 4) & 3, b0 = 16 * w;
+        float xr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (part + 4 * u < i) s = fmaf(A[(b0 + i) * kPadC + b0 + part + 4 * u], xr[u], s);
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            const float x = i == col ? 1.f : (col < i ? -s : 0.f);
+            if (part == (i & 3)) xr[i >> 2] = x;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Tm[(b0 + part + 4 * u) * kChunk + b0 + col] = xr[u];
     }
+    lds_barrier();
+    // Off-diagonal blocks, one block row at a time.
+    float *ysc = kh + w * 16 * 17;   // kh is dead after the products
+    tm_block_row<1>(A, Tm, ysc, w);
+    tm_block_row<2>(A, Tm, ysc, w);
+    tm_block_row<3>(A, Tm, ysc, w);
     float *tm_out = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -422,6 +471,8 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
     float *gam = Bm + kChunk * kPadT;        // [64]
     float *bet = gam + kChunk;               // [64]
     float *fk = bet + kChunk;                // [64]
+    float *sD = fk + kChunk;                 // [64] exp(gamma)
+    float *sF = sD + kChunk;                 // [64] exp(gamma_L - gamma), 0 past L
 
     const int HV = p.HV, V = p.V;
     const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
@@ -429,7 +480,6 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
     const int nc = (len + kChunk - 1) / kChunk;
-    const int tx = tx_of(), ty = ty_of();
 
     if (p.initial_state) {
         StateTileReg<K> r0;
@@ -465,64 +515,68 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
             gam[threadIdx.x] = rg;
             bet[threadIdx.x] = rb;
         }
-        __syncthreads();
-        norm_rows<K>(kh, fk, p.use_l2norm);
+        lds_barrier();
+        if (threadIdx.x < kChunk) {
+            const int r = threadIdx.x;
+            sD[r] = __expf(gam[r]);
+            sF[r] = r < L ? __expf(gam[L - 1] - gam[r]) : 0.f;
+        }
+        norm_rows<K>(kh, fk, p.use_l2norm);   // ends with a barrier
         if (ci + 1 < nc) fetch(ci + 1);
 
+        // Wave w: rows 16w.. of the 64 x 32 products, row tiles 2w, 2w+1 of the K x 32 state.
+        const int w = wave_id();
+        auto ra = [&](int) { return 16 * w; };
+        auto cb = [&](int t) { return 16 * t; };
+        auto rs = [&](int t) { return 16 * (2 * w + (t >> 1)); };
+        auto cs = [&](int t) { return 16 * (t & 1); };
         // B = diag(beta) (V - diag(D) Kh h)
         {
-            float x[4][2];
+            f32x4 x[2];
             zero(x);
-            mm<4, 2, K>(x, [&](int r, int m) { return kh[r * (K + 1) + m]; },
-                        [&](int c, int m) { return h[m * kPadT + c]; });
+            wmm<2, K>(x, ra, cb, [&](int r, int m) { return kh[r * (K + 1) + m]; },
+                      [&](int c, int m) { return h[m * kPadT + c]; });
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ty + 16 * i;
-                const float d = __expf(gam[r]);
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int c = tx + 16 * jj;
-                    Bm[r * kPadT + c] = bet[r] * (vv[r * kPadT + c] - d * x[i][jj]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = lrow(16 * w, e), c = lcol(16 * t);
+                    Bm[r * kPadT + c] = bet[r] * (vv[r * kPadT + c] - sD[r] * x[t][e]);
                 }
-            }
         }
-        __syncthreads();
+        lds_barrier();
         // Vn = Tm B; F = diag(exp(gamma_L - gamma)) Vn into vv
         {
-            float x[4][2];
+            f32x4 x[2];
             zero(x);
-            mm<4, 2, kChunk>(x, [&](int r, int m) { return Tm[r * kPadC + m]; },
-                             [&](int c, int m) { return Bm[m * kPadT + c]; });
-            const float gl = gam[L - 1];
+            wmm<2, kChunk>(x, ra, cb, [&](int r, int m) { return Tm[r * kPadC + m]; },
+                           [&](int c, int m) { return Bm[m * kPadT + c]; });
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ty + 16 * i;
-                const float f = r < L ? __expf(gl - gam[r]) : 0.f;
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int c = tx + 16 * jj;
-                    if (r < L) p.vn[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = x[i][jj];
-                    vv[r * kPadT + c] = f * x[i][jj];
+                for (int e = 0; e < 4; ++e) {
+                    const int r = lrow(16 * w, e), c = lcol(16 * t);
+                    if (r < L) p.vn[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = x[t][e];
+                    vv[r * kPadT + c] = sF[r] * x[t][e];
                 }
-            }
         }
-        __syncthreads();
+        lds_barrier();
         // h <- D_L h + Kh^T F
         {
-            float x[K / 16][2];
+            f32x4 x[4];
             zero(x);
-            mm<K / 16, 2, kChunk>(x, [&](int r, int m) { return kh[m * (K + 1) + r]; },
-                                  [&](int c, int m) { return vv[m * kPadT + c]; });
+            wmm<4, kChunk>(x, rs, cs, [&](int r, int m) { return kh[m * (K + 1) + r]; },
+                           [&](int c, int m) { return vv[m * kPadT + c]; });
             const float dl = __expf(gam[L - 1]);
 #pragma unroll
-            for (int i = 0; i < K / 16; ++i)
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    float &hv = h[(ty + 16 * i) * kPadT + tx + 16 * jj];
-                    hv = fmaf(dl, hv, x[i][jj]);
+                for (int e = 0; e < 4; ++e) {
+                    float &hv = h[lrow(rs(t), e) * kPadT + lcol(cs(t))];
+                    hv = fmaf(dl, hv, x[t][e]);
                 }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -545,6 +599,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
     float *bet = gam + kChunk;               // [64]
     float *fk = bet + kChunk;                // [64]
     float *fq = fk + kChunk;                 // [64]
+    float *sF = fq + kChunk;                 // [64] exp(gamma_L - gamma), 0 past L
+    float *sD = sF + kChunk;                 // [64] scale exp(gamma)
+    float *sB = sD + kChunk;                 // [64] -beta exp(gamma)
 
     const int HV = p.HV, V = p.V;
     const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
@@ -552,7 +609,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
     const int nc = (len + kChunk - 1) / kChunk;
-    const int tx = tx_of(), ty = ty_of();
     const float scale = p.scale;
 
     if (p.dht) {
@@ -593,66 +649,77 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
             gam[threadIdx.x] = rg;
             bet[threadIdx.x] = rb;
         }
-        __syncthreads();
-        norm_rows<K>(kh, fk, p.use_l2norm);
+        lds_barrier();
+        if (threadIdx.x < kChunk) {
+            const int r = threadIdx.x;
+            const float d = __expf(gam[r]);
+            sF[r] = r < L ? __expf(gam[L - 1] - gam[r]) : 0.f;
+            sD[r] = scale * d;
+            sB[r] = -bet[r] * d;
+        }
+        norm_rows<K>(kh, fk, p.use_l2norm);   // ends with a barrier
         norm_rows<K>(qh, fq, p.use_l2norm);
         if (ci > 0) fetch(ci - 1);
         const float gl = gam[L - 1];
+        // Wave w: rows 16w.. of the 64 x 32 products, row tiles 2w, 2w+1 of the K x 32 state.
+        const int w = wave_id();
+        auto ra = [&](int) { return 16 * w; };
+        auto cb = [&](int t) { return 16 * t; };
+        auto rs = [&](int t) { return 16 * (2 * w + (t >> 1)); };
+        auto cs = [&](int t) { return 16 * (t & 1); };
 
         // dVn = scale Pm^T dO + diag(exp(gamma_L - gamma)) Kh dh'
         {
-            float a[4][2], b[4][2];
+            f32x4 a[2], b[2];
             zero(a);
             zero(b);
-            mm<4, 2, kChunk>(a, [&](int r, int m) { return Pm[m * kPadC + r]; },
-                             [&](int c, int m) { return dO[m * kPadT + c]; });
-            mm<4, 2, K>(b, [&](int r, int m) { return kh[r * (K + 1) + m]; },
-                        [&](int c, int m) { return dh[m * kPadT + c]; });
+            wmm<2, kChunk>(a, ra, cb, [&](int r, int m) { return Pm[m * kPadC + r]; },
+                           [&](int c, int m) { return dO[m * kPadT + c]; });
+            wmm<2, K>(b, ra, cb, [&](int r, int m) { return kh[r * (K + 1) + m]; },
+                      [&](int c, int m) { return dh[m * kPadT + c]; });
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ty + 16 * i;
-                const float f = r < L ? __expf(gl - gam[r]) : 0.f;
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) dVn[r * kPadT + tx + 16 * jj] = scale * a[i][jj] + f * b[i][jj];
-            }
+                for (int e = 0; e < 4; ++e) {
+                    const int r = lrow(16 * w, e), c = lcol(16 * t);
+                    dVn[r * kPadT + c] = scale * a[t][e] + sF[r] * b[t][e];
+                }
         }
-        __syncthreads();
+        lds_barrier();
         // dB = Tm^T dVn
         {
-            float a[4][2];
+            f32x4 a[2];
             zero(a);
-            mm<4, 2, kChunk>(a, [&](int r, int m) { return Tm[m * kPadC + r]; },
-                             [&](int c, int m) { return dVn[m * kPadT + c]; });
+            wmm<2, kChunk>(a, ra, cb, [&](int r, int m) { return Tm[m * kPadC + r]; },
+                           [&](int c, int m) { return dVn[m * kPadT + c]; });
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ty + 16 * i;
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int c = tx + 16 * jj;
-                    dB[r * kPadT + c] = a[i][jj];
-                    if (r < L) p.db[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = a[i][jj];
+                for (int e = 0; e < 4; ++e) {
+                    const int r = lrow(16 * w, e), c = lcol(16 * t);
+                    dB[r * kPadT + c] = a[t][e];
+                    if (r < L) p.db[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = a[t][e];
                 }
-            }
         }
-        __syncthreads();
+        lds_barrier();
         // dh <- D_L dh' + scale Qh^T diag(D) dO - Kh^T diag(beta D) dB
         {
-            float a[K / 16][2];
+            f32x4 a[4];
             zero(a);
-            mm<K / 16, 2, kChunk>(a, [&](int r, int m) { return qh[m * (K + 1) + r]; },
-                                  [&](int c, int m) { return scale * __expf(gam[m]) * dO[m * kPadT + c]; });
-            mm<K / 16, 2, kChunk>(a, [&](int r, int m) { return kh[m * (K + 1) + r]; },
-                                  [&](int c, int m) { return -bet[m] * __expf(gam[m]) * dB[m * kPadT + c]; });
+            wmm<4, kChunk>(a, rs, cs, [&](int r, int m) { return qh[m * (K + 1) + r]; },
+                           [&](int c, int m) { return sD[m] * dO[m * kPadT + c]; });
+            wmm<4, kChunk>(a, rs, cs, [&](int r, int m) { return kh[m * (K + 1) + r]; },
+                           [&](int c, int m) { return sB[m] * dB[m * kPadT + c]; });
             const float dl = __expf(gl);
 #pragma unroll
-            for (int i = 0; i < K / 16; ++i)
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    float &x = dh[(ty + 16 * i) * kPadT + tx + 16 * jj];
-                    x = fmaf(dl, x, a[i][jj]);
+                for (int e = 0; e < 4; ++e) {
+                    float &x = dh[lrow(rs(t), e) * kPadT + lcol(cs(t))];
+                    x = fmaf(dl, x, a[t][e]);
                 }
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (p.dh0) store_state_tile<K>(dh, p.dh0 + ((int64_t)n * HV + j) * K * V, V, c0);
 }
@@ -688,9 +755,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
     if (!find_chunk(p, blockIdx.x, cr)) return;
     const int j = blockIdx.y, HV = p.HV, jk = j / (HV / p.H);
     const int cid = blockIdx.x, L = cr.L, t0 = cr.t0;
-    const int tx = tx_of(), ty = ty_of();
     const float scale = p.scale;
     constexpr int KR = K / 16;
+    // Wave w holds rows 16w..16w+15 of every 64 x 64 and 64 x K product.
+    const int w = wave_id(), lane16 = threadIdx.x & 15;
+    auto ra = [&](int) { return 16 * w; };
+    auto cb = [&](int t) { return 16 * t; };
 
     if (threadIdx.x < kChunk) {
         const int r = threadIdx.x;
@@ -718,11 +788,11 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
         rk.commit(kh);
         rq.commit(qh);
     }
-    __syncthreads();
+    lds_barrier();
     norm_rows<K>(kh, fk, p.use_l2norm);
     norm_rows<K>(qh, fq, p.use_l2norm);
 
-    float aP[4][4], aA[4][4], dQ[4][KR], aE[4][KR], aF[4][KR];
+    f32x4 aP[4], aA[4], dQ[KR], aE[KR], aF[KR];
     zero(aP);
     zero(aA);
     zero(dQ);
@@ -737,7 +807,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
         tdb.commit(dbT);
         tdo.commit(doT);
         tv.commit(vvT);
-        __syncthreads();
+        lds_barrier();
         if (c0 + kVT < V) fetch(c0 + kVT);
         // this thread's part of <dh', h>: the elements it wrote
         {
@@ -760,17 +830,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
                 for (int c = part; c < kVT; c += 4)
                     ((E *)p.dv)[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = to_e<E>(bet[r] * dbT[r * kPadT + c]);
         }
-        mm<4, 4, kVT>(aP, [&](int r, int m) { return doT[r * kPadT + m]; },
-                      [&](int c, int m) { return vnT[c * kPadT + m]; });
-        mm<4, 4, kVT>(aA, [&](int r, int m) { return dbT[r * kPadT + m]; },
-                      [&](int c, int m) { return vnT[c * kPadT + m]; });
-        mm<4, KR, kVT>(dQ, [&](int r, int m) { return doT[r * kPadT + m]; },
-                       [&](int c, int m) { return hT[c * kPadT + m]; });
-        mm<4, KR, kVT>(aE, [&](int r, int m) { return dbT[r * kPadT + m]; },
-                       [&](int c, int m) { return hT[c * kPadT + m]; });
-        mm<4, KR, kVT>(aF, [&](int r, int m) { return vnT[r * kPadT + m]; },
-                       [&](int c, int m) { return dhT[c * kPadT + m]; });
-        __syncthreads();
+        wmm<4, kVT>(aP, ra, cb, [&](int r, int m) { return doT[r * kPadT + m]; },
+                    [&](int c, int m) { return vnT[c * kPadT + m]; });
+        wmm<4, kVT>(aA, ra, cb, [&](int r, int m) { return dbT[r * kPadT + m]; },
+                    [&](int c, int m) { return vnT[c * kPadT + m]; });
+        wmm<KR, kVT>(dQ, ra, cb, [&](int r, int m) { return doT[r * kPadT + m]; },
+                     [&](int c, int m) { return hT[c * kPadT + m]; });
+        wmm<KR, kVT>(aE, ra, cb, [&](int r, int m) { return dbT[r * kPadT + m]; },
+                     [&](int c, int m) { return hT[c * kPadT + m]; });
+        wmm<KR, kVT>(aF, ra, cb, [&](int r, int m) { return vnT[r * kPadT + m]; },
+                     [&](int c, int m) { return dhT[c * kPadT + m]; });
+        lds_barrier();
     }
 
     // <dh', h> over the block
@@ -783,66 +853,64 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
     // row scalings and the row dot products with qh / kh
     float t3sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = ty + 16 * i;
+    for (int e = 0; e < 4; ++e) {
+        const int r = lrow(16 * w, e);
         const float d = __expf(gam[r]);
         const float f = r < L ? __expf(gl - gam[r]) : 0.f;
         float t1 = 0.f, t2 = 0.f, t3 = 0.f;
 #pragma unroll
-        for (int c = 0; c < KR; ++c) {
-            const int col = tx + 16 * c;
-            dQ[i][c] *= scale * d;
-            aE[i][c] *= d;
-            aF[i][c] *= f;
-            t1 = fmaf(qh[r * (K + 1) + col], dQ[i][c], t1);
-            t2 = fmaf(kh[r * (K + 1) + col], aE[i][c], t2);
-            t3 = fmaf(kh[r * (K + 1) + col], aF[i][c], t3);
+        for (int t = 0; t < KR; ++t) {
+            const int col = lcol(16 * t);
+            dQ[t][e] *= scale * d;
+            aE[t][e] *= d;
+            aF[t][e] *= f;
+            t1 = fmaf(qh[r * (K + 1) + col], dQ[t][e], t1);
+            t2 = fmaf(kh[r * (K + 1) + col], aE[t][e], t2);
+            t3 = fmaf(kh[r * (K + 1) + col], aF[t][e], t3);
         }
         t1 = sum16(t1);
         t2 = sum16(t2);
         t3 = sum16(t3);
         t3sum += t3;
-        if (tx == 0) {
+        if (lane16 == 0) {
             dgam[r] = t1 - bet[r] * t2 - t3;
             dbet[r] = -t2;
         }
     }
     // dK so far: F dh'^T - diag(beta) E
-    float dK[4][KR];
+    f32x4 dK[KR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int t = 0; t < KR; ++t)
 #pragma unroll
-        for (int c = 0; c < KR; ++c) dK[i][c] = aF[i][c] - bet[ty + 16 * i] * aE[i][c];
+        for (int e = 0; e < 4; ++e) dK[t][e] = aF[t][e] - bet[lrow(16 * w, e)] * aE[t][e];
 
     // the 64 x 64 matrices: dSqk, Ad and Z = dSqk * (qh . kh) + dA * A
     const float *pm = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
     const float *ag = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
     float dbA[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = ty + 16 * i;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int c = tx + 16 * jj;
+        for (int e = 0; e < 4; ++e) {
+            const int r = lrow(16 * w, e), c = lcol(16 * t);
             const bool low = c <= r && r < L;
-            const float e = low ? __expf(gam[r] - gam[c]) : 0.f;
-            const float dpm = scale * aP[i][jj];
-            const float dsq = e * dpm;                   // dSqk
+            const float d = low ? __expf(gam[r] - gam[c]) : 0.f;
+            const float dpm = scale * aP[t][e];
+            const float dsq = d * dpm;                   // dSqk
             const float z1 = dpm * pm[r * kChunk + c];   // dPm * Pm
-            const float dA = c < r && r < L ? -aA[i][jj] : 0.f;
+            const float dA = c < r && r < L ? -aA[t][e] : 0.f;
             const float agv = ag[r * kChunk + c];
             dS[r * kPadC + c] = dsq;
-            Ad[r * kPadC + c] = dA * bet[r] * e;
+            Ad[r * kPadC + c] = dA * bet[r] * d;
             Zm[r * kPadC + c] = z1 + dA * bet[r] * agv;
-            dbA[i] = fmaf(dA, agv, dbA[i]);
+            dbA[e] = fmaf(dA, agv, dbA[e]);
         }
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float s = sum16(dbA[i]);
-        if (tx == 0) dbet[ty + 16 * i] += s;
+    for (int e = 0; e < 4; ++e) {
+        const float s = sum16(dbA[e]);
+        if (lane16 == 0) dbet[lrow(16 * w, e)] += s;
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < kChunk) {
         const int r = threadIdx.x;
         float rs = 0.f, cs = 0.f;
@@ -853,8 +921,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
         dgam[r] += rs - cs;
     }
     if ((threadIdx.x & 3) == 0) dbet[threadIdx.x >> 2] += sbv;
-    if (tx == 0) red[4 + ty] = t3sum;
-    __syncthreads();
+    if (lane16 == 0) red[4 + (threadIdx.x >> 4)] = t3sum;
+    lds_barrier();
     if (threadIdx.x == 0) {
         float s = red[0] + red[1] + red[2] + red[3];
         float t = 0.f;
@@ -863,23 +931,23 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
     }
 
     // dQ += dSqk Kh;  dK += dSqk^T Qh + (Ad + Ad^T) Kh
-    mm<4, KR, kChunk>(dQ, [&](int r, int m) { return dS[r * kPadC + m]; },
-                      [&](int c, int m) { return kh[m * (K + 1) + c]; });
-    mm<4, KR, kChunk>(dK, [&](int r, int m) { return dS[m * kPadC + r]; },
-                      [&](int c, int m) { return qh[m * (K + 1) + c]; });
-    mm<4, KR, kChunk>(dK, [&](int r, int m) { return Ad[r * kPadC + m] + Ad[m * kPadC + r]; },
-                      [&](int c, int m) { return kh[m * (K + 1) + c]; });
+    wmm<KR, kChunk>(dQ, ra, cb, [&](int r, int m) { return dS[r * kPadC + m]; },
+                    [&](int c, int m) { return kh[m * (K + 1) + c]; });
+    wmm<KR, kChunk>(dK, ra, cb, [&](int r, int m) { return dS[m * kPadC + r]; },
+                    [&](int c, int m) { return qh[m * (K + 1) + c]; });
+    wmm<KR, kChunk>(dK, ra, cb, [&](int r, int m) { return Ad[r * kPadC + m] + Ad[m * kPadC + r]; },
+                    [&](int c, int m) { return kh[m * (K + 1) + c]; });
 
     // L2-norm backward and the per-value-head partial dq, dk
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = ty + 16 * i;
+    for (int e = 0; e < 4; ++e) {
+        const int r = lrow(16 * w, e);
         float sq = 0.f, sk = 0.f;
         if (p.use_l2norm) {
 #pragma unroll
-            for (int c = 0; c < KR; ++c) {
-                sq = fmaf(qh[r * (K + 1) + tx + 16 * c], dQ[i][c], sq);
-                sk = fmaf(kh[r * (K + 1) + tx + 16 * c], dK[i][c], sk);
+            for (int t = 0; t < KR; ++t) {
+                sq = fmaf(qh[r * (K + 1) + lcol(16 * t)], dQ[t][e], sq);
+                sk = fmaf(kh[r * (K + 1) + lcol(16 * t)], dK[t][e], sk);
             }
             sq = sum16(sq);
             sk = sum16(sk);
@@ -888,14 +956,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
             float *dq = p.dqp + ((int64_t)(t0 + r) * HV + j) * K;
             float *dk = p.dkp + ((int64_t)(t0 + r) * HV + j) * K;
 #pragma unroll
-            for (int c = 0; c < KR; ++c) {
-                const int col = tx + 16 * c;
-                dq[col] = fq[r] * (dQ[i][c] - qh[r * (K + 1) + col] * sq);
-                dk[col] = fk[r] * (dK[i][c] - kh[r * (K + 1) + col] * sk);
+            for (int t = 0; t < KR; ++t) {
+                const int col = lcol(16 * t);
+                dq[col] = fq[r] * (dQ[t][e] - qh[r * (K + 1) + col] * sq);
+                dk[col] = fk[r] * (dK[t][e] - kh[r * (K + 1) + col] * sk);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dg = reverse cumsum of dgamma inside the chunk; dbeta
     if (threadIdx.x < L) {
         const int r = threadIdx.x;
