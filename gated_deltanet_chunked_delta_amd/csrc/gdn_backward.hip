@@ -66,7 +66,9 @@ constexpr int prep_q_floats() {   // the q rows, then A [64][65] and Tm [64][64]
 template <int K>
 constexpr int prep_floats() { return kChunk * (K + 1) + prep_q_floats<K>() + 4 * kChunk; }
 template <int K>
-constexpr int fwd_scan_floats() { return K * kPadT + kChunk * (K + 1) + kChunk * kPadC + 2 * kChunk * kPadT + 5 * kChunk; }
+constexpr int fwd_scan_floats() { return K * kPadT + kChunk * (K + 1) + kChunk * kPadC + kChunk * kPadT + 5 * kChunk; }
+// two forward-scan workgroups share a CU (160 KB of LDS)
+static_assert(fwd_scan_floats<128>() * 4 <= 80 * 1024, "forward scan must fit twice per CU");
 template <int K>
 constexpr int dh_scan_floats() {
     return K * kPadT + 2 * kChunk * (K + 1) + 2 * kChunk * kPadC + 3 * kChunk * kPadT + 7 * kChunk;
@@ -375,13 +377,16 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     const int j = blockIdx.y, HV = p.HV, jk = j / (HV / p.H);
     const int cid = blockIdx.x, L = cr.L, t0 = cr.t0;
 
-    if (threadIdx.x == 0) {
-        float run = 0.f;
-        for (int r = 0; r < kChunk; ++r) {
-            if (r < L) run += p.g[(int64_t)(t0 + r) * HV + j];
-            gam[r] = run;
-            bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+    if (threadIdx.x < kChunk) {   // wave 0: gamma by an inclusive scan over its 64 lanes
+        const int r = threadIdx.x;
+        float x = r < L ? p.g[(int64_t)(t0 + r) * HV + j] : 0.f;
+#pragma unroll
+        for (int o = 1; o < kChunk; o <<= 1) {
+            const float y = __shfl_up(x, o);
+            if (r >= o) x += y;
         }
+        gam[r] = x;
+        bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
     }
     {
         RowsReg<E, K> rk, rq;
@@ -466,9 +471,8 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
     float *h = sm;                           // [K][33]
     float *kh = h + K * kPadT;               // [64][K+1]
     float *Tm = kh + kChunk * (K + 1);       // [64][65]
-    float *vv = Tm + kChunk * kPadC;         // [64][33]: v, then F
-    float *Bm = vv + kChunk * kPadT;         // [64][33]
-    float *gam = Bm + kChunk * kPadT;        // [64]
+    float *vv = Tm + kChunk * kPadC;         // [64][33]: v, then B (in place), then F
+    float *gam = vv + kChunk * kPadT;        // [64]
     float *bet = gam + kChunk;               // [64]
     float *fk = bet + kChunk;                // [64]
     float *sD = fk + kChunk;                 // [64] exp(gamma)
@@ -541,16 +545,17 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = lrow(16 * w, e), c = lcol(16 * t);
-                    Bm[r * kPadT + c] = bet[r] * (vv[r * kPadT + c] - sD[r] * x[t][e]);
+                    vv[r * kPadT + c] = bet[r] * (vv[r * kPadT + c] - sD[r] * x[t][e]);
                 }
         }
         lds_barrier();
-        // Vn = Tm B; F = diag(exp(gamma_L - gamma)) Vn into vv
+        // Vn = Tm B; F = diag(exp(gamma_L - gamma)) Vn into vv once every wave has read B
         {
             f32x4 x[2];
             zero(x);
             wmm<2, kChunk>(x, ra, cb, [&](int r, int m) { return Tm[r * kPadC + m]; },
-                           [&](int c, int m) { return Bm[m * kPadT + c]; });
+                           [&](int c, int m) { return vv[m * kPadT + c]; });
+            lds_barrier();
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
