@@ -301,6 +301,20 @@ def bwd_path_bytes(w, x, eb):
     return reads + writes
 
 
+def bwd_path_flops(w, x):
+    """Algorithmic flops of one backward pass: the products of the chain rule
+    through the chunked form, per chunk of C = 64 rows with the triangular
+    masks counted (2 flops per multiply-add).  Per token and value head: eight
+    C x K x V products per chunk (the forward rescan's Kh h and Kh^T F, then
+    Kh dh', Qh^T dO, Kh^T dB, dO h^T, dB h^T, Vn dh'^T) give 16 K V; six
+    half-masked C x C x K products (K K^T, Q K^T, dSqk Kh, dSqk^T Qh, Ad Kh,
+    Ad^T Kh) give 6 C K; five half-masked C x C x V products (Tm B, Pm^T dO,
+    Tm^T dVn, dO Vn^T, dB Vn^T) give 5 C V; the triangular inverse C^2 / 3."""
+    C = 64
+    per_tok = 16 * w.K * w.V + 6 * C * w.K + 5 * C * w.V + C * C / 3
+    return int(sum(x["lens"]) * w.HV * per_tok)
+
+
 def bwd_cpu_baseline(x, groups=2):
     """The fp64 backward oracle (numpy, token by token) on `groups` (sequence,
     key head) groups of the same inputs, with all value heads of each group."""
@@ -385,6 +399,8 @@ def run_backward(args):
     # five kernels share the path: the path's algorithmic bytes over the sum of
     # their times per step (the dominant kernel's share of that time is given)
     ach = pb / (path_us * 1e-6) / 1e9
+    flops = bwd_path_flops(w, x)
+    tflops = flops / (path_us * 1e-6) / 1e12
     res = {
         "metric": BWD_METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4),
@@ -394,9 +410,14 @@ def run_backward(args):
                                f"l2norm={w.use_l2norm} initial_state={w.init} dht=yes",
                    "tokens": tokens, "global_batch": N, "seq_len": T if N == B else None,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "scope": "path", "kernel": dom, "achieved": round(ach, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_step": pb, "kernel_us_per_step": round(path_us, 2),
+        # every product runs in fp32 on the matrix cores and the pass does ~260
+        # flops per algorithmic byte, far above the fp32 ridge (157.3 TFLOP/s
+        # over 8 TB/s = 20 flop/B): the bound is fp32 MFMA, the HBM side is given
+        "roofline": {"bound": "mfma", "dtype": "fp32", "scope": "path", "kernel": dom,
+                     "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS["fp32"], "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS["fp32"], 4), "traffic": None,
+                     "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": pb,
+                     "hbm_frac": round(ach / HBM_PEAK_GBS, 4), "kernel_us_per_step": round(path_us, 2),
                      "dominant_kernel_share": round(per_step(dom) / path_us, 3)},
         "kernels": {k: {kk: round(vv, 2) if isinstance(vv, float) else vv for kk, vv in v.items()}
                     for k, v in kernels.items()},

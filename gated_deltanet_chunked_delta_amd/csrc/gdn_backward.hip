@@ -69,10 +69,6 @@ template <int K>
 constexpr int fwd_scan_floats() { return K * kPadT + kChunk * (K + 1) + kChunk * kPadC + kChunk * kPadT + 5 * kChunk; }
 // two forward-scan workgroups share a CU (160 KB of LDS)
 static_assert(fwd_scan_floats<128>() * 4 <= 80 * 1024, "forward scan must fit twice per CU");
-template <int K>
-constexpr int dh_scan_floats() {
-    return K * kPadT + 2 * kChunk * (K + 1) + 2 * kChunk * kPadC + 3 * kChunk * kPadT + 7 * kChunk;
-}
 // grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the three
 // 64 x 65 matrices of the second phase reuse their space.
 template <int K>
@@ -98,7 +94,7 @@ __device__ __forceinline__ void wmm(f32x4 (&acc)[NT], RA ra, CB cb, FA fa, FB fb
     constexpr int G = S <= G0 ? S : (S % G0 == 0 ? G0 : (S % 4 == 0 ? 4 : 1));
     static_assert(S % G == 0, "k-steps must split into whole groups");
     const int i = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
-#pragma unroll
+#pragma unroll 1
     for (int g = 0; g < S; g += G) {
         float av[G][NT], bv[G][NT];
 #pragma unroll
@@ -280,6 +276,130 @@ struct StateTileReg {
         }
     }
 };
+
+// ---- register-staged copies for workgroups of NTH threads and value tiles
+// of VW columns (the scans), with the key/query rows kept raw in the input
+// type in LDS (row stride K + RowPad<E>; the L2 norms are applied as row
+// scales inside the products).
+template <typename E> struct RowPad;
+template <> struct RowPad<bf16> { static constexpr int v = 2; };    // 4-byte rows, odd word stride
+template <> struct RowPad<float> { static constexpr int v = 1; };
+
+template <typename E, int K, int NTH>
+struct RawRowsReg {
+    static constexpr int PER_ROW = K / 8, VPT = kChunk * PER_ROW / NTH, KS = K + RowPad<E>::v;
+    static_assert(VPT >= 1 && kChunk * PER_ROW % NTH == 0, "rows must split evenly");
+    typename VT<E>::v8 v[VPT];
+    __device__ __forceinline__ void load(const E *src, int t0, int L, int H, int jk) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int i = threadIdx.x + NTH * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
+            if (r < L) v[u] = ld8<E>(src + ((int64_t)(t0 + r) * H + jk) * K + c);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[u][e] = to_e<E>(0.f);
+        }
+    }
+    __device__ __forceinline__ void commit(E *dst) const {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int i = threadIdx.x + NTH * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
+            if constexpr (sizeof(E) == 2) {   // even offsets: four 32-bit words
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 x = __builtin_bit_cast(u32x4, v[u]);
+                unsigned int *d = (unsigned int *)(dst + r * KS + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[e] = x[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dst[r * KS + c + e] = v[u][e];
+            }
+        }
+    }
+};
+// A 64 x 64 fp32 matrix (contiguous) into dst[64][65].
+template <int NTH>
+struct Mat64RegN {
+    static constexpr int N4 = kChunk * kChunk / 4 / NTH;
+    f32x4 v[N4];
+    __device__ __forceinline__ void load(const float *src) {
+#pragma unroll
+        for (int u = 0; u < N4; ++u) v[u] = *(const f32x4 *)(src + 4 * (threadIdx.x + NTH * u));
+    }
+    __device__ __forceinline__ void commit(float *dst) const {
+#pragma unroll
+        for (int u = 0; u < N4; ++u) {
+            const int i = threadIdx.x + NTH * u, r = i >> 4, c = (i & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[r * kPadC + c + e] = v[u][e];
+        }
+    }
+};
+// Rows t0..t0+L-1 (zero past L), VW columns from c0, of a [T_tot, HV, V]
+// tensor at value head j, into dst[64][VW+1] as fp32.
+template <typename E, int VW, int NTH>
+struct TileRegN {
+    static_assert(kChunk * VW == 8 * NTH, "one 8-element run per thread");
+    typename VT<E>::v8 v;
+    __device__ __forceinline__ void load(const E *src, int t0, int L, int HV, int j, int V, int c0) {
+        const int r = threadIdx.x / (VW / 8), c = (threadIdx.x % (VW / 8)) * 8;
+        if (r < L) v = ld8<E>(src + ((int64_t)(t0 + r) * HV + j) * V + c0 + c);
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = to_e<E>(0.f);
+    }
+    __device__ __forceinline__ void commit(float *dst) const {
+        const int r = threadIdx.x / (VW / 8), c = (threadIdx.x % (VW / 8)) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[r * (VW + 1) + c + e] = to_f(v[e]);
+    }
+};
+// K rows x VW columns from c0 of a K x V fp32 state (row stride V), to and from dst[K][VW+1].
+template <int K, int VW, int NTH>
+struct StateTileN {
+    static constexpr int N4 = K * VW / 4 / NTH, Q = VW / 4;
+    f32x4 v[N4];
+    __device__ __forceinline__ void load(const float *src, int V, int c0) {
+#pragma unroll
+        for (int u = 0; u < N4; ++u) {
+            const int i = threadIdx.x + NTH * u, r = i / Q, c = (i % Q) * 4;
+            v[u] = *(const f32x4 *)(src + (int64_t)r * V + c0 + c);
+        }
+    }
+    __device__ __forceinline__ void commit(float *dst) const {
+#pragma unroll
+        for (int u = 0; u < N4; ++u) {
+            const int i = threadIdx.x + NTH * u, r = i / Q, c = (i % Q) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[r * (VW + 1) + c + e] = v[u][e];
+        }
+    }
+    static __device__ __forceinline__ void store(const float *tile, float *dst, int V, int c0) {
+#pragma unroll
+        for (int u = 0; u < N4; ++u) {
+            const int i = threadIdx.x + NTH * u, r = i / Q, c = (i % Q) * 4;
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = tile[r * (VW + 1) + c + e];
+            *(f32x4 *)(dst + (int64_t)r * V + c0 + c) = x;
+        }
+    }
+};
+// Sum of squares of row r of a raw row set, over the NTH / 64 lanes that
+// share the row (r = threadIdx.x / (NTH / 64)); every such lane gets the sum.
+template <typename E, int K, int NTH>
+__device__ __forceinline__ float row_sumsq(const E *rows, int r) {
+    constexpr int LPR = NTH / kChunk, KS = K + RowPad<E>::v;
+    const int part = threadIdx.x % LPR;
+    float s = 0.f;
+    for (int c = part; c < K; c += LPR) {
+        const float x = to_f(rows[r * KS + c]);
+        s = fmaf(x, x, s);
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
+    return s;
+}
 
 // L2-normalises the rows of dst[64][K+1] in place when use_l2norm (factor
 // 1/sqrt(|x|^2 + 1e-6) into f[r], else 1).  Call after a barrier that
@@ -586,47 +706,58 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// backward over chunks per (sequence, value head, 32 value columns):
-// dh' per chunk, dB, and the initial-state gradient
+// backward over chunks per (sequence, value head, VW value columns), NTH
+// threads: dh' per chunk, dB, and the initial-state gradient.  The key and
+// query rows stay raw in LDS; their L2 norms enter as the row scales sFk, sD
+// and sB of the three products that use them.
 // ---------------------------------------------------------------------------
-template <typename E, int K>
-__global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
-    __shared__ float sm[dh_scan_floats<K>()];
-    float *dh = sm;                          // [K][33]
-    float *kh = dh + K * kPadT;              // [64][K+1]
-    float *qh = kh + kChunk * (K + 1);       // [64][K+1]
-    float *Tm = qh + kChunk * (K + 1);       // [64][65]
+template <typename E, int K, int VW, int NTH>
+constexpr int dh_scan_floats() {
+    return K * (VW + 1) + 2 * kChunk * kPadC + 3 * kChunk * (VW + 1) + 5 * kChunk +
+           (2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4;
+}
+static_assert(dh_scan_floats<bf16, 128, 64, 512>() * 4 <= 160 * 1024, "bf16 dh scan must fit one CU");
+static_assert(dh_scan_floats<float, 128, 32, 256>() * 4 <= 160 * 1024, "fp32 dh scan must fit one CU");
+
+template <typename E, int K, int VW, int NTH>
+__global__ __launch_bounds__(NTH) void bwd_dh_scan_kernel(BwdParams p) {
+    constexpr int VP = VW + 1, KS = K + RowPad<E>::v, W = NTH / 64, CT = VW / 16;
+    constexpr int NT1 = 4 * CT / W;          // 16 x 16 tiles of a 64 x VW product per wave
+    constexpr int NT2 = (K / 16) * CT / W;   // tiles of the K x VW state per wave
+    static_assert(NT1 >= 1 && NT2 >= 1, "every wave needs a tile");
+    __shared__ float sm[dh_scan_floats<E, K, VW, NTH>()];
+    float *dh = sm;                          // [K][VP]
+    float *Tm = dh + K * VP;                 // [64][65]
     float *Pm = Tm + kChunk * kPadC;         // [64][65]
-    float *dO = Pm + kChunk * kPadC;         // [64][33]
-    float *dVn = dO + kChunk * kPadT;        // [64][33]
-    float *dB = dVn + kChunk * kPadT;        // [64][33]
-    float *gam = dB + kChunk * kPadT;        // [64]
+    float *dO = Pm + kChunk * kPadC;         // [64][VP]
+    float *dVn = dO + kChunk * VP;           // [64][VP]
+    float *dB = dVn + kChunk * VP;           // [64][VP]
+    float *gam = dB + kChunk * VP;           // [64]
     float *bet = gam + kChunk;               // [64]
-    float *fk = bet + kChunk;                // [64]
-    float *fq = fk + kChunk;                 // [64]
-    float *sF = fq + kChunk;                 // [64] exp(gamma_L - gamma), 0 past L
-    float *sD = sF + kChunk;                 // [64] scale exp(gamma)
-    float *sB = sD + kChunk;                 // [64] -beta exp(gamma)
+    float *sFk = bet + kChunk;               // [64] exp(gamma_L - gamma) / |k|, 0 past L
+    float *sD = sFk + kChunk;                // [64] scale exp(gamma) / |q|
+    float *sB = sD + kChunk;                 // [64] -beta exp(gamma) / |k|
+    E *kr = (E *)(sB + kChunk);              // [64][KS] raw k rows
+    E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
 
     const int HV = p.HV, V = p.V;
     const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
-    const int c0 = blockIdx.y * kVT;
+    const int c0 = blockIdx.y * VW;
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
     const int nc = (len + kChunk - 1) / kChunk;
     const float scale = p.scale;
 
     if (p.dht) {
-        StateTileReg<K> r0;
+        StateTileN<K, VW, NTH> r0;
         r0.load(p.dht + ((int64_t)n * HV + j) * K * V, V, c0);
         r0.commit(dh);
     } else {
-        for (int e = threadIdx.x; e < K * kVT; e += kThreads) dh[(e / kVT) * kPadT + e % kVT] = 0.f;
+        for (int e = threadIdx.x; e < K * VW; e += NTH) dh[(e / VW) * VP + e % VW] = 0.f;
     }
-    __syncthreads();
-    RowsReg<E, K> rk, rq;
-    Mat64Reg rt, rp;
-    TileReg<E> ro;
+    RawRowsReg<E, K, NTH> rk, rq;
+    Mat64RegN<NTH> rt, rp;
+    TileRegN<E, VW, NTH> ro;
     float rg = 0.f, rb = 0.f;
     auto fetch = [&](int ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
@@ -642,11 +773,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
         }
     };
     if (nc > 0) fetch(nc - 1);
+    lds_barrier();
+    // tile τ = w NT + t of a product with CT column tiles sits at row tile τ / CT, column tile τ % CT
+    const int w = wave_id();
+    auto ra = [&](int t) { return 16 * ((w * NT1 + t) / CT); };
+    auto cb = [&](int t) { return 16 * ((w * NT1 + t) % CT); };
+    auto rs = [&](int t) { return 16 * ((w * NT2 + t) / CT); };
+    auto cs = [&](int t) { return 16 * ((w * NT2 + t) % CT); };
     for (int ci = nc - 1; ci >= 0; --ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
-        store_state_tile<K>(dh, p.dhs + ((int64_t)cid * HV + j) * K * V, V, c0);
-        rk.commit(kh);
-        rq.commit(qh);
+        StateTileN<K, VW, NTH>::store(dh, p.dhs + ((int64_t)cid * HV + j) * K * V, V, c0);
+        rk.commit(kr);
+        rq.commit(qr);
         rt.commit(Tm);
         rp.commit(Pm);
         ro.commit(dO);
@@ -655,78 +793,77 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_scan_kernel(BwdParams p) {
             bet[threadIdx.x] = rb;
         }
         lds_barrier();
-        if (threadIdx.x < kChunk) {
-            const int r = threadIdx.x;
-            const float d = __expf(gam[r]);
-            sF[r] = r < L ? __expf(gam[L - 1] - gam[r]) : 0.f;
-            sD[r] = scale * d;
-            sB[r] = -bet[r] * d;
+        {
+            constexpr int LPR = NTH / kChunk;   // lanes per row
+            const int r = threadIdx.x / LPR;
+            const float sk = row_sumsq<E, K, NTH>(kr, r), sq = row_sumsq<E, K, NTH>(qr, r);
+            if (threadIdx.x % LPR == 0) {
+                const float fk = p.use_l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
+                const float fq = p.use_l2norm ? 1.f / sqrtf(sq + 1e-6f) : 1.f;
+                const float d = __expf(gam[r]);
+                sFk[r] = r < L ? __expf(gam[L - 1] - gam[r]) * fk : 0.f;
+                sD[r] = scale * d * fq;
+                sB[r] = -bet[r] * d * fk;
+            }
         }
-        norm_rows<K>(kh, fk, p.use_l2norm);   // ends with a barrier
-        norm_rows<K>(qh, fq, p.use_l2norm);
+        lds_barrier();
         if (ci > 0) fetch(ci - 1);
         const float gl = gam[L - 1];
-        // Wave w: rows 16w.. of the 64 x 32 products, row tiles 2w, 2w+1 of the K x 32 state.
-        const int w = wave_id();
-        auto ra = [&](int) { return 16 * w; };
-        auto cb = [&](int t) { return 16 * t; };
-        auto rs = [&](int t) { return 16 * (2 * w + (t >> 1)); };
-        auto cs = [&](int t) { return 16 * (t & 1); };
 
         // dVn = scale Pm^T dO + diag(exp(gamma_L - gamma)) Kh dh'
         {
-            f32x4 a[2], b[2];
+            f32x4 a[NT1], b[NT1];
             zero(a);
             zero(b);
-            wmm<2, kChunk>(a, ra, cb, [&](int r, int m) { return Pm[m * kPadC + r]; },
-                           [&](int c, int m) { return dO[m * kPadT + c]; });
-            wmm<2, K>(b, ra, cb, [&](int r, int m) { return kh[r * (K + 1) + m]; },
-                      [&](int c, int m) { return dh[m * kPadT + c]; });
+            wmm<NT1, kChunk>(a, ra, cb, [&](int r, int m) { return Pm[m * kPadC + r]; },
+                             [&](int c, int m) { return dO[m * VP + c]; });
+            wmm<NT1, K>(b, ra, cb, [&](int r, int m) { return to_f(kr[r * KS + m]); },
+                        [&](int c, int m) { return dh[m * VP + c]; });
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < NT1; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = lrow(16 * w, e), c = lcol(16 * t);
-                    dVn[r * kPadT + c] = scale * a[t][e] + sF[r] * b[t][e];
+                    const int r = lrow(ra(t), e), c = lcol(cb(t));
+                    dVn[r * VP + c] = scale * a[t][e] + sFk[r] * b[t][e];
                 }
         }
         lds_barrier();
         // dB = Tm^T dVn
         {
-            f32x4 a[2];
+            f32x4 a[NT1];
             zero(a);
-            wmm<2, kChunk>(a, ra, cb, [&](int r, int m) { return Tm[m * kPadC + r]; },
-                           [&](int c, int m) { return dVn[m * kPadT + c]; });
+            wmm<NT1, kChunk>(a, ra, cb, [&](int r, int m) { return Tm[m * kPadC + r]; },
+                             [&](int c, int m) { return dVn[m * VP + c]; });
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < NT1; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = lrow(16 * w, e), c = lcol(16 * t);
-                    dB[r * kPadT + c] = a[t][e];
+                    const int r = lrow(ra(t), e), c = lcol(cb(t));
+                    dB[r * VP + c] = a[t][e];
                     if (r < L) p.db[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = a[t][e];
                 }
         }
         lds_barrier();
         // dh <- D_L dh' + scale Qh^T diag(D) dO - Kh^T diag(beta D) dB
         {
-            f32x4 a[4];
+            f32x4 a[NT2];
             zero(a);
-            wmm<4, kChunk>(a, rs, cs, [&](int r, int m) { return qh[m * (K + 1) + r]; },
-                           [&](int c, int m) { return sD[m] * dO[m * kPadT + c]; });
-            wmm<4, kChunk>(a, rs, cs, [&](int r, int m) { return kh[m * (K + 1) + r]; },
-                           [&](int c, int m) { return sB[m] * dB[m * kPadT + c]; });
+            wmm<NT2, kChunk>(a, rs, cs, [&](int r, int m) { return to_f(qr[m * KS + r]); },
+                             [&](int c, int m) { return sD[m] * dO[m * VP + c]; });
+            wmm<NT2, kChunk>(a, rs, cs, [&](int r, int m) { return to_f(kr[m * KS + r]); },
+                             [&](int c, int m) { return sB[m] * dB[m * VP + c]; });
             const float dl = __expf(gl);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < NT2; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float &x = dh[lrow(rs(t), e) * kPadT + lcol(cs(t))];
+                    float &x = dh[lrow(rs(t), e) * VP + lcol(cs(t))];
                     x = fmaf(dl, x, a[t][e]);
                 }
         }
         lds_barrier();
     }
-    if (p.dh0) store_state_tile<K>(dh, p.dh0 + ((int64_t)n * HV + j) * K * V, V, c0);
+    if (p.dh0) StateTileN<K, VW, NTH>::store(dh, p.dh0 + ((int64_t)n * HV + j) * K * V, V, c0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1019,8 +1156,12 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
             hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K>), scan_grid, blk, 0, st, p);
             if (prof) prof->end(kBwdFwdScanKernel, st);
         }
+        // bf16 rows: 64 value columns and 8 waves per workgroup; fp32 rows need
+        // twice the LDS, so 32 columns and 4 waves
+        constexpr bool kB16 = sizeof(E) == 2;
+        constexpr int DVW = kB16 ? 64 : 32, DNTH = kB16 ? 512 : 256;
         if (prof) prof->begin(kBwdDhScanKernel, st);
-        hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K>), scan_grid, blk, 0, st, p);
+        hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K, DVW, DNTH>), dim3(p.N * p.HV, V / DVW), dim3(DNTH), 0, st, p);
         if (prof) prof->end(kBwdDhScanKernel, st);
     }
     if (nc_max > 0) {

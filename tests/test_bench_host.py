@@ -33,6 +33,20 @@ def test_prefill_bytes_and_flops_of_the_gva_workload():
     assert bench.path_flops(w, x) == T_tot * w.HV * (6 * 128 * 128 + 64 * (3 * 128 + 2 * 128))
 
 
+def test_backward_bytes_and_flops_of_the_gva_workload():
+    w = WORKLOADS["gva"]
+    x = {"lens": [w.T] * w.B, "N": w.B, "initial_state": object()}
+    T_tot = w.B * w.T
+    state = w.B * w.HV * w.K * w.V * 4
+    # reads q, k, v, do (bf16), g, beta, the initial state and dht; writes dq, dk, dv, dg, dbeta, dh0
+    reads = 2 * T_tot * w.H * w.K * 2 + 2 * T_tot * w.HV * w.V * 2 + 8 * T_tot * w.HV + 2 * state
+    writes = 2 * T_tot * w.H * w.K * 2 + T_tot * w.HV * w.V * 2 + 8 * T_tot * w.HV + state
+    assert bench.bwd_path_bytes(w, x, 2) == reads + writes == 704643072
+    # 16 K V + 6 C K + 5 C V + C^2 / 3 flops per token and value head, C = 64
+    per_tok = 16 * 128 * 128 + 6 * 64 * 128 + 5 * 64 * 128 + 64 * 64 / 3
+    assert bench.bwd_path_flops(w, x) == int(T_tot * w.HV * per_tok) == 185399421610
+
+
 def test_decode_bytes():
     w = DECODE_WORKLOADS["decode"]
     assert bench.decode_bytes(w, 248, 2) == 1046412288
