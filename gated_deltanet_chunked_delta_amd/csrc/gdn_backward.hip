@@ -65,10 +65,6 @@ constexpr int prep_q_floats() {   // the q rows, then A [64][65] and Tm [64][64]
 }
 template <int K>
 constexpr int prep_floats() { return kChunk * (K + 1) + prep_q_floats<K>() + 4 * kChunk; }
-template <int K>
-constexpr int fwd_scan_floats() { return K * kPadT + kChunk * (K + 1) + kChunk * kPadC + kChunk * kPadT + 5 * kChunk; }
-// two forward-scan workgroups share a CU (160 KB of LDS)
-static_assert(fwd_scan_floats<128>() * 4 <= 80 * 1024, "forward scan must fit twice per CU");
 // grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the three
 // 64 x 65 matrices of the second phase reuse their space.
 template <int K>
@@ -583,39 +579,53 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// forward over chunks per (sequence, value head, 32 value columns): h, Vn
+// forward over chunks per (sequence, value head, VW value columns), NTH
+// threads: the chunk-start states h and Vn.  The key rows stay raw in LDS;
+// their L2 norms enter as the row scales sD and sFk.
 // ---------------------------------------------------------------------------
-template <typename E, int K>
-__global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
-    __shared__ float sm[fwd_scan_floats<K>()];
-    float *h = sm;                           // [K][33]
-    float *kh = h + K * kPadT;               // [64][K+1]
-    float *Tm = kh + kChunk * (K + 1);       // [64][65]
-    float *vv = Tm + kChunk * kPadC;         // [64][33]: v, then B (in place), then F
-    float *gam = vv + kChunk * kPadT;        // [64]
+template <typename E, int K, int VW>
+constexpr int fwd_scan_floats() {
+    return K * (VW + 1) + kChunk * kPadC + kChunk * (VW + 1) + 5 * kChunk +
+           (kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4;
+}
+// fp32 rows: two workgroups share a CU (160 KB of LDS)
+static_assert(fwd_scan_floats<float, 128, 32>() * 4 <= 80 * 1024, "fp32 forward scan must fit twice per CU");
+static_assert(fwd_scan_floats<bf16, 128, 64>() * 4 <= 160 * 1024, "bf16 forward scan must fit one CU");
+
+template <typename E, int K, int VW, int NTH>
+__global__ __launch_bounds__(NTH) void bwd_fwd_scan_kernel(BwdParams p) {
+    constexpr int VP = VW + 1, KS = K + RowPad<E>::v, W = NTH / 64, CT = VW / 16;
+    constexpr int NT1 = 4 * CT / W;          // 16 x 16 tiles of a 64 x VW product per wave
+    constexpr int NT2 = (K / 16) * CT / W;   // tiles of the K x VW state per wave
+    static_assert(NT1 >= 1 && NT2 >= 1, "every wave needs a tile");
+    __shared__ float sm[fwd_scan_floats<E, K, VW>()];
+    float *h = sm;                           // [K][VP]
+    float *Tm = h + K * VP;                  // [64][65]
+    float *vv = Tm + kChunk * kPadC;         // [64][VP]: v, then B (in place), then F / |k|
+    float *gam = vv + kChunk * VP;           // [64]
     float *bet = gam + kChunk;               // [64]
-    float *fk = bet + kChunk;                // [64]
-    float *sD = fk + kChunk;                 // [64] exp(gamma)
+    float *sD = bet + kChunk;                // [64] exp(gamma) / |k|
     float *sF = sD + kChunk;                 // [64] exp(gamma_L - gamma), 0 past L
+    float *sFk = sF + kChunk;                // [64] exp(gamma_L - gamma) / |k|, 0 past L
+    E *kr = (E *)(sFk + kChunk);             // [64][KS] raw k rows
 
     const int HV = p.HV, V = p.V;
     const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
-    const int c0 = blockIdx.y * kVT;
+    const int c0 = blockIdx.y * VW;
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
     const int nc = (len + kChunk - 1) / kChunk;
 
     if (p.initial_state) {
-        StateTileReg<K> r0;
+        StateTileN<K, VW, NTH> r0;
         r0.load(p.initial_state + ((int64_t)n * HV + j) * K * V, V, c0);
         r0.commit(h);
     } else {
-        for (int e = threadIdx.x; e < K * kVT; e += kThreads) h[(e / kVT) * kPadT + e % kVT] = 0.f;
+        for (int e = threadIdx.x; e < K * VW; e += NTH) h[(e / VW) * VP + e % VW] = 0.f;
     }
-    __syncthreads();
-    RowsReg<E, K> rk;
-    Mat64Reg rt;
-    TileReg<E> rv;
+    RawRowsReg<E, K, NTH> rk;
+    Mat64RegN<NTH> rt;
+    TileRegN<E, VW, NTH> rv;
     float rg = 0.f, rb = 0.f;
     auto fetch = [&](int ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
@@ -629,10 +639,16 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
         }
     };
     if (nc > 0) fetch(0);
+    lds_barrier();
+    const int w = wave_id();
+    auto ra = [&](int t) { return 16 * ((w * NT1 + t) / CT); };
+    auto cb = [&](int t) { return 16 * ((w * NT1 + t) % CT); };
+    auto rs = [&](int t) { return 16 * ((w * NT2 + t) / CT); };
+    auto cs = [&](int t) { return 16 * ((w * NT2 + t) % CT); };
     for (int ci = 0; ci < nc; ++ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
-        store_state_tile<K>(h, p.hs + ((int64_t)cid * HV + j) * K * V, V, c0);
-        rk.commit(kh);
+        StateTileN<K, VW, NTH>::store(h, p.hs + ((int64_t)cid * HV + j) * K * V, V, c0);
+        rk.commit(kr);
         rt.commit(Tm);
         rv.commit(vv);
         if (threadIdx.x < kChunk) {
@@ -640,64 +656,65 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd_scan_kernel(BwdParams p) {
             bet[threadIdx.x] = rb;
         }
         lds_barrier();
-        if (threadIdx.x < kChunk) {
-            const int r = threadIdx.x;
-            sD[r] = __expf(gam[r]);
-            sF[r] = r < L ? __expf(gam[L - 1] - gam[r]) : 0.f;
+        {
+            constexpr int LPR = NTH / kChunk;   // lanes per row
+            const int r = threadIdx.x / LPR;
+            const float sk = row_sumsq<E, K, NTH>(kr, r);
+            if (threadIdx.x % LPR == 0) {
+                const float fk = p.use_l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
+                const float f = r < L ? __expf(gam[L - 1] - gam[r]) : 0.f;
+                sD[r] = __expf(gam[r]) * fk;
+                sF[r] = f;
+                sFk[r] = f * fk;
+            }
         }
-        norm_rows<K>(kh, fk, p.use_l2norm);   // ends with a barrier
+        lds_barrier();
         if (ci + 1 < nc) fetch(ci + 1);
 
-        // Wave w: rows 16w.. of the 64 x 32 products, row tiles 2w, 2w+1 of the K x 32 state.
-        const int w = wave_id();
-        auto ra = [&](int) { return 16 * w; };
-        auto cb = [&](int t) { return 16 * t; };
-        auto rs = [&](int t) { return 16 * (2 * w + (t >> 1)); };
-        auto cs = [&](int t) { return 16 * (t & 1); };
-        // B = diag(beta) (V - diag(D) Kh h)
+        // B = diag(beta) (V - diag(D) Kh h), in place over v
         {
-            f32x4 x[2];
+            f32x4 x[NT1];
             zero(x);
-            wmm<2, K>(x, ra, cb, [&](int r, int m) { return kh[r * (K + 1) + m]; },
-                      [&](int c, int m) { return h[m * kPadT + c]; });
+            wmm<NT1, K>(x, ra, cb, [&](int r, int m) { return to_f(kr[r * KS + m]); },
+                        [&](int c, int m) { return h[m * VP + c]; });
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < NT1; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = lrow(16 * w, e), c = lcol(16 * t);
-                    vv[r * kPadT + c] = bet[r] * (vv[r * kPadT + c] - sD[r] * x[t][e]);
+                    const int r = lrow(ra(t), e), c = lcol(cb(t));
+                    vv[r * VP + c] = bet[r] * (vv[r * VP + c] - sD[r] * x[t][e]);
                 }
         }
         lds_barrier();
-        // Vn = Tm B; F = diag(exp(gamma_L - gamma)) Vn into vv once every wave has read B
+        // Vn = Tm B; then, once every wave has read B, diag(exp(gamma_L - gamma) / |k|) Vn into vv
         {
-            f32x4 x[2];
+            f32x4 x[NT1];
             zero(x);
-            wmm<2, kChunk>(x, ra, cb, [&](int r, int m) { return Tm[r * kPadC + m]; },
-                           [&](int c, int m) { return vv[m * kPadT + c]; });
+            wmm<NT1, kChunk>(x, ra, cb, [&](int r, int m) { return Tm[r * kPadC + m]; },
+                             [&](int c, int m) { return vv[m * VP + c]; });
             lds_barrier();
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < NT1; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = lrow(16 * w, e), c = lcol(16 * t);
+                    const int r = lrow(ra(t), e), c = lcol(cb(t));
                     if (r < L) p.vn[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = x[t][e];
-                    vv[r * kPadT + c] = sF[r] * x[t][e];
+                    vv[r * VP + c] = sFk[r] * x[t][e];
                 }
         }
         lds_barrier();
         // h <- D_L h + Kh^T F
         {
-            f32x4 x[4];
+            f32x4 x[NT2];
             zero(x);
-            wmm<4, kChunk>(x, rs, cs, [&](int r, int m) { return kh[m * (K + 1) + r]; },
-                           [&](int c, int m) { return vv[m * kPadT + c]; });
+            wmm<NT2, kChunk>(x, rs, cs, [&](int r, int m) { return to_f(kr[m * KS + r]); },
+                             [&](int c, int m) { return vv[m * VP + c]; });
             const float dl = __expf(gam[L - 1]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < NT2; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float &hv = h[lrow(rs(t), e) * kPadT + lcol(cs(t))];
+                    float &hv = h[lrow(rs(t), e) * VP + lcol(cs(t))];
                     hv = fmaf(dl, hv, x[t][e]);
                 }
         }
@@ -1150,10 +1167,11 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
         if (prof) prof->end(kBwdPrepKernel, st);
     }
     if (p.N > 0) {
-        const dim3 scan_grid(p.N * p.HV, V / kVT);
         if (nc_max > 0) {
+            constexpr int FVW = sizeof(E) == 2 ? 64 : 32, FNTH = sizeof(E) == 2 ? 512 : 256;
             if (prof) prof->begin(kBwdFwdScanKernel, st);
-            hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K>), scan_grid, blk, 0, st, p);
+            hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, FVW, FNTH>), dim3(p.N * p.HV, V / FVW), dim3(FNTH), 0, st,
+                               p);
             if (prof) prof->end(kBwdFwdScanKernel, st);
         }
         // bf16 rows: 64 value columns and 8 waves per workgroup; fp32 rows need
