@@ -70,8 +70,6 @@ constexpr int prep_floats() { return kChunk * (K + 1) + prep_q_floats<K>() + 4 *
 template <int K>
 constexpr int grads_tile_floats() { return 2 * K * kPadT + 4 * kChunk * kPadT; }
 static_assert(grads_tile_floats<64>() >= 3 * kChunk * kPadC, "phase-2 matrices must fit in the tile region");
-template <int K>
-constexpr int grads_floats() { return 2 * kChunk * (K + 1) + grads_tile_floats<K>() + 6 * kChunk + 20; }
 
 // Products on the matrix cores: 16 x 16 fp32 tiles by v_mfma_f32_16x16x4f32
 // (fp32 operands, fp32 accumulation, so the pass keeps fp32 accuracy).
@@ -884,14 +882,41 @@ __global__ __launch_bounds__(NTH) void bwd_dh_scan_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// per (chunk, value head): dq, dk (per value head), dv, dg, dbeta
+// per (chunk, value head): dq, dk (per value head), dv, dg, dbeta.  512
+// threads: wave w holds rows 16 (w & 3).. and column half w >> 2 of every
+// 64 x 64 and 64 x K product; the row sums of the two halves meet in LDS.
+// The key and query rows stay raw in LDS and their L2 norms enter as scales.
 // ---------------------------------------------------------------------------
+constexpr int kGThreads = 512;
+// Rows t0..t0+L-1 (zero past L), 32 columns from c0, of a [T_tot, HV, V]
+// tensor at value head j, into dst[64][33] as fp32: four elements per thread.
+template <typename E>
+struct Tile4Reg {
+    typename VT<E>::v4 v;
+    __device__ __forceinline__ void load(const E *src, int t0, int L, int HV, int j, int V, int c0) {
+        const int r = threadIdx.x >> 3, c = (threadIdx.x & 7) * 4;
+        if (r < L) v = *(const typename VT<E>::v4 *)(src + ((int64_t)(t0 + r) * HV + j) * V + c0 + c);
+        else
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = to_e<E>(0.f);
+    }
+    __device__ __forceinline__ void commit(float *dst) const {
+        const int r = threadIdx.x >> 3, c = (threadIdx.x & 7) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[r * kPadT + c + e] = to_f(v[e]);
+    }
+};
+template <typename E, int K>
+constexpr int grads_floats() {
+    return grads_tile_floats<K>() + 17 * kChunk + 8 + (2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4;
+}
+static_assert(grads_floats<float, 128>() * 4 <= 160 * 1024, "fp32 grads must fit one CU");
+
 template <typename E, int K, int V>
-__global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
-    __shared__ float sm[grads_floats<K>()];
-    float *kh = sm;                          // [64][K+1]
-    float *qh = kh + kChunk * (K + 1);       // [64][K+1]
-    float *tile = qh + kChunk * (K + 1);     // per value tile, then the 64 x 64 matrices
+__global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
+    constexpr int KS = K + RowPad<E>::v, KR = K / 16, NTK = KR / 2;
+    __shared__ float sm[grads_floats<E, K>()];
+    float *tile = sm;                        // per value tile, then the 64 x 64 matrices
     float *hT = tile;                        // [K][33]
     float *dhT = hT + K * kPadT;             // [K][33]
     float *vnT = dhT + K * kPadT;            // [64][33]
@@ -904,22 +929,25 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
     float *rows = tile + grads_tile_floats<K>();   // scalars per row
     float *gam = rows;                       // [64]
     float *bet = gam + kChunk;               // [64]
-    float *fk = bet + kChunk;                // [64]
-    float *fq = fk + kChunk;                 // [64]
-    float *dgam = fq + kChunk;               // [64]
-    float *dbet = dgam + kChunk;             // [64]
-    float *red = dbet + kChunk;              // [kThreads / 64] block reduction slots
+    float *fk = bet + kChunk;                // [64] 1 / |k|
+    float *fq = fk + kChunk;                 // [64] 1 / |q|
+    float *sbvA = fq + kChunk;               // [64] sum_v dB v
+    float *pt = sbvA + kChunk;               // [5][2][64] per column half: q.dQ, k.E, k.F, dA.A, k.dK
+    float *psq = pt + 10 * kChunk;           // [2][64] q.dQ after the second phase
+    float *red = psq + 2 * kChunk;           // [8] <dh', h> per wave
+    E *kr = (E *)(red + 8);                  // [64][KS] raw k rows
+    static_assert(5 + 10 + 2 == 17, "row arrays of grads_floats");
+    E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
 
     ChunkRef cr;
     if (!find_chunk(p, blockIdx.x, cr)) return;
     const int j = blockIdx.y, HV = p.HV, jk = j / (HV / p.H);
     const int cid = blockIdx.x, L = cr.L, t0 = cr.t0;
     const float scale = p.scale;
-    constexpr int KR = K / 16;
-    // Wave w holds rows 16w..16w+15 of every 64 x 64 and 64 x K product.
-    const int w = wave_id(), lane16 = threadIdx.x & 15;
-    auto ra = [&](int) { return 16 * w; };
-    auto cb = [&](int t) { return 16 * t; };
+    const int w = wave_id(), rb = w & 3, hf = w >> 2, lane16 = threadIdx.x & 15;
+    auto ra = [&](int) { return 16 * rb; };
+    auto cbP = [&](int t) { return 16 * (2 * hf + t); };
+    auto cbK = [&](int t) { return 16 * (hf * NTK + t); };
 
     if (threadIdx.x < kChunk) {
         const int r = threadIdx.x;
@@ -928,9 +956,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
     }
     const float *hs = p.hs + ((int64_t)cid * HV + j) * K * V;
     const float *dhs = p.dhs + ((int64_t)cid * HV + j) * K * V;
-    StateTileReg<K> th, tdh;
-    TileReg<float> tvn, tdb;
-    TileReg<E> tdo, tv;
+    StateTileN<K, kVT, kGThreads> th, tdh;
+    Tile4Reg<float> tvn, tdb;
+    Tile4Reg<E> tdo, tv;
     auto fetch = [&](int c0) {
         th.load(hs, V, c0);
         tdh.load(dhs, V, c0);
@@ -940,25 +968,32 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
         tv.load((const E *)p.v, t0, L, HV, j, V, c0);
     };
     {
-        RowsReg<E, K> rk, rq;
+        RawRowsReg<E, K, kGThreads> rk, rq;
         rk.load((const E *)p.k, t0, L, p.H, jk);
         rq.load((const E *)p.q, t0, L, p.H, jk);
         fetch(0);
-        rk.commit(kh);
-        rq.commit(qh);
+        rk.commit(kr);
+        rq.commit(qr);
     }
     lds_barrier();
-    norm_rows<K>(kh, fk, p.use_l2norm);
-    norm_rows<K>(qh, fq, p.use_l2norm);
+    {
+        constexpr int LPR = kGThreads / kChunk;
+        const int r = threadIdx.x / LPR;
+        const float sk = row_sumsq<E, K, kGThreads>(kr, r), sq = row_sumsq<E, K, kGThreads>(qr, r);
+        if (threadIdx.x % LPR == 0) {
+            fk[r] = p.use_l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
+            fq[r] = p.use_l2norm ? 1.f / sqrtf(sq + 1e-6f) : 1.f;
+        }
+    }
 
-    f32x4 aP[4], aA[4], dQ[KR], aE[KR], aF[KR];
+    f32x4 aP[2], aA[2], dQ[NTK], aE[NTK], aF[NTK];
     zero(aP);
     zero(aA);
     zero(dQ);
     zero(aE);
     zero(aF);
     float sdh = 0.f;      // this thread's part of <dh', h>
-    float sbv = 0.f;      // row (threadIdx.x >> 2): sum_v dB v
+    float sbv = 0.f;      // row (threadIdx.x >> 3): sum_v dB v
     for (int c0 = 0; c0 < V; c0 += kVT) {
         th.commit(hT);
         tdh.commit(dhT);
@@ -969,89 +1004,91 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
         lds_barrier();
         if (c0 + kVT < V) fetch(c0 + kVT);
         // this thread's part of <dh', h>: the elements it wrote
-        {
-            constexpr int N4 = K * kVT / 4 / kThreads;
 #pragma unroll
-            for (int u = 0; u < N4; ++u) {
-                const int i = threadIdx.x + kThreads * u, r = i >> 3, c = (i & 7) * 4;
+        for (int u = 0; u < StateTileN<K, kVT, kGThreads>::N4; ++u) {
+            const int i = threadIdx.x + kGThreads * u, r = i >> 3, c = (i & 7) * 4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sdh = fmaf(hT[r * kPadT + c + e], dhT[r * kPadT + c + e], sdh);
-            }
+            for (int e = 0; e < 4; ++e) sdh = fmaf(hT[r * kPadT + c + e], dhT[r * kPadT + c + e], sdh);
         }
         {
-            const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+            const int r = threadIdx.x >> 3, c = (threadIdx.x & 7) * 4;
             float s = 0.f;
-            for (int c = part; c < kVT; c += 4) s = fmaf(dbT[r * kPadT + c], vvT[r * kPadT + c], s);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s = fmaf(dbT[r * kPadT + c + e], vvT[r * kPadT + c + e], s);
             s += __shfl_xor(s, 1);
             s += __shfl_xor(s, 2);
+            s += __shfl_xor(s, 4);
             sbv += s;
-            if (r < L)
-                for (int c = part; c < kVT; c += 4)
-                    ((E *)p.dv)[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = to_e<E>(bet[r] * dbT[r * kPadT + c]);
+            if (r < L) {
+                typename VT<E>::v4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = to_e<E>(bet[r] * dbT[r * kPadT + c + e]);
+                *(typename VT<E>::v4 *)((E *)p.dv + ((int64_t)(t0 + r) * HV + j) * V + c0 + c) = o;
+            }
         }
-        wmm<4, kVT>(aP, ra, cb, [&](int r, int m) { return doT[r * kPadT + m]; },
+        wmm<2, kVT>(aP, ra, cbP, [&](int r, int m) { return doT[r * kPadT + m]; },
                     [&](int c, int m) { return vnT[c * kPadT + m]; });
-        wmm<4, kVT>(aA, ra, cb, [&](int r, int m) { return dbT[r * kPadT + m]; },
+        wmm<2, kVT>(aA, ra, cbP, [&](int r, int m) { return dbT[r * kPadT + m]; },
                     [&](int c, int m) { return vnT[c * kPadT + m]; });
-        wmm<KR, kVT>(dQ, ra, cb, [&](int r, int m) { return doT[r * kPadT + m]; },
-                     [&](int c, int m) { return hT[c * kPadT + m]; });
-        wmm<KR, kVT>(aE, ra, cb, [&](int r, int m) { return dbT[r * kPadT + m]; },
-                     [&](int c, int m) { return hT[c * kPadT + m]; });
-        wmm<KR, kVT>(aF, ra, cb, [&](int r, int m) { return vnT[r * kPadT + m]; },
-                     [&](int c, int m) { return dhT[c * kPadT + m]; });
+        wmm<NTK, kVT>(dQ, ra, cbK, [&](int r, int m) { return doT[r * kPadT + m]; },
+                      [&](int c, int m) { return hT[c * kPadT + m]; });
+        wmm<NTK, kVT>(aE, ra, cbK, [&](int r, int m) { return dbT[r * kPadT + m]; },
+                      [&](int c, int m) { return hT[c * kPadT + m]; });
+        wmm<NTK, kVT>(aF, ra, cbK, [&](int r, int m) { return vnT[r * kPadT + m]; },
+                      [&](int c, int m) { return dhT[c * kPadT + m]; });
         lds_barrier();
     }
 
-    // <dh', h> over the block
+    // <dh', h> per wave; sum_v dB v per row
     {
         float s = sdh;
         for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+        if ((threadIdx.x & 63) == 0) red[w] = s;
+        if ((threadIdx.x & 7) == 0) sbvA[threadIdx.x >> 3] = sbv;
     }
     const float gl = gam[L - 1];
-    // row scalings and the row dot products with qh / kh
-    float t3sum = 0.f;
+    // row scalings and this half's row dot products with the raw q / k rows
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int r = lrow(16 * w, e);
+        const int r = lrow(16 * rb, e);
         const float d = __expf(gam[r]);
         const float f = r < L ? __expf(gl - gam[r]) : 0.f;
         float t1 = 0.f, t2 = 0.f, t3 = 0.f;
 #pragma unroll
-        for (int t = 0; t < KR; ++t) {
-            const int col = lcol(16 * t);
+        for (int t = 0; t < NTK; ++t) {
+            const int col = lcol(cbK(t));
             dQ[t][e] *= scale * d;
             aE[t][e] *= d;
             aF[t][e] *= f;
-            t1 = fmaf(qh[r * (K + 1) + col], dQ[t][e], t1);
-            t2 = fmaf(kh[r * (K + 1) + col], aE[t][e], t2);
-            t3 = fmaf(kh[r * (K + 1) + col], aF[t][e], t3);
+            t1 = fmaf(to_f(qr[r * KS + col]), dQ[t][e], t1);
+            t2 = fmaf(to_f(kr[r * KS + col]), aE[t][e], t2);
+            t3 = fmaf(to_f(kr[r * KS + col]), aF[t][e], t3);
         }
         t1 = sum16(t1);
         t2 = sum16(t2);
         t3 = sum16(t3);
-        t3sum += t3;
         if (lane16 == 0) {
-            dgam[r] = t1 - bet[r] * t2 - t3;
-            dbet[r] = -t2;
+            pt[(0 * 2 + hf) * kChunk + r] = t1;
+            pt[(1 * 2 + hf) * kChunk + r] = t2;
+            pt[(2 * 2 + hf) * kChunk + r] = t3;
         }
     }
     // dK so far: F dh'^T - diag(beta) E
-    f32x4 dK[KR];
+    f32x4 dK[NTK];
 #pragma unroll
-    for (int t = 0; t < KR; ++t)
+    for (int t = 0; t < NTK; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dK[t][e] = aF[t][e] - bet[lrow(16 * w, e)] * aE[t][e];
+        for (int e = 0; e < 4; ++e) dK[t][e] = aF[t][e] - bet[lrow(16 * rb, e)] * aE[t][e];
 
     // the 64 x 64 matrices: dSqk, Ad and Z = dSqk * (qh . kh) + dA * A
     const float *pm = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
     const float *ag = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
     float dbA[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = lrow(16 * w, e), c = lcol(16 * t);
+            const int r = lrow(16 * rb, e), c = lcol(cbP(t));
             const bool low = c <= r && r < L;
             const float d = low ? __expf(gam[r] - gam[c]) : 0.f;
             const float dpm = scale * aP[t][e];
@@ -1067,69 +1104,84 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float s = sum16(dbA[e]);
-        if (lane16 == 0) dbet[lrow(16 * w, e)] += s;
+        if (lane16 == 0) pt[(3 * 2 + hf) * kChunk + lrow(16 * rb, e)] = s;
     }
     lds_barrier();
+    // wave 0: dgamma, dbeta per row (lane = row), then dg by a reverse cumsum over the lanes
     if (threadIdx.x < kChunk) {
         const int r = threadIdx.x;
+        const float t1 = fq[r] * (pt[0 * kChunk + r] + pt[1 * kChunk + r]);
+        const float t2 = fk[r] * (pt[2 * kChunk + r] + pt[3 * kChunk + r]);
+        const float t3 = fk[r] * (pt[4 * kChunk + r] + pt[5 * kChunk + r]);
         float rs = 0.f, cs = 0.f;
         for (int m = 0; m < kChunk; ++m) {
             rs += Zm[r * kPadC + m];
             cs += Zm[m * kPadC + r];
         }
-        dgam[r] += rs - cs;
-    }
-    if ((threadIdx.x & 3) == 0) dbet[threadIdx.x >> 2] += sbv;
-    if (lane16 == 0) red[4 + (threadIdx.x >> 4)] = t3sum;
-    lds_barrier();
-    if (threadIdx.x == 0) {
-        float s = red[0] + red[1] + red[2] + red[3];
-        float t = 0.f;
-        for (int y = 0; y < 16; ++y) t += red[4 + y];
-        dgam[L - 1] += __expf(gl) * s + t;
+        float t3all = t3;
+        for (int o = 32; o >= 1; o >>= 1) t3all += __shfl_xor(t3all, o);
+        float sdh_all = 0.f;
+#pragma unroll
+        for (int u = 0; u < kGThreads / 64; ++u) sdh_all += red[u];
+        float dgr = t1 - bet[r] * t2 - t3 + rs - cs;
+        if (r == L - 1) dgr += __expf(gl) * sdh_all + t3all;
+        const float dbr = -t2 + pt[6 * kChunk + r] + pt[7 * kChunk + r] + sbvA[r];
+        float x = r < L ? dgr : 0.f;
+#pragma unroll
+        for (int o = 1; o < kChunk; o <<= 1) {
+            const float y = __shfl_down(x, o);
+            if (r + o < kChunk) x += y;
+        }
+        if (r < L) {
+            p.dg[(int64_t)(t0 + r) * HV + j] = x;
+            p.dbeta[(int64_t)(t0 + r) * HV + j] = dbr;
+        }
     }
 
-    // dQ += dSqk Kh;  dK += dSqk^T Qh + (Ad + Ad^T) Kh
-    wmm<KR, kChunk>(dQ, ra, cb, [&](int r, int m) { return dS[r * kPadC + m]; },
-                    [&](int c, int m) { return kh[m * (K + 1) + c]; });
-    wmm<KR, kChunk>(dK, ra, cb, [&](int r, int m) { return dS[m * kPadC + r]; },
-                    [&](int c, int m) { return qh[m * (K + 1) + c]; });
-    wmm<KR, kChunk>(dK, ra, cb, [&](int r, int m) { return Ad[r * kPadC + m] + Ad[m * kPadC + r]; },
-                    [&](int c, int m) { return kh[m * (K + 1) + c]; });
+    // dQ += dSqk Kh;  dK += dSqk^T Qh + (Ad + Ad^T) Kh   (Kh = diag(fk) K, Qh = diag(fq) Q)
+    wmm<NTK, kChunk>(dQ, ra, cbK, [&](int r, int m) { return dS[r * kPadC + m]; },
+                     [&](int c, int m) { return fk[m] * to_f(kr[m * KS + c]); });
+    wmm<NTK, kChunk>(dK, ra, cbK, [&](int r, int m) { return dS[m * kPadC + r]; },
+                     [&](int c, int m) { return fq[m] * to_f(qr[m * KS + c]); });
+    wmm<NTK, kChunk>(dK, ra, cbK, [&](int r, int m) { return Ad[r * kPadC + m] + Ad[m * kPadC + r]; },
+                     [&](int c, int m) { return fk[m] * to_f(kr[m * KS + c]); });
 
-    // L2-norm backward and the per-value-head partial dq, dk
+    // L2-norm backward and the per-value-head partial dq, dk: the row dot
+    // products qh . dQ and kh . dK meet across the two column halves
+    if (p.use_l2norm) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int r = lrow(16 * w, e);
-        float sq = 0.f, sk = 0.f;
-        if (p.use_l2norm) {
+        for (int e = 0; e < 4; ++e) {
+            const int r = lrow(16 * rb, e);
+            float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int t = 0; t < KR; ++t) {
-                sq = fmaf(qh[r * (K + 1) + lcol(16 * t)], dQ[t][e], sq);
-                sk = fmaf(kh[r * (K + 1) + lcol(16 * t)], dK[t][e], sk);
+            for (int t = 0; t < NTK; ++t) {
+                sq = fmaf(to_f(qr[r * KS + lcol(cbK(t))]), dQ[t][e], sq);
+                sk = fmaf(to_f(kr[r * KS + lcol(cbK(t))]), dK[t][e], sk);
             }
             sq = sum16(sq);
             sk = sum16(sk);
+            if (lane16 == 0) {
+                psq[hf * kChunk + r] = sq;
+                pt[(8 + hf) * kChunk + r] = sk;
+            }
         }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = lrow(16 * rb, e);
+        const float sq = p.use_l2norm ? fq[r] * (psq[r] + psq[kChunk + r]) : 0.f;
+        const float sk = p.use_l2norm ? fk[r] * (pt[8 * kChunk + r] + pt[9 * kChunk + r]) : 0.f;
         if (r < L) {
             float *dq = p.dqp + ((int64_t)(t0 + r) * HV + j) * K;
             float *dk = p.dkp + ((int64_t)(t0 + r) * HV + j) * K;
 #pragma unroll
-            for (int t = 0; t < KR; ++t) {
-                const int col = lcol(16 * t);
-                dq[col] = fq[r] * (dQ[t][e] - qh[r * (K + 1) + col] * sq);
-                dk[col] = fk[r] * (dK[t][e] - kh[r * (K + 1) + col] * sk);
+            for (int t = 0; t < NTK; ++t) {
+                const int col = lcol(cbK(t));
+                dq[col] = fq[r] * (dQ[t][e] - fq[r] * to_f(qr[r * KS + col]) * sq);
+                dk[col] = fk[r] * (dK[t][e] - fk[r] * to_f(kr[r * KS + col]) * sk);
             }
         }
-    }
-    lds_barrier();
-    // dg = reverse cumsum of dgamma inside the chunk; dbeta
-    if (threadIdx.x < L) {
-        const int r = threadIdx.x;
-        float s = 0.f;
-        for (int m = r; m < L; ++m) s += dgam[m];
-        p.dg[(int64_t)(t0 + r) * HV + j] = s;
-        p.dbeta[(int64_t)(t0 + r) * HV + j] = dbet[r];
     }
 }
 
@@ -1184,7 +1236,7 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
     }
     if (nc_max > 0) {
         if (prof) prof->begin(kBwdGradsKernel, st);
-        hipLaunchKernelGGL((bwd_grads_kernel<E, K, V>), dim3(nc_max, p.HV), blk, 0, st, p);
+        hipLaunchKernelGGL((bwd_grads_kernel<E, K, V>), dim3(nc_max, p.HV), dim3(kGThreads), 0, st, p);
         if (prof) prof->end(kBwdGradsKernel, st);
         const int64_t total = (int64_t)p.T_tot * p.H * K;
         if (total > 0) {
