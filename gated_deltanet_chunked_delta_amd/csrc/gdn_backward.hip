@@ -108,6 +108,38 @@ __device__ __forceinline__ void wmm(f32x4 (&acc)[NT], RA ra, CB cb, FA fa, FB fb
     }
 }
 
+// Two products that share the second operand:
+//   acc1[t] += sum_m fa1(ra(t) + (l & 15), m) fb(cb(t) + (l & 15), m), acc2 likewise with fa2.
+template <int NT, int KD, typename RA, typename CB, typename FA1, typename FA2, typename FB>
+__device__ __forceinline__ void wmm2(f32x4 (&acc1)[NT], f32x4 (&acc2)[NT], RA ra, CB cb, FA1 fa1, FA2 fa2, FB fb) {
+    constexpr int S = KD / 4;
+    constexpr int G0 = NT >= 4 ? 4 : 8;
+    constexpr int G = S <= G0 ? S : (S % G0 == 0 ? G0 : (S % 4 == 0 ? 4 : 1));
+    static_assert(S % G == 0, "k-steps must split into whole groups");
+    const int i = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
+#pragma unroll 1
+    for (int g = 0; g < S; g += G) {
+        float a1[G][NT], a2[G][NT], bv[G][NT];
+#pragma unroll
+        for (int s = 0; s < G; ++s) {
+            const int m = q * S + g + s;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                a1[s][t] = fa1(ra(t) + i, m);
+                a2[s][t] = fa2(ra(t) + i, m);
+                bv[s][t] = fb(cb(t) + i, m);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < G; ++s)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc1[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[s][t], bv[s][t], acc1[t], 0, 0, 0);
+                acc2[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[s][t], bv[s][t], acc2[t], 0, 0, 0);
+            }
+    }
+}
+
 template <int NT>
 __device__ __forceinline__ void zero(f32x4 (&acc)[NT]) {
 #pragma unroll
@@ -1026,14 +1058,12 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
                 *(typename VT<E>::v4 *)((E *)p.dv + ((int64_t)(t0 + r) * HV + j) * V + c0 + c) = o;
             }
         }
-        wmm<2, kVT>(aP, ra, cbP, [&](int r, int m) { return doT[r * kPadT + m]; },
-                    [&](int c, int m) { return vnT[c * kPadT + m]; });
-        wmm<2, kVT>(aA, ra, cbP, [&](int r, int m) { return dbT[r * kPadT + m]; },
-                    [&](int c, int m) { return vnT[c * kPadT + m]; });
-        wmm<NTK, kVT>(dQ, ra, cbK, [&](int r, int m) { return doT[r * kPadT + m]; },
-                      [&](int c, int m) { return hT[c * kPadT + m]; });
-        wmm<NTK, kVT>(aE, ra, cbK, [&](int r, int m) { return dbT[r * kPadT + m]; },
-                      [&](int c, int m) { return hT[c * kPadT + m]; });
+        wmm2<2, kVT>(aP, aA, ra, cbP, [&](int r, int m) { return doT[r * kPadT + m]; },
+                     [&](int r, int m) { return dbT[r * kPadT + m]; },
+                     [&](int c, int m) { return vnT[c * kPadT + m]; });
+        wmm2<NTK, kVT>(dQ, aE, ra, cbK, [&](int r, int m) { return doT[r * kPadT + m]; },
+                       [&](int r, int m) { return dbT[r * kPadT + m]; },
+                       [&](int c, int m) { return hT[c * kPadT + m]; });
         wmm<NTK, kVT>(aF, ra, cbK, [&](int r, int m) { return vnT[r * kPadT + m]; },
                       [&](int c, int m) { return dhT[c * kPadT + m]; });
         lds_barrier();
@@ -1185,24 +1215,32 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
     }
 }
 
-// dq, dk [T_tot, H, K] = sum over the G value heads of each key head
+// dq, dk [T_tot, H, K] = sum over the G value heads of each key head; four
+// consecutive elements per thread (K is a multiple of 4)
 template <typename E>
 __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const float *dqp, const float *dkp, E *dq, E *dk,
-                                                             int64_t total, int H, int G, int K) {
-    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (e >= total) return;
+                                                             int64_t total4, int H, int G, int K) {
+    const int64_t e4 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e4 >= total4) return;
+    const int64_t e = 4 * e4;
     const int64_t row = e / K;   // t * H + jk
     const int c = (int)(e - row * K);
     const int64_t t = row / H;
     const int jk = (int)(row - t * H);
-    float sq = 0.f, sk = 0.f;
+    f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
     for (int g = 0; g < G; ++g) {
         const int64_t at = (t * (int64_t)H * G + (int64_t)jk * G + g) * K + c;
-        sq += dqp[at];
-        sk += dkp[at];
+        sq += *(const f32x4 *)(dqp + at);
+        sk += *(const f32x4 *)(dkp + at);
     }
-    dq[e] = to_e<E>(sq);
-    dk[e] = to_e<E>(sk);
+    typename VT<E>::v4 oq, ok;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        oq[u] = to_e<E>(sq[u]);
+        ok[u] = to_e<E>(sk[u]);
+    }
+    *(typename VT<E>::v4 *)(dq + e) = oq;
+    *(typename VT<E>::v4 *)(dk + e) = ok;
 }
 
 template <typename E, int K, int V>
@@ -1238,11 +1276,11 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
         if (prof) prof->begin(kBwdGradsKernel, st);
         hipLaunchKernelGGL((bwd_grads_kernel<E, K, V>), dim3(nc_max, p.HV), dim3(kGThreads), 0, st, p);
         if (prof) prof->end(kBwdGradsKernel, st);
-        const int64_t total = (int64_t)p.T_tot * p.H * K;
-        if (total > 0) {
+        const int64_t total4 = (int64_t)p.T_tot * p.H * K / 4;
+        if (total4 > 0) {
             if (prof) prof->begin(kBwdReduceKernel, st);
-            hipLaunchKernelGGL(bwd_reduce_kernel<E>, dim3((unsigned)((total + kThreads - 1) / kThreads)), blk, 0, st,
-                               p.dqp, p.dkp, (E *)p.dq, (E *)p.dk, total, p.H, p.HV / p.H, K);
+            hipLaunchKernelGGL(bwd_reduce_kernel<E>, dim3((unsigned)((total4 + kThreads - 1) / kThreads)), blk, 0, st,
+                               p.dqp, p.dkp, (E *)p.dq, (E *)p.dk, total4, p.H, p.HV / p.H, K);
             if (prof) prof->end(kBwdReduceKernel, st);
         }
     }
