@@ -38,6 +38,7 @@ MEASURED_TRAFFIC = {
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
     "decode": ["gated_deltanet_chunked_delta_amd/csrc/gdn_recurrent.hip"],
+    "backward": ["gated_deltanet_chunked_delta_amd/csrc/gdn_backward.hip"],
 }
 DEVICE_HEADERS = ["gated_deltanet_chunked_delta_amd/csrc/gdn_device.h",
                   "gated_deltanet_chunked_delta_amd/csrc/gdn_internal.h"]
@@ -388,6 +389,8 @@ def run_backward(args):
     t1 = time.perf_counter()
     prof = gdn.gdn_profile_read()
     gdn.gdn_profile_enable(False)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, dev)
 
     tokens = sum(x["lens"])
     ms = (t1 - t0) * 1e3 / args.steps
@@ -401,6 +404,8 @@ def run_backward(args):
     ach = pb / (path_us * 1e-6) / 1e9
     flops = bwd_path_flops(w, x)
     tflops = flops / (path_us * 1e-6) / 1e12
+    khash = kernel_hash("backward")
+    traffic = MEASURED_TRAFFIC.get(khash, {}).get(w.name + ":" + dom)
     res = {
         "metric": BWD_METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4),
@@ -415,7 +420,8 @@ def run_backward(args):
         # over 8 TB/s = 20 flop/B): the bound is fp32 MFMA, the HBM side is given
         "roofline": {"bound": "mfma", "dtype": "fp32", "scope": "path", "kernel": dom,
                      "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS["fp32"], "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_PEAK_TFLOPS["fp32"], 4), "traffic": None,
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS["fp32"], 4), "traffic": traffic,
+                     "traffic_scope": "dominant kernel, bytes per launch", "kernel_hash": khash,
                      "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": pb,
                      "hbm_frac": round(ach / HBM_PEAK_GBS, 4), "kernel_us_per_step": round(path_us, 2),
                      "dominant_kernel_share": round(per_step(dom) / path_us, 3)},

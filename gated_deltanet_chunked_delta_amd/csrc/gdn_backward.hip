@@ -59,12 +59,6 @@ constexpr int kPadC = kChunk + 1;
 constexpr int kPadT = kVT + 1;
 
 // LDS sizes in floats.
-template <int K>
-constexpr int prep_q_floats() {   // the q rows, then A [64][65] and Tm [64][64] in the same space
-    return kChunk * (K + 1) > kChunk * kPadC + kChunk * kChunk ? kChunk * (K + 1) : kChunk * kPadC + kChunk * kChunk;
-}
-template <int K>
-constexpr int prep_floats() { return kChunk * (K + 1) + prep_q_floats<K>() + 4 * kChunk; }
 // grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the three
 // 64 x 65 matrices of the second phase reuse their space.
 template <int K>
@@ -205,104 +199,6 @@ __device__ __forceinline__ void seq_of(const BwdParams &p, int n, int &bos, int 
     }
 }
 
-template <int K>
-__device__ __forceinline__ void store_state_tile(const float *tile, float *dst, int V, int c0) {
-    constexpr int N4 = K * kVT / 4 / kThreads;
-#pragma unroll
-    for (int u = 0; u < N4; ++u) {
-        const int i = threadIdx.x + kThreads * u, r = i >> 3, c = (i & 7) * 4;
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = tile[r * kPadT + c + e];
-        *(f32x4 *)(dst + (int64_t)r * V + c0 + c) = x;
-    }
-}
-
-// Register-staged copies: load() issues the global loads of one copy,
-// commit() writes them to LDS.  A chunk step issues the loads of the next
-// step before its own arithmetic, so their latency hides behind it.
-//
-// L rows (zero past L) of a key-head row set [T_tot, H, K] at head jk, into
-// dst[64][K+1] as fp32.
-template <typename E, int K>
-struct RowsReg {
-    static constexpr int PER_ROW = K / 8, VPT = kChunk * PER_ROW / kThreads;
-    typename VT<E>::v8 v[VPT];   // kept in the input type until the LDS write
-    __device__ __forceinline__ void load(const E *src, int t0, int L, int H, int jk) {
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int i = threadIdx.x + kThreads * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
-            if (r < L) v[u] = ld8<E>(src + ((int64_t)(t0 + r) * H + jk) * K + c);
-            else
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[u][e] = to_e<E>(0.f);
-        }
-    }
-    __device__ __forceinline__ void commit(float *dst) const {
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int i = threadIdx.x + kThreads * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dst[r * (K + 1) + c + e] = to_f(v[u][e]);
-        }
-    }
-};
-// A 64 x 64 fp32 matrix (contiguous) into dst[64][65].
-struct Mat64Reg {
-    f32x4 v[4];
-    __device__ __forceinline__ void load(const float *src) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *(const f32x4 *)(src + 4 * (threadIdx.x + kThreads * u));
-    }
-    __device__ __forceinline__ void commit(float *dst) const {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = threadIdx.x + kThreads * u, r = i >> 4, c = (i & 15) * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[r * kPadC + c + e] = v[u][e];
-        }
-    }
-};
-// Rows t0..t0+L-1 (zero past L), 32 columns from c0, of a [T_tot, HV, V]
-// tensor at value head j, into dst[64][33] as fp32.
-template <typename E>
-struct TileReg {
-    typename VT<E>::v8 v;   // kept in the input type until the LDS write
-    __device__ __forceinline__ void load(const E *src, int t0, int L, int HV, int j, int V, int c0) {
-        const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 8;
-        if (r < L) v = ld8<E>(src + ((int64_t)(t0 + r) * HV + j) * V + c0 + c);
-        else
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = to_e<E>(0.f);
-    }
-    __device__ __forceinline__ void commit(float *dst) const {
-        const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[r * kPadT + c + e] = to_f(v[e]);
-    }
-};
-// K rows x 32 columns from c0 of a K x V fp32 state (row stride V), into dst[K][33].
-template <int K>
-struct StateTileReg {
-    static constexpr int N4 = K * kVT / 4 / kThreads;
-    f32x4 v[N4];
-    __device__ __forceinline__ void load(const float *src, int V, int c0) {
-#pragma unroll
-        for (int u = 0; u < N4; ++u) {
-            const int i = threadIdx.x + kThreads * u, r = i >> 3, c = (i & 7) * 4;
-            v[u] = *(const f32x4 *)(src + (int64_t)r * V + c0 + c);
-        }
-    }
-    __device__ __forceinline__ void commit(float *dst) const {
-#pragma unroll
-        for (int u = 0; u < N4; ++u) {
-            const int i = threadIdx.x + kThreads * u, r = i >> 3, c = (i & 7) * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[r * kPadT + c + e] = v[u][e];
-        }
-    }
-};
-
 // ---- register-staged copies for workgroups of NTH threads and value tiles
 // of VW columns (the scans), with the key/query rows kept raw in the input
 // type in LDS (row stride K + RowPad<E>; the L2 norms are applied as row
@@ -427,26 +323,6 @@ __device__ __forceinline__ float row_sumsq(const E *rows, int r) {
     return s;
 }
 
-// L2-normalises the rows of dst[64][K+1] in place when use_l2norm (factor
-// 1/sqrt(|x|^2 + 1e-6) into f[r], else 1).  Call after a barrier that
-// follows the writes of dst; ends with a barrier.
-template <int K>
-__device__ __forceinline__ void norm_rows(float *dst, float *f, int use_l2norm) {
-    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;   // 4 lanes per row
-    float s = 0.f;
-    for (int c = part; c < K; c += 4) {
-        const float x = dst[r * (K + 1) + c];
-        s = fmaf(x, x, s);
-    }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    const float fr = use_l2norm ? 1.f / sqrtf(s + 1e-6f) : 1.f;
-    if (use_l2norm)
-        for (int c = part; c < K; c += 4) dst[r * (K + 1) + c] *= fr;
-    if (part == 0) f[r] = fr;
-    lds_barrier();
-}
-
 // One block row I of Tm = (I + A)^-1 (16-row blocks, diagonal blocks already
 // in Tm, blocks above the diagonal zero): wave J < I computes
 // T_IJ = -X_I sum_{K<I} A_IK T_KJ, staging the sum in its scratch ysc [16][17].
@@ -507,16 +383,28 @@ __global__ __launch_bounds__(kThreads) void bwd_setup_kernel(const int32_t *cu, 
 // per (chunk, value head): gamma, Tm = (I + A)^-1, A / beta and Pm
 // ---------------------------------------------------------------------------
 template <typename E, int K>
+constexpr int prep_floats() {   // raw q/k rows, then A [64][65] and Tm [64][64] in the same space
+    return ((2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4 > kChunk * kPadC + kChunk * kChunk
+                ? (2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4
+                : kChunk * kPadC + kChunk * kChunk) +
+           4 * 16 * 17 + 4 * kChunk;
+}
+// bf16 rows: four workgroups per CU
+static_assert(prep_floats<bf16, 128>() * 4 <= 40 * 1024, "bf16 prep must fit four times per CU");
+
+template <typename E, int K>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
-    __shared__ float sm[prep_floats<K>()];
-    float *kh = sm;                          // [64][K+1]
-    float *qh = kh + kChunk * (K + 1);       // [64][K+1]
-    float *A = qh;                           // [64][65] after the products (qh is dead then)
+    constexpr int KS = K + RowPad<E>::v;
+    __shared__ float sm[prep_floats<E, K>()];
+    E *kr = (E *)sm;                         // [64][KS] raw k rows
+    E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
+    float *A = sm;                           // [64][65] after the products (the rows are dead then)
     float *Tm = A + kChunk * kPadC;          // [64][64]
-    float *gam = qh + prep_q_floats<K>();   // [64]
+    float *ysc = sm + prep_floats<E, K>() - 4 * 16 * 17 - 4 * kChunk;   // [4][16][17] solve scratch
+    float *gam = ysc + 4 * 16 * 17;          // [64]
     float *bet = gam + kChunk;               // [64]
-    float *fk = bet + kChunk;                // [64]
-    float *fq = fk + kChunk;                 // [64]
+    float *fk = bet + kChunk;                // [64] 1 / |k|
+    float *fq = fk + kChunk;                 // [64] 1 / |q|
 
     ChunkRef cr;
     if (!find_chunk(p, blockIdx.x, cr)) return;
@@ -533,30 +421,37 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
         }
         gam[r] = x;
         bet[r] = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+        if (r < L) p.gam[(int64_t)(t0 + r) * HV + j] = x;
     }
     {
-        RowsReg<E, K> rk, rq;
+        RawRowsReg<E, K, kThreads> rk, rq;
         rk.load((const E *)p.k, t0, L, p.H, jk);
         rq.load((const E *)p.q, t0, L, p.H, jk);
-        rk.commit(kh);
-        rq.commit(qh);
+        rk.commit(kr);
+        rq.commit(qr);
     }
-    __syncthreads();
-    norm_rows<K>(kh, fk, p.use_l2norm);
-    norm_rows<K>(qh, fq, p.use_l2norm);
-    if (threadIdx.x < L) p.gam[(int64_t)(t0 + threadIdx.x) * HV + j] = gam[threadIdx.x];
+    lds_barrier();
+    {
+        constexpr int LPR = kThreads / kChunk;
+        const int r = threadIdx.x / LPR;
+        const float sk = row_sumsq<E, K, kThreads>(kr, r), sq = row_sumsq<E, K, kThreads>(qr, r);
+        if (threadIdx.x % LPR == 0) {
+            fk[r] = p.use_l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
+            fq[r] = p.use_l2norm ? 1.f / sqrtf(sq + 1e-6f) : 1.f;
+        }
+    }
 
-    // K K^T and Q K^T: wave w computes rows 16w..16w+15, all four column tiles.
+    // K K^T and Q K^T of the raw rows (the norms scale rows and columns below):
+    // wave w computes rows 16w..16w+15, all four column tiles.
     const int w = wave_id();
     auto ra = [&](int) { return 16 * w; };
     auto cb = [&](int t) { return 16 * t; };
     f32x4 kk[4], qk[4];
     zero(kk);
     zero(qk);
-    wmm<4, K>(kk, ra, cb, [&](int r, int m) { return kh[r * (K + 1) + m]; },
-              [&](int c, int m) { return kh[c * (K + 1) + m]; });
-    wmm<4, K>(qk, ra, cb, [&](int r, int m) { return qh[r * (K + 1) + m]; },
-              [&](int c, int m) { return kh[c * (K + 1) + m]; });
+    wmm2<4, K>(kk, qk, ra, cb, [&](int r, int m) { return to_f(kr[r * KS + m]); },
+               [&](int r, int m) { return to_f(qr[r * KS + m]); },
+               [&](int c, int m) { return to_f(kr[c * KS + m]); });
     float *ag_out = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
     float *pm_out = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
     lds_barrier();   // A overwrites qh
@@ -565,12 +460,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = lrow(16 * w, e), c = lcol(16 * t);
-            const float d = (c <= r && r < L) ? __expf(gam[r] - gam[c]) : 0.f;
-            const float ag = c < r ? d * kk[t][e] : 0.f;
+            const float d = (c <= r && r < L) ? __expf(gam[r] - gam[c]) * fk[c] : 0.f;
+            const float ag = c < r ? d * fk[r] * kk[t][e] : 0.f;
             A[r * kPadC + c] = bet[r] * ag;
             Tm[r * kChunk + c] = 0.f;
             ag_out[r * kChunk + c] = ag;
-            pm_out[r * kChunk + c] = d * qk[t][e];
+            pm_out[r * kChunk + c] = d * fq[r] * qk[t][e];
         }
     lds_barrier();
 
@@ -596,10 +491,9 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     }
     lds_barrier();
     // Off-diagonal blocks, one block row at a time.
-    float *ysc = kh + w * 16 * 17;   // kh is dead after the products
-    tm_block_row<1>(A, Tm, ysc, w);
-    tm_block_row<2>(A, Tm, ysc, w);
-    tm_block_row<3>(A, Tm, ysc, w);
+    tm_block_row<1>(A, Tm, ysc + w * 16 * 17, w);
+    tm_block_row<2>(A, Tm, ysc + w * 16 * 17, w);
+    tm_block_row<3>(A, Tm, ysc + w * 16 * 17, w);
     float *tm_out = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
