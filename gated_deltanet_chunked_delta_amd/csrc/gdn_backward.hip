@@ -59,11 +59,11 @@ constexpr int kPadC = kChunk + 1;
 constexpr int kPadT = kVT + 1;
 
 // LDS sizes in floats.
-// grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the three
+// grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the two
 // 64 x 65 matrices of the second phase reuse their space.
 template <int K>
 constexpr int grads_tile_floats() { return 2 * K * kPadT + 4 * kChunk * kPadT; }
-static_assert(grads_tile_floats<64>() >= 3 * kChunk * kPadC, "phase-2 matrices must fit in the tile region");
+static_assert(grads_tile_floats<64>() >= 2 * kChunk * kPadC, "phase-2 matrices must fit in the tile region");
 
 // Products on the matrix cores: 16 x 16 fp32 tiles by v_mfma_f32_16x16x4f32
 // (fp32 operands, fp32 accumulation, so the pass keeps fp32 accuracy).
@@ -834,7 +834,7 @@ struct Tile4Reg {
 };
 template <typename E, int K>
 constexpr int grads_floats() {
-    return grads_tile_floats<K>() + 17 * kChunk + 8 + (2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4;
+    return grads_tile_floats<K>() + 23 * kChunk + 8 + (2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4;
 }
 static_assert(grads_floats<float, 128>() * 4 <= 160 * 1024, "fp32 grads must fit one CU");
 
@@ -851,7 +851,6 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
     float *vvT = doT + kChunk * kPadT;       // [64][33]
     float *dS = tile;                        // [64][65] dSqk (after the value tiles)
     float *Ad = dS + kChunk * kPadC;         // [64][65]
-    float *Zm = Ad + kChunk * kPadC;         // [64][65]
     float *rows = tile + grads_tile_floats<K>();   // scalars per row
     float *gam = rows;                       // [64]
     float *bet = gam + kChunk;               // [64]
@@ -860,9 +859,11 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
     float *sbvA = fq + kChunk;               // [64] sum_v dB v
     float *pt = sbvA + kChunk;               // [5][2][64] per column half: q.dQ, k.E, k.F, dA.A, k.dK
     float *psq = pt + 10 * kChunk;           // [2][64] q.dQ after the second phase
-    float *red = psq + 2 * kChunk;           // [8] <dh', h> per wave
+    float *prs = psq + 2 * kChunk;           // [2][64] row sums of Z per column half
+    float *pcs = prs + 2 * kChunk;           // [4][64] column sums of Z per row block
+    float *red = pcs + 4 * kChunk;           // [8] <dh', h> per wave
     E *kr = (E *)(red + 8);                  // [64][KS] raw k rows
-    static_assert(5 + 10 + 2 == 17, "row arrays of grads_floats");
+    static_assert(5 + 10 + 2 + 2 + 4 == 23, "row arrays of grads_floats");
     E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
 
     ChunkRef cr;
@@ -1004,10 +1005,11 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) dK[t][e] = aF[t][e] - bet[lrow(16 * rb, e)] * aE[t][e];
 
-    // the 64 x 64 matrices: dSqk, Ad and Z = dSqk * (qh . kh) + dA * A
+    // the 64 x 64 matrices dSqk and Ad; Z = dSqk * (qh . kh) + dA * A only
+    // through its row and column sums, reduced here in registers
     const float *pm = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
     const float *ag = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
-    float dbA[4] = {0.f, 0.f, 0.f, 0.f};
+    float dbA[4] = {0.f, 0.f, 0.f, 0.f}, zr[4] = {0.f, 0.f, 0.f, 0.f}, zc[2] = {0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1022,13 +1024,26 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
             const float agv = ag[r * kChunk + c];
             dS[r * kPadC + c] = dsq;
             Ad[r * kPadC + c] = dA * bet[r] * d;
-            Zm[r * kPadC + c] = z1 + dA * bet[r] * agv;
+            const float z = z1 + dA * bet[r] * agv;
+            zr[e] += z;
+            zc[t] += z;
             dbA[e] = fmaf(dA, agv, dbA[e]);
         }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float s = sum16(dbA[e]);
-        if (lane16 == 0) pt[(3 * 2 + hf) * kChunk + lrow(16 * rb, e)] = s;
+        const float z = sum16(zr[e]);
+        if (lane16 == 0) {
+            pt[(3 * 2 + hf) * kChunk + lrow(16 * rb, e)] = s;
+            prs[hf * kChunk + lrow(16 * rb, e)] = z;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {   // the 16 rows of this block: the four lane groups
+        float z = zc[t];
+        z += __shfl_xor(z, 16);
+        z += __shfl_xor(z, 32);
+        if ((threadIdx.x & 48) == 0) pcs[rb * kChunk + lcol(cbP(t))] = z;
     }
     lds_barrier();
     // wave 0: dgamma, dbeta per row (lane = row), then dg by a reverse cumsum over the lanes
@@ -1037,11 +1052,8 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
         const float t1 = fq[r] * (pt[0 * kChunk + r] + pt[1 * kChunk + r]);
         const float t2 = fk[r] * (pt[2 * kChunk + r] + pt[3 * kChunk + r]);
         const float t3 = fk[r] * (pt[4 * kChunk + r] + pt[5 * kChunk + r]);
-        float rs = 0.f, cs = 0.f;
-        for (int m = 0; m < kChunk; ++m) {
-            rs += Zm[r * kPadC + m];
-            cs += Zm[m * kPadC + r];
-        }
+        const float rs = prs[r] + prs[kChunk + r];
+        const float cs = (pcs[r] + pcs[kChunk + r]) + (pcs[2 * kChunk + r] + pcs[3 * kChunk + r]);
         float t3all = t3;
         for (int o = 32; o >= 1; o >>= 1) t3all += __shfl_xor(t3all, o);
         float sdh_all = 0.f;
