@@ -73,32 +73,46 @@ static_assert(grads_tile_floats<64>() >= 2 * kChunk * kPadC, "phase-2 matrices m
 // operands, so the assignment only fixes the order of the sum.
 //   acc[t] += sum_{m < KD} fa(ra(t) + (l & 15), m) * fb(cb(t) + (l & 15), m)
 // Operand reads that coincide between tiles (same ra or cb) are shared.  The
-// operands of a group of k-steps are read from LDS into registers before the
-// group's products issue, so one LDS latency is paid per group, not per step.
+// k-steps run in groups whose operands are read from LDS into registers ahead
+// of their products: the next group's reads are issued before the current
+// group's products, so LDS latency hides behind matrix-core work.  Groups are
+// sized to keep at most ~15 reads in flight (what the LDS counter tracks).
+template <int NT>
+constexpr int wmm_group(int S) {
+    return (S % 4 == 0 && NT + 1 <= 4) ? 4 : (S % 2 == 0 ? 2 : 1);
+}
 template <int NT, int KD, typename RA, typename CB, typename FA, typename FB>
 __device__ __forceinline__ void wmm(f32x4 (&acc)[NT], RA ra, CB cb, FA fa, FB fb) {
     constexpr int S = KD / 4;
-    constexpr int G0 = NT >= 4 ? 4 : 8;
-    constexpr int G = S <= G0 ? S : (S % G0 == 0 ? G0 : (S % 4 == 0 ? 4 : 1));
+    constexpr int G = wmm_group<NT>(S);
     static_assert(S % G == 0, "k-steps must split into whole groups");
     const int i = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
-#pragma unroll 1
-    for (int g = 0; g < S; g += G) {
-        float av[G][NT], bv[G][NT];
+    float av[2][G][NT], bv[2][G][NT];
+    auto load = [&](int buf, int g) {
 #pragma unroll
         for (int s = 0; s < G; ++s) {
             const int m = q * S + g + s;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                av[s][t] = fa(ra(t) + i, m);
-                bv[s][t] = fb(cb(t) + i, m);
+                av[buf][s][t] = fa(ra(t) + i, m);
+                bv[buf][s][t] = fb(cb(t) + i, m);
             }
         }
+    };
+    auto run = [&](int buf) {
 #pragma unroll
         for (int s = 0; s < G; ++s)
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s][t], bv[s][t], acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[buf][s][t], bv[buf][s][t], acc[t], 0, 0, 0);
+    };
+    load(0, 0);
+#pragma unroll 1
+    for (int g = 0; g < S; g += 2 * G) {
+        if (g + G < S) load(1, g + G);
+        run(0);
+        if (g + 2 * G < S) load(0, g + 2 * G);
+        if (g + G < S) run(1);
     }
 }
 
