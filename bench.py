@@ -29,11 +29,15 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # changes the hash, and the bench then reports traffic as null until it is
 # measured again.
 MEASURED_TRAFFIC = {
-    # fused_ws_kernel, GVA prefill: FETCH 151,985.6 KiB x 2.000 + WRITE 139,776.1 KiB x 1.000
-    "54b35e5aaa83fde3": {"gva": 454397120},
-    # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,370.0 KiB;
-    # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,011.75 KiB
-    "84462a58c8717f5e": {"decode": 1049895936, "decode_bf16pool": 529398528},
+    # fused_ws_kernel, GVA prefill: FETCH 151,985.5 KiB x 2.000 + WRITE 139,776.2 KiB x 1.000
+    "364fcc8c8560cb90": {"gva": 454397120},
+    # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,374.0 KiB;
+    # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB
+    "1e133469e85525fe": {"decode": 1049900032, "decode_bf16pool": 529568973},
+    # backward, GVA: every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md)
+    "500930874e882839": {"gva:bwd_prep_kernel": 614758093, "gva:bwd_fwd_scan_kernel": 1250037760,
+                         "gva:bwd_dh_scan_kernel": 1526922650, "gva:bwd_grads_kernel": 3479681536,
+                         "gva:bwd_reduce_kernel": 671125504},
 }
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
