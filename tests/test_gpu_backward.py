@@ -153,3 +153,38 @@ def test_backward_gva_full_size_sampled():
                 "dv": got["dv"][n:n + 1, :, sl], "dg": got["dg"][n:n + 1, :, sl],
                 "dbeta": got["dbeta"][n:n + 1, :, sl], "dh0": got["dh0"][n:n + 1, sl]}
         compare(part, ref, bars, f"gva n={n} key head {jk}")
+
+
+def test_backward_varlen_full_size_sampled():
+    """The packed 64-sequence workload (about 65k tokens, lengths 1..2048) at full
+    size, as one call; sampled (sequence, key head) groups, with both value heads
+    of each group, against the oracle: the longest sequence, the first and the
+    last, at the first, a middle and the last key head."""
+    w = WORKLOADS["varlen"]
+    _say("[bwd-full] varlen: generating on the GPU")
+    x = make_grad_inputs(oracle.add_gates(make_inputs(w, seed=0, device="cuda:0")), seed=100)
+    got = run_gpu_bwd(x, torch.bfloat16)
+    for name in NAMES:
+        assert torch.isfinite(got[name]).all(), name
+    G = w.HV // w.H
+    bars = _bars(torch.bfloat16)
+    starts = [int(c) for c in x["cu_seqlens"].tolist()]
+    N = x["N"]
+    longest = int(np.argmax(x["lens"]))
+    for n, jk in ((0, 0), (longest, w.H // 2), (N - 1, w.H - 1)):
+        t0, t1 = starts[n], starts[n + 1]
+        sl = slice(jk * G, (jk + 1) * G)
+
+        def rows(t, heads):
+            return t[0, t0:t1, heads].unsqueeze(0).cpu()
+        sub = dict(q=rows(x["q"], slice(jk, jk + 1)), k=rows(x["k"], slice(jk, jk + 1)), v=rows(x["v"], sl),
+                   g=rows(x["g"], sl), beta=rows(x["beta"], sl), do=rows(x["do"], sl),
+                   dht=x["dht"][n:n + 1, sl].cpu(),
+                   initial_state=None if x["initial_state"] is None else x["initial_state"][n:n + 1, sl].cpu(),
+                   cu_seqlens=None, scale=x["scale"], use_l2norm=x["use_l2norm"])
+        _say(f"    group n={n} len={t1 - t0} key head {jk}")
+        ref = run_oracle_bwd(sub)
+        part = {"dq": got["dq"][0:1, t0:t1, jk:jk + 1], "dk": got["dk"][0:1, t0:t1, jk:jk + 1],
+                "dv": got["dv"][0:1, t0:t1, sl], "dg": got["dg"][0:1, t0:t1, sl],
+                "dbeta": got["dbeta"][0:1, t0:t1, sl], "dh0": got["dh0"][n:n + 1, sl]}
+        compare(part, ref, bars, f"varlen n={n} key head {jk}")
