@@ -32,17 +32,20 @@
 //
 // and the L2 norm's backward dx = f (dxh - xh (xh . dxh)), f = 1/sqrt(|x|^2 + 1e-6).
 // The state gradient runs backwards over chunks just as the state runs
-// forwards, so the pass is five launches:
+// forwards, so the pass is five launches (six with packed sequences, whose
+// chunk offsets bwd_setup_kernel computes first):
 //   bwd_prep_kernel      per (chunk, value head): gamma, Tm, A / beta and Pm
-//   bwd_fwd_scan_kernel  per (sequence, value head, 32 value columns), forward
-//                        over chunks: the chunk-start states h and Vn
-//   bwd_dh_scan_kernel   per (sequence, value head, 32 value columns), backward
-//                        over chunks: dh' per chunk, dB, the initial-state gradient
+//   bwd_fwd_scan_kernel  per (sequence, value head, 64 value columns; 32 for
+//                        fp32 rows), forward over chunks: the chunk-start
+//                        states h and Vn
+//   bwd_dh_scan_kernel   the same grid, backward over chunks: dh' per chunk,
+//                        dB, the initial-state gradient
 //   bwd_grads_kernel     per (chunk, value head): dq, dk per value head, dv,
 //                        dg, dbeta
 //   bwd_reduce_kernel    dq, dk summed over the value heads of each key head
-// All arithmetic is fp32 on the VALU with operands staged in LDS; the
-// intermediates live in the caller's workspace (layout in BwdPlan).
+// All arithmetic is fp32: every product runs on the matrix cores with fp32
+// operands staged in LDS; the intermediates live in the caller's workspace
+// (layout in BwdPlan).
 #include <hip/hip_runtime.h>
 
 #include "gdn_device.h"
@@ -54,7 +57,7 @@ namespace {
 using namespace dev;
 
 constexpr int kThreads = 256;
-constexpr int kVT = 32;          // value columns per scan workgroup / grads tile
+constexpr int kVT = 32;          // value columns per tile of the gradients kernel
 constexpr int kPadC = kChunk + 1;
 constexpr int kPadT = kVT + 1;
 
