@@ -43,8 +43,11 @@
 //   bwd_grads_kernel     per (chunk, value head): dq, dk per value head, dv,
 //                        dg, dbeta
 //   bwd_reduce_kernel    dq, dk summed over the value heads of each key head
-// All arithmetic is fp32: every product runs on the matrix cores with fp32
-// operands staged in LDS; the intermediates live in the caller's workspace
+// All arithmetic is fp32-accurate: the products run on the matrix cores with
+// fp32 operands (v_mfma_f32_16x16x4f32), except the gradients kernel's products
+// over the value columns, which split each fp32 operand into bf16 hi + lo parts
+// (hi hi + hi lo + lo hi on v_mfma_f32_16x16x32_bf16, fp32 accumulation; a bf16
+// input is its own hi part).  The intermediates live in the caller's workspace
 // (layout in BwdPlan).
 #include <hip/hip_runtime.h>
 
@@ -64,8 +67,13 @@ constexpr int kPadT = kVT + 1;
 // LDS sizes in floats.
 // grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the two
 // 64 x 65 matrices of the second phase reuse their space.
+// grads: the value tiles as bf16 hi / lo pairs, rows of 32 value columns at a
+// stride of kVS elements (16-byte aligned MFMA operand reads): h, dh' (K rows
+// each), Vn, dB, dO (64 rows each, hi and lo); the two 64 x 65 fp32 matrices of
+// the second phase reuse the space.
+constexpr int kVS = 40;
 template <int K>
-constexpr int grads_tile_floats() { return 2 * K * kPadT + 4 * kChunk * kPadT; }
+constexpr int grads_tile_floats() { return (4 * K + 6 * kChunk) * kVS / 2; }
 static_assert(grads_tile_floats<64>() >= 2 * kChunk * kPadC, "phase-2 matrices must fit in the tile region");
 
 // Products on the matrix cores: 16 x 16 fp32 tiles by v_mfma_f32_16x16x4f32
@@ -831,6 +839,32 @@ __global__ __launch_bounds__(NTH) void bwd_dh_scan_kernel(BwdParams p) {
 // The key and query rows stay raw in LDS and their L2 norms enter as scales.
 // ---------------------------------------------------------------------------
 constexpr int kGThreads = 512;
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): a product of two split
+// values, hi hi + hi lo + lo hi, misses only lo lo (2^-16 of it) and the
+// rounding of the lo parts, so it keeps fp32 accuracy on the bf16 matrix cores.
+__device__ __forceinline__ void split_store4(const float *x, bf16 *hi, bf16 *lo) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = (bf16)x[e];
+        l[e] = (bf16)(x[e] - (float)h[e]);
+    }
+    *(bf16x4 *)hi = h;
+    *(bf16x4 *)lo = l;
+}
+// acc[t] += sum over 32 value columns of X[ra + (l & 15)][.] Y[cb(t) + (l & 15)][.]
+// for bf16 rows X, Y at stride kVS (one v_mfma_f32_16x16x32_bf16 per tile).
+template <int NT, typename CB>
+__device__ __forceinline__ void vmm(f32x4 (&acc)[NT], const bf16 *X, int ra, const bf16 *Y, CB cb) {
+    const int i = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
+    const bf16x8 a = *(const bf16x8 *)(X + (ra + i) * kVS + 8 * q);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const bf16x8 b = *(const bf16x8 *)(Y + (cb(t) + i) * kVS + 8 * q);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[t], 0, 0, 0);
+    }
+}
 // Rows t0..t0+L-1 (zero past L), 32 columns from c0, of a [T_tot, HV, V]
 // tensor at value head j, into dst[64][33] as fp32: four elements per thread.
 template <typename E>
@@ -858,14 +892,13 @@ static_assert(grads_floats<float, 128>() * 4 <= 160 * 1024, "fp32 grads must fit
 template <typename E, int K, int V>
 __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
     constexpr int KS = K + RowPad<E>::v, KR = K / 16, NTK = KR / 2;
-    __shared__ float sm[grads_floats<E, K>()];
+    __shared__ __attribute__((aligned(16))) float sm[grads_floats<E, K>()];   // 16-byte operand reads
     float *tile = sm;                        // per value tile, then the 64 x 64 matrices
-    float *hT = tile;                        // [K][33]
-    float *dhT = hT + K * kPadT;             // [K][33]
-    float *vnT = dhT + K * kPadT;            // [64][33]
-    float *dbT = vnT + kChunk * kPadT;       // [64][33]
-    float *doT = dbT + kChunk * kPadT;       // [64][33]
-    float *vvT = doT + kChunk * kPadT;       // [64][33]
+    bf16 *hHi = (bf16 *)tile, *hLo = hHi + K * kVS;        // [K][kVS] h rows (key index), value columns
+    bf16 *dhHi = hLo + K * kVS, *dhLo = dhHi + K * kVS;   // [K][kVS] dh'
+    bf16 *vnHi = dhLo + K * kVS, *vnLo = vnHi + kChunk * kVS;   // [64][kVS] Vn
+    bf16 *dbHi = vnLo + kChunk * kVS, *dbLo = dbHi + kChunk * kVS;   // [64][kVS] dB
+    bf16 *doHi = dbLo + kChunk * kVS, *doLo = doHi + kChunk * kVS;   // [64][kVS] dO (lo only for fp32 I/O)
     float *dS = tile;                        // [64][65] dSqk (after the value tiles)
     float *Ad = dS + kChunk * kPadC;         // [64][65]
     float *rows = tile + grads_tile_floats<K>();   // scalars per row
@@ -938,27 +971,40 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
     zero(aF);
     float sdh = 0.f;      // this thread's part of <dh', h>
     float sbv = 0.f;      // row (threadIdx.x >> 3): sum_v dB v
+    constexpr bool kExactDo = sizeof(E) == 2;   // bf16 dO is its own hi part
     for (int c0 = 0; c0 < V; c0 += kVT) {
-        th.commit(hT);
-        tdh.commit(dhT);
-        tvn.commit(vnT);
-        tdb.commit(dbT);
-        tdo.commit(doT);
-        tv.commit(vvT);
-        lds_barrier();
-        if (c0 + kVT < V) fetch(c0 + kVT);
-        // this thread's part of <dh', h>: the elements it wrote
+        // stage the tiles as hi / lo pairs; <dh', h>, sum_v dB v and dv from the registers
 #pragma unroll
         for (int u = 0; u < StateTileN<K, kVT, kGThreads>::N4; ++u) {
             const int i = threadIdx.x + kGThreads * u, r = i >> 3, c = (i & 7) * 4;
+            float xh[4], xd[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sdh = fmaf(hT[r * kPadT + c + e], dhT[r * kPadT + c + e], sdh);
+            for (int e = 0; e < 4; ++e) {
+                xh[e] = th.v[u][e];
+                xd[e] = tdh.v[u][e];
+                sdh = fmaf(xh[e], xd[e], sdh);
+            }
+            split_store4(xh, hHi + r * kVS + c, hLo + r * kVS + c);
+            split_store4(xd, dhHi + r * kVS + c, dhLo + r * kVS + c);
         }
         {
             const int r = threadIdx.x >> 3, c = (threadIdx.x & 7) * 4;
+            float xv[4], xb[4], xo[4];
             float s = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s = fmaf(dbT[r * kPadT + c + e], vvT[r * kPadT + c + e], s);
+            for (int e = 0; e < 4; ++e) {
+                xv[e] = tvn.v[e];
+                xb[e] = tdb.v[e];
+                xo[e] = to_f(tdo.v[e]);
+                s = fmaf(xb[e], to_f(tv.v[e]), s);
+            }
+            split_store4(xv, vnHi + r * kVS + c, vnLo + r * kVS + c);
+            split_store4(xb, dbHi + r * kVS + c, dbLo + r * kVS + c);
+            if constexpr (kExactDo) {
+                *(bf16x4 *)(doHi + r * kVS + c) = bf16x4{(bf16)xo[0], (bf16)xo[1], (bf16)xo[2], (bf16)xo[3]};
+            } else {
+                split_store4(xo, doHi + r * kVS + c, doLo + r * kVS + c);
+            }
             s += __shfl_xor(s, 1);
             s += __shfl_xor(s, 2);
             s += __shfl_xor(s, 4);
@@ -966,18 +1012,31 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
             if (r < L) {
                 typename VT<E>::v4 o;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = to_e<E>(bet[r] * dbT[r * kPadT + c + e]);
+                for (int e = 0; e < 4; ++e) o[e] = to_e<E>(bet[r] * xb[e]);
                 *(typename VT<E>::v4 *)((E *)p.dv + ((int64_t)(t0 + r) * HV + j) * V + c0 + c) = o;
             }
         }
-        wmm2<2, kVT>(aP, aA, ra, cbP, [&](int r, int m) { return doT[r * kPadT + m]; },
-                     [&](int r, int m) { return dbT[r * kPadT + m]; },
-                     [&](int c, int m) { return vnT[c * kPadT + m]; });
-        wmm2<NTK, kVT>(dQ, aE, ra, cbK, [&](int r, int m) { return doT[r * kPadT + m]; },
-                       [&](int r, int m) { return dbT[r * kPadT + m]; },
-                       [&](int c, int m) { return hT[c * kPadT + m]; });
-        wmm<NTK, kVT>(aF, ra, cbK, [&](int r, int m) { return vnT[r * kPadT + m]; },
-                      [&](int c, int m) { return dhT[c * kPadT + m]; });
+        lds_barrier();
+        if (c0 + kVT < V) fetch(c0 + kVT);
+        const int r0 = 16 * rb;
+        // aP += dO Vn^T, aA += dB Vn^T, dQ += dO h^T, aE += dB h^T, aF += Vn dh'^T
+        vmm(aP, doHi, r0, vnHi, cbP);
+        vmm(aP, doHi, r0, vnLo, cbP);
+        vmm(aA, dbHi, r0, vnHi, cbP);
+        vmm(aA, dbHi, r0, vnLo, cbP);
+        vmm(aA, dbLo, r0, vnHi, cbP);
+        vmm(dQ, doHi, r0, hHi, cbK);
+        vmm(dQ, doHi, r0, hLo, cbK);
+        vmm(aE, dbHi, r0, hHi, cbK);
+        vmm(aE, dbHi, r0, hLo, cbK);
+        vmm(aE, dbLo, r0, hHi, cbK);
+        vmm(aF, vnHi, r0, dhHi, cbK);
+        vmm(aF, vnHi, r0, dhLo, cbK);
+        vmm(aF, vnLo, r0, dhHi, cbK);
+        if constexpr (!kExactDo) {
+            vmm(aP, doLo, r0, vnHi, cbP);
+            vmm(dQ, doLo, r0, hHi, cbK);
+        }
         lds_barrier();
     }
 

@@ -2,8 +2,9 @@
 the fp64 backward oracle (oracle/backward.py, pinned to finite differences).
 
 Bars, as max|gpu - oracle| / max|oracle| per output: the kernels compute in
-fp32 whatever the I/O type, so fp32 outputs (dg, dbeta, dh0, and everything
-in the fp32 check mode) carry only fp32 rounding: 1e-4.  bf16 outputs (dq, dk,
+fp32 whatever the I/O type (fp32 products, or bf16 hi/lo splits of fp32
+operands that keep about 16 bits of each product), so fp32 outputs (dg, dbeta,
+dh0, and everything in the fp32 check mode) carry only fp32-level rounding: 1e-4.  bf16 outputs (dq, dk,
 dv) are additionally rounded to bf16 once: half an ulp, at most 2^-8 of the
 element (an element just above a power of two), so their bar is 2^-8 + 1e-4.
 """
