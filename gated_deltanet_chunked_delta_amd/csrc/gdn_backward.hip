@@ -232,9 +232,9 @@ template <typename E> struct RowPad;
 template <> struct RowPad<bf16> { static constexpr int v = 2; };    // 4-byte rows, odd word stride
 template <> struct RowPad<float> { static constexpr int v = 1; };
 
-template <typename E, int K, int NTH>
+template <typename E, int K, int NTH, int PAD = RowPad<E>::v>
 struct RawRowsReg {
-    static constexpr int PER_ROW = K / 8, VPT = kChunk * PER_ROW / NTH, KS = K + RowPad<E>::v;
+    static constexpr int PER_ROW = K / 8, VPT = kChunk * PER_ROW / NTH, KS = K + PAD;
     static_assert(VPT >= 1 && kChunk * PER_ROW % NTH == 0, "rows must split evenly");
     typename VT<E>::v8 v[VPT];
     __device__ __forceinline__ void load(const E *src, int t0, int L, int H, int jk) {
@@ -334,9 +334,9 @@ struct StateTileN {
 };
 // Sum of squares of row r of a raw row set, over the NTH / 64 lanes that
 // share the row (r = threadIdx.x / (NTH / 64)); every such lane gets the sum.
-template <typename E, int K, int NTH>
+template <typename E, int K, int NTH, int PAD = RowPad<E>::v>
 __device__ __forceinline__ float row_sumsq(const E *rows, int r) {
-    constexpr int LPR = NTH / kChunk, KS = K + RowPad<E>::v;
+    constexpr int LPR = NTH / kChunk, KS = K + PAD;
     const int part = threadIdx.x % LPR;
     float s = 0.f;
     for (int c = part; c < K; c += LPR) {
@@ -407,10 +407,12 @@ __global__ __launch_bounds__(kThreads) void bwd_setup_kernel(const int32_t *cu, 
 // ---------------------------------------------------------------------------
 // per (chunk, value head): gamma, Tm = (I + A)^-1, A / beta and Pm
 // ---------------------------------------------------------------------------
+// Row padding of prep's raw rows: bf16 rows are MFMA operands read 16 bytes at a time.
+template <typename E> struct PrepPad { static constexpr int v = sizeof(E) == 2 ? 8 : RowPad<E>::v; };
 template <typename E, int K>
 constexpr int prep_floats() {   // raw q/k rows, then A [64][65] and Tm [64][64] in the same space
-    return ((2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4 > kChunk * kPadC + kChunk * kChunk
-                ? (2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4
+    return ((2 * kChunk * (K + PrepPad<E>::v) * (int)sizeof(E) + 3) / 4 > kChunk * kPadC + kChunk * kChunk
+                ? (2 * kChunk * (K + PrepPad<E>::v) * (int)sizeof(E) + 3) / 4
                 : kChunk * kPadC + kChunk * kChunk) +
            4 * 16 * 17 + 4 * kChunk;
 }
@@ -419,8 +421,8 @@ static_assert(prep_floats<bf16, 128>() * 4 <= 40 * 1024, "bf16 prep must fit fou
 
 template <typename E, int K>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
-    constexpr int KS = K + RowPad<E>::v;
-    __shared__ float sm[prep_floats<E, K>()];
+    constexpr int PAD = PrepPad<E>::v, KS = K + PAD;
+    __shared__ __attribute__((aligned(16))) float sm[prep_floats<E, K>()];
     E *kr = (E *)sm;                         // [64][KS] raw k rows
     E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
     float *A = sm;                           // [64][65] after the products (the rows are dead then)
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
         if (r < L) p.gam[(int64_t)(t0 + r) * HV + j] = x;
     }
     {
-        RawRowsReg<E, K, kThreads> rk, rq;
+        RawRowsReg<E, K, kThreads, PAD> rk, rq;
         rk.load((const E *)p.k, t0, L, p.H, jk);
         rq.load((const E *)p.q, t0, L, p.H, jk);
         rk.commit(kr);
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     {
         constexpr int LPR = kThreads / kChunk;
         const int r = threadIdx.x / LPR;
-        const float sk = row_sumsq<E, K, kThreads>(kr, r), sq = row_sumsq<E, K, kThreads>(qr, r);
+        const float sk = row_sumsq<E, K, kThreads, PAD>(kr, r), sq = row_sumsq<E, K, kThreads, PAD>(qr, r);
         if (threadIdx.x % LPR == 0) {
             fk[r] = p.use_l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
             fq[r] = p.use_l2norm ? 1.f / sqrtf(sq + 1e-6f) : 1.f;
@@ -474,9 +476,25 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     f32x4 kk[4], qk[4];
     zero(kk);
     zero(qk);
-    wmm2<4, K>(kk, qk, ra, cb, [&](int r, int m) { return to_f(kr[r * KS + m]); },
-               [&](int r, int m) { return to_f(qr[r * KS + m]); },
-               [&](int c, int m) { return to_f(kr[c * KS + m]); });
+    if constexpr (sizeof(E) == 2) {
+        // bf16 rows are exact bf16 operands: one bf16 product per 32 keys, fp32 accumulation
+        const int i = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            const bf16x8 ak = *(const bf16x8 *)(kr + (16 * w + i) * KS + k0 + 8 * q);
+            const bf16x8 aq = *(const bf16x8 *)(qr + (16 * w + i) * KS + k0 + 8 * q);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8 b = *(const bf16x8 *)(kr + (16 * t + i) * KS + k0 + 8 * q);
+                kk[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, b, kk[t], 0, 0, 0);
+                qk[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, b, qk[t], 0, 0, 0);
+            }
+        }
+    } else {
+        wmm2<4, K>(kk, qk, ra, cb, [&](int r, int m) { return to_f(kr[r * KS + m]); },
+                   [&](int r, int m) { return to_f(qr[r * KS + m]); },
+                   [&](int c, int m) { return to_f(kr[c * KS + m]); });
+    }
     float *ag_out = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
     float *pm_out = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
     lds_barrier();   // A overwrites qh
