@@ -901,11 +901,22 @@ struct Tile4Reg {
         for (int e = 0; e < 4; ++e) dst[r * kPadT + c + e] = to_f(v[e]);
     }
 };
+// bf16 rows: the second phase's four 64 x 64 operands as bf16 hi / lo pairs
+// at a row stride of kMS elements, and the raw q / k rows transposed (exact
+// bf16 operands of the same products).
+constexpr int kMS = 72;
+template <typename E, int K>
+constexpr int grads_region_floats() {
+    return sizeof(E) == 2 && 8 * kChunk * kMS / 2 > grads_tile_floats<K>() ? 8 * kChunk * kMS / 2
+                                                                            : grads_tile_floats<K>();
+}
 template <typename E, int K>
 constexpr int grads_floats() {
-    return grads_tile_floats<K>() + 23 * kChunk + 8 + (2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4;
+    return grads_region_floats<E, K>() + 23 * kChunk + 8 + (2 * kChunk * (K + RowPad<E>::v) * (int)sizeof(E) + 3) / 4 +
+           (sizeof(E) == 2 ? 2 * K * kMS / 2 : 0);
 }
 static_assert(grads_floats<float, 128>() * 4 <= 160 * 1024, "fp32 grads must fit one CU");
+static_assert(grads_floats<bf16, 128>() * 4 <= 160 * 1024, "bf16 grads must fit one CU");
 
 template <typename E, int K, int V>
 __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
@@ -919,7 +930,7 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
     bf16 *doHi = dbLo + kChunk * kVS, *doLo = doHi + kChunk * kVS;   // [64][kVS] dO (lo only for fp32 I/O)
     float *dS = tile;                        // [64][65] dSqk (after the value tiles)
     float *Ad = dS + kChunk * kPadC;         // [64][65]
-    float *rows = tile + grads_tile_floats<K>();   // scalars per row
+    float *rows = tile + grads_region_floats<E, K>();   // scalars per row
     float *gam = rows;                       // [64]
     float *bet = gam + kChunk;               // [64]
     float *fk = bet + kChunk;                // [64] 1 / |k|
@@ -933,6 +944,14 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
     E *kr = (E *)(red + 8);                  // [64][KS] raw k rows
     static_assert(5 + 10 + 2 + 2 + 4 == 23, "row arrays of grads_floats");
     E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
+    constexpr bool kB16 = sizeof(E) == 2;
+    // bf16 rows: the raw rows transposed, [K][kMS] (key index, token), and the
+    // second phase's operands over the tile region, [64][kMS] hi / lo each
+    bf16 *kT = (bf16 *)(qr + kChunk * KS), *qT = kT + K * kMS;
+    bf16 *dSkHi = (bf16 *)tile, *dSkLo = dSkHi + kChunk * kMS;       // dSqk[r][m] / |k_m|
+    bf16 *dSqHi = dSkLo + kChunk * kMS, *dSqLo = dSqHi + kChunk * kMS;   // dSqk[m][r] / |q_m| at [r][m]
+    bf16 *AdkHi = dSqLo + kChunk * kMS, *AdkLo = AdkHi + kChunk * kMS;   // Ad[r][m] / |k_m|
+    bf16 *AtkHi = AdkLo + kChunk * kMS, *AtkLo = AtkHi + kChunk * kMS;   // Ad[m][r] / |k_m| at [r][m]
 
     ChunkRef cr;
     if (!find_chunk(p, blockIdx.x, cr)) return;
@@ -969,6 +988,18 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
         fetch(0);
         rk.commit(kr);
         rq.commit(qr);
+        if constexpr (kB16) {
+#pragma unroll
+            for (int u = 0; u < RawRowsReg<E, K, kGThreads>::VPT; ++u) {
+                constexpr int PER_ROW = K / 8;
+                const int i = threadIdx.x + kGThreads * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kT[(c + e) * kMS + r] = rk.v[u][e];
+                    qT[(c + e) * kMS + r] = rq.v[u][e];
+                }
+            }
+        }
     }
     lds_barrier();
     {
@@ -1116,8 +1147,27 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
             const float z1 = dpm * pm[r * kChunk + c];   // dPm * Pm
             const float dA = c < r && r < L ? -aA[t][e] : 0.f;
             const float agv = ag[r * kChunk + c];
-            dS[r * kPadC + c] = dsq;
-            Ad[r * kPadC + c] = dA * bet[r] * d;
+            const float adv = dA * bet[r] * d;
+            if constexpr (kB16) {
+                const float x4[4] = {dsq * fk[c], dsq * fq[r], adv * fk[c], adv * fk[r]};
+                bf16 h4[4], l4[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    h4[u] = (bf16)x4[u];
+                    l4[u] = (bf16)(x4[u] - (float)h4[u]);
+                }
+                dSkHi[r * kMS + c] = h4[0];
+                dSkLo[r * kMS + c] = l4[0];
+                dSqHi[c * kMS + r] = h4[1];
+                dSqLo[c * kMS + r] = l4[1];
+                AdkHi[r * kMS + c] = h4[2];
+                AdkLo[r * kMS + c] = l4[2];
+                AtkHi[c * kMS + r] = h4[3];
+                AtkLo[c * kMS + r] = l4[3];
+            } else {
+                dS[r * kPadC + c] = dsq;
+                Ad[r * kPadC + c] = adv;
+            }
             const float z = z1 + dA * bet[r] * agv;
             zr[e] += z;
             zc[t] += z;
@@ -1169,12 +1219,38 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
     }
 
     // dQ += dSqk Kh;  dK += dSqk^T Qh + (Ad + Ad^T) Kh   (Kh = diag(fk) K, Qh = diag(fq) Q)
-    wmm<NTK, kChunk>(dQ, ra, cbK, [&](int r, int m) { return dS[r * kPadC + m]; },
-                     [&](int c, int m) { return fk[m] * to_f(kr[m * KS + c]); });
-    wmm<NTK, kChunk>(dK, ra, cbK, [&](int r, int m) { return dS[m * kPadC + r]; },
-                     [&](int c, int m) { return fq[m] * to_f(qr[m * KS + c]); });
-    wmm<NTK, kChunk>(dK, ra, cbK, [&](int r, int m) { return Ad[r * kPadC + m] + Ad[m * kPadC + r]; },
-                     [&](int c, int m) { return fk[m] * to_f(kr[m * KS + c]); });
+    if constexpr (kB16) {
+        // the norms sit in the split operands; the transposed raw rows are exact
+        const int i = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
+#pragma unroll
+        for (int m0 = 0; m0 < kChunk; m0 += 32) {
+            const int ao = (16 * rb + i) * kMS + m0 + 8 * q;
+            const bf16x8 s1 = *(const bf16x8 *)(dSkHi + ao), s2 = *(const bf16x8 *)(dSkLo + ao);
+            const bf16x8 s3 = *(const bf16x8 *)(dSqHi + ao), s4 = *(const bf16x8 *)(dSqLo + ao);
+            const bf16x8 s5 = *(const bf16x8 *)(AdkHi + ao), s6 = *(const bf16x8 *)(AdkLo + ao);
+            const bf16x8 s7 = *(const bf16x8 *)(AtkHi + ao), s8 = *(const bf16x8 *)(AtkLo + ao);
+#pragma unroll
+            for (int t = 0; t < NTK; ++t) {
+                const int bo = (cbK(t) + i) * kMS + m0 + 8 * q;
+                const bf16x8 bk = *(const bf16x8 *)(kT + bo), bq = *(const bf16x8 *)(qT + bo);
+                dQ[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s1, bk, dQ[t], 0, 0, 0);
+                dQ[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s2, bk, dQ[t], 0, 0, 0);
+                dK[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s3, bq, dK[t], 0, 0, 0);
+                dK[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s4, bq, dK[t], 0, 0, 0);
+                dK[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s5, bk, dK[t], 0, 0, 0);
+                dK[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s6, bk, dK[t], 0, 0, 0);
+                dK[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s7, bk, dK[t], 0, 0, 0);
+                dK[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s8, bk, dK[t], 0, 0, 0);
+            }
+        }
+    } else {
+        wmm<NTK, kChunk>(dQ, ra, cbK, [&](int r, int m) { return dS[r * kPadC + m]; },
+                         [&](int c, int m) { return fk[m] * to_f(kr[m * KS + c]); });
+        wmm<NTK, kChunk>(dK, ra, cbK, [&](int r, int m) { return dS[m * kPadC + r]; },
+                         [&](int c, int m) { return fq[m] * to_f(qr[m * KS + c]); });
+        wmm<NTK, kChunk>(dK, ra, cbK, [&](int r, int m) { return Ad[r * kPadC + m] + Ad[m * kPadC + r]; },
+                         [&](int c, int m) { return fk[m] * to_f(kr[m * KS + c]); });
+    }
 
     // L2-norm backward and the per-value-head partial dq, dk: the row dot
     // products qh . dQ and kh . dK meet across the two column halves
