@@ -35,8 +35,8 @@ MEASURED_TRAFFIC = {
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB
     "1e133469e85525fe": {"decode": 1049900032, "decode_bf16pool": 529568973},
     # backward, GVA: every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md)
-    "500930874e882839": {"gva:bwd_prep_kernel": 614758093, "gva:bwd_fwd_scan_kernel": 1250037760,
-                         "gva:bwd_dh_scan_kernel": 1526922650, "gva:bwd_grads_kernel": 3479681536,
+    "b91e1eef6621b5ce": {"gva:bwd_prep_kernel": 611913728, "gva:bwd_fwd_scan_kernel": 1250037760,
+                         "gva:bwd_dh_scan_kernel": 1526923264, "gva:bwd_grads_kernel": 3463572582,
                          "gva:bwd_reduce_kernel": 671125504},
 }
 KERNEL_SOURCES = {
