@@ -35,7 +35,7 @@ MEASURED_TRAFFIC = {
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB
     "1e133469e85525fe": {"decode": 1049900032, "decode_bf16pool": 529568973},
     # backward, GVA: every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md)
-    "b91e1eef6621b5ce": {"gva:bwd_prep_kernel": 611913728, "gva:bwd_fwd_scan_kernel": 1250037760,
+    "1987cd886ba5ae0b": {"gva:bwd_prep_kernel": 611913728, "gva:bwd_fwd_scan_kernel": 1250037760,
                          "gva:bwd_dh_scan_kernel": 1526923264, "gva:bwd_grads_kernel": 3463572582,
                          "gva:bwd_reduce_kernel": 671125504},
 }

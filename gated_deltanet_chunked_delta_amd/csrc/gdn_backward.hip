@@ -62,7 +62,6 @@ using namespace dev;
 constexpr int kThreads = 256;
 constexpr int kVT = 32;          // value columns per tile of the gradients kernel
 constexpr int kPadC = kChunk + 1;
-constexpr int kPadT = kVT + 1;
 
 // LDS sizes in floats.
 // grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the two
@@ -884,7 +883,8 @@ __device__ __forceinline__ void vmm(f32x4 (&acc)[NT], const bf16 *X, int ra, con
     }
 }
 // Rows t0..t0+L-1 (zero past L), 32 columns from c0, of a [T_tot, HV, V]
-// tensor at value head j, into dst[64][33] as fp32: four elements per thread.
+// tensor at value head j, four elements per thread: row threadIdx.x / 8,
+// columns 4 (threadIdx.x % 8) .. +3 (staged into LDS by the caller).
 template <typename E>
 struct Tile4Reg {
     typename VT<E>::v4 v;
@@ -894,11 +894,6 @@ struct Tile4Reg {
         else
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = to_e<E>(0.f);
-    }
-    __device__ __forceinline__ void commit(float *dst) const {
-        const int r = threadIdx.x >> 3, c = (threadIdx.x & 7) * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[r * kPadT + c + e] = to_f(v[e]);
     }
 };
 // bf16 rows: the second phase's four 64 x 64 operands as bf16 hi / lo pairs
