@@ -17,7 +17,8 @@ Two implementations live here:
   debug.
 * ``gating`` -- g and beta from A_log, dt_bias, a, b in float64 (``gating.py``),
   and ``recurrent_gated``, the recurrence fed with those gates rounded to
-  float32 (the gates' type on the page that defines them).
+  float32 (the gates' type on the page that defines them); ``gating_bwd``, the
+  gradients of the gate inputs given those of g and beta.
 
 Parity is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``
 (hand-derived worked example, closed forms, invariants, the matrix-product
@@ -138,7 +139,7 @@ def recurrent(q, k, v, g, beta, scale=None, use_l2norm=False, initial_state=None
     return o.reshape(B, T, HV, V), fin.reshape(N, HV, K, V)
 
 
-from .gating import gating, sigmoid, softplus  # noqa: E402
+from .gating import gating, gating_bwd, sigmoid, softplus  # noqa: E402
 
 
 def recurrent_gated(q, k, v, A_log, dt_bias, a, b, **kw):

@@ -51,3 +51,29 @@ def gating(A_log, dt_bias, a, b):
         raise ValueError("gating expects A_log, dt_bias [HV] and a, b [..., HV]")
     g = -np.exp(A_log) * softplus(a + dt_bias)
     return g, sigmoid(b)
+
+
+def gating_bwd(A_log, dt_bias, a, b, dg, dbeta):
+    """Gradients of the gate inputs in float64, given dg and dbeta [..., HV]
+    (the gradients of g and beta, as the chunked backward pass returns them).
+
+    From the two definitions above, with x = a + dt_bias and the textbook
+    derivatives softplus'(x) = sigmoid(x), sigmoid'(b) = sigmoid(b)(1 -
+    sigmoid(b)), and d/dA_log exp(A_log) = exp(A_log):
+
+        da       = dg * (-exp(A_log) * sigmoid(a + dt_bias))
+        db       = dbeta * beta * (1 - beta)
+        ddt_bias = sum of da over every axis but the head axis
+        dA_log   = sum of dg * g over every axis but the head axis
+
+    Returns da, db (shape of a), dA_log, ddt_bias [HV]."""
+    A_log, dt_bias, a, b, dg, dbeta = (_f64(x) for x in (A_log, dt_bias, a, b, dg, dbeta))
+    if dg.shape != a.shape or dbeta.shape != b.shape:
+        raise ValueError("gating_bwd expects dg, dbeta shaped like a, b")
+    g, beta = gating(A_log, dt_bias, a, b)
+    da = dg * (-np.exp(A_log) * sigmoid(a + dt_bias))
+    db = dbeta * beta * (1.0 - beta)
+    HV = A_log.shape[0]
+    dA_log = (dg * g).reshape(-1, HV).sum(axis=0)
+    ddt_bias = da.reshape(-1, HV).sum(axis=0)
+    return da, db, dA_log, ddt_bias
