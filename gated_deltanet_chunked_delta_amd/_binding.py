@@ -19,7 +19,7 @@ GDN_BF16 = 0
 GDN_F32 = 1
 EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_pool", "gdn_chunk_fwd_workspace_bytes",
             "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
-            "gdn_gating", "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_recurrent_update_pool",
+            "gdn_gating", "gdn_gating_bwd", "gdn_gating_bwd_workspace_bytes", "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_recurrent_update_pool",
             "gdn_profile_enable", "gdn_profile_read", "gdn_status_str")
 
 _DTYPES = {torch.bfloat16: GDN_BF16, torch.float32: GDN_F32}
@@ -90,6 +90,11 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_recurrent_update_gated.restype = ctypes.c_int
     lib.gdn_gating.argtypes = [G, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.gdn_gating.restype = ctypes.c_int
+    lib.gdn_gating_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    lib.gdn_gating_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_gating_bwd.argtypes = [G, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P,
+                                   ctypes.c_size_t, P]
+    lib.gdn_gating_bwd.restype = ctypes.c_int
     SP = ctypes.POINTER(gdn_state_pool)
     lib.gdn_chunk_fwd_pool.argtypes = [P, P, P, P, P, G, ctypes.c_float, ctypes.c_int, SP, P, P,
                                        ctypes.POINTER(gdn_shape), P, ctypes.c_size_t, P]
@@ -436,6 +441,23 @@ def gdn_gating(gates: gdn_gates, rows, HV, dtype, g, beta, stream=None, device=N
                               ctypes.c_void_p(int(stream))))
 
 
+def gdn_gating_bwd_workspace_bytes(rows, HV) -> int:
+    return int(load_library().gdn_gating_bwd_workspace_bytes(int(rows), int(HV)))
+
+
+def gdn_gating_bwd(gates: gdn_gates, rows, HV, dtype, dg, dbeta, da, db, dA_log, ddt_bias, workspace,
+                   workspace_bytes=None, stream=None, device=None) -> int:
+    """Direct call of the C gate-gradient entry point; returns the status code."""
+    lib = load_library()
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(device if device is not None else dA_log.device).cuda_stream
+    return int(lib.gdn_gating_bwd(ctypes.byref(gates), int(rows), int(HV), int(dtype), _ptr(dg), _ptr(dbeta),
+                                  _ptr(da), _ptr(db), _ptr(dA_log), _ptr(ddt_bias), _ptr(workspace),
+                                  int(workspace_bytes), ctypes.c_void_p(int(stream))))
+
+
 def gdn_chunk_fwd_gated(q, k, v, gates: gdn_gates, scale, use_l2norm, initial_state, cu_seqlens, out,
                         final_state, shape: gdn_shape, workspace, workspace_bytes=None, stream=None) -> int:
     """Direct call of the C prefill entry point with in-kernel gating."""
@@ -492,6 +514,32 @@ def fused_gdn_gating(A_log, a, b, dt_bias):
     if st != GDN_OK:
         raise GdnError(st)
     return g, beta
+
+
+def fused_gdn_gating_bwd(A_log, a, b, dt_bias, dg, dbeta):
+    """Gradients of the gate inputs of fused_gdn_gating, given dg and dbeta
+    (float32, a's shape; as chunk_gated_delta_rule_bwd returns them).
+
+    Returns (da, db, dA_log, ddt_bias): da, db with a's shape and dtype,
+    dA_log, ddt_bias [HV] float32."""
+    _check(a.is_cuda, "tensors must be on a GPU device (there is no CPU path)")
+    _check(a.dtype in _DTYPES and b.dtype == a.dtype and tuple(b.shape) == tuple(a.shape) and a.dim() >= 1,
+           "a and b must share one shape [..., HV] and dtype (bfloat16 or float32)")
+    _check(dg.dtype == torch.float32 and dbeta.dtype == torch.float32 and tuple(dg.shape) == tuple(a.shape)
+           and tuple(dbeta.shape) == tuple(a.shape), "dg and dbeta must be float32 with a's shape")
+    HV = a.shape[-1]
+    A_log, dt_bias, ac, bc = _gate_inputs(A_log, dt_bias, a, b, tuple(a.shape), a.dtype, a.device)
+    dg, dbeta = dg.contiguous(), dbeta.contiguous()
+    rows = a.numel() // HV
+    da, db = torch.empty_like(ac), torch.empty_like(bc)
+    dA_log = torch.empty(HV, dtype=torch.float32, device=a.device)
+    ddt_bias = torch.empty_like(dA_log)
+    ws = torch.empty(max(gdn_gating_bwd_workspace_bytes(rows, HV), 1), dtype=torch.uint8, device=a.device)
+    st = gdn_gating_bwd(make_gates(A_log, dt_bias, ac, bc), rows, HV, _DTYPES[a.dtype], dg, dbeta, da, db,
+                        dA_log, ddt_bias, ws)
+    if st != GDN_OK:
+        raise GdnError(st)
+    return da, db, dA_log, ddt_bias
 
 
 def make_state_pool(data, indices, read_initial=True) -> gdn_state_pool:

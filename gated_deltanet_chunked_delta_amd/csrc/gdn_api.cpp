@@ -13,6 +13,13 @@
 #include "gdn_internal.h"
 
 namespace gdn {
+// Gate-input gradients (gdn_gating.hip).
+size_t gating_bwd_workspace_bytes(int64_t rows, int HV);
+hipError_t launch_gating_bwd(const Gates &gt, int64_t rows, int HV, int dtype, const float *dg, const float *dbeta,
+                             void *da, void *db, float *dA_log, float *ddt_bias, float *ws, hipStream_t stream);
+}  // namespace gdn
+
+namespace gdn {
 
 int elem_bytes(int dtype) { return dtype == GDN_BF16 ? 2 : dtype == GDN_F32 ? 4 : 0; }
 
@@ -409,6 +416,31 @@ int gdn_gating(const gdn_gates *gates, int64_t rows, int32_t HV, int32_t dtype, 
         std::lock_guard<std::mutex> lock(g_prof.mu);
         err = gdn::launch_gating(gt, rows, HV, dtype, g, beta, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
     }
+    return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+size_t gdn_gating_bwd_workspace_bytes(int64_t rows, int32_t HV) {
+    if (rows < 0 || HV <= 0 || rows > ((int64_t)1 << 62) / HV) return 0;
+    return gdn::gating_bwd_workspace_bytes(rows, HV);
+}
+
+int gdn_gating_bwd(const gdn_gates *gates, int64_t rows, int32_t HV, int32_t dtype, const float *dg,
+                   const float *dbeta, void *da, void *db, float *dA_log, float *ddt_bias, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    if (rows < 0 || HV <= 0 || rows > ((int64_t)1 << 62) / HV) return GDN_ERR_SHAPE;
+    if (gdn::elem_bytes(dtype) == 0) return GDN_ERR_DTYPE;
+    if (!gates || !gates->A_log || !gates->dt_bias || !dA_log || !ddt_bias) return GDN_ERR_NULL;
+    if (rows > 0) {
+        if (!dg || !dbeta || !da || !db) return GDN_ERR_NULL;
+        const int st = check_gates(*gates);
+        if (st != GDN_OK) return st;
+    }
+    const size_t need = gdn::gating_bwd_workspace_bytes(rows, HV);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0))
+        return GDN_ERR_WORKSPACE;
+    const gdn::Gates gt{gates->A_log, gates->dt_bias, gates->a, gates->b};
+    const hipError_t err = gdn::launch_gating_bwd(gt, rows, HV, dtype, dg, dbeta, da, db, dA_log, ddt_bias,
+                                                  (float *)workspace, (hipStream_t)stream);
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

@@ -76,7 +76,113 @@ __global__ void __launch_bounds__(256) gating_kernel(Gates gt, int64_t n, int HV
     }
 }
 
+// ---------------------------------------------------------------------------
+// Backward of the gate computation.  With x = a + dt_bias, s = sigmoid(x) and
+// beta = sigmoid(b) (softplus' = sigmoid, sigmoid' = sigmoid (1 - sigmoid)):
+//   da = dg * (-exp(A_log) s),  db = dbeta * beta (1 - beta),
+//   dA_log[j] = sum_r dg g,  ddt_bias[j] = sum_r da  (over the rows r).
+// gating_bwd_kernel: 64 rows per workgroup; lanes (row lane rl, column lane
+// cl) walk the tile, write da, db and leave the workgroup's per-head sums in
+// the workspace, reduced over the row lanes in a fixed order.
+// gating_bwd_sum_kernel: one workgroup per head adds the workgroups' sums in a
+// fixed order, so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------
+constexpr int kGateTile = 64, kGateThreads = 256;
+
+template <typename E>
+__global__ void __launch_bounds__(kGateThreads) gating_bwd_kernel(Gates gt, int64_t rows, int HV,
+                                                                 const float *__restrict__ dg,
+                                                                 const float *__restrict__ dbeta, E *__restrict__ da,
+                                                                 E *__restrict__ db, float *__restrict__ part) {
+    __shared__ float red[2][kGateThreads];
+    const E *__restrict__ a = (const E *)gt.a;
+    const E *__restrict__ b = (const E *)gt.b;
+    const int CL = HV < kGateThreads ? HV : kGateThreads;   // column lanes
+    const int P = kGateThreads / CL;                          // row lanes
+    const int cl = threadIdx.x % CL, rl = threadIdx.x / CL;
+    const int64_t r0 = (int64_t)blockIdx.x * kGateTile;
+    const int64_t r1 = r0 + kGateTile < rows ? r0 + kGateTile : rows;
+    const int64_t nblk = gridDim.x;
+    for (int j0 = 0; j0 < HV; j0 += CL) {   // the same trip count in every thread
+        const int j = j0 + cl;
+        float sA = 0.f, sD = 0.f;
+        if (rl < P && j < HV) {
+            const float negA = -expf(gt.A_log[j]), dtb = gt.dt_bias[j];
+            for (int64_t r = r0 + rl; r < r1; r += P) {
+                const int64_t e = r * HV + j;
+                const float x = to_f(a[e]) + dtb;
+                const float dgv = dg[e];
+                const float dav = dgv * negA * gate_beta(x);
+                const float bv = gate_beta(to_f(b[e]));
+                da[e] = to_e<E>(dav);
+                db[e] = to_e<E>(dbeta[e] * bv * (1.f - bv));
+                sA = fmaf(dgv, gate_g(to_f(a[e]), negA, dtb), sA);
+                sD += dav;
+            }
+        }
+        red[0][threadIdx.x] = sA;
+        red[1][threadIdx.x] = sD;
+        __syncthreads();
+        if (rl == 0 && j < HV) {
+            float tA = 0.f, tD = 0.f;
+            for (int u = 0; u < P; ++u) {
+                tA += red[0][u * CL + cl];
+                tD += red[1][u * CL + cl];
+            }
+            part[(int64_t)j * nblk + blockIdx.x] = tA;
+            part[((int64_t)HV + j) * nblk + blockIdx.x] = tD;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(kGateThreads) gating_bwd_sum_kernel(const float *__restrict__ part, int64_t nblk,
+                                                                     int HV, float *__restrict__ dA_log,
+                                                                     float *__restrict__ ddt_bias) {
+    __shared__ float red[2][kGateThreads];
+    const int j = blockIdx.x;
+    float tA = 0.f, tD = 0.f;
+    for (int64_t u = threadIdx.x; u < nblk; u += kGateThreads) {
+        tA += part[(int64_t)j * nblk + u];
+        tD += part[((int64_t)HV + j) * nblk + u];
+    }
+    red[0][threadIdx.x] = tA;
+    red[1][threadIdx.x] = tD;
+    __syncthreads();
+    for (int w = kGateThreads / 2; w > 0; w >>= 1) {   // fixed-order tree
+        if ((int)threadIdx.x < w) {
+            red[0][threadIdx.x] += red[0][threadIdx.x + w];
+            red[1][threadIdx.x] += red[1][threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        dA_log[j] = red[0][0];
+        ddt_bias[j] = red[1][0];
+    }
+}
+
 }  // namespace
+
+size_t gating_bwd_workspace_bytes(int64_t rows, int HV) {
+    const int64_t nblk = (rows + kGateTile - 1) / kGateTile;
+    return (size_t)(2 * nblk * (int64_t)HV) * sizeof(float);
+}
+
+hipError_t launch_gating_bwd(const Gates &gt, int64_t rows, int HV, int dtype, const float *dg, const float *dbeta,
+                             void *da, void *db, float *dA_log, float *ddt_bias, float *ws, hipStream_t stream) {
+    const int64_t nblk = (rows + kGateTile - 1) / kGateTile;
+    if (nblk > 0) {
+        if (dtype == 0)
+            gating_bwd_kernel<bf16><<<(unsigned)nblk, kGateThreads, 0, stream>>>(gt, rows, HV, dg, dbeta, (bf16 *)da,
+                                                                                 (bf16 *)db, ws);
+        else
+            gating_bwd_kernel<float><<<(unsigned)nblk, kGateThreads, 0, stream>>>(gt, rows, HV, dg, dbeta,
+                                                                                  (float *)da, (float *)db, ws);
+    }
+    gating_bwd_sum_kernel<<<(unsigned)HV, kGateThreads, 0, stream>>>(ws, nblk, HV, dA_log, ddt_bias);
+    return hipGetLastError();
+}
 
 hipError_t launch_gating(const Gates &gt, int64_t rows, int HV, int dtype, float *g, float *beta,
                          hipStream_t stream, Profiler *prof) {

@@ -208,6 +208,38 @@ typedef struct gdn_gates {
 int gdn_gating(const gdn_gates *gates, int64_t rows, int32_t HV, int32_t dtype,
                float *g, float *beta, void *stream);
 
+/* Bytes of device workspace gdn_gating_bwd needs for rows x HV (two floats per
+ * head and 64-row block); 0 for invalid sizes or when rows == 0. */
+size_t gdn_gating_bwd_workspace_bytes(int64_t rows, int32_t HV);
+
+/* Backward of gdn_gating (training): the gradients of the raw gate inputs,
+ * given dg and dbeta [rows, HV] fp32 (the gradients of g and beta, as
+ * gdn_chunk_bwd writes them).  By the chain rule through the two gate
+ * definitions above (softplus' = sigmoid, sigmoid' = sigmoid (1 - sigmoid)):
+ *
+ *   da[r, j]    = dg[r, j] * (-exp(A_log[j])) * sigmoid(a[r, j] + dt_bias[j])
+ *   db[r, j]    = dbeta[r, j] * beta (1 - beta),   beta = sigmoid(b[r, j])
+ *   dA_log[j]   = sum_r dg[r, j] * g[r, j]
+ *   ddt_bias[j] = sum_r da[r, j]
+ *
+ *   gates         A_log, dt_bias [HV] fp32 and a, b [rows, HV] of dtype (read)
+ *   dg, dbeta     [rows, HV] fp32 (read)
+ *   da, db        [rows, HV] dtype, written (every element; fp32 arithmetic,
+ *                 rounded once to dtype)
+ *   dA_log, ddt_bias  [HV] fp32, written (zero when rows == 0)
+ *   workspace     gdn_gating_bwd_workspace_bytes bytes, 16-byte aligned
+ *                 (may be NULL when that is 0); contents on entry ignored
+ *
+ * The sums over rows are taken in a fixed order (per 64-row block, then over
+ * the blocks), so the result is the same on every call.  Returns GDN_OK,
+ * GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_NULL (a required pointer NULL: A_log,
+ * dt_bias, dA_log, ddt_bias always, the rest when rows > 0), GDN_ERR_ALIGN (a, b
+ * not 4-byte aligned), GDN_ERR_WORKSPACE, GDN_ERR_LAUNCH. */
+int gdn_gating_bwd(const gdn_gates *gates, int64_t rows, int32_t HV, int32_t dtype,
+                   const float *dg, const float *dbeta,
+                   void *da, void *db, float *dA_log, float *ddt_bias,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* gdn_chunk_fwd with the gates computed in the kernel from `gates` (rows =
  * B * T) instead of read from g and beta: the same result as gdn_gating
  * followed by gdn_chunk_fwd, up to rounding, with no g / beta tensors in

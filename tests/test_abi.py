@@ -175,6 +175,34 @@ def test_gating_argument_errors(rows, HV, dtype, gates, want):
     assert lib.gdn_gating(gs, rows, HV, dtype, P(FAKE), P(FAKE), None) == want
 
 
+@pytest.mark.parametrize("rows,HV,dtype,gates,null,ws,want", [
+    (-1, 4, 0, {}, None, 1, -2), (4, 0, 0, {}, None, 1, -2), (4, 4, 5, {}, None, 1, -3),
+    (4, 4, 0, None, None, 1, -1), (4, 4, 0, dict(dt=0), None, 1, -1),
+    (4, 4, 0, {}, "dA_log", 1, -1), (4, 4, 0, {}, "dg", 1, -1), (4, 4, 0, {}, "db", 1, -1),
+    (4, 4, 0, dict(a=FAKE + 2), None, 1, -7),
+    (4, 4, 0, {}, None, 0, -5),                                  # workspace missing
+    (4, 4, 0, {}, None, 2, -5),                                  # workspace misaligned
+    (4, 4, 0, {}, None, 3, -5),                                  # workspace too small
+])
+def test_gating_bwd_argument_errors(rows, HV, dtype, gates, null, ws, want):
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    gs = None if gates is None else ctypes.byref(_gates(**gates))
+    ptr = {n: (None if n == null else P(FAKE)) for n in ("dg", "dbeta", "da", "db", "dA_log", "ddt_bias")}
+    need = gdn.gdn_gating_bwd_workspace_bytes(max(rows, 0), max(HV, 1))
+    wsp, wsb = {0: (None, 0), 1: (P(FAKE), need), 2: (P(FAKE + 4), need), 3: (P(FAKE), need - 4)}[ws]
+    assert lib.gdn_gating_bwd(gs, rows, HV, dtype, ptr["dg"], ptr["dbeta"], ptr["da"], ptr["db"], ptr["dA_log"],
+                              ptr["ddt_bias"], wsp, wsb, None) == want
+
+
+def test_gating_bwd_workspace_size():
+    # two floats per head and 64-row block
+    assert gdn.gdn_gating_bwd_workspace_bytes(1000, 32) == 2 * 16 * 32 * 4
+    assert gdn.gdn_gating_bwd_workspace_bytes(64, 3) == 2 * 1 * 3 * 4
+    assert gdn.gdn_gating_bwd_workspace_bytes(0, 32) == 0
+    assert gdn.gdn_gating_bwd_workspace_bytes(-1, 32) == 0 and gdn.gdn_gating_bwd_workspace_bytes(8, 0) == 0
+
+
 def test_gating_wrappers_reject_cpu_tensors_and_mixed_gates():
     import torch
     a = torch.zeros(3, 4, dtype=torch.bfloat16)
