@@ -89,3 +89,44 @@ def test_gating_bwd_deterministic_and_matches_chunk_bwd_gate_shapes():
     assert tuple(r1[0].shape) == (2, 700, 8) and tuple(r1[1].shape) == (2, 700, 8)
     for x, y in zip(r1, r2):
         assert torch.equal(x, y)
+
+
+def test_training_chain_gates_to_gate_inputs():
+    """GPU gating, the chunked backward pass and the gate-input gradients in a
+    row (fp32 I/O), against the oracle's float64 chain: gates, backward,
+    gate-input gradients.  The chunked backward's bar (1e-4 of max|dg|, max|dbeta|
+    per element) carries through the linear maps that follow it."""
+    from oracle.backward import backward as oracle_backward
+    from workloads import WORKLOADS, make_grad_inputs, make_inputs, scaled
+
+    gdn = _gdn()
+    w = scaled(WORKLOADS["gva"], "chain", B=2, T=150, H=2, HV=4)
+    x = make_grad_inputs(make_inputs(w, seed=5, io_dtype=torch.float32), seed=105)
+    dev = lambda t: None if t is None else t.to(DEV)
+    g, beta = gdn.fused_gdn_gating(dev(x["A_log"]), dev(x["a"]), dev(x["b"]), dev(x["dt_bias"]))
+    out = gdn.chunk_gated_delta_rule_bwd(dev(x["q"]), dev(x["k"]), dev(x["v"]), g, beta, dev(x["do"]),
+                                         dht=dev(x["dht"]), scale=x["scale"], initial_state=dev(x["initial_state"]),
+                                         use_qk_l2norm_in_kernel=x["use_l2norm"])
+    dg, dbeta = out[3], out[4]
+    da, db, dA, ddt = gdn.fused_gdn_gating_bwd(dev(x["A_log"]), dev(x["a"]), dev(x["b"]), dev(x["dt_bias"]),
+                                               dg, dbeta)
+    torch.cuda.synchronize()
+
+    g64, b64 = oracle.gating(x["A_log"], x["dt_bias"], x["a"], x["b"])
+    ref = oracle_backward(x["q"], x["k"], x["v"], torch.from_numpy(g64), torch.from_numpy(b64), x["do"],
+                          dht=x["dht"], scale=x["scale"], use_l2norm=x["use_l2norm"],
+                          initial_state=x["initial_state"])
+    rda, rdb, rdA, rddt = oracle.gating_bwd(x["A_log"], x["dt_bias"], x["a"], x["b"], ref["dg"], ref["dbeta"])
+    mdg, mdb = float(np.abs(ref["dg"]).max()), float(np.abs(ref["dbeta"]).max())
+    A = np.exp(x["A_log"].double().numpy())
+    fac = A * oracle.sigmoid(x["a"].double().numpy() + x["dt_bias"].double().numpy())   # |d g / d a|
+    bb = b64 * (1 - b64)                                                                  # d beta / d b
+    HV = w.HV
+    err_da = np.abs(da.cpu().numpy() - rda)
+    err_db = np.abs(db.cpu().numpy() - rdb)
+    assert np.all(err_da <= 1e-4 * mdg * fac + 1e-6 * np.abs(rda).max()), float(err_da.max())
+    assert np.all(err_db <= 1e-4 * mdb * bb + 1e-6 * np.abs(rdb).max()), float(err_db.max())
+    bA = 1e-4 * mdg * np.abs(g64).reshape(-1, HV).sum(axis=0) + 1e-6 * np.abs(ref["dg"] * g64).reshape(-1, HV).sum(axis=0)
+    bD = 1e-4 * mdg * fac.reshape(-1, HV).sum(axis=0) + 1e-6 * np.abs(rda).reshape(-1, HV).sum(axis=0)
+    assert np.all(np.abs(dA.cpu().numpy() - rdA) <= bA) and np.all(np.abs(ddt.cpu().numpy() - rddt) <= bD)
+    _say(f"    chain: max|da err| {float(err_da.max()):.2e} max|db err| {float(err_db.max()):.2e}")
