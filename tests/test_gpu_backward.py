@@ -85,6 +85,7 @@ SMALL = {
     "wide_small": scaled(WORKLOADS["wide_stable"], "wide_small", B=3, T=257, H=2, HV=4),
     "k64_v128": scaled(WORKLOADS["gva"], "k64_v128", B=2, T=190, H=2, HV=4, K=64, V=128),
     "k128_v64": scaled(WORKLOADS["gva"], "k128_v64", B=2, T=130, H=1, HV=3, K=128, V=64),
+    "four_per_key_head": scaled(WORKLOADS["gva"], "four_per_key_head", B=1, T=200, H=2, HV=8),
 }
 
 
