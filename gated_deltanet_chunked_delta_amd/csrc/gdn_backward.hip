@@ -51,6 +51,8 @@
 // (layout in BwdPlan).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -285,19 +287,26 @@ struct Mat64RegN {
 // tensor at value head j, into dst[64][VW+1] as fp32.
 template <typename E, int VW, int NTH>
 struct TileRegN {
-    static_assert(kChunk * VW == 8 * NTH, "one 8-element run per thread");
-    typename VT<E>::v8 v;
+    static constexpr int EPT = kChunk * VW / NTH;   // consecutive elements per thread
+    static_assert(EPT == 8 || EPT == 4, "one run of 8 or 4 elements per thread");
+    typedef typename VT<E>::v8 v8t;
+    typedef typename VT<E>::v4 v4t;
+    typename std::conditional<EPT == 8, v8t, v4t>::type v;
     __device__ __forceinline__ void load(const E *src, int t0, int L, int HV, int j, int V, int c0) {
-        const int r = threadIdx.x / (VW / 8), c = (threadIdx.x % (VW / 8)) * 8;
-        if (r < L) v = ld8<E>(src + ((int64_t)(t0 + r) * HV + j) * V + c0 + c);
-        else
+        const int r = threadIdx.x / (VW / EPT), c = (threadIdx.x % (VW / EPT)) * EPT;
+        if (r < L) {
+            const E *at = src + ((int64_t)(t0 + r) * HV + j) * V + c0 + c;
+            if constexpr (EPT == 8) v = ld8<E>(at);
+            else v = *(const v4t *)at;
+        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = to_e<E>(0.f);
+            for (int e = 0; e < EPT; ++e) v[e] = to_e<E>(0.f);
+        }
     }
     __device__ __forceinline__ void commit(float *dst) const {
-        const int r = threadIdx.x / (VW / 8), c = (threadIdx.x % (VW / 8)) * 8;
+        const int r = threadIdx.x / (VW / EPT), c = (threadIdx.x % (VW / EPT)) * EPT;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[r * (VW + 1) + c + e] = to_f(v[e]);
+        for (int e = 0; e < EPT; ++e) dst[r * (VW + 1) + c + e] = to_f(v[e]);
     }
 };
 // K rows x VW columns from c0 of a K x V fp32 state (row stride V), to and from dst[K][VW+1].
@@ -1328,19 +1337,43 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
         if (prof) prof->end(kBwdPrepKernel, st);
     }
     if (p.N > 0) {
+        // Scan tiles (bf16 rows): 64 value columns and 8 waves when the
+        // (sequence, value head, 64-column) workgroups fill the GPU; with fewer,
+        // narrower tiles give each wave half the products of a chunk step, so
+        // the serial chain runs faster while the workgroups still fit in one
+        // round: 32 columns x 8 waves (at most 128 wide workgroups), 16 x 4
+        // (at most 64).  fp32 rows need twice the LDS: 32 columns, 4 waves.
+        const int64_t wide = (int64_t)p.N * p.HV * (V / 64);
+        const int narrow = wide <= 64 ? 2 : wide <= 128 ? 1 : 0;
         if (nc_max > 0) {
-            constexpr int FVW = sizeof(E) == 2 ? 64 : 32, FNTH = sizeof(E) == 2 ? 512 : 256;
             if (prof) prof->begin(kBwdFwdScanKernel, st);
-            hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, FVW, FNTH>), dim3(p.N * p.HV, V / FVW), dim3(FNTH), 0, st,
-                               p);
+            if constexpr (sizeof(E) == 2) {
+                if (narrow == 2)
+                    hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, 16, 256>), dim3(p.N * p.HV, V / 16), dim3(256), 0,
+                                       st, p);
+                else if (narrow == 1)
+                    hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, 32, 512>), dim3(p.N * p.HV, V / 32), dim3(512), 0,
+                                       st, p);
+                else
+                    hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, 64, 512>), dim3(p.N * p.HV, V / 64), dim3(512), 0,
+                                       st, p);
+            } else {
+                hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, 32, 256>), dim3(p.N * p.HV, V / 32), dim3(256), 0, st,
+                                   p);
+            }
             if (prof) prof->end(kBwdFwdScanKernel, st);
         }
-        // bf16 rows: 64 value columns and 8 waves per workgroup; fp32 rows need
-        // twice the LDS, so 32 columns and 4 waves
-        constexpr bool kB16 = sizeof(E) == 2;
-        constexpr int DVW = kB16 ? 64 : 32, DNTH = kB16 ? 512 : 256;
         if (prof) prof->begin(kBwdDhScanKernel, st);
-        hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K, DVW, DNTH>), dim3(p.N * p.HV, V / DVW), dim3(DNTH), 0, st, p);
+        if constexpr (sizeof(E) == 2) {
+            if (narrow == 2)
+                hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K, 16, 256>), dim3(p.N * p.HV, V / 16), dim3(256), 0, st, p);
+            else if (narrow == 1)
+                hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K, 32, 512>), dim3(p.N * p.HV, V / 32), dim3(512), 0, st, p);
+            else
+                hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K, 64, 512>), dim3(p.N * p.HV, V / 64), dim3(512), 0, st, p);
+        } else {
+            hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K, 32, 256>), dim3(p.N * p.HV, V / 32), dim3(256), 0, st, p);
+        }
         if (prof) prof->end(kBwdDhScanKernel, st);
     }
     if (nc_max > 0) {

@@ -86,6 +86,10 @@ SMALL = {
     "k64_v128": scaled(WORKLOADS["gva"], "k64_v128", B=2, T=190, H=2, HV=4, K=64, V=128),
     "k128_v64": scaled(WORKLOADS["gva"], "k128_v64", B=2, T=130, H=1, HV=3, K=128, V=64),
     "four_per_key_head": scaled(WORKLOADS["gva"], "four_per_key_head", B=1, T=200, H=2, HV=8),
+    # the scans' tile width follows the (sequence, value head) count: 3 x 16 heads
+    # take 32-column tiles, 5 x 16 the 64-column ones (the cases above, 16-column)
+    "mid_width_tiles": scaled(WORKLOADS["gva"], "mid_width_tiles", B=3, T=200, H=8, HV=16),
+    "wide_tiles": scaled(WORKLOADS["gva"], "wide_tiles", B=5, T=130, H=8, HV=16),
 }
 
 
