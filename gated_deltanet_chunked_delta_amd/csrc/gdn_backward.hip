@@ -698,6 +698,193 @@ __global__ __launch_bounds__(NTH) void bwd_fwd_scan_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// The forward rescan for bf16 rows with 64 value columns and 8 waves, with its
+// two products over 128 keys / 64 tokens on the bf16 matrix cores: K h with
+// the raw bf16 key rows (exact) against bf16 hi / lo parts of the state, and
+// K^T F with the transposed raw rows against hi / lo parts of F.  The state
+// stays in fp32 (hs and the update use it); its hi / lo copy, transposed to
+// [value column][key], is refreshed by every update.  Tm B keeps fp32 products.
+// ---------------------------------------------------------------------------
+template <int K>
+constexpr int fwd_scan_b16_floats() {
+    return K * 65 + (2 * 64 * (K + 8) * 2) / 4 + (kChunk * (K + 8) * 2) / 4 + (K * 72 * 2) / 4 + 2 * kChunk * kPadC +
+           (2 * 64 * 72 * 2) / 4 + 5 * kChunk;
+}
+static_assert(fwd_scan_b16_floats<128>() * 4 <= 160 * 1024, "bf16 forward rescan must fit one CU");
+
+template <int K>
+__global__ __launch_bounds__(512) void bwd_fwd_scan_b16_kernel(BwdParams p) {
+    typedef bf16 E;
+    constexpr int NTH = 512, VW = 64, VP = VW + 1, KP = K + 8, W = 8, CT = VW / 16;
+    constexpr int NT1 = 4 * CT / W;          // 2 tiles of the 64 x 64 products per wave
+    constexpr int NT2 = (K / 16) * CT / W;   // tiles of the K x 64 state per wave
+    __shared__ __attribute__((aligned(16))) float sm[fwd_scan_b16_floats<K>()];
+    float *h = sm;                           // [K][65] fp32 state
+    bf16 *hTHi = (bf16 *)(h + K * VP);       // [64][KP] state, transposed, hi part
+    bf16 *hTLo = hTHi + 64 * KP;             // [64][KP] lo part
+    bf16 *kr = hTLo + 64 * KP;               // [64][KP] raw k rows
+    bf16 *kT = kr + kChunk * KP;             // [K][72] raw k rows transposed
+    float *Tm = (float *)(kT + K * 72);      // [64][65]
+    float *Bm = Tm + kChunk * kPadC;         // [64][65]: v, then B in place
+    bf16 *FTHi = (bf16 *)(Bm + kChunk * kPadC);   // [64][72] F transposed, hi
+    bf16 *FTLo = FTHi + 64 * 72;                  // lo
+    float *gam = (float *)(FTLo + 64 * 72);  // [64]
+    float *bet = gam + kChunk;               // [64]
+    float *sD = bet + kChunk;                // [64] exp(gamma) / |k|
+    float *sF = sD + kChunk;                 // [64] exp(gamma_L - gamma), 0 past L
+    float *sFk = sF + kChunk;                // [64] exp(gamma_L - gamma) / |k|, 0 past L
+
+    const int HV = p.HV, V = p.V;
+    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int c0 = blockIdx.y * VW;
+    int bos, len, cid0;
+    seq_of(p, n, bos, len, cid0);
+    const int nc = (len + kChunk - 1) / kChunk;
+    const int i16 = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
+
+    if (p.initial_state) {
+        StateTileN<K, VW, NTH> r0;
+        r0.load(p.initial_state + ((int64_t)n * HV + j) * K * V, V, c0);
+        r0.commit(h);
+    } else {
+        for (int e = threadIdx.x; e < K * VW; e += NTH) h[(e / VW) * VP + e % VW] = 0.f;
+    }
+    lds_barrier();
+    for (int e = threadIdx.x; e < K * VW; e += NTH) {   // the transposed hi / lo copy
+        const int r = e / VW, c = e % VW;
+        const float x = h[r * VP + c];
+        const bf16 hi = (bf16)x;
+        hTHi[c * KP + r] = hi;
+        hTLo[c * KP + r] = (bf16)(x - (float)hi);
+    }
+    RawRowsReg<E, K, NTH, 8> rk;
+    Mat64RegN<NTH> rt;
+    TileRegN<E, VW, NTH> rv;
+    float rg = 0.f, rb = 0.f;
+    auto fetch = [&](int ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        rk.load((const E *)p.k, t0, L, p.H, jk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rv.load((const E *)p.v, t0, L, HV, j, V, c0);
+        if (threadIdx.x < kChunk) {
+            const int r = threadIdx.x;
+            rg = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
+            rb = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+        }
+    };
+    if (nc > 0) fetch(0);
+    const int w = wave_id();
+    auto ra = [&](int t) { return 16 * ((w * NT1 + t) / CT); };
+    auto cb = [&](int t) { return 16 * ((w * NT1 + t) % CT); };
+    auto rs = [&](int t) { return 16 * ((w * NT2 + t) / CT); };
+    auto cs = [&](int t) { return 16 * ((w * NT2 + t) % CT); };
+    for (int ci = 0; ci < nc; ++ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        StateTileN<K, VW, NTH>::store(h, p.hs + ((int64_t)cid * HV + j) * K * V, V, c0);
+        rk.commit(kr);
+#pragma unroll
+        for (int u = 0; u < RawRowsReg<E, K, NTH, 8>::VPT; ++u) {
+            constexpr int PER_ROW = K / 8;
+            const int i = threadIdx.x + NTH * u, r = i / PER_ROW, c = (i % PER_ROW) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kT[(c + e) * 72 + r] = rk.v[u][e];
+        }
+        rt.commit(Tm);
+        rv.commit(Bm);
+        if (threadIdx.x < kChunk) {
+            gam[threadIdx.x] = rg;
+            bet[threadIdx.x] = rb;
+        }
+        lds_barrier();
+        {
+            constexpr int LPR = NTH / kChunk;   // lanes per row
+            const int r = threadIdx.x / LPR;
+            const float sk = row_sumsq<E, K, NTH, 8>(kr, r);
+            if (threadIdx.x % LPR == 0) {
+                const float fk = p.use_l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
+                const float f = r < L ? __expf(gam[L - 1] - gam[r]) : 0.f;
+                sD[r] = __expf(gam[r]) * fk;
+                sF[r] = f;
+                sFk[r] = f * fk;
+            }
+        }
+        lds_barrier();
+        if (ci + 1 < nc) fetch(ci + 1);
+
+        // B = diag(beta) (V - diag(D) Kh h): K_raw (exact) times the hi and lo parts of h
+        {
+            f32x4 x[NT1];
+            zero(x);
+#pragma unroll
+            for (int k0 = 0; k0 < K; k0 += 32) {
+                const bf16x8 a = *(const bf16x8 *)(kr + (ra(0) + i16) * KP + k0 + 8 * q);
+#pragma unroll
+                for (int t = 0; t < NT1; ++t) {
+                    const int bo = (cb(t) + i16) * KP + k0 + 8 * q;
+                    x[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, *(const bf16x8 *)(hTHi + bo), x[t], 0, 0, 0);
+                    x[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, *(const bf16x8 *)(hTLo + bo), x[t], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT1; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = lrow(ra(t), e), c = lcol(cb(t));
+                    Bm[r * VP + c] = bet[r] * (Bm[r * VP + c] - sD[r] * x[t][e]);
+                }
+        }
+        lds_barrier();
+        // Vn = Tm B; F = diag(exp(gamma_L - gamma) / |k|) Vn, transposed, as hi / lo parts
+        {
+            f32x4 x[NT1];
+            zero(x);
+            wmm<NT1, kChunk>(x, ra, cb, [&](int r, int m) { return Tm[r * kPadC + m]; },
+                             [&](int c, int m) { return Bm[m * VP + c]; });
+#pragma unroll
+            for (int t = 0; t < NT1; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = lrow(ra(t), e), c = lcol(cb(t));
+                    if (r < L) p.vn[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = x[t][e];
+                    const float f = sFk[r] * x[t][e];
+                    const bf16 hi = (bf16)f;
+                    FTHi[c * 72 + r] = hi;
+                    FTLo[c * 72 + r] = (bf16)(f - (float)hi);
+                }
+        }
+        lds_barrier();
+        // h <- D_L h + Kh^T F: K_raw^T (exact) times the hi and lo parts of F
+        {
+            f32x4 x[NT2];
+            zero(x);
+#pragma unroll
+            for (int m0 = 0; m0 < kChunk; m0 += 32) {
+#pragma unroll
+                for (int t = 0; t < NT2; ++t) {
+                    const bf16x8 a = *(const bf16x8 *)(kT + (rs(t) + i16) * 72 + m0 + 8 * q);
+                    const int bo = (cs(t) + i16) * 72 + m0 + 8 * q;
+                    x[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, *(const bf16x8 *)(FTHi + bo), x[t], 0, 0, 0);
+                    x[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, *(const bf16x8 *)(FTLo + bo), x[t], 0, 0, 0);
+                }
+            }
+            const float dl = __expf(gam[L - 1]);
+#pragma unroll
+            for (int t = 0; t < NT2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = lrow(rs(t), e), c = lcol(cs(t));
+                    float &hv = h[r * VP + c];
+                    hv = fmaf(dl, hv, x[t][e]);
+                    const bf16 hi = (bf16)hv;
+                    hTHi[c * KP + r] = hi;
+                    hTLo[c * KP + r] = (bf16)(hv - (float)hi);
+                }
+        }
+        lds_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // backward over chunks per (sequence, value head, VW value columns), NTH
 // threads: dh' per chunk, dB, and the initial-state gradient.  The key and
 // query rows stay raw in LDS; their L2 norms enter as the row scales sFk, sD
@@ -1355,8 +1542,7 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
                     hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, 32, 512>), dim3(p.N * p.HV, V / 32), dim3(512), 0,
                                        st, p);
                 else
-                    hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, 64, 512>), dim3(p.N * p.HV, V / 64), dim3(512), 0,
-                                       st, p);
+                    hipLaunchKernelGGL((bwd_fwd_scan_b16_kernel<K>), dim3(p.N * p.HV, V / 64), dim3(512), 0, st, p);
             } else {
                 hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, 32, 256>), dim3(p.N * p.HV, V / 32), dim3(256), 0, st,
                                    p);
