@@ -53,30 +53,32 @@ __global__ void __launch_bounds__(256) split_setup_kernel(SplitDims d, const flo
 }
 
 // h_1 = h0_0 (segment 0 ran from the true initial state); h_{s+1} = M_s h_s +
-// h0_s; h_s (s >= 1) are published for the correction, h_S is the final
-// state.  One workgroup per (sequence, value head, 32 state columns): M_s and
-// the workgroup's columns of h_s in LDS, each thread a 4 x 4 block of the
-// product, fp32 throughout.
+// h0_s; h_s (s >= 1) are published for the correction, transposed ([V][K])
+// and rounded to the I/O type once, which is how the correction's products
+// take them; h_S is the final state.  One workgroup per (sequence, value
+// head, 32 state columns): M_s and the workgroup's columns of h_s in LDS,
+// each thread a 4 x 4 block of the product, fp32 throughout.
 constexpr int kCombineCols = 32;
 
+template <typename E>
 __global__ void __launch_bounds__(256) split_combine_kernel(SplitDims d, const float *__restrict__ pool,
-                                                            const float *__restrict__ maps, float *__restrict__ hs,
+                                                            const float *__restrict__ maps, E *__restrict__ hsT,
                                                             float *__restrict__ final_state) {
-    constexpr int CW = kCombineCols, MP = 128 + 4;   // padded rows of M
-    __shared__ float h[128 * CW], m[128 * MP];
+    constexpr int CW = kCombineCols, CP = CW + 4, MP = 128 + 4;   // padded rows of h and M
+    __shared__ __attribute__((aligned(16))) float h[128 * CP], m[128 * MP];
     const int K = d.K, V = d.V, ncb = V / CW;
     const int cb = blockIdx.x % ncb, bj = blockIdx.x / ncb;
     const int b = bj / d.HV, j = bj % d.HV, col0 = cb * CW;
     const int t = threadIdx.x, nb = (K / 4) * (CW / 4);
     const int r0 = 4 * (t / (CW / 4)), c0 = 4 * (t % (CW / 4));
     const float *h0 = pool + ((int64_t)b * d.S * d.HV + j) * K * V;
-    for (int i = t; i < K * CW; i += blockDim.x) h[i] = h0[(i / CW) * V + col0 + i % CW];
+    for (int i = t; i < K * CW; i += blockDim.x) h[(i / CW) * CP + i % CW] = h0[(i / CW) * V + col0 + i % CW];
     __syncthreads();
     for (int s = 1; s < d.S; ++s) {
         const int64_t slot = (int64_t)b * d.S + s;
-        float *hsd = hs + (slot * d.HV + j) * K * V;
+        E *hsd = hsT + (slot * d.HV + j) * K * V + (int64_t)col0 * K;   // rows col0.. of [V][K]
         const float *ms = maps + (slot * d.HV + j) * K * K;
-        for (int i = t; i < K * CW; i += blockDim.x) hsd[(i / CW) * V + col0 + i % CW] = h[i];
+        for (int i = t; i < K * CW; i += blockDim.x) hsd[i] = to_e<E>(h[(i % K) * CP + i / K]);
         for (int i = t; i < K * K; i += blockDim.x) m[(i / K) * MP + i % K] = ms[i];
         __syncthreads();
         float acc[4][4];
@@ -90,7 +92,7 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitDims d, const f
                 float mv[4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) mv[a] = m[(r0 + a) * MP + kk];
-                const f32x4 hv = *(const f32x4 *)&h[kk * CW + c0];
+                const f32x4 hv = *(const f32x4 *)&h[kk * CP + c0];
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -101,13 +103,13 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitDims d, const f
         if (t < nb) {
 #pragma unroll
             for (int a = 0; a < 4; ++a)
-                *(f32x4 *)&h[(r0 + a) * CW + c0] = f32x4{acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
+                *(f32x4 *)&h[(r0 + a) * CP + c0] = f32x4{acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
         }
         __syncthreads();
     }
     if (final_state) {
         float *fd = final_state + ((int64_t)b * d.HV + j) * K * V;
-        for (int i = t; i < K * CW; i += blockDim.x) fd[(i / CW) * V + col0 + i % CW] = h[i];
+        for (int i = t; i < K * CW; i += blockDim.x) fd[(i / CW) * V + col0 + i % CW] = h[(i / CW) * CP + i % CW];
     }
 }
 
@@ -115,13 +117,18 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitDims d, const f
 // sum_k oM[token][k] h_s[k][v] on MFMA (bf16 operands, or fp32 in the check
 // mode), added to the output in fp32 and rounded once.  One workgroup per
 // (sequence, segment, value head, TB x 64 tokens); each wave 16 tokens of a
-// 64-token tile.
-constexpr int kCorrectTiles = 32;
+// 64-token tile.  The product is computed transposed, C^T[v][token], and the
+// two 16-row tiles of each 32-column block of v take their rows in the order
+// v = 32p + 8 (r / 4) + 4 (tile % 2) + r % 4, so that the eight values a lane
+// holds for one token over the pair are consecutive: every output access is
+// one 16-byte (bf16) read and write.  The next tile's rows are loaded while
+// the current one is computed.
+constexpr int kCorrectTiles = 16;
 
 template <typename E, int K, int V>
 __global__ void __launch_bounds__(256) split_correct_kernel(SplitDims d, const E *__restrict__ om,
-                                                            const float *__restrict__ hs, E *__restrict__ out) {
-    constexpr int TB = kCorrectTiles, KP = K + 8;   // padded rows of h^T
+                                                            const E *__restrict__ hsT, E *__restrict__ out) {
+    constexpr int TB = kCorrectTiles, KP = K + 8, KS = K / 32, NP = V / 32;   // KP: padded rows of h^T
     __shared__ __attribute__((aligned(16))) E hT[V * KP];
     const int nblk = (d.L + 64 * TB - 1) / (64 * TB);
     int x = blockIdx.x;
@@ -132,49 +139,76 @@ __global__ void __launch_bounds__(256) split_correct_kernel(SplitDims d, const E
     const int s = 1 + x % (d.S - 1), b = x / (d.S - 1);
     const int seg0 = b * d.T + s * d.L, seg1 = b * d.T + min((s + 1) * d.L, d.T);
     const int64_t slot = (int64_t)b * d.S + s;
-    const float *hsrc = hs + (slot * d.HV + j) * K * V;
-    for (int i = threadIdx.x; i < K * V; i += blockDim.x) hT[(i % V) * KP + i / V] = to_e<E>(hsrc[i]);
+    const E *hsrc = hsT + (slot * d.HV + j) * K * V;   // [V][K], rounded by the combine kernel
+    {
+        typedef typename VT<E>::v16b v16b;
+        constexpr int PV = VT<E>::kVec;                    // elements per 16 bytes
+        for (int i = threadIdx.x; i < V * K / PV; i += blockDim.x) {
+            const int v = i / (K / PV), k = (i % (K / PV)) * PV;
+            *(v16b *)&hT[v * KP + k] = *(const v16b *)(hsrc + v * K + k);
+        }
+    }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, grp = lane >> 4;
+    // this wave's tiles: tokens first + 64 t + (0..15) for t < ntile (each tile starts inside the segment)
+    const int first = seg0 + blk * TB * 64 + 16 * wave;
+    const int ntile = first >= seg1 ? 0 : min(TB, (seg1 - first + 63) / 64);
     typedef typename VT<E>::v8 v8;
-    for (int tile = 0; tile < TB; ++tile) {
-        const int tr0 = seg0 + (blk * TB + tile) * 64 + 16 * wave;   // this wave's 16 tokens
-        if (tr0 >= seg1) break;
-        // computed transposed, C^T[v][token] = sum_k h[k][v] oM[token][k], so
-        // that a lane holds four consecutive v of one token (token l16)
-        const int tt = tr0 + l16;
-        const E *brow = om + ((int64_t)min(tt, seg1 - 1) * d.HV + j) * K;
-        v8 bf[K / 32];
+    v8 bf[KS], ov[NP];
+    auto fetch = [&](int tile, v8 *bo, v8 *oo) {
+        const int64_t t = min(first + 64 * tile + l16, seg1 - 1);   // rows past the segment: clamped, not stored
+        const E *brow = om + (t * d.HV + j) * K + 8 * grp;
+        const E *orow = out + (t * d.HV + j) * V + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < K / 32; ++ks) bf[ks] = ld8<E>(brow + 32 * ks + 8 * grp);
-        E *orow = out + ((int64_t)tt * d.HV + j) * V + 4 * grp;
+        for (int ks = 0; ks < KS; ++ks) bo[ks] = ld8<E>(brow + 32 * ks);
 #pragma unroll
-        for (int nt = 0; nt < V / 16; ++nt) {
-            f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < NP; ++q) oo[q] = ld8<E>(orow + 32 * q);
+    };
+    if (ntile > 0) fetch(0, bf, ov);
+    const int va = 8 * (l16 >> 2) + (l16 & 3);   // A-operand row of this lane inside a 32-column block
+    for (int tile = 0; tile < ntile; ++tile) {
+        v8 nb[KS], no[NP];
+        if (tile + 1 < ntile) fetch(tile + 1, nb, no);
+        const int tt = first + 64 * tile + l16;
+        E *orow = out + ((int64_t)tt * d.HV + j) * V + 8 * grp;
 #pragma unroll
-            for (int ks = 0; ks < K / 32; ++ks) c = mma(ld8<E>(&hT[(16 * nt + l16) * KP + 32 * ks + 8 * grp]), bf[ks], c);
-            if (tt < seg1) {
-                typedef typename VT<E>::v4 v4;
-                v4 *o = (v4 *)(orow + 16 * nt);
-                v4 ov = *o;
+        for (int q = 0; q < NP; ++q) {
+            f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ov[e] = to_e<E>(to_f(ov[e]) + c[e]);
-                *o = ov;
+            for (int ks = 0; ks < KS; ++ks) {
+                c0 = mma(ld8<E>(&hT[(32 * q + va) * KP + 32 * ks + 8 * grp]), bf[ks], c0);
+                c1 = mma(ld8<E>(&hT[(32 * q + 4 + va) * KP + 32 * ks + 8 * grp]), bf[ks], c1);
             }
+            if (tt < seg1) {
+                v8 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    r[e] = to_e<E>(to_f(ov[q][e]) + c0[e]);
+                    r[4 + e] = to_e<E>(to_f(ov[q][4 + e]) + c1[e]);
+                }
+                *(v8 *)(orow + 32 * q) = r;
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one block's h^T fragments live at a time
+        }
+        if (tile + 1 < ntile) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) bf[ks] = nb[ks];
+#pragma unroll
+            for (int q = 0; q < NP; ++q) ov[q] = no[q];
         }
     }
 }
 
 template <typename E>
-hipError_t launch_correct(const SplitDims &d, const void *om, const float *hs, void *out, hipStream_t st) {
+hipError_t launch_correct(const SplitDims &d, const void *om, const void *hs, void *out, hipStream_t st) {
     const int nblk = (d.L + 64 * kCorrectTiles - 1) / (64 * kCorrectTiles);
     const unsigned grid = (unsigned)((int64_t)d.B * (d.S - 1) * d.HV * nblk);
-    const E *o = (const E *)om;
+    const E *o = (const E *)om, *hsT = (const E *)hs;
     E *dst = (E *)out;
-    if (d.K == 64 && d.V == 64) split_correct_kernel<E, 64, 64><<<grid, 256, 0, st>>>(d, o, hs, dst);
-    else if (d.K == 64 && d.V == 128) split_correct_kernel<E, 64, 128><<<grid, 256, 0, st>>>(d, o, hs, dst);
-    else if (d.K == 128 && d.V == 64) split_correct_kernel<E, 128, 64><<<grid, 256, 0, st>>>(d, o, hs, dst);
-    else split_correct_kernel<E, 128, 128><<<grid, 256, 0, st>>>(d, o, hs, dst);
+    if (d.K == 64 && d.V == 64) split_correct_kernel<E, 64, 64><<<grid, 256, 0, st>>>(d, o, hsT, dst);
+    else if (d.K == 64 && d.V == 128) split_correct_kernel<E, 64, 128><<<grid, 256, 0, st>>>(d, o, hsT, dst);
+    else if (d.K == 128 && d.V == 64) split_correct_kernel<E, 128, 64><<<grid, 256, 0, st>>>(d, o, hsT, dst);
+    else split_correct_kernel<E, 128, 128><<<grid, 256, 0, st>>>(d, o, hsT, dst);
     return hipGetLastError();
 }
 
@@ -263,7 +297,11 @@ hipError_t launch_split(const Params &p, int dtype, const SplitPlan &pl, void *w
     if (err != hipSuccess) return err;
 
     if (prof) prof->begin(kSplitCombineKernel, stream);
-    split_combine_kernel<<<p.B * p.HV * (p.V / kCombineCols), 256, 0, stream>>>(d, pool, maps, hs, p.final_state);
+    const unsigned ncomb = (unsigned)(p.B * p.HV * (p.V / kCombineCols));
+    if (dtype == 0)
+        split_combine_kernel<bf16><<<ncomb, 256, 0, stream>>>(d, pool, maps, (bf16 *)hs, p.final_state);
+    else
+        split_combine_kernel<float><<<ncomb, 256, 0, stream>>>(d, pool, maps, (float *)hs, p.final_state);
     err = hipGetLastError();
     if (prof) prof->end(kSplitCombineKernel, stream);
     if (err != hipSuccess) return err;
