@@ -73,14 +73,28 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitDims d, const f
     const int r0 = 4 * (t / (CW / 4)), c0 = 4 * (t % (CW / 4));
     const float *h0 = pool + ((int64_t)b * d.S * d.HV + j) * K * V;
     for (int i = t; i < K * CW; i += blockDim.x) h[(i / CW) * CP + i % CW] = h0[(i / CW) * V + col0 + i % CW];
-    __syncthreads();
+    // M_s moves in 16-byte pieces, M_{s+1} loading into registers during step s
+    constexpr int NM = 128 * 128 / 4 / 256;
+    const int nm4 = K * K / 4;
+    f32x4 mr[NM];
+    auto fetch_m = [&](int s) {
+        const f32x4 *ms = (const f32x4 *)(maps + (((int64_t)b * d.S + s) * d.HV + j) * K * K);
+#pragma unroll
+        for (int u = 0; u < NM; ++u)
+            if (t + 256 * u < nm4) mr[u] = ms[t + 256 * u];
+    };
+    if (d.S > 1) fetch_m(1);
     for (int s = 1; s < d.S; ++s) {
         const int64_t slot = (int64_t)b * d.S + s;
         E *hsd = hsT + (slot * d.HV + j) * K * V + (int64_t)col0 * K;   // rows col0.. of [V][K]
-        const float *ms = maps + (slot * d.HV + j) * K * K;
+#pragma unroll
+        for (int u = 0; u < NM; ++u) {
+            const int i = 4 * (t + 256 * u);
+            if (i < K * K) *(f32x4 *)&m[(i / K) * MP + i % K] = mr[u];
+        }
+        __syncthreads();   // h (step s - 1, or the load above) and M_s are in place
         for (int i = t; i < K * CW; i += blockDim.x) hsd[i] = to_e<E>(h[(i % K) * CP + i / K]);
-        for (int i = t; i < K * K; i += blockDim.x) m[(i / K) * MP + i % K] = ms[i];
-        __syncthreads();
+        if (s + 1 < d.S) fetch_m(s + 1);
         float acc[4][4];
         if (t < nb) {
             const float *h0s = pool + (slot * d.HV + j) * K * V + col0;
@@ -88,6 +102,7 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitDims d, const f
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) acc[a][c] = h0s[(r0 + a) * V + c0 + c];
+#pragma unroll 4
             for (int kk = 0; kk < K; ++kk) {
                 float mv[4];
 #pragma unroll
@@ -105,8 +120,8 @@ __global__ void __launch_bounds__(256) split_combine_kernel(SplitDims d, const f
             for (int a = 0; a < 4; ++a)
                 *(f32x4 *)&h[(r0 + a) * CP + c0] = f32x4{acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
         }
-        __syncthreads();
     }
+    __syncthreads();
     if (final_state) {
         float *fd = final_state + ((int64_t)b * d.HV + j) * K * V;
         for (int i = t; i < K * CW; i += blockDim.x) fd[(i / CW) * V + col0 + i % CW] = h[(i / CW) * CP + i % CW];
