@@ -29,8 +29,9 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # changes the hash, and the bench then reports traffic as null until it is
 # measured again.
 MEASURED_TRAFFIC = {
-    # fused_ws_kernel, GVA prefill: FETCH 151,985.5 KiB x 2.000 + WRITE 139,776.2 KiB x 1.000
-    "364fcc8c8560cb90": {"gva": 454397120},
+    # fused_ws_kernel: GVA prefill FETCH 151,985.5 KiB x 2.000 + WRITE 139,776.2 KiB x 1.000;
+    # varlen FETCH 630,803.6 x 2 + WRITE 638,149.8 KiB; wide FETCH 5,272,324.0 x 2 + WRITE 4,264,010.8 KiB
+    "364fcc8c8560cb90": {"gva": 454397120, "varlen": 1945351168, "wide": 15164066611},
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,374.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB
     "1e133469e85525fe": {"decode": 1049900032, "decode_bf16pool": 529568973},
