@@ -194,3 +194,32 @@ def test_backward_varlen_full_size_sampled():
                 "dv": got["dv"][0:1, t0:t1, sl], "dg": got["dg"][0:1, t0:t1, sl],
                 "dbeta": got["dbeta"][0:1, t0:t1, sl], "dh0": got["dh0"][n:n + 1, sl]}
         compare(part, ref, bars, f"varlen n={n} key head {jk}")
+
+
+def test_backward_wide_full_size_sampled():
+    """The largest workload at full size (16 x 16384 tokens, 64 value heads, no L2
+    norm, the parity inputs of the wide workload): workspace offsets past 2^32
+    elements, 4096 chunks per value head; sampled (sequence, key head) groups,
+    both value heads each, against the oracle."""
+    w = WORKLOADS["wide_stable"]
+    _say("[bwd-full] wide: generating on the GPU")
+    x = make_grad_inputs(oracle.add_gates(make_inputs(w, seed=0, device="cuda:0")), seed=100)
+    got = run_gpu_bwd(x, torch.bfloat16)
+    for name in NAMES:
+        assert torch.isfinite(got[name]).all(), name
+    G = w.HV // w.H
+    bars = _bars(torch.bfloat16)
+    for n, jk in ((0, 0), (w.B - 1, w.H - 1), (7, 13)):
+        sl = slice(jk * G, (jk + 1) * G)
+        sub = dict(q=x["q"][n:n + 1, :, jk:jk + 1].cpu(), k=x["k"][n:n + 1, :, jk:jk + 1].cpu(),
+                   v=x["v"][n:n + 1, :, sl].cpu(), g=x["g"][n:n + 1, :, sl].cpu(),
+                   beta=x["beta"][n:n + 1, :, sl].cpu(), do=x["do"][n:n + 1, :, sl].cpu(),
+                   dht=x["dht"][n:n + 1, sl].cpu(),
+                   initial_state=None if x["initial_state"] is None else x["initial_state"][n:n + 1, sl].cpu(),
+                   cu_seqlens=None, scale=x["scale"], use_l2norm=x["use_l2norm"])
+        _say(f"    group n={n} key head {jk}")
+        ref = run_oracle_bwd(sub)
+        part = {"dq": got["dq"][n:n + 1, :, jk:jk + 1], "dk": got["dk"][n:n + 1, :, jk:jk + 1],
+                "dv": got["dv"][n:n + 1, :, sl], "dg": got["dg"][n:n + 1, :, sl],
+                "dbeta": got["dbeta"][n:n + 1, :, sl], "dh0": got["dh0"][n:n + 1, sl]}
+        compare(part, ref, bars, f"wide n={n} key head {jk}")
