@@ -223,3 +223,28 @@ def test_backward_wide_full_size_sampled():
                 "dv": got["dv"][n:n + 1, :, sl], "dg": got["dg"][n:n + 1, :, sl],
                 "dbeta": got["dbeta"][n:n + 1, :, sl], "dh0": got["dh0"][n:n + 1, sl]}
         compare(part, ref, bars, f"wide n={n} key head {jk}")
+
+
+def test_backward_long_full_size_sampled():
+    """One 131,072-token sequence with slow decay (2048 chunks through the
+    scans' narrowest, 16-column tiles): one key head, both its value heads,
+    against the oracle over the whole sequence."""
+    w = WORKLOADS["long"]
+    _say("[bwd-full] long: generating on the GPU")
+    x = make_grad_inputs(oracle.add_gates(make_inputs(w, seed=0, device="cuda:0")), seed=100)
+    got = run_gpu_bwd(x, torch.bfloat16)
+    for name in NAMES:
+        assert torch.isfinite(got[name]).all(), name
+    G = w.HV // w.H
+    jk = w.H // 2
+    sl = slice(jk * G, (jk + 1) * G)
+    sub = dict(q=x["q"][:, :, jk:jk + 1].cpu(), k=x["k"][:, :, jk:jk + 1].cpu(), v=x["v"][:, :, sl].cpu(),
+               g=x["g"][:, :, sl].cpu(), beta=x["beta"][:, :, sl].cpu(), do=x["do"][:, :, sl].cpu(),
+               dht=x["dht"][:, sl].cpu(),
+               initial_state=None if x["initial_state"] is None else x["initial_state"][:, sl].cpu(),
+               cu_seqlens=None, scale=x["scale"], use_l2norm=x["use_l2norm"])
+    _say(f"    key head {jk}: the oracle over {w.T} tokens")
+    ref = run_oracle_bwd(sub)
+    part = {"dq": got["dq"][:, :, jk:jk + 1], "dk": got["dk"][:, :, jk:jk + 1], "dv": got["dv"][:, :, sl],
+            "dg": got["dg"][:, :, sl], "dbeta": got["dbeta"][:, :, sl], "dh0": got["dh0"][:, sl]}
+    compare(part, ref, _bars(torch.bfloat16), f"long key head {jk}")
