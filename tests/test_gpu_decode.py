@@ -169,3 +169,42 @@ def test_decode_empty_batch():
                                                                                       device=DEV))
     torch.cuda.synchronize()
     assert o.shape == (0, 4, 64) and torch.count_nonzero(pool) == 0
+
+
+@pytest.mark.parametrize("name", ["decode", "decode_bf16pool"])
+def test_decode_bench_workloads_full_size(name):
+    """The decode steps the benchmark times, at their size (256 rows, 8 of them
+    padding, a 512-slot fp32 or bf16 pool, 32 value heads), from the same input
+    generator; the gates come from the oracle and feed both sides."""
+    from workloads import DECODE_WORKLOADS, make_decode_inputs
+    gdn = _gdn()
+    w = DECODE_WORKLOADS[name]
+    x = make_decode_inputs(w, seed=0, device=DEV)
+    g, beta = oracle.gating(x["A_log"].cpu(), x["dt_bias"].cpu(), x["a"].float().cpu(), x["b"].float().cpu())
+    g = torch.as_tensor(g, dtype=torch.float32)
+    beta = torch.as_tensor(beta, dtype=torch.float32)
+    pool0 = x["pool"].cpu()
+    idx = x["idx"].cpu()
+    _say(f"[decode-full] {name}: N={w.N} pool={w.pool_size} ({pool0.dtype})")
+    pool = x["pool"]
+    o = gdn.fused_recurrent_gated_delta_rule_update(x["q"], x["k"], x["v"], g.to(DEV), beta.to(DEV), pool, x["idx"],
+                                                    scale=x["scale"], use_qk_l2norm_in_kernel=x["use_l2norm"])
+    torch.cuda.synchronize()
+    o, pool_after = o.float().cpu(), pool.float().cpu()
+    cpu = lambda t: t.float().cpu().unsqueeze(1)
+    o_ref, after_ref = oracle.recurrent_pool(cpu(x["q"]), cpu(x["k"]), cpu(x["v"]), g.unsqueeze(1),
+                                             beta.unsqueeze(1), pool0, idx, scale=x["scale"],
+                                             use_l2norm=x["use_l2norm"])
+    valid = [r for r in range(w.N) if 0 <= int(idx[r]) < w.pool_size]
+    assert len(valid) == w.N - w.n_pad
+    to, tf = TOL[torch.bfloat16]
+    eo = float(np.abs(o[valid].numpy().astype(np.float64) - o_ref[valid, 0]).max())
+    slots = idx[valid].long()
+    ef = float(np.abs(pool_after[slots].numpy().astype(np.float64) - after_ref[slots.numpy()]).max())
+    _say(f"    max|do|={eo:.3e} (bar {to})  max|dS|={ef:.3e} (bar {tf})")
+    assert eo <= to and ef <= tf
+    pads = [r for r in range(w.N) if r not in valid]
+    assert torch.all(o[pads] == 0)
+    untouched = torch.ones(w.pool_size, dtype=torch.bool)
+    untouched[slots] = False
+    assert torch.equal(pool_after[untouched], pool0[untouched].float())
