@@ -178,3 +178,49 @@ def test_prefill_then_decode_on_a_bf16_pool():
     _say(f"    prefill+decode on bf16 pool: max|do|={eo:.3e} max|dS|={float(ef.max()):.3e}")
     assert eo <= 2e-2 and np.all(ef <= 1e-2 + 2.0 ** -8 * np.abs(f_ref))
     assert torch.all(pool_d[[1, 3, 5]].float() == 7.0)
+
+
+def test_prefill_pool_gated_bf16_full_size_sampled():
+    """The serving call at the size of the packed workload (64 sequences,
+    62,386 tokens, 32 value heads): gates computed in the kernel, a bf16 pool
+    of 80 slots read and updated in place through a shuffled slot map; sampled
+    (sequence, value head) units against the oracle, every slot no sequence
+    names bit-identical."""
+    gdn = _gdn()
+    w = WORKLOADS["varlen"]
+    x = make_inputs(w, seed=0, device="cuda:0")
+    N, HV = x["N"], w.HV
+    P = N + 16
+    pool0 = _pool(P, w, torch.bfloat16, seed=26)
+    idx = torch.randperm(P, generator=torch.Generator().manual_seed(27))[:N].to(torch.int32)
+    pool_d = pool0.to(DEV).contiguous()
+    _say(f"[pool-full] varlen: N={N} tokens={sum(x['lens'])} pool={P} bf16")
+    o, _ = gdn.chunk_gated_delta_rule(x["q"], x["k"], x["v"], A_log=x["A_log"], dt_bias=x["dt_bias"],
+                                      a_raw=x["a"], b_raw=x["b"], scale=x["scale"], cu_seqlens=x["cu_seqlens"],
+                                      use_qk_l2norm_in_kernel=True, ssm_state_pool=pool_d,
+                                      ssm_state_indices=idx.to(DEV))
+    torch.cuda.synchronize()
+    after = pool_d.cpu()
+    starts = [int(c) for c in x["cu_seqlens"].tolist()]
+    longest = int(np.argmax(x["lens"]))
+    G = HV // w.H
+    for n, j in ((0, 0), (longest, HV // 2), (N - 1, HV - 1)):
+        t0, t1 = starts[n], starts[n + 1]
+        jk = j // G
+        rows = lambda t, h: t[0, t0:t1, h:h + 1].unsqueeze(0).float().cpu()
+        g, beta = oracle.gating(x["A_log"][j:j + 1].cpu(), x["dt_bias"][j:j + 1].cpu(), rows(x["a"], j),
+                                rows(x["b"], j))   # [1, L, 1]
+        s0 = pool0[int(idx[n]), j:j + 1].unsqueeze(0).float()
+        o_ref, f_ref = oracle.recurrent(rows(x["q"], jk), rows(x["k"], jk), rows(x["v"], j),
+                                        torch.as_tensor(g, dtype=torch.float32),
+                                        torch.as_tensor(beta, dtype=torch.float32), scale=x["scale"],
+                                        use_l2norm=True, initial_state=s0)
+        og = o[0, t0:t1, j].float().cpu().numpy().astype(np.float64)
+        eo = float(np.abs(og - o_ref[0, :, 0]).max()) if t1 > t0 else 0.0
+        ref = f_ref[0, 0]
+        err = np.abs(after[int(idx[n]), j].float().numpy().astype(np.float64) - ref)
+        ratio = float((err / (1e-2 + 2.0 ** -8 * np.abs(ref))).max())
+        _say(f"    unit n={n} j={j} len={t1 - t0}: max|do|={eo:.3e}  state err/bar {ratio:.2f}")
+        assert eo <= 2e-2 and ratio <= 1.0
+    untouched = [s for s in range(P) if s not in set(idx.tolist())]
+    assert torch.equal(after[untouched], pool0[untouched])
