@@ -35,10 +35,16 @@ MEASURED_TRAFFIC = {
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,374.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB
     "1e133469e85525fe": {"decode": 1049900032, "decode_bf16pool": 529568973},
-    # backward, GVA: every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md)
+    # backward (GVA, varlen, wide): every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md)
     "717f9f10b6a2d65b": {"gva:bwd_prep_kernel": 611056128, "gva:bwd_fwd_scan_kernel": 1250057830,
                          "gva:bwd_dh_scan_kernel": 1526923059, "gva:bwd_grads_kernel": 3462960742,
-                         "gva:bwd_reduce_kernel": 671122432},
+                         "gva:bwd_reduce_kernel": 671122432,
+                         "varlen:bwd_setup_kernel": 3379, "varlen:bwd_prep_kernel": 3206975898,
+                         "varlen:bwd_fwd_scan_kernel": 6119313715, "varlen:bwd_dh_scan_kernel": 8334033715,
+                         "varlen:bwd_grads_kernel": 13159533261, "varlen:bwd_reduce_kernel": 2555364352,
+                         "wide:bwd_prep_kernel": 26682810163, "wide:bwd_fwd_scan_kernel": 49727091302,
+                         "wide:bwd_dh_scan_kernel": 66841029018, "wide:bwd_grads_kernel": 111218403635,
+                         "wide:bwd_reduce_kernel": 21474870272},
 }
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
