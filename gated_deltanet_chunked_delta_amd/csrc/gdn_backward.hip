@@ -1046,6 +1046,165 @@ __global__ __launch_bounds__(NTH) void bwd_dh_scan_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// The dh scan with 16 value columns and 8 waves (bf16 rows, K = 128): the
+// narrowest tiles, for few (sequence, value head) pairs.  Four waves would
+// leave one wave per SIMD and nothing to hide the latency of each chunk
+// step's chained products; here the two 64-row products split their
+// reduction between wave pairs (keys or tokens in halves, the partial sums
+// added where they are read) and the 128-row state update takes one row tile
+// per wave.
+// ---------------------------------------------------------------------------
+constexpr int dh_scan_sk_floats() {
+    return 128 * 17 + 2 * kChunk * kPadC + 5 * kChunk * 17 + 5 * kChunk + (2 * kChunk * (128 + 2) * 2 + 3) / 4;
+}
+
+__global__ __launch_bounds__(512) void bwd_dh_scan_sk_kernel(BwdParams p) {
+    typedef bf16 E;
+    constexpr int K = 128, VW = 16, VP = VW + 1, KS = K + RowPad<E>::v, NTH = 512;
+    __shared__ float sm[dh_scan_sk_floats()];
+    float *dh = sm;                          // [K][VP]
+    float *Tm = dh + K * VP;                 // [64][65]
+    float *Pm = Tm + kChunk * kPadC;         // [64][65]
+    float *dO = Pm + kChunk * kPadC;         // [64][VP]
+    float *dV0 = dO + kChunk * VP;           // [64][VP] dVn, keys 0..63 / tokens 0..31
+    float *dV1 = dV0 + kChunk * VP;          // [64][VP]             keys 64..127 / tokens 32..63
+    float *dB0 = dV1 + kChunk * VP;          // [64][VP] dB, tokens 0..31
+    float *dB1 = dB0 + kChunk * VP;          // [64][VP]     tokens 32..63
+    float *gam = dB1 + kChunk * VP;          // [64]
+    float *bet = gam + kChunk;               // [64]
+    float *sFk = bet + kChunk;               // [64] exp(gamma_L - gamma) / |k|, 0 past L
+    float *sD = sFk + kChunk;                // [64] scale exp(gamma) / |q|
+    float *sB = sD + kChunk;                 // [64] -beta exp(gamma) / |k|
+    E *kr = (E *)(sB + kChunk);              // [64][KS] raw k rows
+    E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
+
+    const int HV = p.HV, V = p.V;
+    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int c0 = blockIdx.y * VW;
+    int bos, len, cid0;
+    seq_of(p, n, bos, len, cid0);
+    const int nc = (len + kChunk - 1) / kChunk;
+    const float scale = p.scale;
+    const bool lo = threadIdx.x < 256;       // the dO tile moves through the first four waves
+
+    if (p.dht) {
+        StateTileN<K, VW, NTH> r0;
+        r0.load(p.dht + ((int64_t)n * HV + j) * K * V, V, c0);
+        r0.commit(dh);
+    } else {
+        for (int e = threadIdx.x; e < K * VW; e += NTH) dh[(e / VW) * VP + e % VW] = 0.f;
+    }
+    RawRowsReg<E, K, NTH> rk, rq;
+    Mat64RegN<NTH> rt, rp;
+    TileRegN<E, VW, 256> ro;
+    float rg = 0.f, rb = 0.f;
+    auto fetch = [&](int ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        rk.load((const E *)p.k, t0, L, p.H, jk);
+        rq.load((const E *)p.q, t0, L, p.H, jk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rp.load(p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        if (lo) ro.load((const E *)p.dout, t0, L, HV, j, V, c0);
+        if (threadIdx.x < kChunk) {
+            const int r = threadIdx.x;
+            rg = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
+            rb = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+        }
+    };
+    if (nc > 0) fetch(nc - 1);
+    lds_barrier();
+    const int w = wave_id(), rt4 = 16 * (w & 3), half = w >> 2;
+    auto ra = [&](int) { return rt4; };
+    auto rs = [&](int) { return 16 * w; };
+    auto cb = [&](int) { return 0; };
+    for (int ci = nc - 1; ci >= 0; --ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        StateTileN<K, VW, NTH>::store(dh, p.dhs + ((int64_t)cid * HV + j) * K * V, V, c0);
+        rk.commit(kr);
+        rq.commit(qr);
+        rt.commit(Tm);
+        rp.commit(Pm);
+        if (lo) ro.commit(dO);
+        if (threadIdx.x < kChunk) {
+            gam[threadIdx.x] = rg;
+            bet[threadIdx.x] = rb;
+        }
+        lds_barrier();
+        {
+            constexpr int LPR = NTH / kChunk;   // lanes per row
+            const int r = threadIdx.x / LPR;
+            const float sk = row_sumsq<E, K, NTH>(kr, r), sq = row_sumsq<E, K, NTH>(qr, r);
+            if (threadIdx.x % LPR == 0) {
+                const float fk = p.use_l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
+                const float fq = p.use_l2norm ? 1.f / sqrtf(sq + 1e-6f) : 1.f;
+                const float d = __expf(gam[r]);
+                sFk[r] = r < L ? __expf(gam[L - 1] - gam[r]) * fk : 0.f;
+                sD[r] = scale * d * fq;
+                sB[r] = -bet[r] * d * fk;
+            }
+        }
+        lds_barrier();
+        if (ci > 0) fetch(ci - 1);
+        const float gl = gam[L - 1];
+
+        // dVn = scale Pm^T dO + diag(exp(gamma_L - gamma)) Kh dh', each half of
+        // the tokens (first product) and of the keys (second) in one wave
+        {
+            const int m0 = 32 * half, k0 = 64 * half;
+            f32x4 a[1], b[1];
+            zero(a);
+            zero(b);
+            wmm<1, 32>(a, ra, cb, [&](int r, int m) { return Pm[(m0 + m) * kPadC + r]; },
+                       [&](int c, int m) { return dO[(m0 + m) * VP + c]; });
+            wmm<1, 64>(b, ra, cb, [&](int r, int m) { return to_f(kr[r * KS + k0 + m]); },
+                       [&](int c, int m) { return dh[(k0 + m) * VP + c]; });
+            float *dst = half ? dV1 : dV0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = lrow(rt4, e), c = lcol(0);
+                dst[r * VP + c] = scale * a[0][e] + sFk[r] * b[0][e];
+            }
+        }
+        lds_barrier();
+        // dB = Tm^T dVn, each half of the tokens in one wave
+        {
+            const int m0 = 32 * half;
+            f32x4 a[1];
+            zero(a);
+            wmm<1, 32>(a, ra, cb, [&](int r, int m) { return Tm[(m0 + m) * kPadC + r]; },
+                       [&](int c, int m) { return dV0[(m0 + m) * VP + c] + dV1[(m0 + m) * VP + c]; });
+            float *dst = half ? dB1 : dB0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[lrow(rt4, e) * VP + lcol(0)] = a[0][e];
+        }
+        lds_barrier();
+        // dh <- D_L dh' + scale Qh^T diag(D) dO - Kh^T diag(beta D) dB: row tile w
+        {
+            f32x4 x[1];
+            zero(x);
+            wmm<1, kChunk>(x, rs, cb, [&](int r, int m) { return to_f(qr[m * KS + r]); },
+                           [&](int c, int m) { return sD[m] * dO[m * VP + c]; });
+            wmm<1, kChunk>(x, rs, cb, [&](int r, int m) { return to_f(kr[m * KS + r]); },
+                           [&](int c, int m) { return sB[m] * (dB0[m * VP + c] + dB1[m * VP + c]); });
+            const float dl = __expf(gl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float &v = dh[lrow(16 * w, e) * VP + lcol(0)];
+                v = fmaf(dl, v, x[0][e]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {   // dB to HBM: 64 x 16 values, two per thread
+                const int i = threadIdx.x + NTH * u, r = i / VW, c = i % VW;
+                if (r < L) p.db[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = dB0[r * VP + c] + dB1[r * VP + c];
+            }
+        }
+        lds_barrier();
+    }
+    if (p.dh0) StateTileN<K, VW, NTH>::store(dh, p.dh0 + ((int64_t)n * HV + j) * K * V, V, c0);
+}
+static_assert(dh_scan_sk_floats() * 4 <= 160 * 1024, "split dh scan must fit one CU");
+
+// ---------------------------------------------------------------------------
 // per (chunk, value head): dq, dk (per value head), dv, dg, dbeta.  512
 // threads: wave w holds rows 16 (w & 3).. and column half w >> 2 of every
 // 64 x 64 and 64 x K product; the row sums of the two halves meet in LDS.
@@ -1551,7 +1710,9 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
         }
         if (prof) prof->begin(kBwdDhScanKernel, st);
         if constexpr (sizeof(E) == 2) {
-            if (narrow == 2)
+            if (narrow == 2 && K == 128)
+                hipLaunchKernelGGL(bwd_dh_scan_sk_kernel, dim3(p.N * p.HV, V / 16), dim3(512), 0, st, p);
+            else if (narrow == 2)
                 hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K, 16, 256>), dim3(p.N * p.HV, V / 16), dim3(256), 0, st, p);
             else if (narrow == 1)
                 hipLaunchKernelGGL((bwd_dh_scan_kernel<E, K, 32, 512>), dim3(p.N * p.HV, V / 32), dim3(512), 0, st, p);
