@@ -37,7 +37,7 @@ MEASURED_TRAFFIC = {
     "1e133469e85525fe": {"decode": 1049900032, "decode_bf16pool": 529568973},
     # backward (GVA, varlen, wide): every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md)
     # (counted under 717f9f10b6a2d65b; the kernels these workloads run assemble identically here)
-    "d8dc1b7e147afed6": {"gva:bwd_prep_kernel": 611056128, "gva:bwd_fwd_scan_kernel": 1250057830,
+    "d442d1d0bfcc74fa": {"gva:bwd_prep_kernel": 611056128, "gva:bwd_fwd_scan_kernel": 1250057830,
                          "gva:bwd_dh_scan_kernel": 1526923059, "gva:bwd_grads_kernel": 3462960742,
                          "gva:bwd_reduce_kernel": 671122432,
                          "varlen:bwd_setup_kernel": 3379, "varlen:bwd_prep_kernel": 3206975898,

@@ -1046,6 +1046,145 @@ __global__ __launch_bounds__(NTH) void bwd_dh_scan_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// The forward rescan with 16 value columns and 8 waves (bf16 rows, K = 128),
+// for few (sequence, value head) pairs, in the same form as the 8-wave dh
+// scan below: the two 64-row products split their reduction between wave
+// pairs (keys, then tokens, in halves; the partial sums added where the next
+// stage reads them) and the state update takes one row tile per wave.
+// ---------------------------------------------------------------------------
+constexpr int fwd_scan_sk_floats() {
+    return 128 * 17 + kChunk * kPadC + 5 * kChunk * 17 + 4 * kChunk + (kChunk * (128 + 2) * 2 + 3) / 4;
+}
+
+__global__ __launch_bounds__(512) void bwd_fwd_scan_sk_kernel(BwdParams p) {
+    typedef bf16 E;
+    constexpr int K = 128, VW = 16, VP = VW + 1, KS = K + RowPad<E>::v, NTH = 512;
+    __shared__ float sm[fwd_scan_sk_floats()];
+    float *h = sm;                           // [K][VP]
+    float *Tm = h + K * VP;                  // [64][65]
+    float *vv = Tm + kChunk * kPadC;         // [64][VP] v
+    float *X0 = vv + kChunk * VP;            // [64][VP] Kh h, keys 0..63
+    float *X1 = X0 + kChunk * VP;            // [64][VP]       keys 64..127
+    float *Y0 = X1 + kChunk * VP;            // [64][VP] Vn = Tm B, tokens 0..31
+    float *Y1 = Y0 + kChunk * VP;            // [64][VP]             tokens 32..63
+    float *gam = Y1 + kChunk * VP;           // [64]
+    float *bet = gam + kChunk;               // [64]
+    float *sD = bet + kChunk;                // [64] exp(gamma) / |k|
+    float *sFk = sD + kChunk;                // [64] exp(gamma_L - gamma) / |k|, 0 past L
+    E *kr = (E *)(sFk + kChunk);             // [64][KS] raw k rows
+
+    const int HV = p.HV, V = p.V;
+    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int c0 = blockIdx.y * VW;
+    int bos, len, cid0;
+    seq_of(p, n, bos, len, cid0);
+    const int nc = (len + kChunk - 1) / kChunk;
+    const bool lo = threadIdx.x < 256;       // the v tile moves through the first four waves
+
+    if (p.initial_state) {
+        StateTileN<K, VW, NTH> r0;
+        r0.load(p.initial_state + ((int64_t)n * HV + j) * K * V, V, c0);
+        r0.commit(h);
+    } else {
+        for (int e = threadIdx.x; e < K * VW; e += NTH) h[(e / VW) * VP + e % VW] = 0.f;
+    }
+    RawRowsReg<E, K, NTH> rk;
+    Mat64RegN<NTH> rt;
+    TileRegN<E, VW, 256> rv;
+    float rg = 0.f, rb = 0.f;
+    auto fetch = [&](int ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        rk.load((const E *)p.k, t0, L, p.H, jk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        if (lo) rv.load((const E *)p.v, t0, L, HV, j, V, c0);
+        if (threadIdx.x < kChunk) {
+            const int r = threadIdx.x;
+            rg = r < L ? p.gam[(int64_t)(t0 + r) * HV + j] : 0.f;
+            rb = r < L ? p.beta[(int64_t)(t0 + r) * HV + j] : 0.f;
+        }
+    };
+    if (nc > 0) fetch(0);
+    lds_barrier();
+    const int w = wave_id(), rt4 = 16 * (w & 3), half = w >> 2;
+    auto ra = [&](int) { return rt4; };
+    auto rs = [&](int) { return 16 * w; };
+    auto cb = [&](int) { return 0; };
+    for (int ci = 0; ci < nc; ++ci) {
+        const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
+        StateTileN<K, VW, NTH>::store(h, p.hs + ((int64_t)cid * HV + j) * K * V, V, c0);
+        rk.commit(kr);
+        rt.commit(Tm);
+        if (lo) rv.commit(vv);
+        if (threadIdx.x < kChunk) {
+            gam[threadIdx.x] = rg;
+            bet[threadIdx.x] = rb;
+        }
+        lds_barrier();
+        {
+            constexpr int LPR = NTH / kChunk;   // lanes per row
+            const int r = threadIdx.x / LPR;
+            const float sk = row_sumsq<E, K, NTH>(kr, r);
+            if (threadIdx.x % LPR == 0) {
+                const float fk = p.use_l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
+                const float f = r < L ? __expf(gam[L - 1] - gam[r]) : 0.f;
+                sD[r] = __expf(gam[r]) * fk;
+                sFk[r] = f * fk;
+            }
+        }
+        lds_barrier();
+        if (ci + 1 < nc) fetch(ci + 1);
+
+        // X = Kh h (raw rows; the norms sit in sD), each half of the keys in one wave
+        {
+            const int k0 = 64 * half;
+            f32x4 x[1];
+            zero(x);
+            wmm<1, 64>(x, ra, cb, [&](int r, int m) { return to_f(kr[r * KS + k0 + m]); },
+                       [&](int c, int m) { return h[(k0 + m) * VP + c]; });
+            float *dst = half ? X1 : X0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[lrow(rt4, e) * VP + lcol(0)] = x[0][e];
+        }
+        lds_barrier();
+        // Vn = Tm B with B = diag(beta) (V - diag(D) X), each half of the tokens in one wave
+        {
+            const int m0 = 32 * half;
+            f32x4 x[1];
+            zero(x);
+            wmm<1, 32>(x, ra, cb, [&](int r, int m) { return Tm[r * kPadC + m0 + m]; },
+                       [&](int c, int m) {
+                           const int t = m0 + m;
+                           return bet[t] * (vv[t * VP + c] - sD[t] * (X0[t * VP + c] + X1[t * VP + c]));
+                       });
+            float *dst = half ? Y1 : Y0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[lrow(rt4, e) * VP + lcol(0)] = x[0][e];
+        }
+        lds_barrier();
+        // h <- D_L h + Kh^T diag(exp(gamma_L - gamma)) Vn: row tile w; Vn to HBM
+        {
+            f32x4 x[1];
+            zero(x);
+            wmm<1, kChunk>(x, rs, cb, [&](int r, int m) { return to_f(kr[m * KS + r]); },
+                           [&](int c, int m) { return sFk[m] * (Y0[m * VP + c] + Y1[m * VP + c]); });
+            const float dl = __expf(gam[L - 1]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float &hv = h[lrow(16 * w, e) * VP + lcol(0)];
+                hv = fmaf(dl, hv, x[0][e]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {   // 64 x 16 values, two per thread
+                const int i = threadIdx.x + NTH * u, r = i / VW, c = i % VW;
+                if (r < L) p.vn[((int64_t)(t0 + r) * HV + j) * V + c0 + c] = Y0[r * VP + c] + Y1[r * VP + c];
+            }
+        }
+        lds_barrier();
+    }
+}
+static_assert(fwd_scan_sk_floats() * 4 <= 160 * 1024, "split forward rescan must fit one CU");
+
+// ---------------------------------------------------------------------------
 // The dh scan with 16 value columns and 8 waves (bf16 rows, K = 128): the
 // narrowest tiles, for few (sequence, value head) pairs.  Four waves would
 // leave one wave per SIMD and nothing to hide the latency of each chunk
@@ -1694,7 +1833,9 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
         if (nc_max > 0) {
             if (prof) prof->begin(kBwdFwdScanKernel, st);
             if constexpr (sizeof(E) == 2) {
-                if (narrow == 2)
+                if (narrow == 2 && K == 128)
+                    hipLaunchKernelGGL(bwd_fwd_scan_sk_kernel, dim3(p.N * p.HV, V / 16), dim3(512), 0, st, p);
+                else if (narrow == 2)
                     hipLaunchKernelGGL((bwd_fwd_scan_kernel<E, K, 16, 256>), dim3(p.N * p.HV, V / 16), dim3(256), 0,
                                        st, p);
                 else if (narrow == 1)
