@@ -40,13 +40,18 @@
 //                        states h and Vn
 //   bwd_dh_scan_kernel   the same grid, backward over chunks: dh' per chunk,
 //                        dB, the initial-state gradient
+// (with few (sequence, value head) pairs both scans take 32- or 16-column
+// tiles; bf16 rows at 64 columns rescan in bwd_fwd_scan_b16_kernel, and at 16
+// columns with K = 128 both scans run the 8-wave *_sk_kernel forms)
 //   bwd_grads_kernel     per (chunk, value head): dq, dk per value head, dv,
 //                        dg, dbeta
 //   bwd_reduce_kernel    dq, dk summed over the value heads of each key head
 // All arithmetic is fp32-accurate: the products run on the matrix cores with
-// fp32 operands (v_mfma_f32_16x16x4f32), except the gradients kernel's products
-// over the value columns, which split each fp32 operand into bf16 hi + lo parts
-// (hi hi + hi lo + lo hi on v_mfma_f32_16x16x32_bf16, fp32 accumulation; a bf16
+// fp32 operands (v_mfma_f32_16x16x4f32), except on v_mfma_f32_16x16x32_bf16
+// with fp32 accumulation where every operand is exact in bf16: the prep
+// kernel's K K^T and Q K^T of raw bf16 rows, and the products of the 64-column
+// bf16 rescan and of the gradients kernel over the value columns, which split
+// each fp32 operand into bf16 hi + lo parts (hi hi + hi lo + lo hi; a bf16
 // input is its own hi part).  The intermediates live in the caller's workspace
 // (layout in BwdPlan).
 #include <hip/hip_runtime.h>
