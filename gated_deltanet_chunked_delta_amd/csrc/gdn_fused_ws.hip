@@ -3,37 +3,63 @@
 // Same mathematics as the single-role kernel in gdn_fused.hip (the step list
 // of the page "NPU Training Operators - GDN", operator-semantics section, in
 // the chunk form written out at the top of that file), scheduled differently:
-// a workgroup has 12 waves, three per SIMD, in three roles.
-//   waves 0-3   chain waves: each owns 16 state columns and runs everything
-//               that depends on the state h: X, the block forward substitution
-//               for V_new, the output, the state update, and Z = K h and
-//               (Q h)^T of the next chunk.
-//   waves 4-7   K-prep waves, one chunk ahead: gate cumsum; wave w computes
-//               its diagonal K K^T tile (A_ww and the diagonal-block inverse
-//               D_w), two off-diagonal tiles (the gated -A tiles) and the
-//               diagonal tiles whose norms those need, spread so that the four
-//               waves carry 5, 5, 5 and 1 tiles; each publishes the per-token
-//               state factors of its own 16 rows.
-//   waves 8-11  Q-prep waves, one chunk ahead: the asynchronous copies of the
-//               raw rows (two chunks ahead), gate cumsum, the ten causal Q K^T
-//               tiles spread 7, 7, 7 and 3 tiles per wave (with the Q Q^T and
-//               K K^T diagonals for the norms they need), the gated P tiles.
-// The SIMDs interleave the serial state chain of chunk c with the
-// preparation of chunk c+1.  Each step ends with the only workgroup barrier
-// of the step; every prep wave computes the cumsum and norm values it needs
-// itself, so the prep waves never wait for each other inside a step.
+// a workgroup has 12 waves, three per SIMD, in two or three roles.
+//   chain waves: each owns 16 state columns and runs everything that depends
+//               on the state h: the block forward substitution for V_new, the
+//               output, the state update, and Z = K h and (Q h)^T of the next
+//               chunk.
+//   K-prep work, one chunk ahead, four row tiles w: gate cumsum; tile w's
+//               diagonal K K^T tile (A_ww and the diagonal-block inverse D_w),
+//               two off-diagonal tiles (the gated -A tiles) and the diagonal
+//               tiles whose norms those need, spread so that the four carry 5,
+//               5, 5 and 1 tiles; the per-token state factors of its 16 rows.
+//   Q-prep work, one chunk ahead, four row tiles w: gate cumsum, the ten
+//               causal Q K^T tiles spread 7, 7, 7 and 3 tiles per tile w (with
+//               the Q Q^T and K K^T diagonals for the norms they need), the
+//               gated P tiles.
+// Two layouts (NCW chain waves):
+//   NCW = 4: a workgroup per (sequence, value head, 64 value columns); waves
+//            0-3 chain, 4-7 K-prep, 8-11 Q-prep.  Used when there are few
+//            (sequence, value head) pairs, so that the grid fills the GPU.
+//   NCW = 8: a workgroup per (sequence, value head) of 128 columns; waves 0-7
+//            chain (two per SIMD, so that each hides the other's latencies),
+//            8-11 prep waves doing both the K- and the Q-prep of their row
+//            tile, once for all 128 columns.
+// The prep waves also issue the asynchronous copies of the raw rows: k, q and
+// the gates two chunks ahead, v one chunk ahead.  The SIMDs interleave the
+// serial state chain of chunk c with the preparation of chunk c+1.  Each step
+// ends with the only workgroup barrier of the step; every prep wave computes
+// the cumsum and norm values it needs itself, so the prep waves never wait for
+// each other inside a step.
 //
-// Buffers: raw k and v rows in rings of three chunks (the chain reads chunk
-// c's while c+1's is resident and c+2's streams in), raw q/g/beta and the prep
+// Gate and norm factors travel as base-2 logarithms: with gamma the gate
+// cumsum in log2 units and l_i = log2 r_i (the L2-norm factor of k_i, 0 when
+// the norm is off),
+//   A_ij = 2^(a_i - c_j) k_i.k_j,       a_i = gamma_i + log2 beta_i + l_i,
+//   P_ij = 2^(a'_i - c_j) q_i.k_j,      a'_i = gamma_i + log2(scale rho_i),
+//                                       c_j = gamma_j - l_j,
+// so each gated element costs one subtraction and one exp2; beta = 0 gives
+// a_i = -inf and a zero row.  The same factors give the per-token scalars:
+// beta e^gamma r = 2^a_i, r e^{gamma_L - gamma} = 2^(gamma_L - c_i) and
+// scale rho e^gamma = 2^a'_i.
+//
+// The diagonal-block inverses are published in three forms, D_b,
+// D_b diag(beta) and -D_b diag(beta e^gamma r), so that the chain forms
+//   V_b = D_b diag(beta) V_b - D_b diag(beta e^gamma r) Z_b
+//         + D_b (-sum_{m<b} A_bm V_m)      (= D_b (X_b - sum A_bm V_m))
+// entirely on the matrix cores, from the raw v rows and Z = K h.
+//
+// Buffers: raw k rows in a ring of three chunks (the chain reads chunk c's
+// while c+1's is resident and c+2's streams in), raw q/g/beta, v and the prep
 // outputs double-buffered by chunk parity.  Rows past the end of a sequence
 // are copies of its last row; the cumsum reads their g and beta as 0, which
-// makes their rows of A, X and V_new zero and leaves gamma_L at the last real
+// makes their rows of A and V_new zero and leaves gamma_L at the last real
 // token, so they contribute nothing.
 //
-// In-kernel gating: the copying wave fetches the raw gate words of chunk c+3
-// (their own ring) and, at the start of the next step, turns those of chunk
-// c+2 into g and beta in the g/beta ring, so every gate is computed once and
-// off the step's barrier-to-barrier path.
+// In-kernel gating: the gate-copying wave fetches the raw gate words of chunk
+// c+3 (their own ring) and, at the start of the next step, turns those of
+// chunk c+2 into g and beta in the g/beta ring, so every gate is computed once
+// and off the step's barrier-to-barrier path.
 #include <stddef.h>
 
 #include "gdn_device.h"
@@ -44,6 +70,9 @@ namespace {
 using namespace dev;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Asynchronous global -> LDS copies: lane l's bytes land at lds + l * size.
 // They are issued from inline assembly on purpose: the compiler does not track
@@ -95,22 +124,40 @@ template <int NSEG> __device__ __forceinline__ int swz(int row) {
     static_assert(NSEG == 8 || NSEG % 16 == 0, "row length");
     return NSEG >= 16 ? (row & 15) : ((row >> 1) & 7);
 }
-template <int W> __device__ __forceinline__ int sw_off(int row, int col) {
-    constexpr int NSEG = W / 8;
-    return row * W + (((col >> 3) ^ swz<NSEG>(row)) << 3) + (col & 7);
+
+// fp32 -> bf16, round to nearest even, two values per conversion instruction
+// (the pairs are joined as 32-bit words, which keeps the compiler from
+// merging them into one four-wide conversion that it would split per value).
+__device__ __forceinline__ bf16x4 cvt4(f32x4 x) {
+    const f32x2 a = {x[0], x[1]}, b = {x[2], x[3]};
+    const bf16x2 ra = __builtin_convertvector(a, bf16x2), rb = __builtin_convertvector(b, bf16x2);
+    const u32x2 u = {__builtin_bit_cast(unsigned, ra), __builtin_bit_cast(unsigned, rb)};
+    return __builtin_bit_cast(bf16x4, u);
 }
+// Byte offset of a ring slot, kept wave-uniform (a scalar register).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// 2^x by the hardware exponential; log2 by the hardware logarithm.
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Per-chunk results of the prep waves that the chain waves read.
 struct alignas(16) PrepOut {
-    bf16 alo[64][68];         // -A in the off-diagonal 16x16 blocks below the diagonal
-    bf16 p[64][72];           // P, columns in the key-slot order (see pcol); blocks (0,1), (2,3) zero
-    bf16 dt[4][16][16];       // D_b transposed: dt[b][j][i] = D_b[i][j]
-    float beta[64];
-    float bgr[64];            // beta e^gamma r
+    bf16 alo[6][16][16];      // -A in the six 16x16 blocks below the diagonal; block (i, m) at i (i - 1) / 2 + m
+    bf16 plo[32][40];         // P rows 0-31 (columns 0-31), columns in the key-slot order (see pcol)
+    bf16 phi[32][72];         // P rows 32-63; blocks (0,1) and (2,3) are zero
+    bf16 dt[3][4][16][16];    // transposed D_b, D_b diag(beta), -D_b diag(beta e^gamma r)
     float osc[64];            // output scale of (Q h)^T: scale rho e^gamma
     float kf[64];             // r e^{gamma_L - gamma}
     float decay;              // e^{gamma_L}
 };
+__device__ __forceinline__ constexpr int alo_blk(int i, int m) { return i * (i - 1) / 2 + m; }
+// Element (i, col) of P (rows below 32 only have the first 32 columns).
+template <typename PO> __device__ __forceinline__ auto pel(PO &po, int i, int col) {
+    return i < 32 ? &po.plo[i][col] : &po.phi[i - 32][col];
+}
 
 // Column of token j in PrepOut::p.  The output product reads P as the B
 // operand of a 16x16x32 product whose lane-group g holds tokens
@@ -123,12 +170,12 @@ __device__ __forceinline__ constexpr int pcol(int jt, int g) {   // first column
 template <int K, int VW> struct WsLds {
     bf16 kb[3][64 * K];       // raw k rows (swizzled), ring of three chunks
     bf16 qb[2][64 * K];       // raw q rows (swizzled)
-    bf16 vb[3][64 * VW];      // raw v rows of this slice (swizzled), ring of three chunks
+    bf16 vb[2][64 * VW];      // raw v rows by chunk parity: per chain wave its 64 x 16 columns, row-major
     float gb[2][64], bb[2][64];
     PrepOut po[2];
-    float adiag[4][16 * 20];  // per K-prep wave: its diagonal block of A, fp32, by column: A_ij at 20 j + 4 (i % 4) + i / 4
-    float stk[4][3][64];      // per K-prep wave: gamma, beta, r of the chunk being prepared
-    float stq[4][2][64];      // per Q-prep wave: gamma, r of the chunk being prepared
+    float adiag[4][16 * 16];  // per K-prep wave: its diagonal block of A, fp32, by column: A_ij at 16 j + i
+    float stk[4][4][64];      // per K-prep wave: gamma + log2 beta, gamma, log2 r, beta of the chunk being prepared
+    float stq[4][4][64];      // per Q-prep wave: the same (the first and last unused)
     float ra[2][64], rb[2][64];  // in-kernel gating: raw gate words by chunk parity (unused otherwise)
 };
 
@@ -149,14 +196,16 @@ __device__ __forceinline__ constexpr int kappa(int mt, int r) {
 // POOL: the states live in a slot-indexed pool and/or are stored as bf16
 // (p.state_indices, p.state_bf16).  Template parameters, so that the plain
 // kernel carries none of their code.
-template <int K, int V, bool GATED, bool POOL>
+template <int K, int V, int NCW, bool GATED, bool POOL>
 __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     typedef bf16 E;
     typedef bf16x8 v8;
     typedef bf16x4 v4;
     typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-    typedef WsLds<K, 64> Lds;
-    constexpr int VW = 64, VEC = 8;
+    constexpr int VW = 16 * NCW, VEC = 8;   // value columns per workgroup
+    constexpr bool MERGED = NCW == 8;       // four prep waves do both K- and Q-prep
+    static_assert((NCW == 4 || NCW == 8) && V % VW == 0, "layout");
+    typedef WsLds<K, VW> Lds;
     constexpr int NSK = K / VEC, NSV = VW / VEC;
     constexpr int KT = K / 16, KS = K / 32;
     constexpr int KROW = 2 * K, VROW = 2 * VW;   // bytes per raw row in LDS
@@ -165,8 +214,9 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int role = wave >> 2;   // 0 chain, 1 K-prep, 2 Q-prep
-    const int w4 = wave & 3;      // chain: column tile; prep: row tile
+    // 0 chain, 1 K-prep, 2 Q-prep, 3 both preps
+    const int role = wave < NCW ? 0 : MERGED ? 3 : (wave >> 2);
+    const int w4 = wave & 3;      // prep: row tile, and index among the four copying waves
     const int l16 = lane & 15, grp = lane >> 4;
 
     // Workgroup -> (sequence n, key head jk, value head j, value slice).  The
@@ -206,9 +256,12 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     const E *__restrict__ vg = (const E *)p.v;
     E *__restrict__ og = (E *)p.out;
     const size_t kq_row = (size_t)p.H * K, v_row = (POOL && p.v_zero) ? 0 : (size_t)p.HV * V;
+    const float l2_scale = fast_log2(p.scale);
 
+    const unsigned lds0 = (unsigned)(size_t)(lds_void *)&s;
     // raw k/q fragment of row tile t, step s2: row 16 t + l16, key slots
-    // 32 s2 + 8 grp .. +7 (one swizzled 16-byte segment)
+    // 32 s2 + 8 grp .. +7 (one swizzled 16-byte segment); byte offsets from the
+    // start of a chunk's rows
     int fo[KS];
     {
         const int sw = swz<NSK>(l16);   // the swizzle of row 16 t + l16 does not depend on t
@@ -237,63 +290,52 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         }
     };
 
-    // ---- asynchronous copies (Q-prep waves) --------------------------------
-    // LDS destinations are byte addresses (wave-uniform); the per-lane source
-    // offsets inside a full chunk are fixed, only the last chunk of a sequence
-    // clamps its rows.
-    const unsigned lds0 = (unsigned)(size_t)(lds_void *)&s;
-    unsigned kqo[NSK / 4], vvo[NSV / 4];
+    // ---- asynchronous copies ------------------------------------------------
+    // Raw k and q rows are copied by the four K-prep and the four Q-prep waves
+    // (NCW = 4), or by the eight chain waves (NCW = 8, where the chain waves
+    // have time to spare and the prep waves do not); the gates by the prep
+    // wave with w4 = 3; each chain wave copies its own v columns.  LDS
+    // destinations are byte addresses (wave-uniform); the per-lane source
+    // offsets inside a full chunk are fixed, only the last chunk of a
+    // sequence clamps its rows.  Copy t of a chunk's rows moves 1 KB.
+    constexpr int NCP = MERGED ? 8 : 4;          // waves sharing the copies of k (and of q)
+    const int cpw = MERGED ? wave : w4;          // this wave's index among them
+    unsigned kqo[NSK / NCP];
 #pragma unroll
-    for (int i = 0; i < NSK / 4; ++i) {
-        const int P = 64 * (w4 + 4 * i) + lane, row = P / NSK;
+    for (int i = 0; i < NSK / NCP; ++i) {
+        const int P = 64 * (cpw + NCP * i) + lane, row = P / NSK;
         kqo[i] = (unsigned)row * (unsigned)kq_row + (((P % NSK) ^ swz<NSK>(row)) * VEC);
     }
-#pragma unroll
-    for (int i = 0; i < NSV / 4; ++i) {
-        const int P = 64 * (w4 + 4 * i) + lane, row = P / NSV;
-        vvo[i] = (unsigned)row * (unsigned)v_row + (((P % NSV) ^ swz<NSV>(row)) * VEC);
-    }
-    auto issue = [&](int c) {
+    // rows of k (or q) of chunk c into the LDS chunk slot at byte address dst
+    auto issue_rows = [&](const E *src, int c, unsigned dst) {
         const int64_t t0 = tok0 + 64LL * c;
         const int last = min(64, len - 64 * c) - 1;
-        const unsigned kl = lds0 + offsetof(Lds, kb) + (c % 3) * (64 * K * 2);
-        const unsigned ql = lds0 + offsetof(Lds, qb) + (c & 1) * (64 * K * 2);
-        const unsigned vl = lds0 + offsetof(Lds, vb) + (c % 3) * (64 * VW * 2);
-        const E *kc = kg + (size_t)t0 * kq_row + (size_t)jk * K;
-        const E *qc = qg + (size_t)t0 * kq_row + (size_t)jk * K;
-        const E *vc = vg + (size_t)t0 * v_row + (size_t)j * V + vcol0;
+        const E *rc = src + (size_t)t0 * kq_row + (size_t)jk * K;
         if (last == 63) {
 #pragma unroll
-            for (int i = 0; i < NSK / 4; ++i) {
-                const unsigned d = 1024u * (w4 + 4 * i);
-                lds_copy16(kc + kqo[i], kl + d);
-                lds_copy16(qc + kqo[i], ql + d);
-            }
-#pragma unroll
-            for (int i = 0; i < NSV / 4; ++i) lds_copy16(vc + vvo[i], vl + 1024u * (w4 + 4 * i));
+            for (int i = 0; i < NSK / NCP; ++i) lds_copy16(rc + kqo[i], dst + 1024u * (cpw + NCP * i));
         } else {
 #pragma unroll
-            for (int i = 0; i < NSK / 4; ++i) {
-                const int t = w4 + 4 * i;
+            for (int i = 0; i < NSK / NCP; ++i) {
+                const int t = cpw + NCP * i;
                 const int P = 64 * t + lane, row = P / NSK, seg = (P % NSK) ^ swz<NSK>(row);
-                const unsigned off = (unsigned)min(row, last) * (unsigned)kq_row + seg * VEC;
-                lds_copy16(kc + off, kl + 1024u * t);
-                lds_copy16(qc + off, ql + 1024u * t);
-            }
-#pragma unroll
-            for (int i = 0; i < NSV / 4; ++i) {
-                const int t = w4 + 4 * i;
-                const int P = 64 * t + lane, row = P / NSV, seg = (P % NSV) ^ swz<NSV>(row);
-                lds_copy16(vc + (unsigned)min(row, last) * (unsigned)v_row + seg * VEC, vl + 1024u * t);
+                lds_copy16(rc + (unsigned)min(row, last) * (unsigned)kq_row + seg * VEC, dst + 1024u * t);
             }
         }
-        if (w4 == 3 && !gated) {
+    };
+    auto issue_k = [&](int c) { issue_rows(kg, c, lds0 + offsetof(Lds, kb) + (c % 3) * (64 * K * 2)); };
+    auto issue_q = [&](int c) { issue_rows(qg, c, lds0 + offsetof(Lds, qb) + (c & 1) * (64 * K * 2)); };
+    // g and beta of chunk c (gates given as tensors; the gate-copying wave only)
+    auto issue_gb = [&](int c) {
+        if (!gated) {
+            const int64_t t0 = tok0 + 64LL * c;
+            const int last = min(64, len - 64 * c) - 1;
             const size_t o = (size_t)(t0 + min(lane, last)) * p.HV + j;
             lds_copy4(p.g + o, lds0 + offsetof(Lds, gb) + (c & 1) * 256);
             lds_copy4(p.beta + o, lds0 + offsetof(Lds, bb) + (c & 1) * 256);
         }
     };
-    // raw gate words of chunk c (in-kernel gating; the copying wave only):
+    // raw gate words of chunk c (in-kernel gating; the gate-copying wave only):
     // the aligned 4-byte word that holds each token's input
     auto issue_gates = [&](int c) {
         if constexpr (GATED) {
@@ -305,282 +347,242 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         }
     };
 
-    if (role == 2 && nchunks > 0) {
-        issue(0);
-        if (gated && w4 == 3) {
+    // the prep wave that copies (and, with raw inputs, computes) the gates
+    const bool gate_wave = role == (MERGED ? 3 : 2) && w4 == 3;
+    if (nchunks > 0) {
+        if (role == (MERGED ? 0 : 1)) issue_k(0);
+        if (role == (MERGED ? 0 : 2)) issue_q(0);
+        if (gate_wave) {
+            issue_gb(0);
             issue_gates(0);
             if (nchunks > 1) issue_gates(1);
         }
-        wait_vmem();
-        if (gated && w4 == 3) gate_chunk(0);
     }
+    wait_vmem();
+    if (gated && gate_wave) gate_chunk(0);
     // P blocks (0,1) and (2,3) are read by the output product but never
     // written by the epilogue: zero them once in both buffers.
     if (role == 0) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int idx = 256 * q4 + tid, b2 = idx >> 9, blk = (idx >> 8) & 1, r = (idx >> 4) & 15, jj = idx & 15;
-            s.po[b2].p[32 * blk + r][pcol(2 * blk + 1, jj >> 2) + (jj & 3)] = (E)0.f;
+        for (int q4 = 0; q4 < 16 / NCW; ++q4) {
+            const int idx = 64 * NCW * q4 + tid, b2 = idx >> 9, blk = (idx >> 8) & 1, r = (idx >> 4) & 15, jj = idx & 15;
+            *pel(s.po[b2], 32 * blk + r, pcol(2 * blk + 1, jj >> 2) + (jj & 3)) = (E)0.f;
         }
     }
     lds_barrier();
 
     // The three roles run separate loops with the same number of barriers, so
     // that none carries another's registers.
-    if (role == 2) {
-        // ============================ Q-prep ==================================
+    // ============================ preparation ===============================
+    // The work of row tile W for chunk cn: with DO_K the -A tiles, D_W (three
+    // forms) and the state factors; with DO_Q the P tiles and the output
+    // scale.  Tile assignment (tiles are transposed: C[j][i] = k_j . k_i or
+    // k_j . q_i), spread so that no wave waits for another inside the step:
+    //   K K^T: the diagonal tile W (for A_WW and D_W) and W = 0: (1,0) (2,0);
+    //          W = 1: (2,1) (3,1);  W = 2: (3,0) (3,2);  W = 3: none
+    //          (5, 5, 5 and 1 tiles, against 1, 3, 5 and 7 for whole rows);
+    //   Q K^T: W = 0: rows 0, 1 ((0,0) (1,0) (1,1));  W = 1: row 2;
+    //          W = 2: (3,0) (3,1) (3,2);  W = 3: (3,3);
+    // and the diagonal K K^T and Q Q^T tiles whose norms those need, all in
+    // one pass over the k and q fragments.
+    auto prep_chunk = [&](auto w_c, auto k_c, auto q_c, int cn) {
+        constexpr int W = decltype(w_c)::value;
+        constexpr bool DO_K = decltype(k_c)::value != 0, DO_Q = decltype(q_c)::value != 0;
+        constexpr int NOFF = (DO_K && W != 3) ? 2 : 0;
+        constexpr int OI0 = W == 0 ? 1 : W == 1 ? 2 : 3, OJ0 = W == 0 ? 0 : W == 1 ? 1 : 0;
+        constexpr int OI1 = W == 0 ? 2 : 3, OJ1 = W == 0 ? 0 : W == 1 ? 1 : 2;
+        constexpr int R0 = W == 0 ? 0 : W == 1 ? 2 : 3, R1 = W == 0 ? 1 : W == 1 ? 2 : 3;
+        constexpr int J0 = W == 3 ? 3 : 0, J1 = W == 0 ? 1 : W == 3 ? 3 : 2;
+        constexpr int NR = DO_Q ? R1 - R0 + 1 : 0;
+        constexpr int KDK = W == 0 ? 0x7 : W == 1 ? 0xE : W == 2 ? 0xD : 0x8;   // norms of the K work
+        constexpr int KDQ = ((2 << J1) - 1) & ~((1 << J0) - 1);                // norms of the Q work
+        constexpr int KD = (DO_K ? KDK : 0) | (DO_Q ? KDQ : 0);
+        PrepOut &po = s.po[cn & 1];
+        // staging of this wave: gamma + log2 beta, gamma, log2 r, beta by token
+        float(*st)[64] = DO_K ? s.stk[w4] : s.stq[w4];
+        float *sgb = st[0], *sg = st[1], *sl = st[2], *sb = st[3];
+        float gam, bt;   // this lane's token: gate cumsum (log2 units) and beta
+        cumsum(cn, gam, bt);
+        if constexpr (DO_K) {
+            sgb[lane] = gam + fast_log2(bt);
+            sb[lane] = bt;
+        }
+        sg[lane] = gam;
+        const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gam), 63));   // gamma_L
+        const E *kb = (const E *)((const char *)s.kb[0] + uni((cn % 3) * 64 * KROW));
+        const E *qb = (const E *)((const char *)s.qb[0] + uni((cn & 1) * 64 * KROW));
+        f32x4 gd[4], go[2], gq[2][4], gqq[2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            gd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            gq[0][t] = gq[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        go[0] = go[1] = gqq[0] = gqq[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            v8 fk[4], fq[2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (KD >> t & 1) fk[t] = frag(kb, t, s2);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) fq[r] = frag(qb, R0 + r, s2);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (KD >> t & 1) gd[t] = mma(fk[t], fk[t], gd[t]);
+            if constexpr (NOFF > 0) {
+                go[0] = mma(fk[OJ0], fk[OI0], go[0]);
+                go[1] = mma(fk[OJ1], fk[OI1], go[1]);
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+#pragma unroll
+                for (int jt = J0; jt <= J1; ++jt)
+                    if (jt <= R0 + r) gq[r][jt] = mma(fk[jt], fq[r], gq[r][jt]);
+                gqq[r] = mma(fq[r], fq[r], gqq[r]);
+            }
+        }
+        // log2 of the norm factors of the k rows of the diagonal tiles: lane
+        // (l16, l16 / 4) holds row l16 at e = l16 % 4
+        {
+            const int e = l16 - 4 * grp;
+            if (e >= 0 && e < 4) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (KD >> t & 1) sl[16 * t + l16] = p.use_l2norm ? -0.5f * fast_log2(gd[t][e] + 1e-6f) : 0.f;
+            }
+        }
+        float la[2];   // a'_i = gamma_i + log2(scale rho_i) of the lane's row in tile R0 + r
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float qq = __shfl(gqq[r][l16 & 3], (l16 >> 2) * 16 + l16);
+            la[r] = l2_scale + (p.use_l2norm ? -0.5f * fast_log2(qq + 1e-6f) : 0.f);
+        }
+        wave_lds_sync();   // the staged factors come from other lanes
+        if constexpr (DO_K) {
+            {   // diagonal tile -> A_WW (fp32, by column).  The raw Gram tile is
+                // symmetric, so the lane's values serve as rows i = 4 grp + e (of
+                // the tile) of column j = l16: four consecutive entries.
+                const f32x4 ai = *(const f32x4 *)&sgb[16 * W + 4 * grp] + *(const f32x4 *)&sl[16 * W + 4 * grp];
+                const int jc = 16 * W + l16;
+                const float cj = sg[jc] - sl[jc];
+                f32x4 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = (4 * grp + e > l16) ? fast_exp2(ai[e] - cj) * gd[W][e] : 0.f;
+                *(f32x4 *)&s.adiag[W][16 * l16 + 4 * grp] = a;
+            }
+            // off-diagonal tiles (i, j) -> -A (bf16): row 16 i + l16, columns
+            // 16 j + 4 grp + e
+            auto off = [&](auto oi_c, auto oj_c, const f32x4 &g) {
+                constexpr int OI = decltype(oi_c)::value, OJ = decltype(oj_c)::value;
+                const int ik = 16 * OI + l16;
+                const float ai = sgb[ik] + sl[ik];
+                const f32x4 cj = *(const f32x4 *)&sg[16 * OJ + 4 * grp] - *(const f32x4 *)&sl[16 * OJ + 4 * grp];
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = -(fast_exp2(ai - cj[e]) * g[e]);
+                *(v4 *)&po.alo[alo_blk(OI, OJ)][l16][4 * grp] = cvt4(v);
+            };
+            if constexpr (NOFF > 0) {
+                off(IC<OI0>(), IC<OJ0>(), go[0]);
+                off(IC<OI1>(), IC<OJ1>(), go[1]);
+            }
+            // r e^{gamma_L - gamma} for the rows of tile W, e^{gamma_L} (W = 0)
+            if (grp == 0) {
+                const int i = 16 * W + l16;
+                po.kf[i] = fast_exp2(gl - (sg[i] - sl[i]));
+                if (W == 0 && l16 == 0) po.decay = fast_exp2(gl);
+            }
+        }
+        if constexpr (DO_Q) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const int itq = R0 + r, iq = 16 * itq + l16;
+                const float ai = sg[iq] + la[r];
+                if (W != 2 && grp == 0) po.osc[iq] = fast_exp2(ai);   // row 3: W = 3 publishes
+#pragma unroll
+                for (int jt = J0; jt <= J1; ++jt) {
+                    if (jt > itq) continue;
+                    const f32x4 cj = *(const f32x4 *)&sg[16 * jt + 4 * grp] - *(const f32x4 *)&sl[16 * jt + 4 * grp];
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = fast_exp2(ai - cj[e]) * gq[r][jt][e];
+                        if (jt == itq) v[e] = iq >= 16 * jt + 4 * grp + e ? v[e] : 0.f;
+                    }
+                    *(v4 *)pel(po, iq, pcol(jt, grp)) = cvt4(v);
+                }
+            }
+        }
+        if constexpr (DO_K) {
+            wave_lds_sync();   // A_WW is read back across lanes by the solve
+            // D_W = (I + A_WW)^-1 by column-oriented forward substitution
+            // with every lane busy: the four lanes of quad cc hold column cc
+            // of D, lane gg of the quad rows 4 gg .. 4 gg + 3.  Once x_m is
+            // final it is broadcast inside each quad (one DPP move) and
+            // updates every row; A being strictly lower, the rows at or
+            // above m take zeros, so each step is four branch-free FMAs.
+            const float *AT = s.adiag[W];
+            const int cc = lane >> 2, gg = lane & 3;
+            float x[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = (4 * gg + q == cc) ? 1.f : 0.f;
+            f32x4 col[15];
+#pragma unroll
+            for (int m = 0; m < 15; ++m) col[m] = *(const f32x4 *)&AT[16 * m + 4 * gg];
+            auto step = [&](auto m_c) {
+                constexpr int m = decltype(m_c)::value, sl4 = m / 4;   // x_m from lane m / 4 of the quad
+                const float xm = dpp_mov<sl4 | (sl4 << 2) | (sl4 << 4) | (sl4 << 6), 0xf>(x[m % 4]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[q] -= col[m][q] * xm;
+            };
+            step(IC<0>()); step(IC<1>()); step(IC<2>()); step(IC<3>()); step(IC<4>());
+            step(IC<5>()); step(IC<6>()); step(IC<7>()); step(IC<8>()); step(IC<9>());
+            step(IC<10>()); step(IC<11>()); step(IC<12>()); step(IC<13>()); step(IC<14>());
+            // column cc of D is row cc of D^T; the column scalings of the two
+            // scaled forms are the factors of token 16 W + cc
+            const int tc = 16 * W + cc;
+            const float bc = sb[tc], bgr = fast_exp2(sgb[tc] + sl[tc]);
+            const f32x4 xv = {x[0], x[1], x[2], x[3]};
+            *(v4 *)&po.dt[0][W][cc][4 * gg] = cvt4(xv);
+            *(v4 *)&po.dt[1][W][cc][4 * gg] = cvt4(xv * bc);
+            *(v4 *)&po.dt[2][W][cc][4 * gg] = cvt4(xv * -bgr);
+        }
+    };
+    auto prep_tile = [&](auto k_c, auto q_c, int cn) {
+        switch (w4) {
+            case 0: prep_chunk(IC<0>(), k_c, q_c, cn); break;
+            case 1: prep_chunk(IC<1>(), k_c, q_c, cn); break;
+            case 2: prep_chunk(IC<2>(), k_c, q_c, cn); break;
+            default: prep_chunk(IC<3>(), k_c, q_c, cn); break;
+        }
+    };
+
+    // The prep waves: at step c, the copies of chunk c+2 (k, q, gates) and the
+    // preparation of chunk c+1.  The chain and the prep waves run
+    // separate loops with the same number of barriers, so that neither
+    // carries the other's registers.
+    auto prep_loop = [&](auto do_k_c, auto do_q_c) {
+        constexpr bool DO_K = decltype(do_k_c)::value != 0, DO_Q = decltype(do_q_c)::value != 0;
         for (int c = -1; c < nchunks; ++c) {
             const int cn = c + 1;
-            if (c + 2 < nchunks) issue(c + 2);
-            if (gated && w4 == 3) {
-                if (c + 2 < nchunks) gate_chunk(c + 2);   // its raw words landed before the last barrier
+            if constexpr (!MERGED) {
+                if (DO_K && c + 2 < nchunks) issue_k(c + 2);
+                if (DO_Q && c + 2 < nchunks) issue_q(c + 2);
+            }
+            if (gate_wave) {
+                if (c + 2 < nchunks) issue_gb(c + 2);
+                if (gated && c + 2 < nchunks) gate_chunk(c + 2);   // its raw words landed before the last barrier
                 if (c + 3 < nchunks) issue_gates(c + 3);
             }
-            if (cn < nchunks) {
-                PrepOut &po = s.po[cn & 1];
-                float *sg = s.stq[w4][0], *sr = s.stq[w4][1];
-                {
-                    float gam, b;
-                    cumsum(cn, gam, b);
-                    sg[lane] = gam;
-                }
-                const E *kb = s.kb[cn % 3], *qb = s.qb[cn & 1];
-                // The ten causal tiles of Q K^T, spread so that no wave waits for
-                // another inside the step; each wave also computes the diagonal
-                // tiles of Q Q^T and K K^T for the norms its tiles need:
-                //   wave 0: rows 0, 1 (tiles (0,0) (1,0) (1,1));  wave 1: row 2;
-                //   wave 2: (3,0) (3,1) (3,2);  wave 3: (3,3)
-                // (7, 7, 7 and 3 tiles, against 3, 5, 7 and 9 for whole row tiles).
-                // Tiles are transposed: C[j][i] = k_j . q_i.
-                auto qprep = [&](auto w_c) {
-                    constexpr int W = decltype(w_c)::value;
-                    constexpr int R0 = W == 0 ? 0 : W == 1 ? 2 : 3, R1 = W == 0 ? 1 : W == 1 ? 2 : 3;
-                    constexpr int J0 = W == 3 ? 3 : 0, J1 = W == 0 ? 1 : W == 3 ? 3 : 2;
-                    constexpr int NR = R1 - R0 + 1, NJ = J1 - J0 + 1;
-                    f32x4 gq[NR][NJ], gd[NJ], gqq[NR];
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        gqq[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) gq[r][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
-#pragma unroll
-                    for (int jj = 0; jj < NJ; ++jj) gd[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s2 = 0; s2 < KS; ++s2) {
-                        v8 fk[NJ], bq[NR];
-#pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) fk[jj] = frag(kb, J0 + jj, s2);
-#pragma unroll
-                        for (int r = 0; r < NR; ++r) bq[r] = frag(qb, R0 + r, s2);
-#pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) {
-                            gd[jj] = mma(fk[jj], fk[jj], gd[jj]);
-#pragma unroll
-                            for (int r = 0; r < NR; ++r)
-                                if (J0 + jj <= R0 + r) gq[r][jj] = mma(fk[jj], bq[r], gq[r][jj]);
-                        }
-#pragma unroll
-                        for (int r = 0; r < NR; ++r) gqq[r] = mma(bq[r], bq[r], gqq[r]);
-                    }
-                    // norms of the k rows of tiles J0..J1 from the diagonals: lane
-                    // (l16, l16 / 4) holds row l16 at e = l16 % 4
-                    {
-                        const int e = l16 - 4 * grp;
-                        if (e >= 0 && e < 4) {
-#pragma unroll
-                            for (int jj = 0; jj < NJ; ++jj)
-                                sr[16 * (J0 + jj) + l16] = p.use_l2norm ? rsqrtf(gd[jj][e] + 1e-6f) : 1.f;
-                        }
-                    }
-                    float rho[NR];
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const float qq = __shfl(gqq[r][l16 & 3], (l16 >> 2) * 16 + l16);
-                        rho[r] = p.use_l2norm ? rsqrtf(qq + 1e-6f) : 1.f;
-                    }
-                    wave_lds_sync();   // the staged gamma and r come from other lanes
-                    f32x4 gj[NJ], rj[NJ];
-#pragma unroll
-                    for (int jj = 0; jj < NJ; ++jj) {
-                        gj[jj] = *(const f32x4 *)&sg[16 * (J0 + jj) + 4 * grp];
-                        rj[jj] = *(const f32x4 *)&sr[16 * (J0 + jj) + 4 * grp];
-                    }
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const int itq = R0 + r, iq = 16 * itq + l16;
-                        const float giq = sg[iq], srq = p.scale * rho[r];
-                        if (W != 2 && grp == 0) po.osc[iq] = srq * fast_exp2(giq);   // row 3: wave 3 publishes
-#pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) {
-                            const int jt = J0 + jj;
-                            if (jt > itq) continue;
-                            v4 o;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float v = srq * rj[jj][e] * fast_exp2(giq - gj[jj][e]) * gq[r][jj][e];
-                                o[e] = (E)((jt < itq || iq >= 16 * jt + 4 * grp + e) ? v : 0.f);
-                            }
-                            *(v4 *)&po.p[iq][pcol(jt, grp)] = o;
-                        }
-                    }
-                };
-                switch (w4) {
-                    case 0: qprep(IC<0>()); break;
-                    case 1: qprep(IC<1>()); break;
-                    case 2: qprep(IC<2>()); break;
-                    default: qprep(IC<3>()); break;
-                }
-            }
-            wait_vmem();   // this wave's copies of chunk c+2
+            if (cn < nchunks) prep_tile(do_k_c, do_q_c, cn);
+            wait_vmem();   // this wave's copies
             lds_barrier();
         }
-        return;
-    }
-
-    if (role == 1) {
-        // ============================ K-prep ==================================
-        for (int c = -1; c < nchunks; ++c) {
-            const int cn = c + 1;
-            if (cn < nchunks) {
-                PrepOut &po = s.po[cn & 1];
-                float *sg = s.stk[w4][0], *sb = s.stk[w4][1], *sr = s.stk[w4][2];
-                {
-                    float gam, b;
-                    cumsum(cn, gam, b);
-                    sg[lane] = gam;
-                    sb[lane] = b;
-                    if (w4 == 0) po.beta[lane] = b;
-                }
-                const E *kb = s.kb[cn % 3];
-                // The ten lower Gram tiles of K K^T are spread so that no wave
-                // waits for another inside the step: wave W computes its own
-                // diagonal tile (for A_WW and D_W), two off-diagonal tiles (i, j)
-                // and the further diagonal tiles whose norms those need:
-                //   W = 0: (1,0) (2,0), diagonals 0 1 2;  W = 1: (2,1) (3,1), 1 2 3;
-                //   W = 2: (3,0) (3,2), diagonals 0 2 3;  W = 3: diagonal 3 only
-                // (5, 5, 5 and 1 tiles, against 1, 3, 5 and 7 for whole row tiles).
-                // Tiles are transposed: C[j][i] = k_j . k_i.
-                auto kprep = [&](auto w_c) {
-                    constexpr int W = decltype(w_c)::value;
-                    constexpr int NOFF = W == 3 ? 0 : 2;
-                    constexpr int OI0 = W == 0 ? 1 : W == 1 ? 2 : 3, OJ0 = W == 0 ? 0 : W == 1 ? 1 : 0;
-                    constexpr int OI1 = W == 0 ? 2 : 3, OJ1 = W == 0 ? 0 : W == 1 ? 1 : 2;
-                    constexpr int DM = W == 0 ? 0x7 : W == 1 ? 0xE : W == 2 ? 0xD : 0x8;
-                    f32x4 gd[4], go[2];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) gd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    go[0] = go[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s2 = 0; s2 < KS; ++s2) {
-                        v8 fk[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            if (DM >> t & 1) fk[t] = frag(kb, t, s2);
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            if (DM >> t & 1) gd[t] = mma(fk[t], fk[t], gd[t]);
-                        if (NOFF > 0) {
-                            go[0] = mma(fk[OJ0], fk[OI0], go[0]);
-                            go[1] = mma(fk[OJ1], fk[OI1], go[1]);
-                        }
-                    }
-                    // norms of the rows of the computed diagonal tiles: lane
-                    // (l16, l16 / 4) holds row l16 at e = l16 % 4
-                    {
-                        const int e = l16 - 4 * grp;
-                        if (e >= 0 && e < 4) {
-#pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                if (DM >> t & 1) sr[16 * t + l16] = p.use_l2norm ? rsqrtf(gd[t][e] + 1e-6f) : 1.f;
-                        }
-                    }
-                    wave_lds_sync();   // the staged gamma / beta / r come from other lanes
-                    {   // diagonal tile -> A_WW (fp32, by column).  The raw Gram tile
-                        // is symmetric, so the lane's values serve as rows i = 4 grp + e
-                        // (of the tile) of column j = l16.  Rows are stored in the
-                        // order the solve's lanes take them (i % 4 major), so that
-                        // each solve step reads one vector.
-                        const f32x4 gw = *(const f32x4 *)&sg[16 * W + 4 * grp];
-                        const f32x4 rw = *(const f32x4 *)&sr[16 * W + 4 * grp];
-                        const f32x4 bw = *(const f32x4 *)&sb[16 * W + 4 * grp];
-                        const int ik = 16 * W + l16;
-                        const float gik = sg[ik], rik = sr[ik];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float v = bw[e] * rw[e] * rik * fast_exp2(gw[e] - gik) * gd[W][e];
-                            s.adiag[W][20 * l16 + 4 * e + grp] = (4 * grp + e > l16) ? v : 0.f;
-                        }
-                    }
-                    // off-diagonal tiles (i, j) -> -A (bf16): row 16 i + l16,
-                    // columns 16 j + 4 grp + e
-                    auto off = [&](auto oi_c, auto oj_c, const f32x4 &g) {
-                        constexpr int OI = decltype(oi_c)::value, OJ = decltype(oj_c)::value;
-                        const int ik = 16 * OI + l16;
-                        const float gik = sg[ik], bri = sb[ik] * sr[ik];
-                        const f32x4 gj = *(const f32x4 *)&sg[16 * OJ + 4 * grp];
-                        const f32x4 rj = *(const f32x4 *)&sr[16 * OJ + 4 * grp];
-                        v4 o;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) o[e] = (E)(-(bri * rj[e] * fast_exp2(gik - gj[e]) * g[e]));
-                        *(v4 *)&po.alo[ik][16 * OJ + 4 * grp] = o;
-                    };
-                    if constexpr (NOFF > 0) {
-                        off(IC<OI0>(), IC<OJ0>(), go[0]);
-                        off(IC<OI1>(), IC<OJ1>(), go[1]);
-                    }
-                    // beta e^gamma r, r e^{gamma_L - gamma} for the rows of tile W,
-                    // e^{gamma_L} (wave 0), for the chain
-                    if (grp == 0) {
-                        const int i = 16 * W + l16;
-                        const float gi = sg[i], gl = sg[63], ri = sr[i];
-                        po.bgr[i] = sb[i] * fast_exp2(gi) * ri;
-                        po.kf[i] = ri * fast_exp2(gl - gi);
-                        if (W == 0 && l16 == 0) po.decay = fast_exp2(gl);
-                    }
-                    wave_lds_sync();   // A_WW is read back across lanes by the solve
-                };
-                switch (w4) {
-                    case 0: kprep(IC<0>()); break;
-                    case 1: kprep(IC<1>()); break;
-                    case 2: kprep(IC<2>()); break;
-                    default: kprep(IC<3>()); break;
-                }
-                // D_w = (I + A_w,w)^-1 by column-oriented forward substitution
-                // with every lane busy: the four lanes of quad c hold column c
-                // of D, lane g of the quad rows g, g+4, g+8, g+12.  Once x_m is
-                // final it is broadcast inside each quad (one DPP move) and
-                // updates every row; A being strictly lower, the rows at or
-                // above m take zeros, so each step is four branch-free FMAs.
-                {
-                    const float *AT = s.adiag[w4];
-                    const int cc = lane >> 2, gg = lane & 3;
-                    float x[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) x[q] = (4 * q + gg == cc) ? 1.f : 0.f;
-                    f32x4 col[16];
-#pragma unroll
-                    for (int m = 0; m < 15; ++m) col[m] = *(const f32x4 *)&AT[20 * m + 4 * gg];
-                    auto bcast = [&](auto m_c) {   // x_m from lane m % 4 of the quad
-                        constexpr int m = decltype(m_c)::value, sl = m % 4;
-                        return dpp_mov<sl | (sl << 2) | (sl << 4) | (sl << 6), 0xf>(x[m / 4]);
-                    };
-                    auto step = [&](auto m_c) {
-                        constexpr int m = decltype(m_c)::value;
-                        const float xm = bcast(m_c);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) x[q] -= col[m][q] * xm;
-                    };
-                    step(IC<0>()); step(IC<1>()); step(IC<2>()); step(IC<3>()); step(IC<4>());
-                    step(IC<5>()); step(IC<6>()); step(IC<7>()); step(IC<8>()); step(IC<9>());
-                    step(IC<10>()); step(IC<11>()); step(IC<12>()); step(IC<13>()); step(IC<14>());
-                    // column cc of D is row cc of D^T
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) po.dt[w4][cc][4 * q + gg] = (E)x[q];
-                }
-            }
-            lds_barrier();
-        }
+    };
+    if (role != 0) {
+        if constexpr (MERGED) prep_loop(IC<1>(), IC<1>());
+        else if (role == 1) prep_loop(IC<1>(), IC<0>());
+        else prep_loop(IC<0>(), IC<1>());
         return;
     }
 
@@ -596,11 +598,25 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
 #pragma unroll
         for (int m2 = 0; m2 < KT / 2; ++m2) to[m2] = rr * KROW + (((4 * m2 + (l16 & 3)) ^ sw) << 4);
     }
+    // This wave's v columns c0 .. c0 + 15 sit in their own 64 x 16 block of the
+    // chunk's v buffer (32-byte rows), copied by this wave one chunk ahead:
+    // copy i moves rows 32 i .. 32 i + 31, lane l one 16-byte half row.
+    const int c0 = 16 * wave;
+    const unsigned vslot0 = lds0 + offsetof(Lds, vb) + 2048u * wave;
+    auto issue_vw = [&](int c) {
+        const int64_t t0 = tok0 + 64LL * c;
+        const int last = min(64, len - 64 * c) - 1;
+        const E *vc = vg + (size_t)j * V + vcol0 + c0 + 8 * (lane & 1);
+        const unsigned dst = vslot0 + (c & 1) * (64 * VROW);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            lds_copy16(vc + (size_t)(t0 + min(32 * i + (lane >> 1), last)) * v_row, dst + 1024u * i);
+    };
     // transpose read of the v tile: token row 16 ti + 4 grp + l16/4, value
-    // columns c0 + 4 (l16 % 4) .. +3 of this wave's 16 columns
-    const int c0 = 16 * w4;
-    const int vo = (4 * grp + (l16 >> 2)) * VROW +
-                   (((2 * w4 + ((l16 & 3) >> 1)) ^ swz<NSV>(4 * grp + (l16 >> 2))) << 4) + 8 * (l16 & 1);
+    // columns c0 + 4 (l16 % 4) .. +3
+    const int vo = (4 * grp + (l16 >> 2)) * 32 + 8 * (l16 & 3);
+    // transpose read of a 16x16 D block: row 4 grp + l16/4, columns 4 (l16 % 4) .. +3
+    const int dto = (4 * grp + (l16 >> 2)) * 32 + 8 * (l16 & 3);
 
     f32x4 h[KT];
     size_t sbase = ((size_t)n * p.HV + j) * K * V + vcol0, sbase_in = sbase;
@@ -636,45 +652,50 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         zk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         zq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     for (int c = -1; c < nchunks; ++c) {
         const int cn = c + 1;
+        // copies: v of chunk c+1 (this wave's columns), with NCW = 8 also k and
+        // q rows of chunk c+2; all landed before the step's barrier
+        if (cn < nchunks) issue_vw(cn);
+        if constexpr (MERGED) {
+            if (c + 2 < nchunks) {
+                issue_k(c + 2);
+                issue_q(c + 2);
+            }
+        }
         if (c >= 0) {
-            const PrepOut &po = s.po[c & 1];
-            const char *kb = (const char *)s.kb[c % 3];
-            const char *vb = (const char *)s.vb[c % 3];
+            const PrepOut &po = *(const PrepOut *)((const char *)s.po + uni((c & 1) * (int)sizeof(PrepOut)));
+            const char *kb = (const char *)s.kb[0] + uni((c % 3) * 64 * KROW);
+            const char *vbp = (const char *)s.vb[0] + 2048 * wave + uni((c & 1) * 64 * VROW) + vo;
+            const char *dtp = (const char *)&po.dt[0][0][0][0] + dto;
             const int64_t t0 = tok0 + 64LL * c;
             const int L = min(64, len - 64 * c);
-            // X = diag(beta) V - diag(beta e^gamma r) Z
-            f32x4 xz[4];
+            // Start of each block of V_new: D_b diag(beta) V_b - D_b diag(beta e^gamma r) Z_b
+            f32x4 acc[4], y[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                const v4 vv = tr(vb + vo + 16 * ti * VROW);
-                const int r0 = 16 * ti + 4 * grp;
-                const f32x4 be = *(const f32x4 *)&po.beta[r0];
-                const f32x4 bgr = *(const f32x4 *)&po.bgr[r0];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xz[ti][e] = be[e] * (float)vv[e] - bgr[e] * zk[ti][e];
+            for (int b = 0; b < 4; ++b) {
+                const v4 vv = tr(vbp + 512 * b);
+                const v4 fb = tr(dtp + (4 + b) * 512), fg = tr(dtp + (8 + b) * 512);
+                acc[b] = mma_k16(fb, vv, zero4);
+                acc[b] = mma_k16(fg, cvt4(zk[b]), acc[b]);
+                y[b] = zero4;
             }
             // V_new by block forward substitution, right-looking: as soon as
             // block m is final it is applied to every later block, so the
-            // updates of different blocks overlap and only one product per block
-            // sits on the dependency chain.
+            // updates of different blocks overlap and only two products per
+            // block sit on the dependency chain.
             v4 vb16[4];
             f32x4 vnf[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                v4 rbv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) rbv[e] = (E)xz[m][e];
-                // D_m (row l16, columns 4 grp..+3) by a transpose read of D_m^T
-                const v4 dfr = tr(&po.dt[m][4 * grp + (l16 >> 2)][4 * (l16 & 3)]);
-                vnf[m] = mma_k16(dfr, rbv, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vb16[m][e] = (E)vnf[m][e];
+                if (m > 0) acc[m] = mma_k16(tr(dtp + m * 512), cvt4(y[m]), acc[m]);
+                vnf[m] = acc[m];
+                vb16[m] = cvt4(acc[m]);
 #pragma unroll
                 for (int bi = m + 1; bi < 4; ++bi)
-                    xz[bi] = mma_k16(*(const v4 *)&po.alo[16 * bi + l16][16 * m + 4 * grp], vb16[m], xz[bi]);
+                    y[bi] = mma_k16(*(const v4 *)&po.alo[alo_blk(bi, m)][l16][4 * grp], vb16[m], y[bi]);
             }
             // V_new for the output product, diag(kf) V_new for the state
             v8 vnb[2], vkb[2];
@@ -682,13 +703,8 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
             for (int s2 = 0; s2 < 2; ++s2) {
                 const f32x4 k0 = *(const f32x4 *)&po.kf[32 * s2 + 4 * grp];
                 const f32x4 k1 = *(const f32x4 *)&po.kf[32 * s2 + 16 + 4 * grp];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vnb[s2][e] = vb16[2 * s2][e];
-                    vnb[s2][4 + e] = vb16[2 * s2 + 1][e];
-                    vkb[s2][e] = (E)(k0[e] * vnf[2 * s2][e]);
-                    vkb[s2][4 + e] = (E)(k1[e] * vnf[2 * s2 + 1][e]);
-                }
+                vnb[s2] = cat8(vb16[2 * s2], vb16[2 * s2 + 1]);
+                vkb[s2] = cat8(cvt4(k0 * vnf[2 * s2]), cvt4(k1 * vnf[2 * s2 + 1]));
             }
             // O^T tiles [value][token]: (Q h)^T scaled by scale rho e^gamma per
             // token, plus (P V_new)^T; and h <- e^{gamma_L} h + K^T diag(kf) V_new
@@ -700,64 +716,48 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                 const int i = 16 * ti + l16;
                 o[ti] = zq[ti] * po.osc[i];
 #pragma unroll
-                for (int s2 = 0; s2 <= ti / 2; ++s2) o[ti] = mma(vnb[s2], *(const v8 *)&po.p[i][pcol(2 * s2, grp)], o[ti]);
+                for (int s2 = 0; s2 <= ti / 2; ++s2) o[ti] = mma(vnb[s2], *(const v8 *)pel(po, i, pcol(2 * s2, grp)), o[ti]);
             }
             const float dec = po.decay;
 #pragma unroll
-            for (int mt = 0; mt < KT; ++mt) {
-                f32x4 acc = h[mt] * dec;
+            for (int m2 = 0; m2 < KT / 2; ++m2) {
+                const char *pm = kb + to[m2];
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const char *pa = kb + to[mt >> 1] + 8 * (mt & 1) + 32 * s2 * KROW;
-                    const v4 a0 = tr(pa), a1 = tr(pa + 16 * KROW);
-                    v8 a;
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int mt = 2 * m2 + hf;
+                    f32x4 acc2 = h[mt] * dec;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        a[e] = a0[e];
-                        a[4 + e] = a1[e];
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const char *pa = pm + 8 * hf + 32 * s2 * KROW;
+                        acc2 = mma(cat8(tr(pa), tr(pa + 16 * KROW)), vkb[s2], acc2);
                     }
-                    acc = mma(a, vkb[s2], acc);
+                    h[mt] = acc2;
                 }
-                h[mt] = acc;
             }
             E *dst = og + ((size_t)t0 * p.HV + j) * V + vcol0 + c0 + 4 * grp;
             const size_t orow = (size_t)p.HV * V;
             if (L == 64) {
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    v4 ov;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ov[e] = (E)o[ti][e];
-                    *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = ov;
-                }
+                for (int ti = 0; ti < 4; ++ti)
+                    *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = cvt4(o[ti]);
             } else {
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    if (16 * ti + l16 < L) {
-                        v4 ov;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) ov[e] = (E)o[ti][e];
-                        *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = ov;
-                    }
-                }
+                for (int ti = 0; ti < 4; ++ti)
+                    if (16 * ti + l16 < L) *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = cvt4(o[ti]);
             }
         }
         if (cn < nchunks) {
             // Z = K h and (Q h)^T of chunk cn with the updated state
-            const E *kb = s.kb[cn % 3], *qb = s.qb[cn & 1];
+            const E *kb = (const E *)((const char *)s.kb[0] + uni((cn % 3) * 64 * KROW));
+            const E *qb = (const E *)((const char *)s.qb[0] + uni((cn & 1) * 64 * KROW));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                zk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                zq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                zk[t] = zero4;
+                zq[t] = zero4;
             }
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2) {
-                v8 hb;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    hb[e] = (E)h[2 * s2][e];
-                    hb[4 + e] = (E)h[2 * s2 + 1][e];
-                }
+                const v8 hb = cat8(cvt4(h[2 * s2]), cvt4(h[2 * s2 + 1]));
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     zk[t] = mma(frag(kb, t, s2), hb, zk[t]);
@@ -765,6 +765,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                 }
             }
         }
+        wait_vmem();   // this wave's copies
         lds_barrier();
     }
 
@@ -783,30 +784,42 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     }
 }
 
-template <bool GATED, bool POOL>
-hipError_t launch_ws_kv(const Params &p, unsigned grid, hipStream_t st) {
-    if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, GATED, POOL><<<grid, 768, 0, st>>>(p);
-    else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, GATED, POOL><<<grid, 768, 0, st>>>(p);
-    else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, GATED, POOL><<<grid, 768, 0, st>>>(p);
-    else fused_ws_kernel<128, 128, GATED, POOL><<<grid, 768, 0, st>>>(p);
+template <int NCW, bool GATED, bool POOL>
+hipError_t launch_ws_kv(const Params &p, hipStream_t st) {
+    const int per_group = (p.HV / p.H) * (p.V / (16 * NCW));
+    const unsigned grid = (unsigned)((p.N * p.H + 7) / 8) * 8 * per_group;
+    if constexpr (NCW == 8) {
+        if (p.K == 64) fused_ws_kernel<64, 128, 8, GATED, POOL><<<grid, 768, 0, st>>>(p);
+        else fused_ws_kernel<128, 128, 8, GATED, POOL><<<grid, 768, 0, st>>>(p);
+    } else {
+        if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, 4, GATED, POOL><<<grid, 768, 0, st>>>(p);
+        else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, 4, GATED, POOL><<<grid, 768, 0, st>>>(p);
+        else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, 4, GATED, POOL><<<grid, 768, 0, st>>>(p);
+        else fused_ws_kernel<128, 128, 4, GATED, POOL><<<grid, 768, 0, st>>>(p);
+    }
     return hipGetLastError();
+}
+
+template <bool GATED, bool POOL>
+hipError_t launch_ws_layout(const Params &p, hipStream_t st) {
+    // whole 128-column value heads once there are enough (sequence, value
+    // head) pairs to give every CU a workgroup; 64-column slices otherwise
+    if (p.V == 128 && (int64_t)p.N * p.HV >= 256) return launch_ws_kv<8, GATED, POOL>(p, st);
+    return launch_ws_kv<4, GATED, POOL>(p, st);
 }
 
 }  // namespace
 
-// One workgroup of 768 threads per (sequence, value head, 64 value columns).
+// One workgroup of 768 threads per (sequence, value head) or per (sequence,
+// value head, 64 value columns).
 hipError_t launch_fused_ws(const Params &p, hipStream_t st) {
-    constexpr int VW = 64;
-    const int groups = p.N * p.H;
-    if (groups == 0) return hipSuccess;
-    const int per_group = (p.HV / p.H) * (p.V / VW);
-    const unsigned grid = (unsigned)((groups + 7) / 8) * 8 * per_group;
+    if (p.N * p.H == 0) return hipSuccess;
     const bool gated = p.gates.A_log != nullptr,
                pool = p.state_indices != nullptr || p.state_bf16 || p.v_zero || p.init_shared;
-    if (gated && pool) return launch_ws_kv<true, true>(p, grid, st);
-    if (gated) return launch_ws_kv<true, false>(p, grid, st);
-    if (pool) return launch_ws_kv<false, true>(p, grid, st);
-    return launch_ws_kv<false, false>(p, grid, st);
+    if (gated && pool) return launch_ws_layout<true, true>(p, st);
+    if (gated) return launch_ws_layout<true, false>(p, st);
+    if (pool) return launch_ws_layout<false, true>(p, st);
+    return launch_ws_layout<false, false>(p, st);
 }
 
 }  // namespace gdn
