@@ -81,9 +81,11 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // explicitly (wait_vmem, then a barrier).  Vector memory counters retire in
 // order, so the compiler's own counter waits stay correct (at worst they wait
 // longer).
-__device__ __forceinline__ void lds_copy16(const void *g, unsigned lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds) : "memory", "m0");
+// lds_copy16s: 16 bytes per lane from a wave-uniform 64-bit base address plus
+// a 32-bit per-lane byte offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void lds_copy16s(const void *base, unsigned off, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_copy4(const void *g, unsigned lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -119,10 +121,15 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// XOR swizzle of the 16-byte segments of a row of NSEG segments.
+// XOR swizzle of the 16-byte segments of a row of NSEG segments.  Rows of 16
+// segments (256 bytes, every bank once) use the row index with its two bit
+// pairs exchanged: the sixteen rows of a 16-lane row read (one segment each)
+// still hit sixteen different segments, and a transposing read of K^T (lane
+// quads reading segments 4 m + 0..3 of eight rows per half wave) spreads over
+// all sixteen instead of eight.
 template <int NSEG> __device__ __forceinline__ int swz(int row) {
-    static_assert(NSEG == 8 || NSEG % 16 == 0, "row length");
-    return NSEG >= 16 ? (row & 15) : ((row >> 1) & 7);
+    static_assert(NSEG == 8 || NSEG == 16, "row length");
+    return NSEG == 16 ? (4 * (row & 3) + ((row >> 2) & 3)) : ((row >> 1) & 7);
 }
 
 // fp32 -> bf16, round to nearest even, two values per conversion instruction
@@ -206,7 +213,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     constexpr bool MERGED = NCW == 8;       // four prep waves do both K- and Q-prep
     static_assert((NCW == 4 || NCW == 8) && V % VW == 0, "layout");
     typedef WsLds<K, VW> Lds;
-    constexpr int NSK = K / VEC, NSV = VW / VEC;
+    constexpr int NSK = K / VEC;
     constexpr int KT = K / 16, KS = K / 32;
     constexpr int KROW = 2 * K, VROW = 2 * VW;   // bytes per raw row in LDS
     static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget");
@@ -300,11 +307,11 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     // sequence clamps its rows.  Copy t of a chunk's rows moves 1 KB.
     constexpr int NCP = MERGED ? 8 : 4;          // waves sharing the copies of k (and of q)
     const int cpw = MERGED ? wave : w4;          // this wave's index among them
-    unsigned kqo[NSK / NCP];
+    unsigned kqo[NSK / NCP];   // byte offsets from the chunk's first row
 #pragma unroll
     for (int i = 0; i < NSK / NCP; ++i) {
         const int P = 64 * (cpw + NCP * i) + lane, row = P / NSK;
-        kqo[i] = (unsigned)row * (unsigned)kq_row + (((P % NSK) ^ swz<NSK>(row)) * VEC);
+        kqo[i] = ((unsigned)row * (unsigned)kq_row + (((P % NSK) ^ swz<NSK>(row)) * VEC)) * sizeof(E);
     }
     // rows of k (or q) of chunk c into the LDS chunk slot at byte address dst
     auto issue_rows = [&](const E *src, int c, unsigned dst) {
@@ -313,13 +320,13 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         const E *rc = src + (size_t)t0 * kq_row + (size_t)jk * K;
         if (last == 63) {
 #pragma unroll
-            for (int i = 0; i < NSK / NCP; ++i) lds_copy16(rc + kqo[i], dst + 1024u * (cpw + NCP * i));
+            for (int i = 0; i < NSK / NCP; ++i) lds_copy16s(rc, kqo[i], dst + 1024u * (cpw + NCP * i));
         } else {
 #pragma unroll
             for (int i = 0; i < NSK / NCP; ++i) {
                 const int t = cpw + NCP * i;
                 const int P = 64 * t + lane, row = P / NSK, seg = (P % NSK) ^ swz<NSK>(row);
-                lds_copy16(rc + (unsigned)min(row, last) * (unsigned)kq_row + seg * VEC, dst + 1024u * t);
+                lds_copy16s(rc, ((unsigned)min(row, last) * (unsigned)kq_row + seg * VEC) * sizeof(E), dst + 1024u * t);
             }
         }
     };
@@ -603,14 +610,21 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     // copy i moves rows 32 i .. 32 i + 31, lane l one 16-byte half row.
     const int c0 = 16 * wave;
     const unsigned vslot0 = lds0 + offsetof(Lds, vb) + 2048u * wave;
+    const unsigned vlo = (unsigned)(lane >> 1) * (unsigned)v_row * sizeof(E) + 16 * (lane & 1);
     auto issue_vw = [&](int c) {
         const int64_t t0 = tok0 + 64LL * c;
         const int last = min(64, len - 64 * c) - 1;
-        const E *vc = vg + (size_t)j * V + vcol0 + c0 + 8 * (lane & 1);
+        const E *vc = vg + (size_t)t0 * v_row + (size_t)j * V + vcol0 + c0;
         const unsigned dst = vslot0 + (c & 1) * (64 * VROW);
+        if (last == 63) {
+            lds_copy16s(vc, vlo, dst);
+            lds_copy16s(vc, vlo + 32u * (unsigned)v_row * sizeof(E), dst + 1024u);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            lds_copy16(vc + (size_t)(t0 + min(32 * i + (lane >> 1), last)) * v_row, dst + 1024u * i);
+            for (int i = 0; i < 2; ++i)
+                lds_copy16s(vc, (unsigned)min(32 * i + (lane >> 1), last) * (unsigned)v_row * sizeof(E) + 16 * (lane & 1),
+                            dst + 1024u * i);
+        }
     };
     // transpose read of the v tile: token row 16 ti + 4 grp + l16/4, value
     // columns c0 + 4 (l16 % 4) .. +3
