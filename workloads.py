@@ -10,8 +10,9 @@ kernel for qwen3.5" (FastDeploy PR #7024), "Usage or Command", item 5), which
 each side computes itself: the oracle in float64, the GPU path in its kernels.
 
 Draw order (one torch.Generator on the target device, seeded): q, k, v, a, b,
-A_log, dt_bias, initial_state; packed workloads first draw their sequence
-lengths from a separate CPU generator with the same seed.  (CPU and GPU
+A_log, dt_bias, initial_state, then (only when qk_common is set) the shared
+key-head directions; packed workloads first draw their sequence lengths from a
+separate CPU generator with the same seed.  (CPU and GPU
 generators produce different streams: a workload drawn on the GPU has the same
 shapes and lengths as on the CPU but other values.)  q/k/v and a/b are drawn
 in float32 and rounded to bfloat16 (round to nearest even), the type a model's
@@ -40,8 +41,11 @@ class Workload:
     use_l2norm: bool = True
     scale: Optional[float] = None          # None -> 1/sqrt(K)
     a_log_hi: float = math.log(16.0)      # A_log ~ U(0, a_log_hi)
-    b_std: float = 1.0                     # b ~ N(0, b_std)
+    b_std: float = 1.0                     # b ~ N(b_mean, b_std)
+    b_mean: float = 0.0
+    a_mean: float = 0.0                    # a ~ N(a_mean, 1)
     qk_std: float = 1.0                    # q, k ~ N(0, qk_std)
+    qk_common: float = 0.0                 # q, k += qk_common * c_h, c_h ~ N(0, qk_std) per key head
     init: str = "none"                     # "none" | "all" | "odd"
     init_std: float = 0.05
     n_seqs: int = 0                        # varlen: number of sequences
@@ -129,11 +133,11 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", io_dtype=torch.bfloat1
     def io(x):
         return x.to(torch.bfloat16).to(io_dtype)
 
-    q = io(randn(B, T, H, K, std=w.qk_std))
-    k = io(randn(B, T, H, K, std=w.qk_std))
+    q = randn(B, T, H, K, std=w.qk_std)
+    k = randn(B, T, H, K, std=w.qk_std)
     v = io(randn(B, T, HV, V))
-    a = io(randn(B, T, HV))
-    b = io(randn(B, T, HV, std=w.b_std))
+    a = io(randn(B, T, HV) + w.a_mean)
+    b = io(randn(B, T, HV, std=w.b_std) + w.b_mean)
     a_log = torch.rand(HV, generator=gen, device=dev, dtype=f32) * w.a_log_hi
     dt_bias = torch.rand(HV, generator=gen, device=dev, dtype=f32)
     if w.init == "none":
@@ -142,6 +146,12 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", io_dtype=torch.bfloat1
         s0 = randn(N, HV, K, V, std=w.init_std)
         if w.init == "odd":
             s0[0::2] = 0.0
+    if w.qk_common:
+        # keys and queries of one key head share a direction: neighbouring keys
+        # overlap, so the delta rule's erase term is large
+        c = randn(1, 1, H, K, std=w.qk_std) * w.qk_common
+        q, k = q + c, k + c
+    q, k = io(q), io(k)
     return dict(q=q, k=k, v=v, a=a, b=b, A_log=a_log, dt_bias=dt_bias, initial_state=s0,
                 cu_seqlens=cu, scale=w.eff_scale, use_l2norm=w.use_l2norm, lens=lens,
                 N=N, workload=w)
