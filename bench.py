@@ -3,13 +3,17 @@
 (``--path bwd``: its backward pass; a decode workload: the decode step).
 
 One step = one full forward pass (every kernel of the path) over one batch of
-seeded synthetic inputs already resident in HBM.  Default workload: the
-equal-length GVA prefill, B=4, T=4096, H=16 key heads, HV=32 value heads,
-K=V=128, bf16, in-kernel L2 norm, fp32 initial and final state.
+seeded synthetic inputs already resident in HBM.  Default workload (the
+headline): the wide large-batch prefill, B=16, T=16384, H=32 key heads, HV=64
+value heads, K=V=128, bf16, no L2 norm, scale 1/sqrt(128), fp32 initial and
+final state -- the largest configuration of the five, timed on its literal
+inputs (which diverge; timing does not depend on the values).  After the
+headline's timed region the other four configurations (tiny, GVA, packed
+varlen, long) are timed the same way and reported under "configs".
 
-Prints one JSON line: tokens/s, the roofline position of the dominant kernel
-(timed live with HIP events through the library's timing hook), the whole-path
-roofline, and the fp64 oracle timed on this host's cores on a bounded sample.
+Prints one JSON line: tokens/s, the roofline position of the path (timed live
+with HIP events through the library's timing hook), and the fp64 oracle timed
+on this host's cores on a bounded sample.
 """
 import argparse
 import json
@@ -96,7 +100,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gva")
+    ap.add_argument("--workload", default="wide")
+    ap.add_argument("--configs", default="tiny,gva,varlen,long",
+                    help="further forward workloads timed after the headline (comma list; empty: none)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle units for the CPU baseline (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -145,7 +151,7 @@ def cpu_baseline(x, units_wanted):
     w = x["workload"]
     N, HV = x["N"], w.HV
     ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    U = units_wanted or min(N * HV, max(4 * ncpu, 16))
+    U = units_wanted or min(N * HV, max(6 * ncpu, 16))
     units = np.unique(np.linspace(0, N * HV - 1, U).round().astype(np.int64))
     threads = int(min(ncpu, len(units)))
     cpu = lambda t: None if t is None else t.cpu()
@@ -159,7 +165,14 @@ def cpu_baseline(x, units_wanted):
     dt = time.perf_counter() - t0
     lens = x["lens"]
     unit_tokens = sum(lens[int(u) // HV] for u in units)
-    return {"value": unit_tokens / HV / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), model)
+    except OSError:
+        pass
+    return {"value": unit_tokens / HV / dt, "unit": "tokens/s", "cores": threads, "nproc": os.cpu_count(),
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{len(units)} of {N * HV} (sequence, value head) units of the same inputs "
                       f"({unit_tokens} unit-tokens, fp64 gates and token recurrence, {dt:.2f} s wall)",
             "seconds": dt}
@@ -461,11 +474,25 @@ def main():
         run_backward(args)
         return
 
+    res = run_forward(args, args.workload, args.steps, args.warmup, headline=True)
+    if args.configs and args.dtype == "bf16" and args.gating == "tensors":
+        # the other configurations, measured after the headline's timed region
+        res["configs"] = {}
+        for name in [c for c in args.configs.split(",") if c and c != args.workload]:
+            r = run_forward(args, name, max(5, args.steps // 2), max(2, args.warmup // 2), headline=False)
+            res["configs"][name] = r
+    print(json.dumps(res), flush=True)
+
+
+def run_forward(args, name, steps, warmup, headline):
+    """Times `steps` forward passes of workload `name` (after the clocks settle
+    and `warmup` untimed passes) and returns the bench record (headline) or a
+    short summary (the other configurations)."""
     import torch
     import gated_deltanet_chunked_delta_amd as gdn
     from workloads import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
+    w = WORKLOADS[name]
     dtype = torch.bfloat16 if args.dtype == "bf16" else torch.float32
     eb = 2 if args.dtype == "bf16" else 4
     dev = torch.device("cuda:0")
@@ -511,13 +538,13 @@ def main():
             step()
         settle += 10
         torch.cuda.synchronize()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     gdn.gdn_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -528,25 +555,26 @@ def main():
         copy_calibration(args.copy_calibration_mib, dev)
 
     tokens = sum(x["lens"])
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms = (t1 - t0) * 1e3 / steps
     value = tokens / (ms / 1e3)
     pb = path_bytes(w, x, eb, fused=args.gating == "fused")
     kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in prof.items() if n}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dom_us = kernels[dom]["avg_us"]
-    per_step = lambda k: kernels[k]["avg_us"] * kernels[k]["launches"] / args.steps
-    dom_step_us = per_step(dom)
-    # the fused kernel is the whole path (a split long sequence launches it twice
-    # per step): the path's algorithmic bytes over its time per step
-    ach = pb / (dom_step_us * 1e-6) / 1e9
+    per_step = lambda k: kernels[k]["avg_us"] * kernels[k]["launches"] / steps
+    path_us = sum(per_step(k) for k in kernels)
+    # the path's algorithmic bytes over the time of every kernel of a step (the
+    # fused kernel alone for most sizes; a split long sequence adds its setup,
+    # combine and correction kernels and launches the fused kernel twice)
+    ach = pb / (path_us * 1e-6) / 1e9
     khash = kernel_hash("prefill")
     traffic = (MEASURED_TRAFFIC.get(khash, {}).get(w.name)
                if args.dtype == "bf16" and args.gating == "tensors" else None)
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2),
-            "launches_per_step": round(kernels[dom]["launches"] / args.steps, 2), "kernel_hash": khash}
-    path_us = sum(per_step(k) for k in kernels)
+            "launches_per_step": round(kernels[dom]["launches"] / steps, 2), "kernel_hash": khash,
+            "scope": "path" if len(kernels) > 1 else "kernel"}
     flops = path_flops(w, x)
     path = {"algorithmic_bytes": pb, "algorithmic_flops": flops, "kernel_us": round(path_us, 2),
             "hbm_frac": round(pb / (path_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -554,8 +582,8 @@ def main():
             "roofline_tokens_per_s": round(tokens / max(pb / (HBM_PEAK_GBS * 1e9),
                                                          flops / (MFMA_PEAK_TFLOPS[args.dtype] * 1e12)))}
     res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "settle_steps": settle, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "settle_steps": settle, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} T={T} N={N} H={w.H} HV={w.HV} K={w.K} V={w.V} "
                                f"l2norm={w.use_l2norm} initial_state={w.init} gating={args.gating}",
@@ -565,12 +593,21 @@ def main():
         "kernels": {k: {kk: round(vv, 2) if isinstance(vv, float) else vv for kk, vv in v.items()}
                     for k, v in kernels.items()},
     }
+    if w.name == "wide":
+        # the literal wide inputs diverge (no L2 norm, |k|^2 ~ K): the share of
+        # finite outputs, for the record; timing does not depend on the values
+        res["finite_output_fraction"] = round(float(torch.isfinite(out).float().mean()), 6)
+    if not headline:
+        return {"tokens": tokens, "tokens_per_s": round(value, 1), "ms_per_step": round(ms, 4),
+                "steps": steps, "hbm_frac": path["hbm_frac"], "mfma_frac": path["mfma_frac"],
+                "kernel_us": path["kernel_us"], "traffic": traffic,
+                "workload": res["config"]["workload"], "kernels": res["kernels"]}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(x, args.cpu_units)
         cb.pop("seconds")
         cb["value"] = round(cb["value"], 1)
         res["cpu_baseline"] = cb
-    print(json.dumps(res), flush=True)
+    return res
 
 
 if __name__ == "__main__":
