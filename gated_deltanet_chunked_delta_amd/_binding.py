@@ -232,6 +232,20 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None, initial_state
     if initial_state is not None:
         _check(tuple(initial_state.shape) == (N, HV, K, V) and initial_state.dtype == torch.float32,
                f"initial_state must be float32 [{N},{HV},{K},{V}]")
+    # buffers the caller hands in are written in place, so they must already
+    # have the layout the kernels write
+    if out is not None:
+        _check(tuple(out.shape) == (B, T, HV, V) and out.dtype == q.dtype and out.is_contiguous()
+               and out.device == q.device, f"out must be a contiguous {q.dtype} [{B},{T},{HV},{V}] on {q.device}")
+    if final_state is not None and output_final_state:
+        _check(tuple(final_state.shape) == (N, HV, K, V) and final_state.dtype == torch.float32
+               and final_state.is_contiguous() and final_state.device == q.device,
+               f"final_state must be a contiguous float32 [{N},{HV},{K},{V}] on {q.device}")
+    if workspace is not None:
+        _check(workspace.device == q.device and workspace.is_contiguous(),
+               f"workspace must be a contiguous buffer on {q.device}")
+    if cu_seqlens is not None:
+        cu_seqlens = cu_seqlens.contiguous()
     if scale is None:
         scale = K ** -0.5
     q, k, v = (t.contiguous() for t in (q, k, v))

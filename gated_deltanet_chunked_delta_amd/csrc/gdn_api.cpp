@@ -4,6 +4,7 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -56,7 +57,7 @@ struct EventProfiler : gdn::Profiler {
         hipEvent_t a, b;
     };
     std::mutex mu;
-    bool on = false;
+    std::atomic<bool> on{false};
     std::vector<hipEvent_t> pool;
     std::vector<Rec> pending;
     hipEvent_t open[gdn::kNumKernelKinds] = {};
@@ -109,6 +110,15 @@ struct EventProfiler : gdn::Profiler {
 
 EventProfiler g_prof;
 
+// Runs launch(prof) with the timing hook while it is enabled, else with none;
+// the hook's lock is taken only while timing is on.
+template <class F>
+hipError_t with_profiler(F &&launch) {
+    if (!g_prof.on.load(std::memory_order_acquire)) return launch(nullptr);
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    return launch(g_prof.on.load(std::memory_order_relaxed) ? static_cast<gdn::Profiler *>(&g_prof) : nullptr);
+}
+
 const gdn_gates kNoGates = {nullptr, nullptr, nullptr, nullptr};
 
 // Raw gate inputs: all four pointers given, a and b 4-byte aligned.
@@ -142,6 +152,12 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
     const bool any_tokens = (int64_t)s.B * s.T > 0;
     if (any_tokens && (!q || !k || !v || !out)) return GDN_ERR_NULL;
     if (any_tokens && !gates && (!g || !beta)) return GDN_ERR_NULL;
+    // the kernels move q, k, v, out and the states in 16-byte pieces and read
+    // g, beta and cu_seqlens in 4-byte words
+    const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out |
+                          (uintptr_t)initial_state | (uintptr_t)final_state;
+    const uintptr_t a4 = (uintptr_t)g | (uintptr_t)beta | (uintptr_t)cu_seqlens;
+    if ((a16 & 15u) != 0 || (a4 & 3u) != 0) return GDN_ERR_ALIGN;
     if (any_tokens && gates) {
         const int gs = check_gates(*gates);
         if (gs != GDN_OK) return gs;
@@ -189,13 +205,10 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
         p.pool_size = pool->pool_size;
         p.state_bf16 = pool->dtype == GDN_BF16;
     }
-    hipError_t err;
-    {
-        std::lock_guard<std::mutex> lock(g_prof.mu);
-        gdn::Profiler *prof = g_prof.on ? &g_prof : nullptr;
-        err = split.active ? gdn::launch_split(p, s.dtype, split, workspace, (hipStream_t)stream, prof)
-                           : gdn::launch_forward(p, s.dtype, (hipStream_t)stream, prof);
-    }
+    const hipError_t err = with_profiler([&](gdn::Profiler *prof) {
+        return split.active ? gdn::launch_split(p, s.dtype, split, workspace, (hipStream_t)stream, prof)
+                            : gdn::launch_forward(p, s.dtype, (hipStream_t)stream, prof);
+    });
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -239,11 +252,8 @@ int recurrent_update(const void *q, const void *k, const void *v, const float *g
     p.scale = scale;
     p.use_l2norm = use_l2norm ? 1 : 0;
     p.state_bf16 = state_bf16 ? 1 : 0;
-    hipError_t err;
-    {
-        std::lock_guard<std::mutex> lock(g_prof.mu);
-        err = gdn::launch_recurrent(p, s.dtype, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
-    }
+    const hipError_t err =
+        with_profiler([&](gdn::Profiler *prof) { return gdn::launch_recurrent(p, s.dtype, (hipStream_t)stream, prof); });
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -300,11 +310,8 @@ int chunk_bwd(const void *q, const void *k, const void *v, const float *g, const
     p.N = s.N;
     p.scale = scale;
     p.use_l2norm = use_l2norm ? 1 : 0;
-    hipError_t err;
-    {
-        std::lock_guard<std::mutex> lock(g_prof.mu);
-        err = gdn::launch_backward(p, s.dtype, plan, workspace, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
-    }
+    const hipError_t err = with_profiler(
+        [&](gdn::Profiler *prof) { return gdn::launch_backward(p, s.dtype, plan, workspace, (hipStream_t)stream, prof); });
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -329,7 +336,7 @@ int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
 int gdn_profile_enable(int enable) {
     std::lock_guard<std::mutex> lock(g_prof.mu);
     g_prof.reset();
-    g_prof.on = enable != 0;
+    g_prof.on.store(enable != 0, std::memory_order_release);
     return GDN_OK;
 }
 
@@ -411,11 +418,8 @@ int gdn_gating(const gdn_gates *gates, int64_t rows, int32_t HV, int32_t dtype, 
     const int st = check_gates(*gates);
     if (st != GDN_OK) return st;
     const gdn::Gates gt{gates->A_log, gates->dt_bias, gates->a, gates->b};
-    hipError_t err;
-    {
-        std::lock_guard<std::mutex> lock(g_prof.mu);
-        err = gdn::launch_gating(gt, rows, HV, dtype, g, beta, (hipStream_t)stream, g_prof.on ? &g_prof : nullptr);
-    }
+    const hipError_t err = with_profiler(
+        [&](gdn::Profiler *prof) { return gdn::launch_gating(gt, rows, HV, dtype, g, beta, (hipStream_t)stream, prof); });
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

@@ -119,6 +119,9 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape);
  *
  * `out` must not overlap any input.  Sequences of length 0 produce no rows and
  * their final state equals their initial state (or zero).
+ * q, k, v, out, initial_state and final_state must be 16-byte aligned and g,
+ * beta and cu_seqlens 4-byte aligned (GDN_ERR_ALIGN otherwise): the kernels
+ * move the tensors in 16-byte pieces.
  * Returns GDN_OK or a negative gdn_status (see above). */
 int gdn_chunk_fwd(const void *q, const void *k, const void *v,
                   const float *g, const float *beta,

@@ -86,6 +86,24 @@ def test_null_tensor_errors():
     assert _call(s, ptrs=0) == -1
 
 
+@pytest.mark.parametrize("arg,offset", [("q", 8), ("k", 2), ("v", 4), ("out", 8), ("initial_state", 4),
+                                         ("final_state", 12), ("g", 2), ("beta", 1), ("cu_seqlens", 2)])
+def test_forward_misaligned_pointers(arg, offset):
+    """q, k, v, out and the states need 16-byte alignment, g, beta and
+    cu_seqlens 4-byte: anything less is GDN_ERR_ALIGN, found on the host."""
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    ptr = {n: FAKE for n in ("q", "k", "v", "g", "beta", "initial_state", "out", "final_state")}
+    ptr["cu_seqlens"] = None
+    ptr[arg] = FAKE + offset
+    s = gdn.make_shape(1, 64, 2, 4, 128, 128, 1, 0)
+    args = [P(ptr[n]) if ptr[n] else None for n in ("q", "k", "v", "g", "beta")]
+    st = lib.gdn_chunk_fwd(*args, 1.0, 1, P(ptr["initial_state"]),
+                           None if ptr["cu_seqlens"] is None else P(ptr["cu_seqlens"]),
+                           P(ptr["out"]), P(ptr["final_state"]), ctypes.byref(s), None, 0, None)
+    assert st == -7
+
+
 def test_status_strings():
     for st in range(-7, 1):
         assert gdn.gdn_status_str(st).startswith("GDN_")

@@ -174,6 +174,23 @@ def test_outputs_fully_written():
     assert not torch.isnan(o).any() and not torch.isnan(f).any()
 
 
+def test_wrapper_rejects_bad_caller_buffers():
+    """Caller-given out / final_state buffers are written in place: a wrong
+    shape, dtype or a non-contiguous view is refused before any launch."""
+    x = oracle.add_gates(make_inputs(SMALL["varlen_mix"], seed=5, io_dtype=torch.float32))
+    T, HV, V = x["v"].shape[1], x["v"].shape[2], x["v"].shape[3]
+    N, K = x["initial_state"].shape[0], x["initial_state"].shape[2]
+    dev = "cuda:0"
+    bad_outs = [torch.empty((1, T, HV, V), dtype=torch.float32, device=dev),          # dtype
+                torch.empty((1, T, HV, V + 1), dtype=torch.bfloat16, device=dev)[..., :V],   # strided view
+                torch.empty((1, T + 1, HV, V), dtype=torch.bfloat16, device=dev)]          # shape
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            run_gpu(x, torch.bfloat16, out=out)
+    with pytest.raises(ValueError):
+        run_gpu(x, torch.bfloat16, final_state=torch.empty((N, HV, V, K + 1), device=dev))
+
+
 def test_empty_batch():
     w = scaled(WORKLOADS["varlen"], "empty", H=2, HV=4, lengths=(0, 0, 0))
     x = oracle.add_gates(make_inputs(w, seed=6, io_dtype=torch.float32))
