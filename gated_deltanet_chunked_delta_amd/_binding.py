@@ -17,7 +17,9 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK = 0
 GDN_BF16 = 0
 GDN_F32 = 1
-EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_pool", "gdn_chunk_fwd_workspace_bytes",
+GDN_ERR_SCRATCH = -8
+GDN_STATIC_SCRATCH_BYTES = 128 << 20     # the static scratch of gdn_chunk_fwd_noalloc, per GPU
+EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_pool", "gdn_chunk_fwd_workspace_bytes",
             "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
             "gdn_gating", "gdn_gating_bwd", "gdn_gating_bwd_workspace_bytes", "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_recurrent_update_pool",
             "gdn_profile_enable", "gdn_profile_read", "gdn_status_str")
@@ -73,6 +75,9 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P, P,
                                   ctypes.POINTER(gdn_shape), P, ctypes.c_size_t, P]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P, P,
+                                          ctypes.POINTER(gdn_shape), P]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(gdn_shape)]
     lib.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_chunk_bwd.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P, P, P, P, P, P,
@@ -164,6 +169,19 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale, use_l2norm, initial_state, cu_seqlens
                                  int(bool(use_l2norm)), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
                                  _ptr(final_state), ctypes.byref(shape), _ptr(workspace),
                                  int(workspace_bytes), ctypes.c_void_p(int(stream))))
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale, use_l2norm, initial_state, cu_seqlens, out, final_state,
+                          shape: gdn_shape, stream=None) -> int:
+    """Direct call of the allocation-free forward entry point (gdn_chunk_fwd
+    without a workspace: a split uses the library's static scratch); returns
+    the status code.  ``stream`` as for gdn_chunk_fwd."""
+    lib = load_library()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    return int(lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                                         int(bool(use_l2norm)), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
+                                         _ptr(final_state), ctypes.byref(shape), ctypes.c_void_p(int(stream))))
 
 
 def _check(cond, msg):

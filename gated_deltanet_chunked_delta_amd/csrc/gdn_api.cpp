@@ -143,7 +143,8 @@ int check_pool(const gdn_state_pool &pl) {
 int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
               const gdn_gates *gates, float scale, int use_l2norm, const float *initial_state,
               const int32_t *cu_seqlens, void *out, float *final_state, const gdn_shape *shape, void *workspace,
-              size_t workspace_bytes, void *stream, const gdn_state_pool *pool = nullptr) {
+              size_t workspace_bytes, void *stream, const gdn_state_pool *pool = nullptr,
+              bool check_only = false) {
     const int st = check_shape(shape);
     if (st != GDN_OK) return st;
     const gdn_shape &s = *shape;
@@ -169,6 +170,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
         const int ps = check_pool(*pool);
         if (ps != GDN_OK) return ps;
     }
+    if (check_only) return GDN_OK;
     // The split runs only where it applies and the caller gave the workspace
     // for it (256-byte aligned); otherwise the sequences run unsplit.
     gdn::SplitPlan split;
@@ -365,6 +367,27 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                      shape, workspace, workspace_bytes, stream);
 }
 
+int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                          float scale, int use_l2norm, const float *initial_state, const int32_t *cu_seqlens,
+                          void *out, float *final_state, const gdn_shape *shape, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN_OK) return st;
+    // only the split of equal-length sequences uses scratch
+    const size_t need = cu_seqlens ? 0 : workspace_of(*shape);
+    if (need > GDN_STATIC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+    void *scratch = nullptr;
+    if (need > 0) {
+        // chunk_fwd's checks come first, so that a call it refuses never
+        // reaches the device; this second pass then runs it
+        const int pre = chunk_fwd(q, k, v, g, beta, nullptr, scale, use_l2norm, initial_state, cu_seqlens, out,
+                                  final_state, shape, nullptr, 0, stream, nullptr, /*check_only=*/true);
+        if (pre != GDN_OK) return pre;
+        if (gdn::static_scratch((hipStream_t)stream, &scratch) != hipSuccess) return GDN_ERR_LAUNCH;
+    }
+    return chunk_fwd(q, k, v, g, beta, nullptr, scale, use_l2norm, initial_state, cu_seqlens, out, final_state,
+                     shape, scratch, need > 0 ? GDN_STATIC_SCRATCH_BYTES : 0, stream);
+}
+
 int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v, const gdn_gates *gates, float scale,
                         int use_l2norm, const float *initial_state, const int32_t *cu_seqlens, void *out,
                         float *final_state, const gdn_shape *shape, void *workspace, size_t workspace_bytes,
@@ -458,6 +481,8 @@ const char *gdn_status_str(int status) {
         case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: a kernel launch failed";
         case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is not aligned as its argument requires";
+        case GDN_ERR_SCRATCH:
+            return "GDN_ERR_SCRATCH: the sizes need more than the static scratch (GDN_STATIC_SCRATCH_BYTES)";
         default: return "unknown gdn_status";
     }
 }

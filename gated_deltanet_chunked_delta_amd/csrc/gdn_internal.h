@@ -119,6 +119,10 @@ SplitPlan plan_split(int B, int T, int H, int HV, int K, int V, int elem_bytes);
 // Enqueues the split forward pass of p (cu_seqlens null) with workspace ws.
 hipError_t launch_split(const Params &p, int dtype, const SplitPlan &plan, void *ws, hipStream_t stream,
                         Profiler *prof);
+// Device address of the library's static scratch (GDN_STATIC_SCRATCH_BYTES
+// bytes) on the device of `stream` (the current device for the null stream),
+// looked up on the first call for that device.
+hipError_t static_scratch(hipStream_t stream, void **ptr);
 
 // Everything the backward pass needs (gdn_backward.hip).  Pointers are device
 // pointers; the intermediates point into the caller's workspace.

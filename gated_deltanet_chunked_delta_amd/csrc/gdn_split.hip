@@ -10,6 +10,9 @@
 // M_t is what the same recurrence computes from the identity with v = 0, and
 // its output scale M_t^T q_t turns o_t = scale S_t^T q_t into o0_t + h^T
 // (scale M_t^T q_t).
+#include <mutex>
+
+#include "gdn.h"
 #include "gdn_device.h"
 
 namespace gdn {
@@ -228,6 +231,43 @@ hipError_t launch_correct(const SplitDims &d, const void *om, const void *hs, vo
 }
 
 }  // namespace
+
+// The split's workspace for callers that cannot allocate
+// (gdn_chunk_fwd_noalloc): one copy of this array on every GPU the library
+// runs on, held until the process ends.  In host code `scratch` is a host-side
+// stand-in, never the device address: kernels and copies take the address
+// static_scratch() looked up for the device.
+static __device__ __align__(256) unsigned char scratch[GDN_STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(hipStream_t stream, void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int cur = -1, dev = -1;
+    hipError_t err = hipGetDevice(&cur);
+    if (err != hipSuccess) return err;
+    dev = cur;
+    if (stream) {   // the stream's device, which need not be the current one
+        err = hipStreamGetDevice(stream, &dev);
+        if (err != hipSuccess) return err;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // once per device, with that device current
+        if (dev != cur && (err = hipSetDevice(dev)) != hipSuccess) return err;
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess) return err;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 SplitPlan plan_split(int B, int T, int H, int HV, int K, int V, int elem_bytes) {
     (void)H;

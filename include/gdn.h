@@ -57,7 +57,8 @@ typedef enum gdn_status {
     GDN_ERR_UNSUPPORTED = -4, /* K or V not in {64, 128}, or HV not a multiple of H */
     GDN_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or too small where required (gdn_chunk_bwd) */
     GDN_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
-    GDN_ERR_ALIGN = -7        /* a pointer lacks the alignment its argument requires */
+    GDN_ERR_ALIGN = -7,       /* a pointer lacks the alignment its argument requires */
+    GDN_ERR_SCRATCH = -8      /* gdn_chunk_fwd_noalloc: the sizes need more than the static scratch */
 } gdn_status;
 
 /* Element type of q, k, v and out.  g, beta and both states are always fp32.
@@ -130,6 +131,37 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v,
                   void *out, float *final_state,
                   const gdn_shape *shape, void *workspace, size_t workspace_bytes,
                   void *stream);
+
+/* Bytes of the static device scratch that gdn_chunk_fwd_noalloc uses (one
+ * array per GPU the library runs on, held until the process ends). */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* gdn_chunk_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that keep allocation out of the step,
+ * harnesses that forbid hipMalloc.  Same arguments, checks and results as
+ * gdn_chunk_fwd given a workspace, minus the workspace: where gdn_chunk_fwd
+ * would split long sequences (gdn_chunk_fwd_workspace_bytes(shape) > 0) this
+ * call uses the library's static scratch array instead, and neither it nor any
+ * routine it calls allocates.  Sizes whose split needs more than
+ * GDN_STATIC_SCRATCH_BYTES (compare gdn_chunk_fwd_workspace_bytes) are
+ * refused with GDN_ERR_SCRATCH before anything is enqueued; call gdn_chunk_fwd
+ * with a workspace for those.  Sizes that are not split use no scratch.
+ *
+ * The first call for a device looks up that device's address of the array
+ * (hipGetSymbolAddress, with the device of `stream` made current for the
+ * lookup); later calls reuse it.  The array keeps whatever the last call left
+ * in it; every call writes each part of it before reading it, so nothing
+ * needs clearing.  All calls on one GPU share the one array: two split calls
+ * that can run at the same time on one GPU (on different streams, or on
+ * unordered streams of different host threads) race and give wrong results;
+ * enqueue them on one stream.
+ * Returns the statuses of gdn_chunk_fwd and GDN_ERR_SCRATCH. */
+int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          float scale, int use_l2norm,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          void *out, float *final_state,
+                          const gdn_shape *shape, void *stream);
 
 /* Sizes of a decode step (one token per sequence).
  *   N         : sequences in the step (rows of q/k/v/out)

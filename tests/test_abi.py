@@ -104,8 +104,27 @@ def test_forward_misaligned_pointers(arg, offset):
     assert st == -7
 
 
+def test_noalloc_refuses_on_the_host():
+    """gdn_chunk_fwd_noalloc checks like gdn_chunk_fwd, and refuses sizes whose
+    split needs more than the static scratch before anything is enqueued."""
+    lib = gdn.load_library()
+    P = ctypes.c_void_p
+    call = lambda s, ptrs=FAKE: lib.gdn_chunk_fwd_noalloc(P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), 1.0, 1,
+                                                          None, None, P(ptrs), None,
+                                                          None if s is None else ctypes.byref(s), None)
+    assert call(None) == -1
+    assert call(gdn.make_shape(1, 64, 2, 4, 96, 128, 1, 0)) == -4
+    big = gdn.make_shape(1, 131072, 16, 32, 128, 128, 1, 0)
+    assert gdn.gdn_chunk_fwd_workspace_bytes(big) > gdn.GDN_STATIC_SCRATCH_BYTES
+    assert call(big) == gdn.GDN_ERR_SCRATCH == -8
+    # the constant of the header and of the binding agree
+    hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    assert "#define GDN_STATIC_SCRATCH_BYTES ((size_t)128 << 20)" in hdr
+    assert gdn.GDN_STATIC_SCRATCH_BYTES == 128 << 20
+
+
 def test_status_strings():
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         assert gdn.gdn_status_str(st).startswith("GDN_")
     assert gdn.gdn_status_str(-99) == "unknown gdn_status"
 
