@@ -390,24 +390,32 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     //          (5, 5, 5 and 1 tiles, against 1, 3, 5 and 7 for whole rows);
     //   Q K^T: W = 0: rows 0, 1 ((0,0) (1,0) (1,1));  W = 1: row 2;
     //          W = 2: (3,0) (3,1) (3,2);  W = 3: (3,3);
-    // and the diagonal K K^T and Q Q^T tiles whose norms those need, all in
-    // one pass over the k and q fragments.
-    auto prep_chunk = [&](auto w_c, auto k_c, auto q_c, int cn) {
+    // and, with the L2 norm (NORM), the diagonal K K^T and Q Q^T tiles whose
+    // norms those need.  With DO_K the diagonal tile W comes first, so that
+    // the forward substitution for D_W (a chain of dependent steps) overlaps
+    // the other products.
+    auto prep_chunk = [&](auto w_c, auto k_c, auto q_c, auto n_c, int cn) {
         constexpr int W = decltype(w_c)::value;
         constexpr bool DO_K = decltype(k_c)::value != 0, DO_Q = decltype(q_c)::value != 0;
+        constexpr bool NORM = decltype(n_c)::value != 0;
         constexpr int NOFF = (DO_K && W != 3) ? 2 : 0;
         constexpr int OI0 = W == 0 ? 1 : W == 1 ? 2 : 3, OJ0 = W == 0 ? 0 : W == 1 ? 1 : 0;
         constexpr int OI1 = W == 0 ? 2 : 3, OJ1 = W == 0 ? 0 : W == 1 ? 1 : 2;
         constexpr int R0 = W == 0 ? 0 : W == 1 ? 2 : 3, R1 = W == 0 ? 1 : W == 1 ? 2 : 3;
         constexpr int J0 = W == 3 ? 3 : 0, J1 = W == 0 ? 1 : W == 3 ? 3 : 2;
         constexpr int NR = DO_Q ? R1 - R0 + 1 : 0;
-        constexpr int KDK = W == 0 ? 0x7 : W == 1 ? 0xE : W == 2 ? 0xD : 0x8;   // norms of the K work
-        constexpr int KDQ = ((2 << J1) - 1) & ~((1 << J0) - 1);                // norms of the Q work
+        constexpr int KDK = W == 0 ? 0x7 : W == 1 ? 0xE : W == 2 ? 0xD : 0x8;   // k tiles of the K work
+        constexpr int KDQ = ((2 << J1) - 1) & ~((1 << J0) - 1);                // k tiles of the Q work
         constexpr int KD = (DO_K ? KDK : 0) | (DO_Q ? KDQ : 0);
+        // k tiles whose fragments phase 2 loads (tile W's stay in registers from phase 1)
+        constexpr int KL = DO_K ? (KD & ~(1 << W)) : KD;
         PrepOut &po = s.po[cn & 1];
         // staging of this wave: gamma + log2 beta, gamma, log2 r, beta by token
         float(*st)[64] = DO_K ? s.stk[w4] : s.stq[w4];
         float *sgb = st[0], *sg = st[1], *sl = st[2], *sb = st[3];
+        // log2 r of token i, and of tokens i..i+3 (0 without the norm)
+        auto lr = [&](int i) { return NORM ? sl[i] : 0.f; };
+        auto lr4 = [&](int i) { return NORM ? *(const f32x4 *)&sl[i] : f32x4{0.f, 0.f, 0.f, 0.f}; };
         float gam, bt;   // this lane's token: gate cumsum (log2 units) and beta
         cumsum(cn, gam, bt);
         if constexpr (DO_K) {
@@ -418,24 +426,60 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gam), 63));   // gamma_L
         const E *kb = (const E *)((const char *)s.kb[0] + uni((cn % 3) * 64 * KROW));
         const E *qb = (const E *)((const char *)s.qb[0] + uni((cn & 1) * 64 * KROW));
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        // lane (l16, l16 / 4) holds the diagonal entry of row l16 at e = l16 % 4
+        const int ed = l16 - 4 * grp;
+        const bool on_diag = ed >= 0 && ed < 4;
+
+        // ---- phase 1 (DO_K): the diagonal tile W, A_WW, and the solve's operands
+        v8 fkW[KS];
+        f32x4 col[15];
+        if constexpr (DO_K) {
+            f32x4 gW = z4;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+                fkW[s2] = frag(kb, W, s2);
+                gW = mma(fkW[s2], fkW[s2], gW);
+            }
+            if (NORM && on_diag) sl[16 * W + l16] = -0.5f * fast_log2(gW[ed] + 1e-6f);
+            wave_lds_sync();   // the staged factors come from other lanes
+            {   // diagonal tile -> A_WW (fp32, by column).  The raw Gram tile is
+                // symmetric, so the lane's values serve as rows i = 4 grp + e (of
+                // the tile) of column j = l16: four consecutive entries.
+                const f32x4 ai = *(const f32x4 *)&sgb[16 * W + 4 * grp] + lr4(16 * W + 4 * grp);
+                const int jc = 16 * W + l16;
+                const float cj = sg[jc] - lr(jc);
+                f32x4 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = (4 * grp + e > l16) ? fast_exp2(ai[e] - cj) * gW[e] : 0.f;
+                *(f32x4 *)&s.adiag[W][16 * l16 + 4 * grp] = a;
+            }
+            wave_lds_sync();   // A_WW is read back across lanes by the solve
+        }
+
+        // ---- phase 2: the other products, with the solve in between
         f32x4 gd[4], go[2], gq[2][4], gqq[2];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            gd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            gq[0][t] = gq[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            gd[t] = z4;
+            gq[0][t] = gq[1][t] = z4;
         }
-        go[0] = go[1] = gqq[0] = gqq[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        go[0] = go[1] = gqq[0] = gqq[1] = z4;
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) {
             v8 fk[4], fq[2];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                if (KD >> t & 1) fk[t] = frag(kb, t, s2);
+            for (int t = 0; t < 4; ++t) {
+                if (KL >> t & 1) fk[t] = frag(kb, t, s2);
+                else if (DO_K && t == W) fk[t] = fkW[s2];
+            }
 #pragma unroll
             for (int r = 0; r < NR; ++r) fq[r] = frag(qb, R0 + r, s2);
+            if constexpr (NORM) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                if (KD >> t & 1) gd[t] = mma(fk[t], fk[t], gd[t]);
+                for (int t = 0; t < 4; ++t)
+                    if (KL >> t & 1) gd[t] = mma(fk[t], fk[t], gd[t]);
+            }
             if constexpr (NOFF > 0) {
                 go[0] = mma(fk[OJ0], fk[OI0], go[0]);
                 go[1] = mma(fk[OJ1], fk[OI1], go[1]);
@@ -445,45 +489,67 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
 #pragma unroll
                 for (int jt = J0; jt <= J1; ++jt)
                     if (jt <= R0 + r) gq[r][jt] = mma(fk[jt], fq[r], gq[r][jt]);
-                gqq[r] = mma(fq[r], fq[r], gqq[r]);
+                if constexpr (NORM) gqq[r] = mma(fq[r], fq[r], gqq[r]);
             }
         }
-        // log2 of the norm factors of the k rows of the diagonal tiles: lane
-        // (l16, l16 / 4) holds row l16 at e = l16 % 4
-        {
-            const int e = l16 - 4 * grp;
-            if (e >= 0 && e < 4) {
+        // D_W = (I + A_WW)^-1 by column-oriented forward substitution with
+        // every lane busy: the four lanes of quad cc hold column cc of D, lane
+        // gg of the quad rows 4 gg .. 4 gg + 3.  Once x_m is final it is
+        // broadcast inside each quad (one DPP move) and updates every row; A
+        // being strictly lower, the rows at or above m take zeros, so each
+        // step is four branch-free FMAs.
+        float x[4];
+        if constexpr (DO_K) {
+            const int cc = lane >> 2, gg = lane & 3;
+#pragma unroll
+            for (int m = 0; m < 15; ++m) col[m] = *(const f32x4 *)&s.adiag[W][16 * m + 4 * gg];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = (4 * gg + q == cc) ? 1.f : 0.f;
+            auto step = [&](auto m_c) {
+                constexpr int m = decltype(m_c)::value, sl4 = m / 4;   // x_m from lane m / 4 of the quad
+                const float xm = dpp_mov<sl4 | (sl4 << 2) | (sl4 << 4) | (sl4 << 6), 0xf>(x[m % 4]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[q] -= col[m][q] * xm;
+            };
+            step(IC<0>()); step(IC<1>()); step(IC<2>()); step(IC<3>()); step(IC<4>());
+            step(IC<5>()); step(IC<6>()); step(IC<7>()); step(IC<8>()); step(IC<9>());
+            step(IC<10>()); step(IC<11>()); step(IC<12>()); step(IC<13>()); step(IC<14>());
+            // interleave the substitution's dependent steps with the products
+            // above: one product, then four VALU instructions, in turn
+            constexpr int NQ = DO_Q ? (W == 3 ? 1 : 3) : 0;
+            constexpr int NM = KS * ((NORM ? __builtin_popcount(KL) + NR : 0) + NOFF + NQ);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+        }
+        // log2 of the norm factors of the other k rows this wave needs
+        if constexpr (NORM) {
+            if (on_diag) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    if (KD >> t & 1) sl[16 * t + l16] = p.use_l2norm ? -0.5f * fast_log2(gd[t][e] + 1e-6f) : 0.f;
+                    if (KL >> t & 1) sl[16 * t + l16] = -0.5f * fast_log2(gd[t][ed] + 1e-6f);
             }
         }
         float la[2];   // a'_i = gamma_i + log2(scale rho_i) of the lane's row in tile R0 + r
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const float qq = __shfl(gqq[r][l16 & 3], (l16 >> 2) * 16 + l16);
-            la[r] = l2_scale + (p.use_l2norm ? -0.5f * fast_log2(qq + 1e-6f) : 0.f);
-        }
-        wave_lds_sync();   // the staged factors come from other lanes
-        if constexpr (DO_K) {
-            {   // diagonal tile -> A_WW (fp32, by column).  The raw Gram tile is
-                // symmetric, so the lane's values serve as rows i = 4 grp + e (of
-                // the tile) of column j = l16: four consecutive entries.
-                const f32x4 ai = *(const f32x4 *)&sgb[16 * W + 4 * grp] + *(const f32x4 *)&sl[16 * W + 4 * grp];
-                const int jc = 16 * W + l16;
-                const float cj = sg[jc] - sl[jc];
-                f32x4 a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = (4 * grp + e > l16) ? fast_exp2(ai[e] - cj) * gd[W][e] : 0.f;
-                *(f32x4 *)&s.adiag[W][16 * l16 + 4 * grp] = a;
+            la[r] = l2_scale;
+            if constexpr (NORM) {
+                const float qq = __shfl(gqq[r][l16 & 3], (l16 >> 2) * 16 + l16);
+                la[r] += -0.5f * fast_log2(qq + 1e-6f);
             }
+        }
+        if constexpr (NORM || !DO_K) wave_lds_sync();   // the staged factors come from other lanes
+        if constexpr (DO_K) {
             // off-diagonal tiles (i, j) -> -A (bf16): row 16 i + l16, columns
             // 16 j + 4 grp + e
             auto off = [&](auto oi_c, auto oj_c, const f32x4 &g) {
                 constexpr int OI = decltype(oi_c)::value, OJ = decltype(oj_c)::value;
                 const int ik = 16 * OI + l16;
-                const float ai = sgb[ik] + sl[ik];
-                const f32x4 cj = *(const f32x4 *)&sg[16 * OJ + 4 * grp] - *(const f32x4 *)&sl[16 * OJ + 4 * grp];
+                const float ai = sgb[ik] + lr(ik);
+                const f32x4 cj = *(const f32x4 *)&sg[16 * OJ + 4 * grp] - lr4(16 * OJ + 4 * grp);
                 f32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = -(fast_exp2(ai - cj[e]) * g[e]);
@@ -496,7 +562,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
             // r e^{gamma_L - gamma} for the rows of tile W, e^{gamma_L} (W = 0)
             if (grp == 0) {
                 const int i = 16 * W + l16;
-                po.kf[i] = fast_exp2(gl - (sg[i] - sl[i]));
+                po.kf[i] = fast_exp2(gl - (sg[i] - lr(i)));
                 if (W == 0 && l16 == 0) po.decay = fast_exp2(gl);
             }
         }
@@ -509,7 +575,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
 #pragma unroll
                 for (int jt = J0; jt <= J1; ++jt) {
                     if (jt > itq) continue;
-                    const f32x4 cj = *(const f32x4 *)&sg[16 * jt + 4 * grp] - *(const f32x4 *)&sl[16 * jt + 4 * grp];
+                    const f32x4 cj = *(const f32x4 *)&sg[16 * jt + 4 * grp] - lr4(16 * jt + 4 * grp);
                     f32x4 v;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -521,46 +587,23 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
             }
         }
         if constexpr (DO_K) {
-            wave_lds_sync();   // A_WW is read back across lanes by the solve
-            // D_W = (I + A_WW)^-1 by column-oriented forward substitution
-            // with every lane busy: the four lanes of quad cc hold column cc
-            // of D, lane gg of the quad rows 4 gg .. 4 gg + 3.  Once x_m is
-            // final it is broadcast inside each quad (one DPP move) and
-            // updates every row; A being strictly lower, the rows at or
-            // above m take zeros, so each step is four branch-free FMAs.
-            const float *AT = s.adiag[W];
-            const int cc = lane >> 2, gg = lane & 3;
-            float x[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) x[q] = (4 * gg + q == cc) ? 1.f : 0.f;
-            f32x4 col[15];
-#pragma unroll
-            for (int m = 0; m < 15; ++m) col[m] = *(const f32x4 *)&AT[16 * m + 4 * gg];
-            auto step = [&](auto m_c) {
-                constexpr int m = decltype(m_c)::value, sl4 = m / 4;   // x_m from lane m / 4 of the quad
-                const float xm = dpp_mov<sl4 | (sl4 << 2) | (sl4 << 4) | (sl4 << 6), 0xf>(x[m % 4]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) x[q] -= col[m][q] * xm;
-            };
-            step(IC<0>()); step(IC<1>()); step(IC<2>()); step(IC<3>()); step(IC<4>());
-            step(IC<5>()); step(IC<6>()); step(IC<7>()); step(IC<8>()); step(IC<9>());
-            step(IC<10>()); step(IC<11>()); step(IC<12>()); step(IC<13>()); step(IC<14>());
             // column cc of D is row cc of D^T; the column scalings of the two
             // scaled forms are the factors of token 16 W + cc
+            const int cc = lane >> 2, gg = lane & 3;
             const int tc = 16 * W + cc;
-            const float bc = sb[tc], bgr = fast_exp2(sgb[tc] + sl[tc]);
+            const float bc = sb[tc], bgr = fast_exp2(sgb[tc] + lr(tc));
             const f32x4 xv = {x[0], x[1], x[2], x[3]};
             *(v4 *)&po.dt[0][W][cc][4 * gg] = cvt4(xv);
             *(v4 *)&po.dt[1][W][cc][4 * gg] = cvt4(xv * bc);
             *(v4 *)&po.dt[2][W][cc][4 * gg] = cvt4(xv * -bgr);
         }
     };
-    auto prep_tile = [&](auto k_c, auto q_c, int cn) {
+    auto prep_tile = [&](auto k_c, auto q_c, auto n_c, int cn) {
         switch (w4) {
-            case 0: prep_chunk(IC<0>(), k_c, q_c, cn); break;
-            case 1: prep_chunk(IC<1>(), k_c, q_c, cn); break;
-            case 2: prep_chunk(IC<2>(), k_c, q_c, cn); break;
-            default: prep_chunk(IC<3>(), k_c, q_c, cn); break;
+            case 0: prep_chunk(IC<0>(), k_c, q_c, n_c, cn); break;
+            case 1: prep_chunk(IC<1>(), k_c, q_c, n_c, cn); break;
+            case 2: prep_chunk(IC<2>(), k_c, q_c, n_c, cn); break;
+            default: prep_chunk(IC<3>(), k_c, q_c, n_c, cn); break;
         }
     };
 
@@ -568,7 +611,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     // preparation of chunk c+1.  The chain and the prep waves run
     // separate loops with the same number of barriers, so that neither
     // carries the other's registers.
-    auto prep_loop = [&](auto do_k_c, auto do_q_c) {
+    auto prep_loop = [&](auto do_k_c, auto do_q_c, auto n_c) {
         constexpr bool DO_K = decltype(do_k_c)::value != 0, DO_Q = decltype(do_q_c)::value != 0;
         for (int c = -1; c < nchunks; ++c) {
             const int cn = c + 1;
@@ -581,15 +624,20 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                 if (gated && c + 2 < nchunks) gate_chunk(c + 2);   // its raw words landed before the last barrier
                 if (c + 3 < nchunks) issue_gates(c + 3);
             }
-            if (cn < nchunks) prep_tile(do_k_c, do_q_c, cn);
+            if (cn < nchunks) prep_tile(do_k_c, do_q_c, n_c, cn);
             wait_vmem();   // this wave's copies
             lds_barrier();
         }
     };
     if (role != 0) {
-        if constexpr (MERGED) prep_loop(IC<1>(), IC<1>());
-        else if (role == 1) prep_loop(IC<1>(), IC<0>());
-        else prep_loop(IC<0>(), IC<1>());
+        // the prep code is compiled with and without the L2 norm
+        auto roles = [&](auto n_c) {
+            if constexpr (MERGED) prep_loop(IC<1>(), IC<1>(), n_c);
+            else if (role == 1) prep_loop(IC<1>(), IC<0>(), n_c);
+            else prep_loop(IC<0>(), IC<1>(), n_c);
+        };
+        if (p.use_l2norm) roles(IC<1>());
+        else roles(IC<0>());
         return;
     }
 

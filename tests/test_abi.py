@@ -55,7 +55,7 @@ def test_workspace_size_and_bad_shapes():
     b1, b2 = gdn.gdn_chunk_fwd_workspace_bytes(s1), gdn.gdn_chunk_fwd_workspace_bytes(s2)
     assert 0 <= b1 <= b2
     assert b1 == b2 == 0                      # 256 workgroups: not split
-    # one long sequence (64 workgroups): split, workspace for 4 segments incl. the
+    # one long sequence (64 workgroups): split, workspace for 8 segments incl. the
     # transfer outputs [T, HV, K] of the dtype
     b3 = gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 131072, 16, 32, 128, 128, 1, gdn.GDN_BF16))
     b4 = gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 131072, 16, 32, 128, 128, 1, gdn.GDN_F32))

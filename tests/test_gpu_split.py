@@ -40,10 +40,11 @@ CASES = {
     "ragged_k64": scaled(WORKLOADS["gva"], "split_ragged", B=2, T=2100, H=1, HV=2, K=64, V=128, init="none"),
     "k128_v64": scaled(WORKLOADS["gva"], "split_v64", B=1, T=3000, H=2, HV=4, K=128, V=64),
     "slow_decay": scaled(WORKLOADS["long"], "split_long", T=4096, H=1, HV=2),
-    # 64 workgroups unsplit -> 4 segments of 1152 tokens (the last 1044): the
-    # correction of each segment spans two workgroups of 1024 tokens, the
-    # second one partly filled, one of its waves ragged and two idle
-    "multi_block": scaled(WORKLOADS["gva"], "split_multi_block", B=1, T=4500, H=16, HV=32),
+    # 64 workgroups unsplit -> 8 segments of 1152 tokens (the last 936), run
+    # as whole 128-column value heads: the correction of each segment spans
+    # two workgroups of 1024 tokens, the second one partly filled, one of its
+    # waves ragged and the others idle
+    "multi_block": scaled(WORKLOADS["gva"], "split_multi_block", B=1, T=9000, H=16, HV=32),
 }
 
 
