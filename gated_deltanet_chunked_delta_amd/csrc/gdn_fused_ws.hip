@@ -122,14 +122,22 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // XOR swizzle of the 16-byte segments of a row of NSEG segments.  Rows of 16
-// segments (256 bytes, every bank once) use the row index with its two bit
-// pairs exchanged: the sixteen rows of a 16-lane row read (one segment each)
-// still hit sixteen different segments, and a transposing read of K^T (lane
-// quads reading segments 4 m + 0..3 of eight rows per half wave) spreads over
-// all sixteen instead of eight.
+// segments (256 bytes) are swizzled in row pairs: rows 2x and 2x+1 take
+// segments 2 h(x) and 2 h(x) + 1 (XOR the segment index), so the two lanes of
+// each pair of a 16-byte fragment read (rows 16 t + l16) read the two halves
+// of one 32-byte block, the form of a 16-byte-per-lane read that runs without
+// bank conflicts on gfx950 (measured: the previous bit-pair exchange took
+// twice the LDS cycles); and h(x) = 2 ((x & 3) ^ (x >> 2)) + (x >> 2) keeps
+// the transposing reads of K^T (lane quads reading segments 4 m + 0..3 of
+// eight rows per half wave) spread over all sixteen segments.
 template <int NSEG> __device__ __forceinline__ int swz(int row) {
     static_assert(NSEG == 8 || NSEG == 16, "row length");
-    return NSEG == 16 ? (4 * (row & 3) + ((row >> 2) & 3)) : ((row >> 1) & 7);
+    if constexpr (NSEG == 16) {
+        const int x = (row >> 1) & 7, h = 2 * ((x & 3) ^ (x >> 2)) + (x >> 2);
+        return 2 * h + (row & 1);
+    } else {
+        return (row >> 1) & 7;
+    }
 }
 
 // fp32 -> bf16, round to nearest even, two values per conversion instruction
@@ -152,21 +160,30 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 // Per-chunk results of the prep waves that the chain waves read.
 struct alignas(16) PrepOut {
-    bf16 alo[6][16][16];      // -A in the six 16x16 blocks below the diagonal; block (i, m) at i (i - 1) / 2 + m
-    bf16 plo[32][40];         // P rows 0-31 (columns 0-31), columns in the key-slot order (see pcol)
-    bf16 phi[32][72];         // P rows 32-63; blocks (0,1) and (2,3) are zero
+    // -A in the six 16x16 blocks below the diagonal, block (i, m) at
+    // i (i - 1) / 2 + m; element (r, 4 g + e) of a block at [g][r][e], so that
+    // the 8-byte operand reads (lane: row l16, columns 4 grp ..) are linear
+    bf16 alo[6][4][16][4];
+    bf16 pp[3072];            // P by row pairs (see pel), columns in the key-slot order (see pcol)
     bf16 dt[3][4][16][16];    // transposed D_b, D_b diag(beta), -D_b diag(beta e^gamma r)
     float osc[64];            // output scale of (Q h)^T: scale rho e^gamma
     float kf[64];             // r e^{gamma_L - gamma}
     float decay;              // e^{gamma_L}
 };
 __device__ __forceinline__ constexpr int alo_blk(int i, int m) { return i * (i - 1) / 2 + m; }
-// Element (i, col) of P (rows below 32 only have the first 32 columns).
+// Element (i, col) of P.  Rows go in pairs: the 16-byte column units j of
+// rows 2p and 2p+1 sit side by side, so that the two lanes of a pair read one
+// 32-byte block; rows 0-31 keep the first four units (32 columns), rows 32-63
+// all eight (blocks (0,1) and (2,3) are zero); the unit index is XOR-swizzled
+// by the pair index so that the eight pairs of a 16-lane read hit different
+// banks.
 template <typename PO> __device__ __forceinline__ auto pel(PO &po, int i, int col) {
-    return i < 32 ? &po.plo[i][col] : &po.phi[i - 32][col];
+    const int p = i >> 1, j = col >> 3;
+    const int e = i < 32 ? p * 64 + 16 * (j ^ ((p >> 1) & 3)) : 1024 + (p - 16) * 128 + 16 * (j ^ (p & 7));
+    return &po.pp[e + 8 * (i & 1) + (col & 7)];
 }
 
-// Column of token j in PrepOut::p.  The output product reads P as the B
+// Column of token j in P (PrepOut::pp).  The output product reads P as the B
 // operand of a 16x16x32 product whose lane-group g holds tokens
 // 32 s + 4 g + e and 32 s + 16 + 4 g + e (e = 0..3); storing those eight
 // columns next to each other makes each operand one 16-byte read.
@@ -553,7 +570,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                 f32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = -(fast_exp2(ai - cj[e]) * g[e]);
-                *(v4 *)&po.alo[alo_blk(OI, OJ)][l16][4 * grp] = cvt4(v);
+                *(v4 *)&po.alo[alo_blk(OI, OJ)][grp][l16][0] = cvt4(v);
             };
             if constexpr (NOFF > 0) {
                 off(IC<OI0>(), IC<OJ0>(), go[0]);
@@ -719,14 +736,20 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     for (int c = -1; c < nchunks; ++c) {
         const int cn = c + 1;
         // copies: v of chunk c+1 (this wave's columns), with NCW = 8 also k and
-        // q rows of chunk c+2; all landed before the step's barrier
-        if (cn < nchunks) issue_vw(cn);
-        if constexpr (MERGED) {
-            if (c + 2 < nchunks) {
-                issue_k(c + 2);
-                issue_q(c + 2);
+        // q rows of chunk c+2, into ring slots nothing reads in this step; all
+        // landed before the step's barrier.  They are issued after the block
+        // substitution: issued at the start of the step, the copies of all
+        // chain waves queue up at once and hold back the first products.
+        auto issue_copies = [&]() {
+            if (cn < nchunks) issue_vw(cn);
+            if constexpr (MERGED) {
+                if (c + 2 < nchunks) {
+                    issue_k(c + 2);
+                    issue_q(c + 2);
+                }
             }
-        }
+        };
+        if (c < 0) issue_copies();
         if (c >= 0) {
             const PrepOut &po = *(const PrepOut *)((const char *)s.po + uni((c & 1) * (int)sizeof(PrepOut)));
             const char *kb = (const char *)s.kb[0] + uni((c % 3) * 64 * KROW);
@@ -757,8 +780,9 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                 vb16[m] = cvt4(acc[m]);
 #pragma unroll
                 for (int bi = m + 1; bi < 4; ++bi)
-                    y[bi] = mma_k16(*(const v4 *)&po.alo[alo_blk(bi, m)][l16][4 * grp], vb16[m], y[bi]);
+                    y[bi] = mma_k16(*(const v4 *)&po.alo[alo_blk(bi, m)][grp][l16][0], vb16[m], y[bi]);
             }
+            issue_copies();
             // V_new for the output product, diag(kf) V_new for the state
             v8 vnb[2], vkb[2];
 #pragma unroll
