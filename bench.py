@@ -33,9 +33,11 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # changes the hash, and the bench then reports traffic as null until it is
 # measured again.
 MEASURED_TRAFFIC = {
-    # fused_ws_kernel: GVA prefill FETCH 151,985.5 KiB x 2.000 + WRITE 139,776.2 KiB x 1.000;
-    # varlen FETCH 630,803.6 x 2 + WRITE 638,149.8 KiB; wide FETCH 5,272,324.0 x 2 + WRITE 4,264,010.8 KiB
-    "364fcc8c8560cb90": {"gva": 454397120, "varlen": 1945351168, "wide": 15164066611},
+    # fused_ws_kernel (profiles/fused_ws_kernel_*_hbm_traffic.md, split_long_hbm_traffic.md):
+    # wide FETCH 6,246,534.0 KiB x 2.000 + WRITE 4,259,922.9 KiB x 1.000; GVA 151,888.6 x 2 + 139,272.5;
+    # varlen 630,935.6 x 2 + 630,172.6; long: the mean of its two fused launches per step
+    # (1,479,981.8 x 2 + 1,065,012.9 and 939,866.4 x 2 + 1,064,989.2)
+    "4184d8f5f59f25d0": {"wide": 17154745521, "gva": 453668391, "varlen": 1937379328, "long": 3568393800},
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,374.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB
     "1e133469e85525fe": {"decode": 1049900032, "decode_bf16pool": 529568973},
@@ -50,6 +52,13 @@ MEASURED_TRAFFIC = {
                          "wide:bwd_prep_kernel": 26682810163, "wide:bwd_fwd_scan_kernel": 49727091302,
                          "wide:bwd_dh_scan_kernel": 66841029018, "wide:bwd_grads_kernel": 111218403635,
                          "wide:bwd_reduce_kernel": 21474870272},
+}
+# Counter-based utilisation of the prefill kernel (profiles/fused_ws_kernel_wide_gva_sq_counters.md),
+# keyed like MEASURED_TRAFFIC: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles, LDS busy and
+# LDS bank-conflict stalls from SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT over cycles.
+MEASURED_COUNTERS = {
+    "4184d8f5f59f25d0": {"wide": {"mfma_busy": 0.405, "lds_busy": 0.629, "lds_bank_conflict": 0.111},
+                         "gva": {"mfma_busy": 0.314, "lds_busy": 0.483, "lds_bank_conflict": 0.075}},
 }
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
@@ -574,7 +583,9 @@ def run_forward(args, name, steps, warmup, headline):
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": pb, "avg_launch_us": round(dom_us, 2),
             "launches_per_step": round(kernels[dom]["launches"] / steps, 2), "kernel_hash": khash,
-            "scope": "path" if len(kernels) > 1 else "kernel"}
+            "scope": "path" if len(kernels) > 1 else "kernel",
+            "counters": (MEASURED_COUNTERS.get(khash, {}).get(w.name)
+                         if args.dtype == "bf16" and args.gating == "tensors" else None)}
     flops = path_flops(w, x)
     path = {"algorithmic_bytes": pb, "algorithmic_flops": flops, "kernel_us": round(path_us, 2),
             "hbm_frac": round(pb / (path_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
