@@ -90,6 +90,13 @@ SMALL = {
     # take 32-column tiles, 5 x 16 the 64-column ones (the cases above, 16-column)
     "mid_width_tiles": scaled(WORKLOADS["gva"], "mid_width_tiles", B=3, T=200, H=8, HV=16),
     "wide_tiles": scaled(WORKLOADS["gva"], "wide_tiles", B=5, T=130, H=8, HV=16),
+    # the same tile widths with K = 64 (the K = 64 variants of both scans): (sequence,
+    # value head, 64-column) units 96 and 160 with V = 128, 80 and 160 with V = 64
+    "mid_width_tiles_k64": scaled(WORKLOADS["gva"], "mid_width_tiles_k64", B=3, T=200, H=8, HV=16, K=64),
+    "wide_tiles_k64": scaled(WORKLOADS["gva"], "wide_tiles_k64", B=5, T=130, H=8, HV=16, K=64),
+    "mid_width_tiles_k64_v64": scaled(WORKLOADS["gva"], "mid_width_tiles_k64_v64", B=5, T=150, H=8, HV=16,
+                                      K=64, V=64),
+    "wide_tiles_k64_v64": scaled(WORKLOADS["gva"], "wide_tiles_k64_v64", B=10, T=100, H=8, HV=16, K=64, V=64),
 }
 
 
