@@ -18,7 +18,7 @@ GDN_OK = 0
 GDN_BF16 = 0
 GDN_F32 = 1
 GDN_ERR_SCRATCH = -8
-GDN_STATIC_SCRATCH_BYTES = 128 << 20     # the static scratch of gdn_chunk_fwd_noalloc, per GPU
+GDN_STATIC_SCRATCH_BYTES = 64 << 20      # the static scratch of gdn_chunk_fwd_noalloc, per GPU
 EXPORTED = ("gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_pool", "gdn_chunk_fwd_workspace_bytes",
             "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
             "gdn_gating", "gdn_gating_bwd", "gdn_gating_bwd_workspace_bytes", "gdn_recurrent_update", "gdn_recurrent_update_gated", "gdn_recurrent_update_pool",

@@ -510,7 +510,7 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
                 f32x4 o = zq[ti] * s.oq[i];
 #pragma unroll
                 for (int s2 = 0; s2 <= ti / 2; ++s2) o = mma(vnb[s2], ld4x2<E>(&s.p[i][32 * s2 + 4 * grp]), o);
-                if (i < L) {
+                if (i < L && og) {   // no output: the sequence split's state passes
                     v4 ov;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) ov[e] = to_e<E>(o[e]);
@@ -594,7 +594,7 @@ const char *kernel_name(int kind) {
         case kGatingKernel: return "gating_kernel";
         case kSplitSetupKernel: return "split_setup_kernel";
         case kSplitCombineKernel: return "split_combine_kernel";
-        case kSplitCorrectKernel: return "split_correct_kernel";
+        case kSplitFinalKernel: return "split_final_kernel";
         case kBwdSetupKernel: return "bwd_setup_kernel";
         case kBwdPrepKernel: return "bwd_prep_kernel";
         case kBwdFwdScanKernel: return "bwd_fwd_scan_kernel";

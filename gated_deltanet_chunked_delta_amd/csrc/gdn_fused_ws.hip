@@ -220,7 +220,7 @@ __device__ __forceinline__ constexpr int kappa(int mt, int r) {
 // POOL: the states live in a slot-indexed pool and/or are stored as bf16
 // (p.state_indices, p.state_bf16).  Template parameters, so that the plain
 // kernel carries none of their code.
-template <int K, int V, int NCW, bool GATED, bool POOL>
+template <int K, int V, int NCW, bool GATED, bool POOL, bool OUT>
 __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     typedef bf16 E;
     typedef bf16x8 v8;
@@ -266,6 +266,11 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         len = p.T;
     }
     const int nchunks = (len + 63) / 64;
+    // OUT = false (with POOL only): no output.  The sequence split's state and
+    // transfer-map passes need only the final states, so the q rows, the P
+    // tiles, (Q h)^T and the output product are skipped.
+    static_assert(OUT || POOL, "the no-output variant is a pool variant");
+    constexpr bool want_o = OUT;
 
     // Raw gate inputs, when given: the head's constants, and which half of its
     // aligned 4-byte word a bf16 input occupies (HV is even, so the half is
@@ -375,7 +380,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     const bool gate_wave = role == (MERGED ? 3 : 2) && w4 == 3;
     if (nchunks > 0) {
         if (role == (MERGED ? 0 : 1)) issue_k(0);
-        if (role == (MERGED ? 0 : 2)) issue_q(0);
+        if (role == (MERGED ? 0 : 2) && want_o) issue_q(0);
         if (gate_wave) {
             issue_gb(0);
             issue_gates(0);
@@ -634,14 +639,14 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
             const int cn = c + 1;
             if constexpr (!MERGED) {
                 if (DO_K && c + 2 < nchunks) issue_k(c + 2);
-                if (DO_Q && c + 2 < nchunks) issue_q(c + 2);
+                if (DO_Q && want_o && c + 2 < nchunks) issue_q(c + 2);
             }
             if (gate_wave) {
                 if (c + 2 < nchunks) issue_gb(c + 2);
                 if (gated && c + 2 < nchunks) gate_chunk(c + 2);   // its raw words landed before the last barrier
                 if (c + 3 < nchunks) issue_gates(c + 3);
             }
-            if (cn < nchunks) prep_tile(do_k_c, do_q_c, n_c, cn);
+            if (cn < nchunks && (DO_K || want_o)) prep_tile(do_k_c, do_q_c, n_c, cn);
             wait_vmem();   // this wave's copies
             lds_barrier();
         }
@@ -649,9 +654,14 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     if (role != 0) {
         // the prep code is compiled with and without the L2 norm
         auto roles = [&](auto n_c) {
-            if constexpr (MERGED) prep_loop(IC<1>(), IC<1>(), n_c);
-            else if (role == 1) prep_loop(IC<1>(), IC<0>(), n_c);
-            else prep_loop(IC<0>(), IC<1>(), n_c);
+            if constexpr (MERGED) {
+                if constexpr (!want_o) prep_loop(IC<1>(), IC<0>(), n_c);   // no P tiles
+                else prep_loop(IC<1>(), IC<1>(), n_c);
+            } else if (role == 1) {
+                prep_loop(IC<1>(), IC<0>(), n_c);
+            } else {
+                prep_loop(IC<0>(), IC<1>(), n_c);
+            }
         };
         if (p.use_l2norm) roles(IC<1>());
         else roles(IC<0>());
@@ -733,6 +743,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     }
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+    constexpr bool WO = want_o;
     for (int c = -1; c < nchunks; ++c) {
         const int cn = c + 1;
         // copies: v of chunk c+1 (this wave's columns), with NCW = 8 also k and
@@ -745,7 +756,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
             if constexpr (MERGED) {
                 if (c + 2 < nchunks) {
                     issue_k(c + 2);
-                    issue_q(c + 2);
+                    if (want_o) issue_q(c + 2);
                 }
             }
         };
@@ -797,12 +808,14 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
             // (K^T by transpose loads).  The two are independent, so they sit in
             // one branch-free block and the scheduler interleaves them.
             f32x4 o[4];
+            if constexpr (WO) {
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                const int i = 16 * ti + l16;
-                o[ti] = zq[ti] * po.osc[i];
+                for (int ti = 0; ti < 4; ++ti) {
+                    const int i = 16 * ti + l16;
+                    o[ti] = zq[ti] * po.osc[i];
 #pragma unroll
-                for (int s2 = 0; s2 <= ti / 2; ++s2) o[ti] = mma(vnb[s2], *(const v8 *)pel(po, i, pcol(2 * s2, grp)), o[ti]);
+                    for (int s2 = 0; s2 <= ti / 2; ++s2) o[ti] = mma(vnb[s2], *(const v8 *)pel(po, i, pcol(2 * s2, grp)), o[ti]);
+                }
             }
             const float dec = po.decay;
 #pragma unroll
@@ -820,16 +833,18 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                     h[mt] = acc2;
                 }
             }
-            E *dst = og + ((size_t)t0 * p.HV + j) * V + vcol0 + c0 + 4 * grp;
-            const size_t orow = (size_t)p.HV * V;
-            if (L == 64) {
+            if constexpr (WO) {
+                E *dst = og + ((size_t)t0 * p.HV + j) * V + vcol0 + c0 + 4 * grp;
+                const size_t orow = (size_t)p.HV * V;
+                if (L == 64) {
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti)
-                    *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = cvt4(o[ti]);
-            } else {
+                    for (int ti = 0; ti < 4; ++ti)
+                        *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = cvt4(o[ti]);
+                } else {
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti)
-                    if (16 * ti + l16 < L) *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = cvt4(o[ti]);
+                    for (int ti = 0; ti < 4; ++ti)
+                        if (16 * ti + l16 < L) *(v4 *)__builtin_assume_aligned(dst + (16 * ti + l16) * orow, 8) = cvt4(o[ti]);
+                }
             }
         }
         if (cn < nchunks) {
@@ -847,7 +862,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     zk[t] = mma(frag(kb, t, s2), hb, zk[t]);
-                    zq[t] = mma(hb, frag(qb, t, s2), zq[t]);
+                    if constexpr (WO) zq[t] = mma(hb, frag(qb, t, s2), zq[t]);
                 }
             }
         }
@@ -870,28 +885,28 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     }
 }
 
-template <int NCW, bool GATED, bool POOL>
+template <int NCW, bool GATED, bool POOL, bool OUT>
 hipError_t launch_ws_kv(const Params &p, hipStream_t st) {
     const int per_group = (p.HV / p.H) * (p.V / (16 * NCW));
     const unsigned grid = (unsigned)((p.N * p.H + 7) / 8) * 8 * per_group;
     if constexpr (NCW == 8) {
-        if (p.K == 64) fused_ws_kernel<64, 128, 8, GATED, POOL><<<grid, 768, 0, st>>>(p);
-        else fused_ws_kernel<128, 128, 8, GATED, POOL><<<grid, 768, 0, st>>>(p);
+        if (p.K == 64) fused_ws_kernel<64, 128, 8, GATED, POOL, OUT><<<grid, 768, 0, st>>>(p);
+        else fused_ws_kernel<128, 128, 8, GATED, POOL, OUT><<<grid, 768, 0, st>>>(p);
     } else {
-        if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, 4, GATED, POOL><<<grid, 768, 0, st>>>(p);
-        else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, 4, GATED, POOL><<<grid, 768, 0, st>>>(p);
-        else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, 4, GATED, POOL><<<grid, 768, 0, st>>>(p);
-        else fused_ws_kernel<128, 128, 4, GATED, POOL><<<grid, 768, 0, st>>>(p);
+        if (p.K == 64 && p.V == 64) fused_ws_kernel<64, 64, 4, GATED, POOL, OUT><<<grid, 768, 0, st>>>(p);
+        else if (p.K == 64 && p.V == 128) fused_ws_kernel<64, 128, 4, GATED, POOL, OUT><<<grid, 768, 0, st>>>(p);
+        else if (p.K == 128 && p.V == 64) fused_ws_kernel<128, 64, 4, GATED, POOL, OUT><<<grid, 768, 0, st>>>(p);
+        else fused_ws_kernel<128, 128, 4, GATED, POOL, OUT><<<grid, 768, 0, st>>>(p);
     }
     return hipGetLastError();
 }
 
-template <bool GATED, bool POOL>
+template <bool GATED, bool POOL, bool OUT = true>
 hipError_t launch_ws_layout(const Params &p, hipStream_t st) {
     // whole 128-column value heads once there are enough (sequence, value
     // head) pairs to give every CU a workgroup; 64-column slices otherwise
-    if (p.V == 128 && (int64_t)p.N * p.HV >= 256) return launch_ws_kv<8, GATED, POOL>(p, st);
-    return launch_ws_kv<4, GATED, POOL>(p, st);
+    if (p.V == 128 && (int64_t)p.N * p.HV >= 256) return launch_ws_kv<8, GATED, POOL, OUT>(p, st);
+    return launch_ws_kv<4, GATED, POOL, OUT>(p, st);
 }
 
 }  // namespace
@@ -902,6 +917,10 @@ hipError_t launch_fused_ws(const Params &p, hipStream_t st) {
     if (p.N * p.H == 0) return hipSuccess;
     const bool gated = p.gates.A_log != nullptr,
                pool = p.state_indices != nullptr || p.state_bf16 || p.v_zero || p.init_shared;
+    if (pool && !p.out) {   // the sequence split's state and transfer-map passes
+        if (gated) return launch_ws_layout<true, true, false>(p, st);
+        return launch_ws_layout<false, true, false>(p, st);
+    }
     if (gated && pool) return launch_ws_layout<true, true>(p, st);
     if (gated) return launch_ws_layout<true, false>(p, st);
     if (pool) return launch_ws_layout<false, true>(p, st);

@@ -55,11 +55,11 @@ struct Params {
 // fused_ws_kernel: warp-specialized prefill kernel (bf16);
 // recurrent_update_kernel: the decode step;
 // gating_kernel: the stand-alone gate computation.
-// split_setup_kernel, split_combine_kernel, split_correct_kernel: the
+// split_setup_kernel, split_combine_kernel, split_final_kernel: the
 // sequence split of long sequences (gdn_split.hip).
 // bwd_*_kernel: the backward pass (gdn_backward.hip).
 enum KernelKind { kFusedKernel = 0, kFusedWsKernel = 1, kRecurrentKernel = 2, kGatingKernel = 3,
-                  kSplitSetupKernel = 4, kSplitCombineKernel = 5, kSplitCorrectKernel = 6,
+                  kSplitSetupKernel = 4, kSplitCombineKernel = 5, kSplitFinalKernel = 6,
                   kBwdSetupKernel = 7, kBwdPrepKernel = 8, kBwdFwdScanKernel = 9, kBwdDhScanKernel = 10,
                   kBwdGradsKernel = 11, kBwdReduceKernel = 12, kNumKernelKinds = 13 };
 const char *kernel_name(int kind);
@@ -100,18 +100,20 @@ hipError_t launch_gating(const Gates &gt, int64_t rows, int HV, int dtype, float
 // Sequence split (gdn_split.hip).  A batch of few, long, equal-length
 // sequences gives too few workgroups to fill the GPU; each sequence is then
 // cut into S segments of L tokens that run side by side.  The state is affine
-// in a segment's initial state h_a: S_t = S0_t + M_t h_a, with S0_t the state
-// from a zero start and M_t the segment's K x K transfer map so far.  So
-//   1. every segment runs from zero (segment 0 from the true initial state)
-//      -> outputs o0, final states h0;
-//   2. every segment runs again with v = 0 from the identity (K state
-//      columns) -> final maps M and outputs oM_t = scale M_t^T q_t;
-//   3. h_{s+1} = M_s h_s + h0_s in segment order (h_1 = h0_0);
-//   4. o_t += h_s^T oM_t for the tokens of segments s >= 1.
+// in a segment's initial state h_s: its end state is F_s + M_s h_s, with F_s
+// the end state from a zero start and M_s the segment's K x K transfer map.  So
+//   1. every segment runs without outputs from zero (segment 0 from the true
+//      initial state) -> end states F;
+//   2. every segment runs without outputs with v = 0 from the identity (K
+//      state columns) -> transfer maps M;
+//   3. h_1 = F_0, h_{s+1} = M_s h_s + F_s in segment order;
+//   4. every segment runs from h_s with outputs (the outputs and end states
+//      of the unsplit pass, up to rounding); the last segments' end states
+//      are the final states.
 struct SplitPlan {
     bool active = false;
     int S = 1, L = 0;                 // segments per sequence, tokens per segment (multiple of 64)
-    size_t off_cu = 0, off_idx = 0, off_pool = 0, off_map = 0, off_hs = 0, off_om = 0, off_id = 0,
+    size_t off_cu = 0, off_idx = 0, off_pool = 0, off_map = 0, off_fin = 0, off_id = 0,
            off_zero = 0, bytes = 0;   // workspace carve-up (256-byte aligned)
 };
 // The split for these sizes (equal-length sequences only); bytes = 0 when none.

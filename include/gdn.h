@@ -86,14 +86,16 @@ typedef struct gdn_shape {
  *
  * The split: a batch of few equal-length sequences (B * HV * V/64 <= 64
  * workgroups, T >= 2048) is too narrow to fill the GPU, so each sequence is
- * cut into 2-8 segments that run side by side.  The state is affine in a
- * segment's initial state (the recurrence below is linear in S), so every
- * segment runs from zero and, a second time, from the identity with v = 0
- * (its transfer map); the segment states are then chained in order and each
- * segment's outputs corrected by one product.  Results equal the unsplit pass
- * up to rounding.  The workspace holds the maps and the transfer outputs
- * (about B * T * HV * K elements of dtype plus 3 * B * 8 * HV * K * max(K, V)
- * floats: ~1 GiB for one 131072-token sequence with HV = 32, K = V = 128). */
+ * cut into 2-8 segments that run side by side.  The recurrence below is linear
+ * in S, so a segment's end state is F + M h for a segment started from h, with
+ * F its end state from zero and M its K x K transfer map (what the same
+ * recurrence computes from the identity with v = 0).  Every segment runs
+ * twice without outputs (from zero, and for its map), the segments' starting
+ * states follow in order, and every segment runs once more from its starting
+ * state, writing the outputs and end states.  Results equal the unsplit pass
+ * up to rounding.  The workspace holds the segments' starting states, end
+ * states and maps, 4 * B * S * HV * K * (2 V + K) bytes plus small tables:
+ * 48 MiB for one sequence of any length with HV = 32, K = V = 128 (S = 8). */
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape);
 
 /* Chunked gated delta rule forward pass (prefill).
@@ -134,7 +136,7 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v,
 
 /* Bytes of the static device scratch that gdn_chunk_fwd_noalloc uses (one
  * array per GPU the library runs on, held until the process ends). */
-#define GDN_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* gdn_chunk_fwd for callers that cannot allocate device memory: code under HIP
  * graph capture, serving loops that keep allocation out of the step,
@@ -142,10 +144,11 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v,
  * gdn_chunk_fwd given a workspace, minus the workspace: where gdn_chunk_fwd
  * would split long sequences (gdn_chunk_fwd_workspace_bytes(shape) > 0) this
  * call uses the library's static scratch array instead, and neither it nor any
- * routine it calls allocates.  Sizes whose split needs more than
- * GDN_STATIC_SCRATCH_BYTES (compare gdn_chunk_fwd_workspace_bytes) are
- * refused with GDN_ERR_SCRATCH before anything is enqueued; call gdn_chunk_fwd
- * with a workspace for those.  Sizes that are not split use no scratch.
+ * routine it calls allocates.  Every split the library plans fits in
+ * GDN_STATIC_SCRATCH_BYTES (at most about 50 MiB: the workspace grows with
+ * the heads and segments, not with T); a split that did not would be refused
+ * with GDN_ERR_SCRATCH before anything is enqueued.  Sizes that are not split
+ * use no scratch.
  *
  * The first call for a device looks up that device's address of the array
  * (hipGetSymbolAddress, with the device of `stream` made current for the

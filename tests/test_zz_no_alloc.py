@@ -3,8 +3,7 @@ gdn_chunk_fwd given a workspace, both through the C ABI.
 
 Two split calls in a row, the second on smaller sizes (so it runs over what
 the first left in the static scratch), then a packed batch that needs no
-scratch, then sizes beyond the scratch, which are refused before anything is
-enqueued.  Both entry points run the same deterministic kernels, so their
+scratch and one long sequence at the largest scratch use.  Both entry points run the same deterministic kernels, so their
 results must be bitwise equal; each result is also held to the bf16 bars of
 the split parity tests against the fp64 oracle (2e-2 on o, 1e-2 on the final
 state).
@@ -94,7 +93,7 @@ def test_noalloc_matches_workspace_entry_point_twice():
         _check_oracle(x, o2, f2, label)
 
 
-def test_noalloc_without_split_and_too_large():
+def test_noalloc_without_split_and_long():
     gdn = _gdn()
     # a packed batch: no split, no scratch
     w = scaled(WORKLOADS["varlen"], "noalloc_packed", H=2, HV=4, lengths=(1, 300, 0, 65))
@@ -104,15 +103,14 @@ def test_noalloc_without_split_and_too_large():
     assert need == 0
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
     _check_oracle(x, o2, f2, "packed")
-    # one sequence whose split needs more than the scratch: refused, nothing written
-    B, T, H, HV, K, V = 1, 65536, 1, 32, 128, 128
-    shape = gdn.make_shape(B, T, H, HV, K, V, B, gdn.GDN_BF16)
-    assert gdn.gdn_chunk_fwd_workspace_bytes(shape) > gdn.GDN_STATIC_SCRATCH_BYTES
-    q = torch.zeros((B, T, H, K), dtype=torch.bfloat16, device=DEV)
-    v = torch.zeros((B, T, HV, V), dtype=torch.bfloat16, device=DEV)
-    g = torch.zeros((B, T, HV), device=DEV)
-    out = torch.full((B, T, HV, V), float("nan"), dtype=torch.bfloat16, device=DEV)
-    st = gdn.gdn_chunk_fwd_noalloc(q, q, v, g, g, 1.0, True, None, None, out, None, shape)
-    torch.cuda.synchronize()
-    assert st == gdn.GDN_ERR_SCRATCH
-    assert torch.isnan(out).all()
+    # one long sequence at the long workload's head count (8 segments of 2048,
+    # the static scratch's largest use), against the workspace entry point
+    w = scaled(WORKLOADS["long"], "noalloc_long", T=16384)
+    x = make_inputs(w, seed=44, device="cuda:0")
+    g, beta = gdn.fused_gdn_gating(x["A_log"], x["a"], x["b"], x["dt_bias"])
+    x["g"], x["beta"] = g, beta
+    _say("[noalloc] one sequence of 16384 tokens, 32 value heads")
+    need, (o1, f1), (o2, f2) = _both(x)
+    assert 0 < need <= gdn.GDN_STATIC_SCRATCH_BYTES
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    assert torch.isfinite(o2).all() and torch.isfinite(f2).all()
