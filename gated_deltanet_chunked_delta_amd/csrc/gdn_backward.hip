@@ -70,6 +70,17 @@ constexpr int kThreads = 256;
 constexpr int kVT = 32;          // value columns per tile of the gradients kernel
 constexpr int kPadC = kChunk + 1;
 
+// Tm, A / beta and Pm are zero above their diagonal 16 x 16 blocks, so the
+// workspace keeps only the ten blocks on and below the diagonal: block
+// (bi, bj), bj <= bi, at bi (bi + 1) / 2 + bj, row-major inside the block
+// (10 of the 16 blocks of a full 64 x 64 tile).
+constexpr int kTriFloats = 10 * 16 * 16;
+__device__ __forceinline__ bool tri_in(int r, int c) { return (c >> 4) <= (r >> 4); }
+__device__ __forceinline__ int tri_off(int r, int c) {
+    const int bi = r >> 4, bj = c >> 4;
+    return (bi * (bi + 1) / 2 + bj) * 256 + (r & 15) * 16 + (c & 15);
+}
+
 // LDS sizes in floats.
 // grads: the value tiles (2 K x 33 + 4 x 64 x 33) come first and the two
 // 64 x 65 matrices of the second phase reuse their space.
@@ -275,9 +286,14 @@ template <int NTH>
 struct Mat64RegN {
     static constexpr int N4 = kChunk * kChunk / 4 / NTH;
     f32x4 v[N4];
+    // from the lower block-triangular storage (tri_off); the blocks above the
+    // diagonal are zero
     __device__ __forceinline__ void load(const float *src) {
 #pragma unroll
-        for (int u = 0; u < N4; ++u) v[u] = *(const f32x4 *)(src + 4 * (threadIdx.x + NTH * u));
+        for (int u = 0; u < N4; ++u) {
+            const int i = threadIdx.x + NTH * u, r = i >> 4, c = (i & 15) * 4;
+            v[u] = tri_in(r, c) ? *(const f32x4 *)(src + tri_off(r, c)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     __device__ __forceinline__ void commit(float *dst) const {
 #pragma unroll
@@ -508,8 +524,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
                    [&](int r, int m) { return to_f(qr[r * KS + m]); },
                    [&](int c, int m) { return to_f(kr[c * KS + m]); });
     }
-    float *ag_out = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
-    float *pm_out = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+    float *ag_out = p.ag + ((int64_t)cid * HV + j) * kTriFloats;
+    float *pm_out = p.pm + ((int64_t)cid * HV + j) * kTriFloats;
     lds_barrier();   // A overwrites qh
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -520,8 +536,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
             const float ag = c < r ? d * fk[r] * kk[t][e] : 0.f;
             A[r * kPadC + c] = bet[r] * ag;
             Tm[r * kChunk + c] = 0.f;
-            ag_out[r * kChunk + c] = ag;
-            pm_out[r * kChunk + c] = d * fq[r] * qk[t][e];
+            if (tri_in(r, c)) {   // t <= w: the tile is on or below the diagonal
+                ag_out[tri_off(r, c)] = ag;
+                pm_out[tri_off(r, c)] = d * fq[r] * qk[t][e];
+            }
         }
     lds_barrier();
 
@@ -550,11 +568,11 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     tm_block_row<1>(A, Tm, ysc + w * 16 * 17, w);
     tm_block_row<2>(A, Tm, ysc + w * 16 * 17, w);
     tm_block_row<3>(A, Tm, ysc + w * 16 * 17, w);
-    float *tm_out = p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk;
+    float *tm_out = p.tm + ((int64_t)cid * HV + j) * kTriFloats;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int i = 4 * (threadIdx.x + kThreads * u);
-        *(f32x4 *)(tm_out + i) = f32x4{Tm[i], Tm[i + 1], Tm[i + 2], Tm[i + 3]};
+        const int i = 4 * (threadIdx.x + kThreads * u), r = i >> 6, c = i & 63;
+        if (tri_in(r, c)) *(f32x4 *)(tm_out + tri_off(r, c)) = f32x4{Tm[i], Tm[i + 1], Tm[i + 2], Tm[i + 3]};
     }
 }
 
@@ -610,7 +628,7 @@ __global__ __launch_bounds__(NTH) void bwd_fwd_scan_kernel(BwdParams p) {
     auto fetch = [&](int ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
         rk.load((const E *)p.k, t0, L, p.H, jk);
-        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kTriFloats);
         rv.load((const E *)p.v, t0, L, HV, j, V, c0);
         if (threadIdx.x < kChunk) {
             const int r = threadIdx.x;
@@ -769,7 +787,7 @@ __global__ __launch_bounds__(512) void bwd_fwd_scan_b16_kernel(BwdParams p) {
     auto fetch = [&](int ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
         rk.load((const E *)p.k, t0, L, p.H, jk);
-        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kTriFloats);
         rv.load((const E *)p.v, t0, L, HV, j, V, c0);
         if (threadIdx.x < kChunk) {
             const int r = threadIdx.x;
@@ -947,8 +965,8 @@ __global__ __launch_bounds__(NTH) void bwd_dh_scan_kernel(BwdParams p) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
         rk.load((const E *)p.k, t0, L, p.H, jk);
         rq.load((const E *)p.q, t0, L, p.H, jk);
-        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
-        rp.load(p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kTriFloats);
+        rp.load(p.pm + ((int64_t)cid * HV + j) * kTriFloats);
         ro.load((const E *)p.dout, t0, L, HV, j, V, c0);
         if (threadIdx.x < kChunk) {
             const int r = threadIdx.x;
@@ -1100,7 +1118,7 @@ __global__ __launch_bounds__(512) void bwd_fwd_scan_sk_kernel(BwdParams p) {
     auto fetch = [&](int ci) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
         rk.load((const E *)p.k, t0, L, p.H, jk);
-        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kTriFloats);
         if (lo) rv.load((const E *)p.v, t0, L, HV, j, V, c0);
         if (threadIdx.x < kChunk) {
             const int r = threadIdx.x;
@@ -1246,8 +1264,8 @@ __global__ __launch_bounds__(512) void bwd_dh_scan_sk_kernel(BwdParams p) {
         const int cid = cid0 + ci, t0 = bos + ci * kChunk, L = min(kChunk, len - ci * kChunk);
         rk.load((const E *)p.k, t0, L, p.H, jk);
         rq.load((const E *)p.q, t0, L, p.H, jk);
-        rt.load(p.tm + ((int64_t)cid * HV + j) * kChunk * kChunk);
-        rp.load(p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk);
+        rt.load(p.tm + ((int64_t)cid * HV + j) * kTriFloats);
+        rp.load(p.pm + ((int64_t)cid * HV + j) * kTriFloats);
         if (lo) ro.load((const E *)p.dout, t0, L, HV, j, V, c0);
         if (threadIdx.x < kChunk) {
             const int r = threadIdx.x;
@@ -1626,8 +1644,8 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
 
     // the 64 x 64 matrices dSqk and Ad; Z = dSqk * (qh . kh) + dA * A only
     // through its row and column sums, reduced here in registers
-    const float *pm = p.pm + ((int64_t)cid * HV + j) * kChunk * kChunk;
-    const float *ag = p.ag + ((int64_t)cid * HV + j) * kChunk * kChunk;
+    const float *pm = p.pm + ((int64_t)cid * HV + j) * kTriFloats;
+    const float *ag = p.ag + ((int64_t)cid * HV + j) * kTriFloats;
     float dbA[4] = {0.f, 0.f, 0.f, 0.f}, zr[4] = {0.f, 0.f, 0.f, 0.f}, zc[2] = {0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -1638,9 +1656,14 @@ __global__ __launch_bounds__(kGThreads) void bwd_grads_kernel(BwdParams p) {
             const float d = low ? __expf(gam[r] - gam[c]) : 0.f;
             const float dpm = scale * aP[t][e];
             const float dsq = d * dpm;                   // dSqk
-            const float z1 = dpm * pm[r * kChunk + c];   // dPm * Pm
+            // zero above the diagonal blocks; the reads stay unconditional (a
+            // block above the diagonal reads element 0 and discards it)
+            const bool tin = tri_in(r, c);
+            const int to = tin ? tri_off(r, c) : 0;
+            const float pmv = pm[to], agr = ag[to];
+            const float z1 = tin ? dpm * pmv : 0.f;      // dPm * Pm
             const float dA = c < r && r < L ? -aA[t][e] : 0.f;
-            const float agv = ag[r * kChunk + c];
+            const float agv = tin ? agr : 0.f;
             const float adv = dA * bet[r] * d;
             if constexpr (kB16) {
                 const float x4[4] = {dsq * fk[c], dsq * fq[r], adv * fk[c], adv * fk[r]};
@@ -1914,9 +1937,9 @@ BwdPlan plan_backward(int B, int T, int H, int HV, int K, int V, int N, bool var
     };
     pl.off_co = take(sizeof(int32_t) * (size_t)(N + 1));
     pl.off_gam = take(sizeof(float) * (size_t)t_tot * HV);
-    pl.off_tm = take(sizeof(float) * nc * HV * kChunk * kChunk);
-    pl.off_ag = take(sizeof(float) * nc * HV * kChunk * kChunk);
-    pl.off_pm = take(sizeof(float) * nc * HV * kChunk * kChunk);
+    pl.off_tm = take(sizeof(float) * nc * HV * kTriFloats);
+    pl.off_ag = take(sizeof(float) * nc * HV * kTriFloats);
+    pl.off_pm = take(sizeof(float) * nc * HV * kTriFloats);
     pl.off_hs = take(sizeof(float) * nc * HV * K * V);
     pl.off_dhs = take(sizeof(float) * nc * HV * K * V);
     pl.off_vn = take(sizeof(float) * (size_t)t_tot * HV * V);

@@ -357,8 +357,9 @@ int gdn_recurrent_update_pool(const void *q, const void *k, const void *v,
 /* Bytes of device workspace gdn_chunk_bwd needs for `shape` (0 for invalid
  * shapes).  The backward pass keeps, per 64-token chunk and value head, the
  * chunk-start state and its gradient (2 K V floats) and three 64 x 64 fp32
- * matrices, and per token and value head 2 V + 2 K + 1 floats:
- * about 2.4 GiB at B = 4, T = 4096, HV = 32, K = V = 128.  Chunk slots are
+ * matrices that are zero above their diagonal 16 x 16 blocks (stored as the
+ * ten blocks on and below it), and per token and value head 2 V + 2 K + 1
+ * floats: about 2.24 GiB at B = 4, T = 4096, HV = 32, K = V = 128.  Chunk slots are
  * counted for packed sequences (ceil(T/64) + N) when B == 1, else B ceil(T/64). */
 size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape *shape);
 

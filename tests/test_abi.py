@@ -335,18 +335,20 @@ def _bcall(shape, ws=FAKE, ws_bytes=1 << 40, cu=None, ptrs=FAKE, dout=FAKE):
 
 
 def test_backward_workspace_size():
-    # equal-length: per chunk and value head 2 K V + 3 * 64 * 64 floats, per
+    # equal-length: per chunk and value head 2 K V floats and three 64 x 64
+    # matrices kept as their ten 16 x 16 blocks on and below the diagonal, per
     # token and value head 2 V + 2 K + 1 floats, N + 1 chunk offsets; each
     # region rounded up to 256 bytes
+    tri = 10 * 16 * 16
     B, T, H, HV, K, V = 4, 4096, 16, 32, 128, 128
     got = gdn.gdn_chunk_bwd_workspace_bytes(gdn.make_shape(B, T, H, HV, K, V, B, gdn.GDN_BF16))
     chunks = B * T // 64
-    want = 256 + 4 * (chunks * HV * (2 * K * V + 3 * 64 * 64) + B * T * HV * (2 * V + 2 * K + 1))
+    want = 256 + 4 * (chunks * HV * (2 * K * V + 3 * tri) + B * T * HV * (2 * V + 2 * K + 1))
     assert want <= got <= want + 11 * 256
     # B == 1: slots for packed sequences, ceil(T/64) + N chunks
     g1 = gdn.gdn_chunk_bwd_workspace_bytes(gdn.make_shape(1, 1000, 2, 4, 64, 64, 7, gdn.GDN_F32))
     slots = (1000 + 63) // 64 + 7
-    want1 = 4 * (slots * 4 * (2 * 64 * 64 + 3 * 64 * 64) + 1000 * 4 * (2 * 64 + 2 * 64 + 1))
+    want1 = 4 * (slots * 4 * (2 * 64 * 64 + 3 * tri) + 1000 * 4 * (2 * 64 + 2 * 64 + 1))
     assert want1 <= g1 <= want1 + 12 * 256
     assert gdn.gdn_chunk_bwd_workspace_bytes(gdn.make_shape(1, 64, 2, 4, 96, 64, 1, 0)) == 0   # K unsupported
 
