@@ -114,3 +114,57 @@ def test_noalloc_without_split_and_long():
     assert 0 < need <= gdn.GDN_STATIC_SCRATCH_BYTES
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
     assert torch.isfinite(o2).all() and torch.isfinite(f2).all()
+
+
+def test_noalloc_graph_capture():
+    """The call the entry point exists for: captured into a HIP graph (no
+    allocation, no memory fill inside), replayed three times, with another
+    split call of other sizes overwriting the static scratch between the
+    replays; every replay equals the eager call bit for bit."""
+    gdn = _gdn()
+    w = CALLS[0][1]
+    x = oracle.add_gates(make_inputs(w, seed=45, io_dtype=torch.float32))
+    q, k, v, g, beta, s0, cu = _device_inputs(x)
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    shape = gdn.make_shape(B, T, H, HV, K, V, B, gdn.GDN_BF16)
+    assert gdn.gdn_chunk_fwd_workspace_bytes(shape) > 0
+    out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=DEV)
+    fin = torch.empty((B, HV, K, V), device=DEV)
+
+    def call():
+        st = gdn.gdn_chunk_fwd_noalloc(q, k, v, g, beta, x["scale"], x["use_l2norm"], s0, cu, out, fin, shape)
+        assert st == 0, gdn.gdn_status_str(st)
+
+    call()
+    torch.cuda.synchronize()
+    ref_o, ref_f = out.clone(), fin.clone()
+    # the other split call that overwrites the scratch between replays
+    x2 = oracle.add_gates(make_inputs(CALLS[1][1], seed=46, io_dtype=torch.float32))
+    q2, k2, v2, g2, b2, s02, _ = _device_inputs(x2)
+    B2, T2, H2, K2 = q2.shape
+    HV2, V2 = v2.shape[2], v2.shape[3]
+    shape2 = gdn.make_shape(B2, T2, H2, HV2, K2, V2, B2, gdn.GDN_BF16)
+    out2 = torch.empty((B2, T2, HV2, V2), dtype=torch.bfloat16, device=DEV)
+    fin2 = torch.empty((B2, HV2, K2, V2), device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up off the default stream before capture
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(7)
+        fin.fill_(7)
+        st = gdn.gdn_chunk_fwd_noalloc(q2, k2, v2, g2, b2, x2["scale"], x2["use_l2norm"], s02, None, out2, fin2,
+                                       shape2)
+        assert st == 0
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(fin, ref_f), f"replay {i} differs from the eager call"
+    _say("[noalloc] graph: 3 replays equal to the eager call")
