@@ -575,7 +575,7 @@ def run_forward(args, name, steps, warmup, headline):
     path_us = sum(per_step(k) for k in kernels)
     # the path's algorithmic bytes over the time of every kernel of a step (the
     # fused kernel alone for most sizes; a split long sequence adds its setup,
-    # combine and correction kernels and launches the fused kernel twice)
+    # combine and final-copy kernels and launches the fused kernel three times)
     ach = pb / (path_us * 1e-6) / 1e9
     khash = kernel_hash("prefill")
     traffic = (MEASURED_TRAFFIC.get(khash, {}).get(w.name)
