@@ -25,8 +25,9 @@
 //            chain (two per SIMD, so that each hides the other's latencies),
 //            8-11 prep waves doing both the K- and the Q-prep of their row
 //            tile, once for all 128 columns.
-// The prep waves also issue the asynchronous copies of the raw rows: k, q and
-// the gates two chunks ahead, v one chunk ahead.  The SIMDs interleave the
+// The prep waves also issue the asynchronous copies of the raw k and q rows
+// and of the gates two chunks ahead; each chain wave copies its own v columns
+// one chunk ahead.  The SIMDs interleave the
 // serial state chain of chunk c with the preparation of chunk c+1.  Each step
 // ends with the only workgroup barrier of the step; every prep wave computes
 // the cumsum and norm values it needs itself, so the prep waves never wait for
@@ -321,17 +322,20 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
 
     // ---- asynchronous copies ------------------------------------------------
     // Raw k and q rows are copied by the four K-prep and the four Q-prep waves
-    // (NCW = 4), or by the eight chain waves (NCW = 8, where the chain waves
-    // have time to spare and the prep waves do not); the gates by the prep
-    // wave with w4 = 3; each chain wave copies its own v columns.  LDS
+    // (NCW = 4), or by the prep wave with w4 = 3 alone (NCW = 8: its row tile
+    // carries the least preparation work, and copies issued by the chain waves
+    // stall them while the memory pipeline accepts a burst of eight waves'
+    // copies); the gates by the prep wave with w4 = 3; each chain wave copies
+    // its own v columns.  LDS
     // destinations are byte addresses (wave-uniform); the per-lane source
     // offsets inside a full chunk are fixed, only the last chunk of a
     // sequence clamps its rows.  Copy t of a chunk's rows moves 1 KB.
-    constexpr int NCP = MERGED ? 8 : 4;          // waves sharing the copies of k (and of q)
-    const int cpw = MERGED ? wave : w4;          // this wave's index among them
-    unsigned kqo[NSK / NCP];   // byte offsets from the chunk's first row
+    constexpr int NCP = MERGED ? 1 : 4;          // waves sharing the copies of k (and of q)
+    const int cpw = MERGED ? 0 : w4;             // this wave's index among them
+    constexpr int NKQO = MERGED ? 1 : NSK / NCP;
+    unsigned kqo[NKQO];   // byte offsets from the chunk's first row (NCP = 4)
 #pragma unroll
-    for (int i = 0; i < NSK / NCP; ++i) {
+    for (int i = 0; i < NKQO; ++i) {
         const int P = 64 * (cpw + NCP * i) + lane, row = P / NSK;
         kqo[i] = ((unsigned)row * (unsigned)kq_row + (((P % NSK) ^ swz<NSK>(row)) * VEC)) * sizeof(E);
     }
@@ -340,7 +344,15 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
         const int64_t t0 = tok0 + 64LL * c;
         const int last = min(64, len - 64 * c) - 1;
         const E *rc = src + (size_t)t0 * kq_row + (size_t)jk * K;
-        if (last == 63) {
+        if constexpr (NCP == 1) {
+            // one wave copies all rows; its offsets are formed per copy instead
+            // of being held in registers across the loop
+#pragma unroll
+            for (int t = 0; t < NSK; ++t) {
+                const int P = 64 * t + lane, row = P / NSK, seg = (P % NSK) ^ swz<NSK>(row);
+                lds_copy16s(rc, ((unsigned)min(row, last) * (unsigned)kq_row + seg * VEC) * sizeof(E), dst + 1024u * t);
+            }
+        } else if (last == 63) {
 #pragma unroll
             for (int i = 0; i < NSK / NCP; ++i) lds_copy16s(rc, kqo[i], dst + 1024u * (cpw + NCP * i));
         } else {
@@ -379,8 +391,8 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     // the prep wave that copies (and, with raw inputs, computes) the gates
     const bool gate_wave = role == (MERGED ? 3 : 2) && w4 == 3;
     if (nchunks > 0) {
-        if (role == (MERGED ? 0 : 1)) issue_k(0);
-        if (role == (MERGED ? 0 : 2) && want_o) issue_q(0);
+        if (MERGED ? gate_wave : role == 1) issue_k(0);
+        if ((MERGED ? gate_wave : role == 2) && want_o) issue_q(0);
         if (gate_wave) {
             issue_gb(0);
             issue_gates(0);
@@ -645,6 +657,12 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                 if (c + 2 < nchunks) issue_gb(c + 2);
                 if (gated && c + 2 < nchunks) gate_chunk(c + 2);   // its raw words landed before the last barrier
                 if (c + 3 < nchunks) issue_gates(c + 3);
+                if constexpr (MERGED) {
+                    if (c + 2 < nchunks) {
+                        issue_k(c + 2);
+                        if (want_o) issue_q(c + 2);
+                    }
+                }
             }
             if (cn < nchunks && (DO_K || want_o)) prep_tile(do_k_c, do_q_c, n_c, cn);
             wait_vmem();   // this wave's copies
@@ -746,19 +764,12 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     constexpr bool WO = want_o;
     for (int c = -1; c < nchunks; ++c) {
         const int cn = c + 1;
-        // copies: v of chunk c+1 (this wave's columns), with NCW = 8 also k and
-        // q rows of chunk c+2, into ring slots nothing reads in this step; all
-        // landed before the step's barrier.  They are issued after the block
-        // substitution: issued at the start of the step, the copies of all
-        // chain waves queue up at once and hold back the first products.
+        // copy of v of chunk c+1 (this wave's columns) into the slot nothing
+        // reads in this step; landed before the step's barrier.  Issued after
+        // the block substitution: issued at the start of the step, the copies
+        // of all chain waves queue up at once and hold back the first products.
         auto issue_copies = [&]() {
             if (cn < nchunks) issue_vw(cn);
-            if constexpr (MERGED) {
-                if (c + 2 < nchunks) {
-                    issue_k(c + 2);
-                    if (want_o) issue_q(c + 2);
-                }
-            }
         };
         if (c < 0) issue_copies();
         if (c >= 0) {
