@@ -34,10 +34,10 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # measured again.
 MEASURED_TRAFFIC = {
     # fused_ws_kernel (profiles/fused_ws_kernel_*_hbm_traffic.md, split_long_hbm_traffic.md):
-    # wide FETCH 6,247,950.9 KiB x 2.000 + WRITE 4,259,934.0 KiB x 1.000; GVA 151,831.2 x 2 + 139,269.7;
-    # varlen 631,323.7 x 2 + 630,174.0; long: the mean of its three fused launches per step
-    # (926,844.7 x 2 + 16,384.0, 556,350.6 x 2 + 16,384.0 and 1,479,523.0 x 2 + 1,065,039.7)
-    "5d269cda4c044a80": {"wide": 17157658665, "gva": 453547716, "varlen": 1938171256, "long": 2397195973},
+    # wide FETCH 4,935,301.2 KiB x 2.000 + WRITE 4,259,883.3 KiB x 1.000; GVA 151,905.9 x 2 + 139,269.7;
+    # varlen 627,222.2 x 2 + 630,167.3; long: the mean of its three fused launches per step
+    # (925,847.2 x 2 + 16,384.0, 394,411.5 x 2 + 16,384.0 and 1,237,193.6 x 2 + 1,064,967.3)
+    "0e4c255e7a701abe": {"wide": 14469366857, "gva": 453703779, "varlen": 1929767765, "long": 2120521795},
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,374.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB (counted under 1e133469e85525fe;
     # the headers changed since in declarations the decode kernel does not use, and its gfx950
@@ -58,8 +58,8 @@ MEASURED_TRAFFIC = {
 # keyed like MEASURED_TRAFFIC: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles, LDS busy and
 # LDS bank-conflict stalls from SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT over cycles.
 MEASURED_COUNTERS = {
-    "5d269cda4c044a80": {"wide": {"mfma_busy": 0.400, "lds_busy": 0.622, "lds_bank_conflict": 0.110},
-                         "gva": {"mfma_busy": 0.315, "lds_busy": 0.484, "lds_bank_conflict": 0.075}},
+    "0e4c255e7a701abe": {"wide": {"mfma_busy": 0.435, "lds_busy": 0.655, "lds_bank_conflict": 0.120},
+                         "gva": {"mfma_busy": 0.315, "lds_busy": 0.485, "lds_bank_conflict": 0.075}},
 }
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
