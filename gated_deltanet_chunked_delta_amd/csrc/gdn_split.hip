@@ -41,16 +41,20 @@ __global__ void __launch_bounds__(256) split_setup_kernel(SplitDims d, const flo
         cu[i] = i == nseg ? d.B * d.T : b * d.T + min(s * d.L, d.T);
         if (i < nseg) idx[i] = (int32_t)i;
     }
-    const int64_t st = (int64_t)d.HV * d.K * d.V;
-    for (int64_t i = tid; i < nseg * st; i += nth) {
-        const int64_t slot = i / st, r = i % st;
-        const int64_t b = slot / d.S, s = slot % d.S;
-        pool[i] = (s == 0 && init) ? init[b * st + r] : 0.f;
+    // 16 bytes per store (HV K V and K K are multiples of 4)
+    const int64_t st4 = (int64_t)d.HV * d.K * d.V / 4;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = tid; i < nseg * st4; i += nth) {
+        const int64_t slot = i / st4, r = i - slot * st4;
+        const int64_t b = slot / d.S, s = slot - b * d.S;
+        ((f32x4 *)pool)[i] = (s == 0 && init) ? ((const f32x4 *)init)[b * st4 + r] : z4;
     }
-    const int64_t kk = (int64_t)d.K * d.K;
-    for (int64_t i = tid; i < (int64_t)d.HV * kk; i += nth) {
-        const int64_t r = i % kk;
-        ident[i] = (r / d.K == r % d.K) ? 1.f : 0.f;
+    const int kk4 = d.K * d.K / 4;
+    for (int64_t i = tid; i < (int64_t)d.HV * kk4; i += nth) {
+        const int r = (int)(i % kk4), row = r / (d.K / 4), c0 = 4 * (r - row * (d.K / 4));
+        f32x4 v = z4;
+        if (row >= c0 && row < c0 + 4) v[row - c0] = 1.f;
+        ((f32x4 *)ident)[i] = v;
     }
     for (int64_t i = tid; i < (int64_t)d.HV * d.K; i += nth) zrow[i] = to_e<E>(0.f);
 }
@@ -58,72 +62,93 @@ __global__ void __launch_bounds__(256) split_setup_kernel(SplitDims d, const flo
 // The segments' starting states: h_0 is the caller's state (already in slot
 // (b, 0) of the start pool), h_1 = F_0 (segment 0 ran from h_0), and
 // h_{s+1} = M_s h_s + F_s in segment order; h_s (s >= 1) is written into slot
-// (b, s) of the start pool.  One workgroup per (sequence, value head, 32
-// state columns): M_s and the workgroup's columns of h_s in LDS, each thread
-// a 4 x 4 block of the product, fp32 throughout.
+// (b, s) of the start pool.  One workgroup of four waves per (sequence, value
+// head, 32 state columns), fp32 throughout: wave w computes rows
+// 16 RT w .. 16 RT (w + 1) - 1 of h_{s+1} (both 16-column tiles) with fp32
+// matrix-core products (16x16x4); its rows of M_s go from global memory
+// straight into registers, a step ahead, and F_s's tiles start the sums; h_s
+// sits in LDS transposed (a column's K entries contiguous, padded by four so
+// that the sixteen columns of a read fall in different banks), double-buffered
+// so that each step needs one barrier.
 constexpr int kCombineCols = 32;
-
+template <int K>
 __global__ void __launch_bounds__(256) split_combine_kernel(SplitDims d, const float *__restrict__ fin,
                                                             const float *__restrict__ maps,
                                                             float *__restrict__ starts) {
-    constexpr int CW = kCombineCols, CP = CW + 4, MP = 128 + 4;   // padded rows of h and M
-    __shared__ __attribute__((aligned(16))) float h[128 * CP], m[128 * MP];
-    const int K = d.K, V = d.V, ncb = V / CW;
+    constexpr int CW = kCombineCols, RT = K / 64, KB = K / 32, HP = K + 4;
+    __shared__ __attribute__((aligned(16))) float ht[2][CW * HP];
+    const int V = d.V, ncb = V / CW;
     const int cb = blockIdx.x % ncb, bj = blockIdx.x / ncb;
     const int b = bj / d.HV, j = bj % d.HV, col0 = cb * CW;
-    const int t = threadIdx.x, nb = (K / 4) * (CW / 4);
-    const int r0 = 4 * (t / (CW / 4)), c0 = 4 * (t % (CW / 4));
-    const float *f0 = fin + ((int64_t)b * d.S * d.HV + j) * K * V;
-    for (int i = t; i < K * CW; i += blockDim.x) h[(i / CW) * CP + i % CW] = f0[(i / CW) * V + col0 + i % CW];
-    // M_s moves in 16-byte pieces, M_{s+1} loading into registers during step s
-    constexpr int NM = 128 * 128 / 4 / 256;
-    const int nm4 = K * K / 4;
-    f32x4 mr[NM];
-    auto fetch_m = [&](int s) {
-        const f32x4 *ms = (const f32x4 *)(maps + (((int64_t)b * d.S + s) * d.HV + j) * K * K);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l16 = lane & 15, grp = lane >> 4;
+    const int row0 = wave * 16 * RT;
+    // offset of this workgroup's columns of state (b, s)
+    auto soff = [&](int s) { return (((int64_t)b * d.S + s) * d.HV + j) * K * V + col0; };
+    // h_1 = F_0
+    {
+        const float *f0 = fin + soff(0);
+        for (int i = t; i < K * CW; i += 256) ht[0][(i % CW) * HP + i / CW] = f0[(int64_t)(i / CW) * V + i % CW];
+    }
+    // M_s's rows of this wave as A fragments (slot e of lane (l16, grp) in
+    // block kb: column 32 kb + 8 grp + e), F_s's tiles in the accumulator layout
+    f32x8 mn[RT][KB];
+    f32x4 fn[RT][2];
+    auto fetch = [&](int s) {
+        const float *ms = maps + (((int64_t)b * d.S + s) * d.HV + j) * K * K;
+        const float *fs = fin + soff(s);
 #pragma unroll
-        for (int u = 0; u < NM; ++u)
-            if (t + 256 * u < nm4) mr[u] = ms[t + 256 * u];
-    };
-    if (d.S > 2) fetch_m(1);
-    for (int s = 1; s < d.S; ++s) {
-        const int64_t slot = (int64_t)b * d.S + s;
-        __syncthreads();   // h_s is in place (the load above, or step s - 1)
-        float *hd = starts + (slot * d.HV + j) * K * V + col0;
-        for (int i = t; i < K * CW; i += blockDim.x) hd[(i / CW) * V + i % CW] = h[(i / CW) * CP + i % CW];
-        if (s + 1 == d.S) break;   // the last segment's start is the last one needed
+        for (int rt = 0; rt < RT; ++rt) {
+            const float *pr = ms + (int64_t)(row0 + 16 * rt + l16) * K + 8 * grp;
 #pragma unroll
-        for (int u = 0; u < NM; ++u) {
-            const int i = 4 * (t + 256 * u);
-            if (i < K * K) *(f32x4 *)&m[(i / K) * MP + i % K] = mr[u];
-        }
-        __syncthreads();   // M_s is in place
-        if (s + 2 < d.S) fetch_m(s + 1);
-        float acc[4][4];
-        if (t < nb) {
-            const float *fs = fin + (slot * d.HV + j) * K * V + col0;
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[a][c] = fs[(r0 + a) * V + c0 + c];
-#pragma unroll 4
-            for (int kk = 0; kk < K; ++kk) {
-                float mv[4];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) mv[a] = m[(r0 + a) * MP + kk];
-                const f32x4 hv = *(const f32x4 *)&h[kk * CP + c0];
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[a][c] += mv[a] * hv[c];
+            for (int kb = 0; kb < KB; ++kb) {
+                const f32x4 lo = *(const f32x4 *)(pr + 32 * kb), hi = *(const f32x4 *)(pr + 32 * kb + 4);
+                mn[rt][kb] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
-        }
-        __syncthreads();   // every thread is done reading h and m
-        if (t < nb) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-                *(f32x4 *)&h[(r0 + a) * CP + c0] = f32x4{acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fn[rt][ct][e] = fs[(int64_t)(row0 + 16 * rt + 4 * grp + e) * V + 16 * ct + l16];
         }
+    };
+    if (d.S > 2) fetch(1);
+    __syncthreads();   // h_1 is in place
+    int buf = 0;
+    for (int s = 1; s < d.S; ++s) {
+        const float *hs = ht[buf];
+        float *hd = starts + soff(s);
+        for (int i = t; i < K * CW; i += 256) hd[(int64_t)(i / CW) * V + i % CW] = hs[(i % CW) * HP + i / CW];
+        if (s + 1 == d.S) break;   // the last segment's start is the last one needed
+        f32x8 mc[RT][KB];
+        f32x4 acc[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) mc[rt][kb] = mn[rt][kb];
+            acc[rt][0] = fn[rt][0];
+            acc[rt][1] = fn[rt][1];
+        }
+        if (s + 2 < d.S) fetch(s + 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            f32x8 bf[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const float *pc = hs + (16 * ct + l16) * HP + 32 * kb + 8 * grp;
+                const f32x4 lo = *(const f32x4 *)pc, hi = *(const f32x4 *)(pc + 4);
+                bf[ct] = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mma(mc[rt][kb], bf[ct], acc[rt][ct]);
+        }
+        float *hn = ht[buf ^ 1];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) *(f32x4 *)&hn[(16 * ct + l16) * HP + row0 + 16 * rt + 4 * grp] = acc[rt][ct];
+        __syncthreads();   // h_{s+1} is in place; h_s is no longer read
+        buf ^= 1;
     }
 }
 
@@ -271,7 +296,8 @@ hipError_t launch_split(const Params &p, int dtype, const SplitPlan &pl, void *w
     // 3. the segments' starting states into the start pool
     if (prof) prof->begin(kSplitCombineKernel, stream);
     const unsigned ncomb = (unsigned)(p.B * p.HV * (p.V / kCombineCols));
-    split_combine_kernel<<<ncomb, 256, 0, stream>>>(d, fin, maps, pool);
+    if (p.K == 64) split_combine_kernel<64><<<ncomb, 256, 0, stream>>>(d, fin, maps, pool);
+    else split_combine_kernel<128><<<ncomb, 256, 0, stream>>>(d, fin, maps, pool);
     err = hipGetLastError();
     if (prof) prof->end(kSplitCombineKernel, stream);
     if (err != hipSuccess) return err;

@@ -41,9 +41,8 @@ CASES = {
     "k128_v64": scaled(WORKLOADS["gva"], "split_v64", B=1, T=3000, H=2, HV=4, K=128, V=64),
     "slow_decay": scaled(WORKLOADS["long"], "split_long", T=4096, H=1, HV=2),
     # 64 workgroups unsplit -> 8 segments of 1152 tokens (the last 936), run
-    # as whole 128-column value heads: the correction of each segment spans
-    # two workgroups of 1024 tokens, the second one partly filled, one of its
-    # waves ragged and the others idle
+    # as whole 128-column value heads; the combine chains 32 value heads x 4
+    # column blocks through seven transfer maps
     "multi_block": scaled(WORKLOADS["gva"], "split_multi_block", B=1, T=9000, H=16, HV=32),
 }
 
