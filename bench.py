@@ -36,8 +36,8 @@ MEASURED_TRAFFIC = {
     # fused_ws_kernel (profiles/fused_ws_kernel_*_hbm_traffic.md, split_long_hbm_traffic.md):
     # wide FETCH 4,935,301.2 KiB x 2.000 + WRITE 4,259,883.3 KiB x 1.000; GVA 151,905.9 x 2 + 139,269.7;
     # varlen 627,222.2 x 2 + 630,167.3; long: the mean of its three fused launches per step
-    # (925,847.2 x 2 + 16,384.0, 394,411.5 x 2 + 16,384.0 and 1,237,193.6 x 2 + 1,064,967.3)
-    "0e4c255e7a701abe": {"wide": 14469366857, "gva": 453703779, "varlen": 1929767765, "long": 2120521795},
+    # (925,849.5 x 2 + 16,384.0, 394,402.8 x 2 + 16,384.0 and 1,214,907.2 x 2 + 1,064,966.7)
+    "0e4c255e7a701abe": {"wide": 14469366857, "gva": 453703779, "varlen": 1929767765, "long": 2105300835},
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,374.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB (counted under 1e133469e85525fe;
     # the headers changed since in declarations the decode kernel does not use, and its gfx950
