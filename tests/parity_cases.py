@@ -6,7 +6,9 @@ The standard workloads use fast gates (the memory of the state is a few tokens),
 a small initial state and nearly orthogonal unit keys, so several wrong
 algorithms (no delta term, a dropped initial state, an erase that skips the
 decay) change the outputs by less than the bf16 tolerance of the throughput
-configurations.  The two cases here are built so that they do not:
+configurations.  The two cases here (each with and without the L2 norm, as
+the kernel forms the gated Q K^T tiles in different waves for the two) are
+built so that they do not:
 
 * slow_recall: slow gates (a ~ N(-5, 1), A_log ~ U(0, ln 4), so |g| is of the
   order of 1e-2 and the state remembers hundreds of tokens), beta near 0.9
@@ -20,7 +22,9 @@ configurations.  The two cases here are built so that they do not:
 Bars are max-abs errors against the fp64 oracle, per case, about three times
 the largest error the bf16 kernel shows on the case and its larger variants
 (measured: slow_recall 1.6e-3 on o, 7.0e-3 on S; fast_overlap 1.7e-3 and
-3.5e-3).  ``test_parity_gate_power`` checks on the CPU that every mutant
+3.5e-3; without the norm, slow_recall_nonorm 1.3e-3 and 6.4e-3, and
+fast_overlap_nonorm 3.7e-3 and 5.5e-3, whose keys of squared length about 2
+give outputs of about twice the size).  ``test_parity_gate_power`` checks on the CPU that every mutant
 misses these bars by at least a factor of five on the same inputs.
 """
 import math
@@ -34,6 +38,12 @@ FAST = dict(a_mean=0.0, b_mean=2.2, b_std=0.25, qk_common=1.0, init="all", init_
 BASE = {
     "slow_recall": (scaled(WORKLOADS["gva"], "slow_recall", B=2, T=320, H=2, HV=4, **SLOW), 5e-3, 2e-2),
     "fast_overlap": (scaled(WORKLOADS["gva"], "fast_overlap", B=2, T=320, H=2, HV=4, **FAST), 5e-3, 1e-2),
+    # the same gates without the L2 norm (keys of length about 1, the
+    # stable form of the wide configuration)
+    "slow_recall_nonorm": (scaled(WORKLOADS["wide_stable"], "slow_recall_nonorm", B=2, T=320, H=2, HV=4, **SLOW),
+                           5e-3, 2e-2),
+    "fast_overlap_nonorm": (scaled(WORKLOADS["wide_stable"], "fast_overlap_nonorm", B=2, T=320, H=2, HV=4, **FAST),
+                            1.2e-2, 1.5e-2),
 }
 
 # the same inputs at the sizes of the kernel's other layouts (whole 128-column
@@ -46,6 +56,11 @@ VARIANTS = {
                                                   **FAST)),
     "slow_recall_packed": ("slow_recall", scaled(WORKLOADS["varlen"], "slow_recall_packed", H=16, HV=32,
                                                  lengths=(1, 64, 65, 127, 0, 200, 3, 129), **SLOW)),
+    "slow_recall_nonorm_heads": ("slow_recall_nonorm", scaled(WORKLOADS["wide_stable"], "slow_recall_nonorm_heads",
+                                                              B=2, T=200, H=8, HV=128, **SLOW)),
+    "fast_overlap_nonorm_heads": ("fast_overlap_nonorm", scaled(WORKLOADS["wide_stable"],
+                                                                "fast_overlap_nonorm_heads", B=2, T=200, H=8,
+                                                                HV=128, **FAST)),
 }
 
 

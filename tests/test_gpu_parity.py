@@ -94,11 +94,17 @@ SMALL = {
     "heads_varlen": scaled(WORKLOADS["varlen"], "heads_varlen", H=16, HV=32,
                            lengths=(1, 64, 65, 127, 0, 200, 3, 129)),
     "heads_k64": scaled(WORKLOADS["gva"], "heads_k64", B=4, T=100, H=16, HV=64, K=64, V=128),
+    # the same layout without the L2 norm (its P tiles are formed by chain waves)
+    "heads_nonorm": scaled(WORKLOADS["wide_stable"], "heads_nonorm", B=2, T=200, H=8, HV=128),
+    "heads_nonorm_k64": scaled(WORKLOADS["wide_stable"], "heads_nonorm_k64", B=4, T=100, H=16, HV=64, K=64,
+                               V=128, qk_std=64 ** -0.5),
+    "heads_nonorm_varlen": scaled(WORKLOADS["varlen"], "heads_nonorm_varlen", H=16, HV=32, use_l2norm=False,
+                                  qk_std=128 ** -0.5, lengths=(1, 64, 65, 127, 0, 200, 3, 129)),
 }
 
 
 # the 128-column layout exists for bf16 only (the fp32 check mode has one layout)
-BF16_ONLY = {"heads_ragged", "heads_varlen", "heads_k64"}
+BF16_ONLY = {"heads_ragged", "heads_varlen", "heads_k64", "heads_nonorm", "heads_nonorm_k64", "heads_nonorm_varlen"}
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])

@@ -32,7 +32,7 @@ def _control(name):
     if name not in _CACHE:
         w = BASE[name][0]
         x, q, k, v, g, beta, s0 = _inputs(w)
-        o, fin = py_recurrent(q, k, v, g, beta, x["scale"], True, s0)
+        o, fin = py_recurrent(q, k, v, g, beta, x["scale"], w.use_l2norm, s0)
         _CACHE[name] = (x, q, k, v, g, beta, s0, o, fin)
     return _CACHE[name]
 
@@ -41,18 +41,24 @@ def _control(name):
 def test_control_matches_oracle(name):
     x, q, k, v, g, beta, s0, o, fin = _control(name)
     o_ref, f_ref = oracle.recurrent(x["q"][:1], x["k"][:1], x["v"][:1], x["g"][:1], x["beta"][:1],
-                                    scale=x["scale"], use_l2norm=True, initial_state=x["initial_state"][:1])
+                                    scale=x["scale"], use_l2norm=x["use_l2norm"],
+                                    initial_state=x["initial_state"][:1])
     np.testing.assert_allclose(o, o_ref[0], rtol=0, atol=1e-12)
     np.testing.assert_allclose(fin, f_ref[0], rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("norm", [True, False], ids=["l2norm", "no_l2norm"])
 @pytest.mark.parametrize("mutant", MUTANTS)
-def test_mutant_misses_bf16_bars(mutant):
+def test_mutant_misses_bf16_bars(mutant, norm):
+    """Each family of cases (with and without the L2 norm, which the kernel
+    runs through different code) rejects every mutant on its own."""
     powers = {}
     for name, (w, bar_o, bar_s) in BASE.items():
+        if w.use_l2norm != norm:
+            continue
         x, q, k, v, g, beta, s0, o, fin = _control(name)
-        om, fm = py_recurrent(q, k, v, g, beta, x["scale"], True, s0, mutant)
+        om, fm = py_recurrent(q, k, v, g, beta, x["scale"], norm, s0, mutant)
         d_o, d_s = float(np.abs(om - o).max()), float(np.abs(fm - fin).max())
         powers[name] = max(d_o / bar_o, d_s / bar_s)
         print(f"{mutant} on {name}: max|do| {d_o:.3g} (bar {bar_o}), max|dS| {d_s:.3g} (bar {bar_s})")
-    assert max(powers.values()) >= MARGIN, f"{mutant}: largest miss {max(powers.values()):.2f}x the bar"
+    assert powers and max(powers.values()) >= MARGIN, f"{mutant}: largest miss {max(powers.values()):.2f}x the bar"
