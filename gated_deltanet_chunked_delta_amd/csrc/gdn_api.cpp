@@ -41,13 +41,18 @@ int check_shape(const gdn_shape *s) {
 }
 
 // Workspace for the sequence split of few, long, equal-length sequences
-// (gdn_split.hip); 0 when these sizes are not split.  The fused kernel itself
-// needs none.
+// (gdn_split.hip); 0 when these sizes are not split.
 gdn::SplitPlan split_of(const gdn_shape &s) {
     if (s.N != s.B) return gdn::SplitPlan{};
     return gdn::plan_split(s.B, s.T, s.H, s.HV, s.K, s.V, gdn::elem_bytes(s.dtype));
 }
-size_t workspace_of(const gdn_shape &s) { return split_of(s).bytes; }
+// Workspace for the longest-first order of a packed batch of 2..kSeqOrderMax
+// sequences (one int32 per sequence, 256-byte granules); 0 otherwise.
+size_t order_bytes(const gdn_shape &s) {
+    if (s.B != 1 || s.N < 2 || s.N > gdn::kSeqOrderMax) return 0;
+    return ((size_t)s.N * 4 + 255) & ~(size_t)255;
+}
+size_t workspace_of(const gdn_shape &s) { return s.N != s.B ? order_bytes(s) : split_of(s).bytes; }
 
 // Kernel timing hook (gdn_profile_enable / gdn_profile_read): HIP events
 // recorded on the caller's stream around each kernel of every forward pass.
@@ -179,6 +184,11 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
         if (split.active && (!workspace || workspace_bytes < split.bytes || ((uintptr_t)workspace & 255u) != 0))
             split.active = false;
     }
+    // A packed batch takes its sequences longest first where the caller gave
+    // the workspace for the order (4-byte aligned); otherwise in index order.
+    // Either way every sequence is computed the same, so the results are equal.
+    const size_t ob = varlen ? order_bytes(s) : 0;
+    const bool ordered = ob > 0 && workspace && workspace_bytes >= (size_t)s.N * 4 && ((uintptr_t)workspace & 3u) == 0;
 
     gdn::Params p{};
     p.q = q;
@@ -200,6 +210,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, const float *g, const
     p.N = s.N;
     p.scale = scale;
     p.use_l2norm = use_l2norm ? 1 : 0;
+    if (ordered) p.seq_order = (const int32_t *)workspace;
     if (pool && s.N > 0) {
         p.initial_state = pool->read_initial ? (const float *)pool->data : nullptr;
         p.final_state = (float *)pool->data;
@@ -372,8 +383,9 @@ int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const flo
                           void *out, float *final_state, const gdn_shape *shape, void *stream) {
     const int st = check_shape(shape);
     if (st != GDN_OK) return st;
-    // only the split of equal-length sequences uses scratch
-    const size_t need = cu_seqlens ? 0 : workspace_of(*shape);
+    // the split of equal-length sequences and the order of a packed batch
+    // use scratch
+    const size_t need = cu_seqlens ? order_bytes(*shape) : split_of(*shape).bytes;
     if (need > GDN_STATIC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
     void *scratch = nullptr;
     if (need > 0) {

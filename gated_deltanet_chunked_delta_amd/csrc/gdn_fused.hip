@@ -120,7 +120,8 @@ __global__ void __launch_bounds__(64 * NW) fused_kernel(Params p) {
     const int member = slot % per_group;
     const int group = (slot / per_group) * 8 + xcd;
     if (group >= p.N * p.H) return;
-    const int n = group / p.H, jk = group % p.H;
+    // sequence n (longest first when the batch is packed and ordered), key head jk
+    const int n = p.seq_order ? p.seq_order[group / p.H] : group / p.H, jk = group % p.H;
     const int j = jk * G + member / VS;
     const int vcol0 = (member % VS) * VW;
 
@@ -586,6 +587,38 @@ hipError_t launch_fused(const Params &p, int dtype, hipStream_t st) {
     return launch_fused_cfg<float, 128, 128, 2, 1>(p, st);
 }
 
+namespace {
+
+// The sequences of a packed batch longest first: order[r] is the sequence of
+// rank r by chunk count, descending, ties in index order (a strict total
+// order, so the ranks are a permutation).  The prefill kernels take their
+// sequences in this order, so that the workgroups of the longest sequences
+// start first and the short ones fill in behind them (greedy longest-first
+// list scheduling over the CUs) instead of a long sequence starting last.
+// One workgroup: the chunk counts in LDS (padded with -1, which ranks below
+// every count), each thread ranks one sequence against all of them, four
+// counts per read.
+__global__ void __launch_bounds__(1024) seq_order_kernel(const int32_t *__restrict__ cu, int N, int T,
+                                                         int32_t *__restrict__ order) {
+    __shared__ __attribute__((aligned(16))) int nc[kSeqOrderMax];
+    const int t = threadIdx.x, N4 = (N + 3) & ~3;
+    for (int n = t; n < N4; n += blockDim.x)
+        nc[n] = n < N ? (max(dev::cu_at(cu, n + 1, T) - dev::cu_at(cu, n, T), 0) + 63) / 64 : -1;
+    __syncthreads();
+    for (int n = t; n < N; n += blockDim.x) {
+        const int c = nc[n];
+        int r = 0;
+        for (int m = 0; m < N4; m += 4) {
+            const int4 d = *(const int4 *)&nc[m];
+            r += (d.x > c || (d.x == c && m < n)) + (d.y > c || (d.y == c && m + 1 < n)) +
+                 (d.z > c || (d.z == c && m + 2 < n)) + (d.w > c || (d.w == c && m + 3 < n));
+        }
+        order[r] = n;
+    }
+}
+
+}  // namespace
+
 const char *kernel_name(int kind) {
     switch (kind) {
         case kFusedKernel: return "fused_kernel";
@@ -601,11 +634,20 @@ const char *kernel_name(int kind) {
         case kBwdDhScanKernel: return "bwd_dh_scan_kernel";
         case kBwdGradsKernel: return "bwd_grads_kernel";
         case kBwdReduceKernel: return "bwd_reduce_kernel";
+        case kSeqOrderKernel: return "seq_order_kernel";
         default: return "?";
     }
 }
 
 hipError_t launch_forward(const Params &p, int dtype, hipStream_t stream, Profiler *prof) {
+    if (p.seq_order) {
+        if (p.N < 2 || p.N > kSeqOrderMax || !p.cu_seqlens) return hipErrorInvalidValue;
+        if (prof) prof->begin(kSeqOrderKernel, stream);
+        seq_order_kernel<<<1, 1024, 0, stream>>>(p.cu_seqlens, p.N, p.T, (int32_t *)p.seq_order);
+        const hipError_t e = hipGetLastError();
+        if (prof) prof->end(kSeqOrderKernel, stream);
+        if (e != hipSuccess) return e;
+    }
     const int kind = dtype == 0 ? kFusedWsKernel : kFusedKernel;
     if (prof) prof->begin(kind, stream);
     const hipError_t err = dtype == 0 ? launch_fused_ws(p, stream) : launch_fused(p, dtype, stream);

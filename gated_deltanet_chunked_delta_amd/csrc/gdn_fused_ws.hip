@@ -253,7 +253,8 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
     const int member = slot % per_group;
     const int group = (slot / per_group) * 8 + xcd;
     if (group >= p.N * p.H) return;
-    const int n = group / p.H, jk = group % p.H;
+    // sequence n (longest first when the batch is packed and ordered), key head jk
+    const int n = p.seq_order ? p.seq_order[group / p.H] : group / p.H, jk = group % p.H;
     const int j = jk * G + member / VS;
     const int vcol0 = (member % VS) * VW;
 

@@ -48,6 +48,9 @@ struct Params {
     // holds one [HV, K, V] state used by every sequence.
     int v_zero;
     int init_shared;
+    // Packed batches: when non-null, the sequences in the order the
+    // workgroups take them, longest first ([N]; see launch_seq_order).
+    const int32_t *seq_order;
 };
 
 // The kernels of one forward pass, for the timing hook.
@@ -56,12 +59,13 @@ struct Params {
 // recurrent_update_kernel: the decode step;
 // gating_kernel: the stand-alone gate computation.
 // split_setup_kernel, split_combine_kernel, split_final_kernel: the
-// sequence split of long sequences (gdn_split.hip).
+// sequence split of long sequences (gdn_split.hip);
+// seq_order_kernel: the longest-first order of a packed batch's sequences.
 // bwd_*_kernel: the backward pass (gdn_backward.hip).
 enum KernelKind { kFusedKernel = 0, kFusedWsKernel = 1, kRecurrentKernel = 2, kGatingKernel = 3,
                   kSplitSetupKernel = 4, kSplitCombineKernel = 5, kSplitFinalKernel = 6,
                   kBwdSetupKernel = 7, kBwdPrepKernel = 8, kBwdFwdScanKernel = 9, kBwdDhScanKernel = 10,
-                  kBwdGradsKernel = 11, kBwdReduceKernel = 12, kNumKernelKinds = 13 };
+                  kBwdGradsKernel = 11, kBwdReduceKernel = 12, kSeqOrderKernel = 13, kNumKernelKinds = 14 };
 const char *kernel_name(int kind);
 
 // Timing hook: when given, the launch sequence calls begin/end around each
@@ -73,7 +77,11 @@ struct Profiler {
 };
 
 // Enqueues the whole forward pass.  Returns the HIP error of the launches.
+// With p.seq_order set (a packed batch of 2..kSeqOrderMax sequences and N
+// int32 of workspace), a one-workgroup kernel first writes the longest-first
+// order of the sequences there.
 hipError_t launch_forward(const Params &p, int dtype, hipStream_t stream, Profiler *prof);
+constexpr int kSeqOrderMax = 1024;
 
 // Everything a decode-step launch needs.  Pointers are device pointers.
 struct DecodeParams {

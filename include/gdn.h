@@ -79,10 +79,18 @@ typedef struct gdn_shape {
     int32_t dtype;
 } gdn_shape;
 
-/* Bytes of device workspace that let gdn_chunk_fwd (and gdn_chunk_fwd_gated)
- * split long sequences for `shape`; depends only on the sizes and the dtype.
- * 0 means the sizes are not split and no workspace is used; invalid shapes
- * also give 0, and gdn_chunk_fwd reports why.
+/* Bytes of device workspace that let gdn_chunk_fwd (and gdn_chunk_fwd_gated,
+ * gdn_chunk_fwd_pool) split long sequences or order a packed batch for
+ * `shape`; depends only on the sizes and the dtype.  0 means no workspace is
+ * used; invalid shapes also give 0, and gdn_chunk_fwd reports why.
+ *
+ * The order: a packed batch (cu_seqlens, B = 1) of 2 to 1024 sequences asks
+ * for one int32 per sequence (rounded up to 256 bytes).  A one-workgroup
+ * kernel ranks the sequences by chunk count, longest first, and the prefill
+ * kernel's workgroups take the sequences in that order, so that a long
+ * sequence never starts last and sets the tail of the launch (greedy
+ * longest-first list scheduling over the CUs).  Results are identical with or
+ * without it: only which workgroup computes which sequence changes.
  *
  * The split: a batch of few equal-length sequences (B * HV * V/64 <= 64
  * workgroups, T >= 2048) is too narrow to fill the GPU, so each sequence is
@@ -115,9 +123,10 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape *shape);
  *                 must not overlap any other argument.
  *   shape         sizes, see gdn_shape (host pointer)
  *   workspace     device scratch of gdn_chunk_fwd_workspace_bytes bytes
- *                 (256-byte aligned), or NULL: long sequences are split only
- *                 when it is given and large enough, and otherwise run unsplit
- *                 (never an error); contents on entry are ignored
+ *                 (256-byte aligned), or NULL: long sequences are split, and
+ *                 a packed batch ordered, only when it is given and large
+ *                 enough, and otherwise run unsplit or in index order (never
+ *                 an error); contents on entry are ignored
  *   stream        hipStream_t to enqueue on (NULL = the default stream)
  *
  * `out` must not overlap any input.  Sequences of length 0 produce no rows and
@@ -147,17 +156,18 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v,
  * routine it calls allocates.  Every split the library plans fits in
  * GDN_STATIC_SCRATCH_BYTES (at most about 50 MiB: the workspace grows with
  * the heads and segments, not with T); a split that did not would be refused
- * with GDN_ERR_SCRATCH before anything is enqueued.  Sizes that are not split
- * use no scratch.
+ * with GDN_ERR_SCRATCH before anything is enqueued.  A packed batch of 2 to
+ * 1024 sequences keeps its longest-first order there (4 bytes per sequence);
+ * other sizes use no scratch.
  *
  * The first call for a device looks up that device's address of the array
  * (hipGetSymbolAddress, with the device of `stream` made current for the
  * lookup); later calls reuse it.  The array keeps whatever the last call left
  * in it; every call writes each part of it before reading it, so nothing
- * needs clearing.  All calls on one GPU share the one array: two split calls
- * that can run at the same time on one GPU (on different streams, or on
- * unordered streams of different host threads) race and give wrong results;
- * enqueue them on one stream.
+ * needs clearing.  All calls on one GPU share the one array: two calls that
+ * use it (a split, or an ordered packed batch) and can run at the same time on
+ * one GPU (on different streams, or on unordered streams of different host
+ * threads) race and give wrong results; enqueue them on one stream.
  * Returns the statuses of gdn_chunk_fwd and GDN_ERR_SCRATCH. */
 int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
                           const float *g, const float *beta,

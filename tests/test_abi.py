@@ -64,7 +64,14 @@ def test_workspace_size_and_bad_shapes():
     states = 4 * 8 * 32 * 128 * (2 * 128 + 128) + 4 * 32 * 128 * 128
     assert states <= b3 < states + (1 << 20) and b4 >= b3 and b5 == b3
     assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 1024, 16, 32, 128, 128, 1, 0)) == 0   # short
-    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 1, 16, 32, 128, 128, 4, 0)) == 0      # varlen
+    # a packed batch: one int32 per sequence for the longest-first order, in
+    # 256-byte granules, for 2..1024 sequences; none for one or for more
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 1, 16, 32, 128, 128, 4, 0)) == 256
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 5000, 16, 32, 128, 128, 64, 0)) == 256
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 5000, 16, 32, 128, 128, 65, 0)) == 512
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 5000, 2, 4, 64, 64, 1024, 1)) == 4096
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 5000, 2, 4, 64, 64, 1025, 0)) == 0
+    assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(1, 5000, 2, 4, 64, 64, 0, 0)) == 0
     assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 16, 32, 96, 128, 4, 0)) == 0
     assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 3, 32, 128, 128, 4, 0)) == 0
     assert gdn.gdn_chunk_fwd_workspace_bytes(gdn.make_shape(4, 4096, 16, 32, 128, 128, 4, 7)) == 0

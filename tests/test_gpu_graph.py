@@ -83,7 +83,9 @@ def test_graph_prefill(name):
     B, T, H, K = d["q"].shape
     shape = gdn.make_shape(B, T, H, w.HV, K, w.V, x["N"], gdn.GDN_BF16)
     need = gdn.gdn_chunk_fwd_workspace_bytes(shape)
-    assert (need > 0) == (name == "split_long")
+    # the split runs its five kernels in the workspace; a packed batch keeps the
+    # longest-first order of its sequences there (one kernel before the prefill)
+    assert (need > 0) == (name in ("split_long", "varlen_mix"))
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
     _say(f"[graph] prefill {name}: workspace {need} bytes")
 

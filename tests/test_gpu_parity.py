@@ -154,6 +154,36 @@ def test_deterministic_bitwise():
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
+@pytest.mark.parametrize("name,dtype", [("heads_varlen", torch.bfloat16), ("varlen_mix", torch.bfloat16),
+                                        ("varlen_mix", torch.float32)])
+def test_packed_order_is_bitwise_neutral(name, dtype):
+    """A packed batch given the workspace takes its sequences longest first;
+    without it, in index order.  Only the assignment of sequences to
+    workgroups differs, so outputs and final states are bitwise equal."""
+    gdn = _gdn()
+    dev = torch.device("cuda:0")
+    x = oracle.add_gates(make_inputs(SMALL[name], seed=5, io_dtype=torch.float32))
+    q, k, v = (x[n].to(dev, dtype) for n in ("q", "k", "v"))
+    g, beta, cu = x["g"].to(dev), x["beta"].to(dev), x["cu_seqlens"].to(dev)
+    s0 = None if x["initial_state"] is None else x["initial_state"].to(dev)
+    _, T, H, K = q.shape
+    HV, V, N = v.shape[2], v.shape[3], x["N"]
+    shape = gdn.make_shape(1, T, H, HV, K, V, N, gdn.GDN_BF16 if dtype == torch.bfloat16 else gdn.GDN_F32)
+    need = gdn.gdn_chunk_fwd_workspace_bytes(shape)
+    assert need == ((4 * N + 255) // 256) * 256
+    res = []
+    for ws in (torch.empty(need, dtype=torch.uint8, device=dev), None):
+        o = torch.full((1, T, HV, V), float("nan"), dtype=dtype, device=dev)
+        f = torch.full((N, HV, K, V), float("nan"), device=dev)
+        st = gdn.gdn_chunk_fwd(q, k, v, g, beta, x["scale"], x["use_l2norm"], s0, cu, o, f, shape, ws)
+        torch.cuda.synchronize()
+        assert st == 0, gdn.gdn_status_str(st)
+        res.append((o, f))
+    (o1, f1), (o2, f2) = res
+    _say(f"[order] {name} {dtype}: N={N} lens={x['lens']}")
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
 def test_varlen_sequences_are_isolated():
     """NaN in one packed sequence stays inside that sequence."""
     x = oracle.add_gates(make_inputs(SMALL["varlen_mix"], seed=4, io_dtype=torch.float32))
