@@ -33,7 +33,8 @@
 // and the L2 norm's backward dx = f (dxh - xh (xh . dxh)), f = 1/sqrt(|x|^2 + 1e-6).
 // The state gradient runs backwards over chunks just as the state runs
 // forwards, so the pass is five launches (six with packed sequences, whose
-// chunk offsets bwd_setup_kernel computes first):
+// chunk offsets, and for 2..kSeqOrderMax sequences the longest-first order the
+// two scans take them in, bwd_setup_kernel computes first):
 //   bwd_prep_kernel      per (chunk, value head): gamma, Tm, A / beta and Pm
 //   bwd_fwd_scan_kernel  per (sequence, value head, 64 value columns; 32 for
 //                        fp32 rows), forward over chunks: the chunk-start
@@ -406,10 +407,14 @@ __device__ __forceinline__ void tm_block_row(const float *A, float *Tm, float *y
 }
 
 // ---------------------------------------------------------------------------
-// chunk offsets of packed sequences: co[n] = sum_{m < n} ceil(len_m / 64)
+// chunk offsets of packed sequences: co[n] = sum_{m < n} ceil(len_m / 64);
+// with ord, also the sequences longest first (by chunk count, ties in index
+// order: ord[rank] = n), which the two scans take their sequences in, so that
+// a long sequence's serial scan never starts last (N <= kSeqOrderMax)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void bwd_setup_kernel(const int32_t *cu, int N, int32_t *co) {
+__global__ __launch_bounds__(kThreads) void bwd_setup_kernel(const int32_t *cu, int N, int32_t *co, int32_t *ord) {
     __shared__ int part[kThreads];
+    __shared__ int ncs[kSeqOrderMax];
     const int per = (N + kThreads - 1) / kThreads;
     const int a = min(N, (int)threadIdx.x * per), b = min(N, a + per);
     int s = 0;
@@ -430,6 +435,16 @@ __global__ __launch_bounds__(kThreads) void bwd_setup_kernel(const int32_t *cu, 
     for (int n = a; n < b; ++n) {
         co[n] = run;
         run += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    }
+    if (ord) {
+        for (int n = threadIdx.x; n < N; n += kThreads) ncs[n] = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+        __syncthreads();
+        for (int n = threadIdx.x; n < N; n += kThreads) {
+            const int c = ncs[n];
+            int r = 0;
+            for (int m = 0; m < N; ++m) r += ncs[m] > c || (ncs[m] == c && m < n);
+            ord[r] = n;
+        }
     }
 }
 
@@ -608,7 +623,8 @@ __global__ __launch_bounds__(NTH) void bwd_fwd_scan_kernel(BwdParams p) {
     E *kr = (E *)(sFk + kChunk);             // [64][KS] raw k rows
 
     const int HV = p.HV, V = p.V;
-    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int seq_rank = blockIdx.x / HV, j = blockIdx.x - seq_rank * HV, jk = j / (HV / p.H);
+    const int n = p.seq_order ? p.seq_order[seq_rank] : seq_rank;   // longest first for packed batches
     const int c0 = blockIdx.y * VW;
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
@@ -758,7 +774,8 @@ __global__ __launch_bounds__(512) void bwd_fwd_scan_b16_kernel(BwdParams p) {
     float *sFk = sF + kChunk;                // [64] exp(gamma_L - gamma) / |k|, 0 past L
 
     const int HV = p.HV, V = p.V;
-    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int seq_rank = blockIdx.x / HV, j = blockIdx.x - seq_rank * HV, jk = j / (HV / p.H);
+    const int n = p.seq_order ? p.seq_order[seq_rank] : seq_rank;   // longest first for packed batches
     const int c0 = blockIdx.y * VW;
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
@@ -943,7 +960,8 @@ __global__ __launch_bounds__(NTH) void bwd_dh_scan_kernel(BwdParams p) {
     E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
 
     const int HV = p.HV, V = p.V;
-    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int seq_rank = blockIdx.x / HV, j = blockIdx.x - seq_rank * HV, jk = j / (HV / p.H);
+    const int n = p.seq_order ? p.seq_order[seq_rank] : seq_rank;   // longest first for packed batches
     const int c0 = blockIdx.y * VW;
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
@@ -1097,7 +1115,8 @@ __global__ __launch_bounds__(512) void bwd_fwd_scan_sk_kernel(BwdParams p) {
     E *kr = (E *)(sFk + kChunk);             // [64][KS] raw k rows
 
     const int HV = p.HV, V = p.V;
-    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int seq_rank = blockIdx.x / HV, j = blockIdx.x - seq_rank * HV, jk = j / (HV / p.H);
+    const int n = p.seq_order ? p.seq_order[seq_rank] : seq_rank;   // longest first for packed batches
     const int c0 = blockIdx.y * VW;
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
@@ -1241,7 +1260,8 @@ __global__ __launch_bounds__(512) void bwd_dh_scan_sk_kernel(BwdParams p) {
     E *qr = kr + kChunk * KS;                // [64][KS] raw q rows
 
     const int HV = p.HV, V = p.V;
-    const int n = blockIdx.x / HV, j = blockIdx.x - n * HV, jk = j / (HV / p.H);
+    const int seq_rank = blockIdx.x / HV, j = blockIdx.x - seq_rank * HV, jk = j / (HV / p.H);
+    const int n = p.seq_order ? p.seq_order[seq_rank] : seq_rank;   // longest first for packed batches
     const int c0 = blockIdx.y * VW;
     int bos, len, cid0;
     seq_of(p, n, bos, len, cid0);
@@ -1841,7 +1861,7 @@ hipError_t launch_kv(const BwdParams &p, int nc_max, hipStream_t st, Profiler *p
     const dim3 blk(kThreads);
     if (p.cu_seqlens && p.N > 0) {
         if (prof) prof->begin(kBwdSetupKernel, st);
-        hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), blk, 0, st, p.cu_seqlens, p.N, p.chunk_offsets);
+        hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), blk, 0, st, p.cu_seqlens, p.N, p.chunk_offsets, p.seq_order);
         if (prof) prof->end(kBwdSetupKernel, st);
     }
     if (nc_max > 0) {
@@ -1946,6 +1966,10 @@ BwdPlan plan_backward(int B, int T, int H, int HV, int K, int V, int N, bool var
     pl.off_db = take(sizeof(float) * (size_t)t_tot * HV * V);
     pl.off_dqp = take(sizeof(float) * (size_t)t_tot * HV * K);
     pl.off_dkp = take(sizeof(float) * (size_t)t_tot * HV * K);
+    if (varlen && N >= 2 && N <= kSeqOrderMax) {
+        pl.ordered = true;
+        pl.off_ord = take(sizeof(int32_t) * (size_t)N);
+    }
     pl.bytes = off;
     return pl;
 }
@@ -1964,6 +1988,7 @@ hipError_t launch_backward(BwdParams p, int dtype, const BwdPlan &plan, void *ws
     p.db = (float *)(w + plan.off_db);
     p.dqp = (float *)(w + plan.off_dqp);
     p.dkp = (float *)(w + plan.off_dkp);
+    p.seq_order = plan.ordered && p.cu_seqlens ? (int32_t *)(w + plan.off_ord) : nullptr;
     p.T_tot = p.B * p.T;
     const int nc = p.T_tot > 0 ? plan.nc_max : 0;
     return dtype == 0 ? launch_dtype<bf16>(p, nc, stream, prof) : launch_dtype<float>(p, nc, stream, prof);

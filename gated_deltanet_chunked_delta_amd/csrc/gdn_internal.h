@@ -155,6 +155,7 @@ struct BwdParams {
     float *hs, *dhs;                 // [chunks, HV, K, V]: state at chunk start, its gradient at chunk end
     float *vn, *db;                  // [T_tot, HV, V]: delta-rule errors and their B-gradient
     float *dqp, *dkp;                // [T_tot, HV, K]: dq, dk per value head
+    int32_t *seq_order;              // [N] packed sequences longest first, or null (index order)
     // sizes
     int B, T, H, HV, K, V, N, T_tot;
     float scale;
@@ -165,6 +166,8 @@ struct BwdPlan {
     int nc_max = 0;                   // chunk slots (an upper bound on the chunks of packed sequences)
     size_t off_co = 0, off_gam = 0, off_tm = 0, off_ag = 0, off_pm = 0, off_hs = 0, off_dhs = 0, off_vn = 0,
            off_db = 0, off_dqp = 0, off_dkp = 0, bytes = 0;
+    bool ordered = false;             // packed batch of 2..kSeqOrderMax sequences: an order at off_ord
+    size_t off_ord = 0;
 };
 BwdPlan plan_backward(int B, int T, int H, int HV, int K, int V, int N, bool varlen);
 hipError_t launch_backward(BwdParams p, int dtype, const BwdPlan &plan, void *ws, hipStream_t stream,

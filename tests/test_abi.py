@@ -352,11 +352,12 @@ def test_backward_workspace_size():
     chunks = B * T // 64
     want = 256 + 4 * (chunks * HV * (2 * K * V + 3 * tri) + B * T * HV * (2 * V + 2 * K + 1))
     assert want <= got <= want + 11 * 256
-    # B == 1: slots for packed sequences, ceil(T/64) + N chunks
+    # B == 1: slots for packed sequences, ceil(T/64) + N chunks, and the
+    # longest-first order of the N sequences (N int32)
     g1 = gdn.gdn_chunk_bwd_workspace_bytes(gdn.make_shape(1, 1000, 2, 4, 64, 64, 7, gdn.GDN_F32))
     slots = (1000 + 63) // 64 + 7
-    want1 = 4 * (slots * 4 * (2 * 64 * 64 + 3 * tri) + 1000 * 4 * (2 * 64 + 2 * 64 + 1))
-    assert want1 <= g1 <= want1 + 12 * 256
+    want1 = 4 * (slots * 4 * (2 * 64 * 64 + 3 * tri) + 1000 * 4 * (2 * 64 + 2 * 64 + 1) + 7)
+    assert want1 <= g1 <= want1 + 13 * 256
     assert gdn.gdn_chunk_bwd_workspace_bytes(gdn.make_shape(1, 64, 2, 4, 96, 64, 1, 0)) == 0   # K unsupported
 
 
