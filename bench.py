@@ -43,18 +43,15 @@ MEASURED_TRAFFIC = {
     # the headers changed since in declarations the decode kernel does not use, and its gfx950
     # assembly is identical)
     "9fdef1b5c68d6bbc": {"decode": 1049900032, "decode_bf16pool": 529568973},
-    # backward (GVA, varlen, wide): every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md;
-    # counted under 1f063335502e3701, whose gfx950 assembly the current sources reproduce: the headers
-    # changed since only in declarations the backward kernels do not use)
-    "46743e94fcaa76e1": {"gva:bwd_prep_kernel": 420007139, "gva:bwd_fwd_scan_kernel": 1199710867,
-                         "gva:bwd_dh_scan_kernel": 1426222516, "gva:bwd_grads_kernel": 3361609985,
-                         "gva:bwd_reduce_kernel": 671098175,
-                         "varlen:bwd_setup_kernel": 4255, "varlen:bwd_prep_kernel": 2589378806,
-                         "varlen:bwd_fwd_scan_kernel": 5722404894, "varlen:bwd_dh_scan_kernel": 7541948725,
-                         "varlen:bwd_grads_kernel": 12763814137, "varlen:bwd_reduce_kernel": 2555244606,
-                         "wide:bwd_prep_kernel": 21515561159, "wide:bwd_fwd_scan_kernel": 46526746840,
-                         "wide:bwd_dh_scan_kernel": 60462659822, "wide:bwd_grads_kernel": 109053861860,
-                         "wide:bwd_reduce_kernel": 21474318352},
+    # backward (GVA, varlen, wide): every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md)
+    "4d0f866784339036": {"gva:bwd_prep_kernel": 420070202, "gva:bwd_fwd_scan_kernel": 1199725144,
+                         "gva:bwd_dh_scan_kernel": 1426231011, "gva:bwd_grads_kernel": 3359121488,
+                         "gva:bwd_reduce_kernel": 671081344, "varlen:bwd_setup_kernel": 6047,
+                         "varlen:bwd_prep_kernel": 2589382046, "varlen:bwd_fwd_scan_kernel": 5722425038,
+                         "varlen:bwd_dh_scan_kernel": 7540025768, "varlen:bwd_grads_kernel": 12755039888,
+                         "varlen:bwd_reduce_kernel": 2555238216, "wide:bwd_prep_kernel": 21515179463,
+                         "wide:bwd_fwd_scan_kernel": 46239522806, "wide:bwd_dh_scan_kernel": 60475926204,
+                         "wide:bwd_grads_kernel": 108938610336, "wide:bwd_reduce_kernel": 21474298897},
 }
 # Counter-based utilisation of the prefill kernel (profiles/fused_ws_kernel_wide_gva_sq_counters.md),
 # keyed like MEASURED_TRAFFIC: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles, LDS busy and
