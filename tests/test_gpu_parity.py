@@ -184,6 +184,42 @@ def test_packed_order_is_bitwise_neutral(name, dtype):
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
+def _many(n_seqs):
+    """A packed batch of n_seqs short sequences (lengths 0..24, so that many
+    share a chunk count and the order's ties are exercised)."""
+    rng = np.random.default_rng(n_seqs)
+    lens = tuple(int(x) for x in rng.integers(0, 25, n_seqs))
+    return scaled(WORKLOADS["varlen"], f"many_{n_seqs}", H=2, HV=4, K=64, V=64, lengths=lens)
+
+
+@pytest.mark.parametrize("n_seqs", [1024, 1025])
+def test_packed_order_many_sequences(n_seqs):
+    """The order at its largest batch (1024 sequences, ranked in one
+    workgroup) and just past it (1025: index order): parity with the oracle,
+    and bitwise equal with and without the workspace."""
+    gdn = _gdn()
+    dev = torch.device("cuda:0")
+    x = oracle.add_gates(make_inputs(_many(n_seqs), seed=7, io_dtype=torch.float32))
+    check_full(x, torch.bfloat16)
+    q, k, v = (x[n].to(dev, torch.bfloat16) for n in ("q", "k", "v"))
+    g, beta, cu = x["g"].to(dev), x["beta"].to(dev), x["cu_seqlens"].to(dev)
+    s0 = None if x["initial_state"] is None else x["initial_state"].to(dev)
+    _, T, H, K = q.shape
+    HV, V, N = v.shape[2], v.shape[3], x["N"]
+    shape = gdn.make_shape(1, T, H, HV, K, V, N, gdn.GDN_BF16)
+    need = gdn.gdn_chunk_fwd_workspace_bytes(shape)
+    assert need == (4096 if n_seqs == 1024 else 0)
+    res = []
+    for ws in (torch.empty(max(need, 1), dtype=torch.uint8, device=dev), None):
+        o = torch.full((1, T, HV, V), float("nan"), dtype=torch.bfloat16, device=dev)
+        f = torch.full((N, HV, K, V), float("nan"), device=dev)
+        st = gdn.gdn_chunk_fwd(q, k, v, g, beta, x["scale"], x["use_l2norm"], s0, cu, o, f, shape, ws)
+        torch.cuda.synchronize()
+        assert st == 0, gdn.gdn_status_str(st)
+        res.append((o, f))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 def test_varlen_sequences_are_isolated():
     """NaN in one packed sequence stays inside that sequence."""
     x = oracle.add_gates(make_inputs(SMALL["varlen_mix"], seed=4, io_dtype=torch.float32))
