@@ -37,12 +37,14 @@ MEASURED_TRAFFIC = {
     # wide FETCH 5,324,399.2 KiB x 2.000 + WRITE 4,259,881.0 KiB x 1.000; GVA 152,346.8 x 2 + 139,269.3;
     # varlen 627,202.1 x 2 + 630,163.7; long: the mean of its three fused launches per step
     # (925,848.7 x 2 + 16,384.0, 394,399.5 x 2 + 16,384.0 and the output pass's median)
-    "c9265d2507b9cc79": {"wide": 15266227673, "gva": 454603856, "varlen": 1929721501, "long": 2134182626},
+    # (counted under c9265d2507b9cc79; the headers changed since only in the backward's
+    # declarations, and the prefill kernels' gfx950 assembly is identical)
+    "9c7ae1cef2d36690": {"wide": 15266227673, "gva": 454603856, "varlen": 1929721501, "long": 2134182626},
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,374.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB (counted under 1e133469e85525fe;
     # the headers changed since in declarations the decode kernel does not use, and its gfx950
     # assembly is identical)
-    "9fdef1b5c68d6bbc": {"decode": 1049900032, "decode_bf16pool": 529568973},
+    "7353cb8091568e35": {"decode": 1049900032, "decode_bf16pool": 529568973},
     # backward (GVA, varlen, wide): every kernel's FETCH x 2.000 + WRITE (profiles/backward_gva_hbm_traffic.md)
     "4d0f866784339036": {"gva:bwd_prep_kernel": 420070202, "gva:bwd_fwd_scan_kernel": 1199725144,
                          "gva:bwd_dh_scan_kernel": 1426231011, "gva:bwd_grads_kernel": 3359121488,
@@ -57,7 +59,7 @@ MEASURED_TRAFFIC = {
 # keyed like MEASURED_TRAFFIC: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles, LDS busy and
 # LDS bank-conflict stalls from SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT over cycles.
 MEASURED_COUNTERS = {
-    "c9265d2507b9cc79": {"wide": {"mfma_busy": 0.437, "lds_busy": 0.657, "lds_bank_conflict": 0.120},
+    "9c7ae1cef2d36690": {"wide": {"mfma_busy": 0.437, "lds_busy": 0.657, "lds_bank_conflict": 0.120},
                          "gva": {"mfma_busy": 0.318, "lds_busy": 0.490, "lds_bank_conflict": 0.076}},
 }
 KERNEL_SOURCES = {
