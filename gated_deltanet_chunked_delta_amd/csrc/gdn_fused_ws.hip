@@ -492,7 +492,12 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
             wave_lds_sync();   // A_WW is read back across lanes by the solve
         }
 
-        // ---- phase 2: the other products, with the solve in between
+        // ---- phase 2: the other products, with the solve in between.  The
+        // solve's 15 dependent steps are the prep's critical path; the chain
+        // waves (priority 3) take the SIMD's issue slots first, so the K-side
+        // prep raises its priority to 2 for this phase (wide and long 1-2 %
+        // faster than at 0)
+        if constexpr (DO_K) __builtin_amdgcn_s_setprio(2);
         f32x4 gd[4], go[2], gq[2][4], gqq[2];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -559,6 +564,7 @@ __global__ void __launch_bounds__(768) fused_ws_kernel(Params p) {
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
         }
+        if constexpr (DO_K) __builtin_amdgcn_s_setprio(0);
         // log2 of the norm factors of the other k rows this wave needs
         if constexpr (NORM) {
             if (on_diag) {
