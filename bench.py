@@ -34,12 +34,10 @@ METRIC = "chunk GDN prefill tokens/s on 1 MI355X; % of bf16 MFMA / HBM roofline"
 # measured again.
 MEASURED_TRAFFIC = {
     # fused_ws_kernel (profiles/fused_ws_kernel_*_hbm_traffic.md, split_long_hbm_traffic.md):
-    # wide FETCH 5,324,399.2 KiB x 2.000 + WRITE 4,259,881.0 KiB x 1.000; GVA 152,346.8 x 2 + 139,269.3;
-    # varlen 627,202.1 x 2 + 630,163.7; long: the mean of its three fused launches per step
-    # (925,848.7 x 2 + 16,384.0, 394,399.5 x 2 + 16,384.0 and the output pass's median)
-    # (counted under c9265d2507b9cc79; the headers changed since only in the backward's
-    # declarations, and the prefill kernels' gfx950 assembly is identical)
-    "9c7ae1cef2d36690": {"wide": 15266227673, "gva": 454603856, "varlen": 1929721501, "long": 2134182626},
+    # wide FETCH 4,929,002.3 KiB x 2.000 + WRITE 4,259,873.5 KiB x 1.000; GVA 151,794.4 x 2 + 139,269.4;
+    # varlen 627,216.9 x 2 + 630,164.0; long: the mean of its three fused launches per step
+    # (925,869.2 x 2 + 16,384.0, 394,391.0 x 2 + 16,384.0 and the output pass's median)
+    "4727c299a14c8c66": {"wide": 14456456905, "gva": 453471854, "varlen": 1929757539, "long": 2130635945},
     # recurrent_update_kernel: decode (fp32 pool) FETCH 257,459.5 x 2 + WRITE 510,374.0 KiB;
     # decode_bf16pool FETCH 130,489.5 x 2 + WRITE 256,178.2 KiB (counted under 1e133469e85525fe;
     # the headers changed since in declarations the decode kernel does not use, and its gfx950
@@ -59,8 +57,8 @@ MEASURED_TRAFFIC = {
 # keyed like MEASURED_TRAFFIC: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles, LDS busy and
 # LDS bank-conflict stalls from SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT over cycles.
 MEASURED_COUNTERS = {
-    "9c7ae1cef2d36690": {"wide": {"mfma_busy": 0.437, "lds_busy": 0.657, "lds_bank_conflict": 0.120},
-                         "gva": {"mfma_busy": 0.318, "lds_busy": 0.490, "lds_bank_conflict": 0.076}},
+    "4727c299a14c8c66": {"wide": {"mfma_busy": 0.450, "lds_busy": 0.677, "lds_bank_conflict": 0.124},
+                         "gva": {"mfma_busy": 0.314, "lds_busy": 0.483, "lds_bank_conflict": 0.075}},
 }
 KERNEL_SOURCES = {
     "prefill": ["gated_deltanet_chunked_delta_amd/csrc/gdn_fused_ws.hip"],
